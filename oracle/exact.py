@@ -1,0 +1,227 @@
+"""ORACLE -- test infrastructure only.
+
+Only tests/, the smoke check and the bench's CPU-baseline leg may import this
+module.  It shares no code with the HIP path.
+
+Exact references for every intermediate of the sliced double-double product
+(the method of "Multiple Double Arithmetic on NVIDIA Tensor Cores"):
+
+* balancing exponents and 13-bit slicing (§2 "quartering" and its worked
+  example; §3 balancing, Problems 3.3 and 3.4),
+* the level sums of slice-pair products (§2, eqs. (1)-(4)),
+* the level-ordered renormalisation of the level sums into (hi, lo) (§2, the
+  fifth step: sum the parts of each product entry in double-double arithmetic),
+* the exact rational value of a double-double inner product.
+
+Readings of points the pages leave open (each one is listed in the design doc):
+
+* A double-double x = hi + lo is cut as a 104-bit fixed-point window below a
+  balancing exponent E with |hi + lo| < 2^E: N = floor(|hi + lo| * 2^(104-E)),
+  digit s = bits [13(7-s), 13(7-s)+13) of N, slice s = sign * digit * 2^(-13(s+1)).
+  Eight slices sit at relative exponents 0, -13, ..., -91 (the pages' quarters at
+  0, -13, -26, -39 for hi, continued for lo).  Truncation toward zero, as the
+  pages' bit fields are.
+* E for a row of A (column of B) is the largest frexp exponent of RN(hi + lo)
+  over its nonzero entries, 0 when all are zero.
+* Level l collects the pairs s + t = l for l = 0..7 (36 pairs); pairs below the
+  double-double window (s + t >= 8) are not formed.
+* The cascade starts from the smallest level: (h, t) = (S_7, 0); for l = 6..0:
+  (s, e) = TwoSum(h, S_l), t = t + e, (h, t) = TwoSum(s, t); then both words are
+  scaled by 2^(E_i + F_j).
+
+Parity status: pinned (the pages' worked example, reconstruction identities,
+brute force on tiny inputs, closed forms; see tests/test_oracle_pins.py).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+WINDOW_BITS = 104
+DIGIT_BITS = 13
+N_SLICES = 8
+N_LEVELS = 8
+DIGIT_MASK = (1 << DIGIT_BITS) - 1
+
+# ---------------------------------------------------------------------------
+# exact conversions
+# ---------------------------------------------------------------------------
+_SCALE_BITS = 1074  # every finite double is an integer multiple of 2^-1074
+
+
+def double_to_scaled_int(x: float) -> int:
+    """Return X with x == X * 2^-1074 exactly (x finite)."""
+    p, q = float(x).as_integer_ratio()
+    return p << (_SCALE_BITS - (q.bit_length() - 1))
+
+
+def dd_to_fraction(hi: float, lo: float) -> Fraction:
+    return Fraction(float(hi)) + Fraction(float(lo))
+
+
+# ---------------------------------------------------------------------------
+# balancing exponents
+# ---------------------------------------------------------------------------
+def entry_exponent(hi: float, lo: float) -> int | None:
+    """frexp exponent of RN(hi + lo) (smallest e with |RN(hi+lo)| < 2^e); None for zero."""
+    s = float(hi) + float(lo)
+    if s == 0.0:
+        return None
+    return math.frexp(s)[1]
+
+
+def balancing_exponents(hi: np.ndarray, lo: np.ndarray | None, axis: int) -> np.ndarray:
+    """One exponent per row (axis=0, the A operand) or per column (axis=1, the B operand)."""
+    hi = np.asarray(hi, dtype=np.float64)
+    lo = np.zeros_like(hi) if lo is None else np.asarray(lo, dtype=np.float64)
+    s = hi + lo
+    _, ex = np.frexp(s)
+    ex = np.where(s != 0.0, ex, np.iinfo(np.int64).min).astype(np.int64)
+    red = ex.max(axis=1 if axis == 0 else 0) if ex.size else np.zeros(
+        hi.shape[0] if axis == 0 else hi.shape[1], dtype=np.int64)
+    return np.where(red == np.iinfo(np.int64).min, 0, red).astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# slicing
+# ---------------------------------------------------------------------------
+def window_integer(hi: float, lo: float, E: int) -> tuple[int, int]:
+    """(sign, N) with N = floor(|hi + lo| * 2^(104 - E)), sign in {-1, 0, 1}."""
+    H = double_to_scaled_int(hi)
+    L = double_to_scaled_int(lo)
+    V = H + L  # (hi + lo) * 2^1074, exact
+    sign = (V > 0) - (V < 0)
+    shift = WINDOW_BITS - E - _SCALE_BITS  # N = floor(|V| * 2^shift)
+    a = abs(V)
+    N = a << shift if shift >= 0 else a >> (-shift)
+    return sign, N
+
+
+def slice_entry(hi: float, lo: float, E: int) -> list[int]:
+    """Signed 13-bit digits d_0..d_7 of one entry; slice s = d_s * 2^(E - 13(s+1))."""
+    sign, N = window_integer(hi, lo, E)
+    if N >= 1 << WINDOW_BITS:
+        raise ValueError("balancing exponent too small for this entry")
+    return [sign * ((N >> (DIGIT_BITS * (N_SLICES - 1 - s))) & DIGIT_MASK)
+            for s in range(N_SLICES)]
+
+
+def slice_rows(hi, lo, rows=None):
+    """Slice the A operand (per-row exponents).
+
+    Returns (E, D) with E[r] for the selected rows and D[s, r, k] the signed
+    digits (int64), r indexing ``rows`` (all rows when None).
+    """
+    hi = np.asarray(hi, dtype=np.float64)
+    lo = np.zeros_like(hi) if lo is None else np.asarray(lo, dtype=np.float64)
+    rows = range(hi.shape[0]) if rows is None else list(rows)
+    E = balancing_exponents(hi[rows, :], lo[rows, :], axis=0)
+    D = np.zeros((N_SLICES, len(rows), hi.shape[1]), dtype=np.int64)
+    for r, i in enumerate(rows):
+        for p in range(hi.shape[1]):
+            D[:, r, p] = slice_entry(hi[i, p], lo[i, p], int(E[r]))
+    return E, D
+
+
+def slice_cols(hi, lo, cols=None):
+    """Slice the B operand (per-column exponents); D[t, k, c] for the selected columns."""
+    hi = np.asarray(hi, dtype=np.float64)
+    lo = np.zeros_like(hi) if lo is None else np.asarray(lo, dtype=np.float64)
+    F, Dt = slice_rows(hi.T, lo.T, cols)
+    return F, np.ascontiguousarray(Dt.transpose(0, 2, 1))
+
+
+def slice_values(D: np.ndarray, E) -> np.ndarray:
+    """Unit-scaled slice values d_s * 2^(-13(s+1)) (the scale 2^E is kept apart)."""
+    scale = np.array([2.0 ** (-DIGIT_BITS * (s + 1)) for s in range(N_SLICES)])
+    return D.astype(np.float64) * scale.reshape((N_SLICES,) + (1,) * (D.ndim - 1))
+
+
+def reconstruct_entry(digits, E: int) -> Fraction:
+    """sum_s d_s * 2^(E - 13(s+1)) as an exact rational."""
+    return sum((Fraction(int(d)) * Fraction(2) ** (E - DIGIT_BITS * (s + 1))
+                for s, d in enumerate(digits)), Fraction(0))
+
+
+# ---------------------------------------------------------------------------
+# level sums
+# ---------------------------------------------------------------------------
+def level_sums_units(DA: np.ndarray, DB: np.ndarray) -> np.ndarray:
+    """S[l] = sum_{s+t=l} DA[s] @ DB[t] in integer units, l = 0..7.
+
+    DA[s] is m×k, DB[t] is k×n (int64 digits).  Level l has weight
+    2^(E_i + F_j - 13(l+2)).  Every term fits in int64 for k < 2^21.
+    """
+    m, k = DA.shape[1], DA.shape[2]
+    n = DB.shape[2]
+    S = np.zeros((N_LEVELS, m, n), dtype=np.int64)
+    for l in range(N_LEVELS):
+        for s in range(l + 1):
+            S[l] += DA[s] @ DB[l - s]
+    return S
+
+
+def level_values(S_units: np.ndarray) -> np.ndarray:
+    """Level sums as unit-scaled doubles, S_l = S_units[l] * 2^(-13(l+2)) (exact when < 2^53)."""
+    if np.abs(S_units).max(initial=0) >= 2 ** 53:
+        raise ValueError("level sum exceeds 53 bits")
+    out = S_units.astype(np.float64)
+    for l in range(N_LEVELS):
+        out[l] *= 2.0 ** (-DIGIT_BITS * (l + 2))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# renormalisation cascade
+# ---------------------------------------------------------------------------
+def two_sum(a, b):
+    """Knuth's TwoSum, elementwise: s = RN(a + b), e = a + b - s exactly."""
+    s = a + b
+    bv = s - a
+    av = s - bv
+    e = (a - av) + (b - bv)
+    return s, e
+
+
+def renorm_levels(S: np.ndarray, E, F):
+    """Cascade the 8 unit-scaled level planes S[l] (m×n) into (C_hi, C_lo).
+
+    E (length m) and F (length n) are the balancing exponents of A's rows and
+    B's columns.  Smallest level first, as described in the module docstring.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    h = S[N_LEVELS - 1].copy()
+    t = np.zeros_like(h)
+    for l in range(N_LEVELS - 2, -1, -1):
+        s, e = two_sum(h, S[l])
+        t = t + e
+        h, t = two_sum(s, t)
+    sc = np.asarray(E, dtype=np.int64).reshape(-1, 1) + np.asarray(F, dtype=np.int64).reshape(1, -1)
+    return np.ldexp(h, sc), np.ldexp(t, sc)
+
+
+def level_target(S_units: np.ndarray, E: int, F: int, i: int, j: int) -> Fraction:
+    """Exact value sum_l S_units[l][i,j] * 2^(E + F - 13(l+2)) of one output entry."""
+    return sum((Fraction(int(S_units[l, i, j])) * Fraction(2) ** (E + F - DIGIT_BITS * (l + 2))
+                for l in range(N_LEVELS)), Fraction(0))
+
+
+# ---------------------------------------------------------------------------
+# exact double-double inner products
+# ---------------------------------------------------------------------------
+def exact_dot(a_hi, a_lo, b_hi, b_lo) -> Fraction:
+    """sum_k (a_hi[k] + a_lo[k]) * (b_hi[k] + b_lo[k]) exactly."""
+    tot = 0
+    for ah, al, bh, bl in zip(a_hi, a_lo, b_hi, b_lo):
+        tot += (double_to_scaled_int(ah) + double_to_scaled_int(al)) * \
+               (double_to_scaled_int(bh) + double_to_scaled_int(bl))
+    return Fraction(tot, 1 << (2 * _SCALE_BITS))
+
+
+def exact_entries(A_hi, A_lo, B_hi, B_lo, rows, cols) -> list[Fraction]:
+    """Exact C[rows[q], cols[q]] for every q (A_lo / B_lo may be None)."""
+    A_lo = np.zeros_like(A_hi) if A_lo is None else A_lo
+    B_lo = np.zeros_like(B_hi) if B_lo is None else B_lo
+    return [exact_dot(A_hi[i, :], A_lo[i, :], B_hi[:, j], B_lo[:, j]) for i, j in zip(rows, cols)]
