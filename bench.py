@@ -1,0 +1,200 @@
+"""Benchmark: effective double-double GFLOP/s (2mnk/t) of C = A·B on one MI355X.
+
+One step is one pass of the whole product over resident inputs, issued through
+the library's stage entry points in exactly the order dd_gemm_ws issues them:
+slice A (row exponents), slice B (column exponents), fused sliced GEMM +
+renormalisation epilogue.  HIP events on the same stream bracket each stage, so
+the dominant kernel's launch duration is measured live inside the timed region.
+
+Prints ONE JSON line.  Default workload: the 4096^3 product with per-entry
+exponents in [-20, 20].
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective double-double GFLOP/s (2mnk/t) at 4096³; % of sliced FP64-MFMA roof"
+PEAK_FP64_MFMA_TFLOPS = 78.6   # MI355X dense FP64 matrix peak (AMD datasheet)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PAIRS = 36                     # slice pairs with s + t <= 7
+# The pages' own full-path time for a 4096^3 double-double product (build the
+# sliced operands, tensor-core product, assemble; unstated NVIDIA GPU): 7.93621 s
+# ("Multiple Double Arithmetic on NVIDIA Tensor Cores", §4.2, Table 1, t_TC).
+PAGES_TTC_4096_S = 7.93621
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dd4096_exp20")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def _traffic_from_profile(workload: str):
+    """HBM bytes per GEMM launch from the committed counter summary, if it was
+    taken on the current kernel source; None otherwise."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"sliced_gemm_renorm_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            key, val = line.split(":", 1)
+            vals[key.strip()] = val.strip()
+    src = os.path.join(ROOT, "extended_precision_gemm_amd", "csrc", "sliced_gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if vals.get("kernel_source_sha256_16") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              "the product shards by output tiles with no exchange, but multi-GPU runs are not part of it.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import extended_precision_gemm_amd as ddg
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = workloads.by_name(args.workload)
+    m, n, k = w.m, w.n, w.k
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.name} (m={m} n={n} k={k})", file=sys.stderr, flush=True)
+    Ah, Al, Bh, Bl = workloads.make_operands(w)
+    A_hi, A_lo, B_hi, B_lo = (torch.from_numpy(x).to(dev) for x in (Ah, Al, Bh, Bl))
+    C_hi = torch.empty((m, n), dtype=torch.float64, device=dev)
+    C_lo = torch.empty((m, n), dtype=torch.float64, device=dev)
+    E = torch.empty(m, dtype=torch.int32, device=dev)
+    F = torch.empty(n, dtype=torch.int32, device=dev)
+    As = torch.empty(ddg.slices_bytes(m, k) // 8, dtype=torch.float64, device=dev)
+    Bs = torch.empty(ddg.slices_bytes(n, k) // 8, dtype=torch.float64, device=dev)
+
+    if args.calib_copy_mib > 0:
+        x = torch.ones(args.calib_copy_mib * (1 << 20) // 8, dtype=torch.float64, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(events=None):
+        if events:
+            events[0].record(stream)
+        ddg.split_balanced(A_hi, A_lo, 0, E, As, stream)
+        ddg.split_balanced(B_hi, B_lo, 1, F, Bs, stream)
+        if events:
+            events[1].record(stream)
+        ddg.sliced_gemm_renorm(m, n, k, As, E, Bs, F, C_hi, C_lo, stream)
+        if events:
+            events[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = 2.0 * m * n * k / (elapsed / args.steps) / 1e9
+    sliced_roof_gflops = PEAK_FP64_MFMA_TFLOPS * 1e3 / PAIRS
+    gemm_tflops = PAIRS * 2.0 * m * n * k / (gemm_ms * 1e-3) / 1e12
+    traffic = _traffic_from_profile(w.name)
+    split_bytes = 80.0 * (m * k + k * n)   # 16 B read + 64 B of slices written per entry
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (2.0 * 4096 ** 3 / PAGES_TTC_4096_S / 1e9), 3) if (m, n, k) == (4096,) * 3 else None,
+        "vs_baseline_ref": "pages' t_TC = 7.93621 s at n = 4096 (17.32 GFLOP/s, unstated NVIDIA GPU, random inputs)",
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "m": m, "n": n, "k": k, "description": w.description,
+                   "slices": 8, "slice_bits": 13, "pairs": PAIRS},
+        "pct_sliced_roof": round(100.0 * value / sliced_roof_gflops, 2),
+        "roofline": {
+            "kernel": "sliced_gemm_kernel (fused renormalisation epilogue)",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 3),
+            "peak": PEAK_FP64_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP64_MFMA_TFLOPS, 4),
+            "traffic": traffic,
+            "flops_per_launch": PAIRS * 2.0 * m * n * k,
+            "launch_ms": round(gemm_ms, 4),
+        },
+        "stages": {
+            "split_ms": round(split_ms, 4),
+            "split_GBps": round(split_bytes / (split_ms * 1e-3) / 1e9, 1),
+            "split_frac_hbm": round(split_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gemm_ms": round(gemm_ms, 4),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import compare, native
+        threads = native.max_threads()
+        print(f"[bench] cpu baseline: oracle on {threads} threads", file=sys.stderr, flush=True)
+        # calibrate on one row, then take as many leading rows as fit the budget
+        t = time.perf_counter()
+        native.dd_gemm(Ah[:1], Al[:1], Bh, Bl)
+        per_row = max(time.perf_counter() - t, 1e-4)
+        rows = int(max(1, min(m, args.cpu_seconds / per_row)))
+        t = time.perf_counter()
+        Rh, Rl, used = native.dd_gemm(Ah[:rows], Al[:rows], Bh, Bl)
+        t_cpu = time.perf_counter() - t
+        cpu_gflops = 2.0 * rows * n * k / t_cpu / 1e9
+        gh, gl = C_hi[:rows].cpu().numpy(), C_lo[:rows].cpu().numpy()
+        ratio = compare.error_ratio(gh, gl, Rh, Rl, compare.abs_product(Ah[:rows], Bh))
+        rec["cpu_baseline"] = {
+            "value": round(cpu_gflops, 3), "unit": "GFLOP/s", "cores": used, "kind": "oracle",
+            "sample": f"first {rows} rows of C ({rows}x{n}x{k}, classical dd GEMM, {t_cpu:.1f} s)",
+        }
+        rec["parity_sample"] = {"rows": rows, "max_err_over_absAB": ratio, "tol": compare.TOL,
+                                "ok": bool(ratio <= compare.TOL)}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,221 @@
+"""Double-double matrix product C = A·B on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding of ``libddgemm.so`` (C ABI in ``include/ddgemm.h``).  It
+only marshals arguments: every step of the product runs in the library's HIP
+kernels; PyTorch supplies device memory and the current stream.  Importing
+this module fails loudly when the library has not been built.
+
+The method ("Multiple Double Arithmetic on NVIDIA Tensor Cores", §2-§3): each
+double-double entry is cut into eight 13-bit slices below a per-row (A) or
+per-column (B) balancing exponent, the 36 slice pairs inside the double-double
+window are multiplied exactly on FP64 matrix cores and summed per level, and
+the eight level sums of every output entry are renormalised into (hi, lo) once.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import layout  # noqa: F401  (host-side description of the packed slice layout)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libddgemm.so")
+
+NUM_SLICES = 8
+NUM_LEVELS = 8
+SLICE_BITS = 13
+K_MAX = 8388608
+
+SUCCESS = 0
+ERROR_INVALID_VALUE = 1
+ERROR_WORKSPACE = 2
+ERROR_LAUNCH = 3
+ERROR_DEVICE = 4
+
+
+class DDGemmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_st = ctypes.c_int
+
+# name -> (restype, argtypes); mirrors include/ddgemm.h
+_SIGNATURES = {
+    "dd_split_slices_bytes": (_sz, [_i64, _i64]),
+    "dd_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "dd_split_balanced": (_st, [_i64, _i64, _vp, _vp, _i64, ctypes.c_int, _vp, _vp, _vp]),
+    "dd_sliced_gemm": (_st, [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
+    "dd_renorm_levels": (_st, [_i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "dd_sliced_gemm_renorm": (_st, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "dd_gemm": (_st, [_i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp]),
+    "dd_gemm_ws": (_st, [_i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp]),
+    "ddgemm_status_string": (ctypes.c_char_p, [_st]),
+    "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.ddgemm_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != SUCCESS:
+        raise DDGemmError(status, status_string(status))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _matrix(t, name, shape=None):
+    """Validate a float64 row-major device matrix; return its leading dimension."""
+    if t.dtype != torch.float64:
+        raise TypeError(f"{name} must be float64, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return max(t.stride(0), cols, 1) if rows > 1 else max(cols, 1)
+
+
+def _check_lo(lo, hi, name):
+    if lo is None:
+        return
+    _matrix(lo, name, hi.shape)
+    if lo.stride() != hi.stride():
+        raise ValueError(f"{name} must have the same strides as its hi plane")
+
+
+def slices_bytes(outer: int, k: int) -> int:
+    return lib.dd_split_slices_bytes(outer, k)
+
+
+def workspace_size(m: int, n: int, k: int) -> int:
+    return lib.dd_gemm_workspace_size(m, n, k)
+
+
+def split_balanced(X_hi, X_lo, axis: int, exps=None, slices=None, stream=None):
+    """Balancing exponents and packed slices of one operand (axis 0: A, axis 1: B)."""
+    ldx = _matrix(X_hi, "X_hi")
+    _check_lo(X_lo, X_hi, "X_lo")
+    rows, cols = X_hi.shape
+    outer = rows if axis == 0 else cols
+    k = cols if axis == 0 else rows
+    dev = X_hi.device
+    if exps is None:
+        exps = torch.empty(outer, dtype=torch.int32, device=dev)
+    if slices is None:
+        slices = torch.empty(slices_bytes(outer, k) // 8, dtype=torch.float64, device=dev)
+    _check(lib.dd_split_balanced(rows, cols, _ptr(X_hi), _ptr(X_lo), ldx, axis, _ptr(exps), _ptr(slices),
+                                 _stream(stream)))
+    return exps, slices
+
+
+def sliced_gemm(m: int, n: int, k: int, A_slices, B_slices, levels=None, stream=None):
+    """The eight exact level sums, returned as a (8, m, n) float64 tensor."""
+    if levels is None:
+        levels = torch.empty((NUM_LEVELS, m, n), dtype=torch.float64, device=A_slices.device)
+    ldl = max(n, 1)
+    if tuple(levels.shape) != (NUM_LEVELS, m, n) or not levels.is_contiguous():
+        raise ValueError("levels must be a contiguous (8, m, n) tensor")
+    _check(lib.dd_sliced_gemm(m, n, k, _ptr(A_slices), _ptr(B_slices), _ptr(levels), ldl, _stream(stream)))
+    return levels
+
+
+def renorm_levels(levels, E, F, C_hi=None, C_lo=None, stream=None):
+    _, m, n = levels.shape
+    if not levels.is_contiguous():
+        raise ValueError("levels must be contiguous")
+    C_hi = torch.empty((m, n), dtype=torch.float64, device=levels.device) if C_hi is None else C_hi
+    C_lo = torch.empty((m, n), dtype=torch.float64, device=levels.device) if C_lo is None else C_lo
+    ldc = _matrix(C_hi, "C_hi", (m, n))
+    _check_lo(C_lo, C_hi, "C_lo")
+    _check(lib.dd_renorm_levels(m, n, _ptr(levels), max(n, 1), _ptr(E), _ptr(F), _ptr(C_hi), _ptr(C_lo), ldc,
+                                _stream(stream)))
+    return C_hi, C_lo
+
+
+def sliced_gemm_renorm(m, n, k, A_slices, E, B_slices, F, C_hi=None, C_lo=None, stream=None):
+    dev = A_slices.device
+    C_hi = torch.empty((m, n), dtype=torch.float64, device=dev) if C_hi is None else C_hi
+    C_lo = torch.empty((m, n), dtype=torch.float64, device=dev) if C_lo is None else C_lo
+    ldc = _matrix(C_hi, "C_hi", (m, n))
+    _check_lo(C_lo, C_hi, "C_lo")
+    _check(lib.dd_sliced_gemm_renorm(m, n, k, _ptr(A_slices), _ptr(E), _ptr(B_slices), _ptr(F),
+                                     _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
+    return C_hi, C_lo
+
+
+def _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo):
+    lda = _matrix(A_hi, "A_hi")
+    _check_lo(A_lo, A_hi, "A_lo")
+    ldb = _matrix(B_hi, "B_hi")
+    _check_lo(B_lo, B_hi, "B_lo")
+    m, k = A_hi.shape
+    k2, n = B_hi.shape
+    if k != k2:
+        raise ValueError(f"inner dimensions differ: {k} vs {k2}")
+    dev = A_hi.device
+    C_hi = torch.empty((m, n), dtype=torch.float64, device=dev) if C_hi is None else C_hi
+    C_lo = torch.empty((m, n), dtype=torch.float64, device=dev) if C_lo is None else C_lo
+    ldc = _matrix(C_hi, "C_hi", (m, n))
+    _check_lo(C_lo, C_hi, "C_lo")
+    return m, n, k, lda, ldb, ldc, C_hi, C_lo
+
+
+def dd_gemm(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, workspace=None, stream=None):
+    """C = A·B; returns (C_hi, C_lo).  The workspace comes from PyTorch's allocator
+    unless a uint8 device tensor of at least workspace_size(m, n, k) bytes is given."""
+    m, n, k, lda, ldb, ldc, C_hi, C_lo = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
+    need = workspace_size(m, n, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=A_hi.device)
+    _check(lib.dd_gemm_ws(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
+                          _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(), _stream(stream)))
+    return C_hi, C_lo
+
+
+def dd_gemm_alloc(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, stream=None):
+    """C = A·B through the entry point that allocates its own (stream-ordered) workspace."""
+    m, n, k, lda, ldb, ldc, C_hi, C_lo = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
+    _check(lib.dd_gemm(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
+                       _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
+    return C_hi, C_lo
+
+
+def probe_mfma_f64(device="cuda", stream=None):
+    out = torch.empty((64, 4), dtype=torch.float64, device=device)
+    _check(lib.ddgemm_probe_mfma_f64(_ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,211 @@
+// Host side of the C ABI declared in include/ddgemm.h: argument validation,
+// device check, workspace layout and stream-ordered launches.  Every argument
+// error is detected before any HIP call, so it is reported even on a machine
+// without a GPU.
+#include <atomic>
+#include <cstring>
+
+#include "common.hpp"
+
+using namespace ddg;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Elements spanned by a rows×cols matrix with row stride ld (0 when empty).
+inline int64_t extent(int64_t rows, int64_t cols, int64_t ld) {
+    return (rows == 0 || cols == 0) ? 0 : (rows - 1) * ld + cols;
+}
+
+inline bool overlaps(const void* a, int64_t a_elems, const void* b, int64_t b_elems) {
+    if (!a || !b || a_elems == 0 || b_elems == 0) return false;
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + b_elems * 8 && pb < pa + a_elems * 8;
+}
+
+inline bool ld_ok(int64_t ld, int64_t cols) { return ld >= (cols > 1 ? cols : 1); }
+
+// Sizes beyond this would overflow the 64-bit byte counts below.
+inline bool size_ok(int64_t a, int64_t b) {
+    return a >= 0 && b >= 0 && (a == 0 || b <= (int64_t(1) << 58) / (a > 0 ? a : 1));
+}
+
+std::atomic<int> g_device_state[256];  // 0 unknown, 1 gfx950, 2 unsupported
+
+ddgemm_status_t check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DDGEMM_ERROR_DEVICE;
+    if (dev >= 256) return DDGEMM_ERROR_DEVICE;
+    int st = g_device_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DDGEMM_ERROR_DEVICE;
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? DDGEMM_SUCCESS : DDGEMM_ERROR_DEVICE;
+}
+
+inline ddgemm_status_t launched(hipError_t e) { return e == hipSuccess ? DDGEMM_SUCCESS : DDGEMM_ERROR_LAUNCH; }
+
+ddgemm_status_t validate_split(int64_t rows, int64_t cols, const double* X_hi, int64_t ldx, int axis,
+                               const int32_t* exps, const double* slices) {
+    if (!size_ok(rows, cols) || !ld_ok(ldx, cols) || (axis != 0 && axis != 1)) return DDGEMM_ERROR_INVALID_VALUE;
+    const int64_t outer = axis == 0 ? rows : cols;
+    const int64_t k = axis == 0 ? cols : rows;
+    if (k > DDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
+    if (rows * cols > 0 && !X_hi) return DDGEMM_ERROR_INVALID_VALUE;
+    if (outer > 0 && !exps) return DDGEMM_ERROR_INVALID_VALUE;
+    if (dd_split_slices_bytes(outer, k) > 0 && !slices) return DDGEMM_ERROR_INVALID_VALUE;
+    return DDGEMM_SUCCESS;
+}
+
+ddgemm_status_t validate_gemm_dims(int64_t m, int64_t n, int64_t k) {
+    if (!size_ok(m, k) || !size_ok(k, n) || !size_ok(m, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (k > DDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
+    return DDGEMM_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dd_split_slices_bytes(int64_t outer, int64_t k) {
+    if (!size_ok(outer, k)) return 0;
+    return static_cast<size_t>(PackGeom(outer, k).doubles()) * sizeof(double);
+}
+
+size_t dd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
+    if (validate_gemm_dims(m, n, k) != DDGEMM_SUCCESS) return 0;
+    return align_up(dd_split_slices_bytes(m, k)) + align_up(dd_split_slices_bytes(n, k)) +
+           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4);
+}
+
+ddgemm_status_t dd_split_balanced(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
+                                  int64_t ldx, int axis, int32_t* exps, double* slices, void* stream) {
+    ddgemm_status_t st = validate_split(rows, cols, X_hi, ldx, axis, exps, slices);
+    if (st != DDGEMM_SUCCESS) return st;
+    if ((axis == 0 ? rows : cols) == 0) return DDGEMM_SUCCESS;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+    return launched(launch_split(rows, cols, X_hi, X_lo, ldx, axis, exps, slices,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+ddgemm_status_t dd_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices,
+                               const double* B_slices, double* levels, int64_t ldl, void* stream) {
+    ddgemm_status_t st = validate_gemm_dims(m, n, k);
+    if (st != DDGEMM_SUCCESS || !ld_ok(ldl, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
+    if (!levels || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!size_ok(m * ldl, DDGEMM_NUM_LEVELS)) return DDGEMM_ERROR_INVALID_VALUE;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+    return launched(launch_sliced_gemm(m, n, k, A_slices, B_slices, levels, ldl, nullptr, nullptr,
+                                       nullptr, nullptr, 0, false, static_cast<hipStream_t>(stream)));
+}
+
+ddgemm_status_t dd_renorm_levels(int64_t m, int64_t n, const double* levels, int64_t ldl,
+                                 const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
+                                 int64_t ldc, void* stream) {
+    if (!size_ok(m, n) || !ld_ok(ldl, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
+    if (!levels || !E || !F || !C_hi || !C_lo) return DDGEMM_ERROR_INVALID_VALUE;
+    const int64_t ce = extent(m, n, ldc);
+    if (overlaps(C_hi, ce, C_lo, ce) || overlaps(C_hi, ce, levels, 8 * m * ldl) ||
+        overlaps(C_lo, ce, levels, 8 * m * ldl))
+        return DDGEMM_ERROR_INVALID_VALUE;
+    ddgemm_status_t st = check_device();
+    if (st != DDGEMM_SUCCESS) return st;
+    return launched(launch_renorm(m, n, levels, ldl, E, F, C_hi, C_lo, ldc, static_cast<hipStream_t>(stream)));
+}
+
+ddgemm_status_t dd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k, const double* A_slices,
+                                      const int32_t* E, const double* B_slices, const int32_t* F,
+                                      double* C_hi, double* C_lo, int64_t ldc, void* stream) {
+    ddgemm_status_t st = validate_gemm_dims(m, n, k);
+    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
+    if (!E || !F || !C_hi || !C_lo || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
+    const int64_t ce = extent(m, n, ldc);
+    if (overlaps(C_hi, ce, C_lo, ce)) return DDGEMM_ERROR_INVALID_VALUE;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+    return launched(launch_sliced_gemm(m, n, k, A_slices, B_slices, nullptr, 0, E, F, C_hi, C_lo, ldc,
+                                       true, static_cast<hipStream_t>(stream)));
+}
+
+ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* A_hi, const double* A_lo,
+                           int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb,
+                           double* C_hi, double* C_lo, int64_t ldc, void* workspace, size_t ws_bytes,
+                           void* stream) {
+    ddgemm_status_t st = validate_gemm_dims(m, n, k);
+    if (st != DDGEMM_SUCCESS) return st;
+    if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
+    if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return DDGEMM_ERROR_INVALID_VALUE;
+    const int64_t ae = extent(m, k, lda), be = extent(k, n, ldb), ce = extent(m, n, ldc);
+    for (const double* C : {static_cast<const double*>(C_hi), static_cast<const double*>(C_lo)})
+        if (overlaps(C, ce, A_hi, ae) || overlaps(C, ce, A_lo, ae) || overlaps(C, ce, B_hi, be) ||
+            overlaps(C, ce, B_lo, be))
+            return DDGEMM_ERROR_INVALID_VALUE;
+    if (overlaps(C_hi, ce, C_lo, ce)) return DDGEMM_ERROR_INVALID_VALUE;
+    const size_t need = dd_gemm_workspace_size(m, n, k);
+    if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return DDGEMM_ERROR_WORKSPACE;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+
+    char* w = static_cast<char*>(workspace);
+    double* A_sl = reinterpret_cast<double*>(w);
+    w += align_up(dd_split_slices_bytes(m, k));
+    double* B_sl = reinterpret_cast<double*>(w);
+    w += align_up(dd_split_slices_bytes(n, k));
+    int32_t* E = reinterpret_cast<int32_t*>(w);
+    w += align_up(static_cast<size_t>(m) * 4);
+    int32_t* F = reinterpret_cast<int32_t*>(w);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_split(m, k, A_hi, A_lo, lda, 0, E, A_sl, s);
+    if (e == hipSuccess) e = launch_split(k, n, B_hi, B_lo, ldb, 1, F, B_sl, s);
+    if (e == hipSuccess) e = launch_sliced_gemm(m, n, k, A_sl, B_sl, nullptr, 0, E, F, C_hi, C_lo, ldc, true, s);
+    return launched(e);
+}
+
+ddgemm_status_t dd_gemm(int64_t m, int64_t n, int64_t k, const double* A_hi, const double* A_lo,
+                        int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb, double* C_hi,
+                        double* C_lo, int64_t ldc, void* stream) {
+    ddgemm_status_t st = validate_gemm_dims(m, n, k);
+    if (st != DDGEMM_SUCCESS) return st;
+    if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
+    if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return DDGEMM_ERROR_INVALID_VALUE;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t need = dd_gemm_workspace_size(m, n, k);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, need, s) != hipSuccess || !ws) return DDGEMM_ERROR_WORKSPACE;
+    st = dd_gemm_ws(m, n, k, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc, ws, need, stream);
+    if (hipFreeAsync(ws, s) != hipSuccess && st == DDGEMM_SUCCESS) st = DDGEMM_ERROR_LAUNCH;
+    return st;
+}
+
+const char* ddgemm_status_string(ddgemm_status_t status) {
+    switch (status) {
+        case DDGEMM_SUCCESS: return "DDGEMM_SUCCESS";
+        case DDGEMM_ERROR_INVALID_VALUE: return "DDGEMM_ERROR_INVALID_VALUE: invalid argument";
+        case DDGEMM_ERROR_WORKSPACE: return "DDGEMM_ERROR_WORKSPACE: workspace missing, too small or misaligned";
+        case DDGEMM_ERROR_LAUNCH: return "DDGEMM_ERROR_LAUNCH: a HIP launch or runtime call failed";
+        case DDGEMM_ERROR_DEVICE: return "DDGEMM_ERROR_DEVICE: no current gfx950 device";
+    }
+    return "unknown ddgemm status";
+}
+
+ddgemm_status_t ddgemm_probe_mfma_f64(double* out, void* stream) {
+    if (!out) return DDGEMM_ERROR_INVALID_VALUE;
+    ddgemm_status_t st = check_device();
+    if (st != DDGEMM_SUCCESS) return st;
+    return launched(launch_probe_mfma(out, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Shared host/device definitions of the gfx950 double-double GEMM library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ddgemm.h"
+
+namespace ddg {
+
+constexpr int kSliceBits = DDGEMM_SLICE_BITS;
+constexpr int kSlices = DDGEMM_NUM_SLICES;
+constexpr int kLevels = DDGEMM_NUM_LEVELS;
+constexpr int kWindowBits = kSliceBits * kSlices;  // 104
+constexpr int kPackOuter = DDGEMM_PACK_OUTER;
+constexpr int kPackK = DDGEMM_PACK_K;
+constexpr int kFragDoubles = 64;                    // one 16x4 / 4x16 FP64 MFMA operand
+constexpr int kFragSetDoubles = kFragDoubles * kSlices;  // all 8 slices of one fragment
+
+typedef double double4_t __attribute__((ext_vector_type(4)));
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Packed-operand geometry for `outer` rows (A) / columns (B) and inner dimension k.
+struct PackGeom {
+    int64_t outer, k, Op, Kp, KB, RB;  // RB = Op / 16 fragment rows, KB = Kp / 4
+    PackGeom(int64_t outer_, int64_t k_)
+        : outer(outer_), k(k_), Op(round_up(outer_, kPackOuter)), Kp(round_up(k_, kPackK)),
+          KB(round_up(k_, kPackK) / 4), RB(round_up(outer_, kPackOuter) / 16) {}
+    int64_t doubles() const { return Op * Kp * kSlices; }
+};
+
+// Host-side launch helpers implemented next to their kernels.
+hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
+                        int64_t ldx, int axis, int32_t* exps, double* slices, hipStream_t stream);
+hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices,
+                              const double* B_slices, double* levels, int64_t ldl,
+                              const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
+                              int64_t ldc, bool fused, hipStream_t stream);
+hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
+                         const int32_t* F, double* C_hi, double* C_lo, int64_t ldc,
+                         hipStream_t stream);
+hipError_t launch_probe_mfma(double* out, hipStream_t stream);
+
+}  // namespace ddg

@@ -1,0 +1,41 @@
+// Error-free transformations and the level renormalisation, device side.
+//
+// Everything here is addition only (no products), so fused multiply-add
+// contraction cannot change it; the library is still built with
+// -ffp-contract=off and never with fast-math, which would license the
+// compiler to reassociate the bookkeeping away.
+#pragma once
+
+#include "common.hpp"
+
+namespace ddg {
+
+// Knuth's TwoSum: s = RN(a + b) and e = (a + b) - s exactly, any ordering of |a|, |b|.
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+    s = a + b;
+    const double bv = s - a;
+    const double av = s - bv;
+    e = (a - av) + (b - bv);
+}
+
+// Level renormalisation ("Multiple Double Arithmetic on NVIDIA Tensor Cores",
+// §2, fifth step): add the 8 exact level sums of one output entry into a
+// double-double, smallest level first, then apply the entry's scale 2^sc.
+// TwoSum is used for the renormalising step too (FastTwoSum gives the same bits
+// whenever its precondition holds, and TwoSum needs no branch when it does not).
+__device__ __forceinline__ void renorm_levels(const double (&S)[kLevels], int sc, double& c_hi,
+                                              double& c_lo) {
+    double h = S[kLevels - 1];
+    double t = 0.0;
+#pragma unroll
+    for (int l = kLevels - 2; l >= 0; --l) {
+        double s, e;
+        two_sum(h, S[l], s, e);
+        t = t + e;
+        two_sum(s, t, h, t);
+    }
+    c_hi = ldexp(h, sc);
+    c_lo = ldexp(t, sc);
+}
+
+}  // namespace ddg

@@ -1,0 +1,236 @@
+// Balancing exponents and 13-bit slicing of one double-double operand
+// ("Multiple Double Arithmetic on NVIDIA Tensor Cores", §2 quartering and its
+// worked example; §3 balancing, Problems 3.3 and 3.4).
+//
+// Every entry x = hi + lo is cut as the 104-bit fixed-point window below the
+// balancing exponent E of its row (A) or column (B): N = floor(|x| 2^(104-E)),
+// slice s = sign(x) * ((N >> 13(7-s)) & 8191) * 2^(-13(s+1)).  N is formed in
+// integer arithmetic from the exact error-free sum of (hi, lo), so opposite
+// signs (the pages' Problem 3.3), leading-zero slices (Problem 3.4), unnormalised
+// pairs and subnormals need no special borrow steps, and no 2^(104-E) factor
+// (which overflows for E < -919) is ever formed in floating point.
+#include "common.hpp"
+#include "eft.hpp"
+
+namespace ddg {
+namespace {
+
+constexpr int kNoExp = 0;          // encoded "no nonzero entry seen"
+constexpr int kExpBias = 4096;     // encoded exponent = frexp exponent + bias (>= 1)
+constexpr uint64_t kMant = (1ull << 52) - 1;
+
+// frexp exponent of a nonzero finite double: smallest e with |x| < 2^e.
+__device__ __forceinline__ int frexp_exponent(double x) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x)) & 0x7FFFFFFFFFFFFFFFull;
+    const int be = static_cast<int>(b >> 52);
+    if (be != 0) return be - 1022;
+    return (64 - __clzll(static_cast<long long>(b & kMant))) - 1074;
+}
+
+// Encoded exponent of RN(hi + lo), kNoExp for zero.
+__device__ __forceinline__ int entry_exp_code(double hi, double lo) {
+    const double s = hi + lo;
+    return s == 0.0 ? kNoExp : frexp_exponent(s) + kExpBias;
+}
+
+__device__ __forceinline__ int decode_exp(int code) { return code == kNoExp ? 0 : code - kExpBias; }
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// |x| = mant * 2^exp for a finite double (sign ignored); mant < 2^53.
+__device__ __forceinline__ void decompose(double x, uint64_t& mant, int& exp) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x)) & 0x7FFFFFFFFFFFFFFFull;
+    const int be = static_cast<int>(b >> 52);
+    mant = b & kMant;
+    if (be != 0) {
+        mant |= 1ull << 52;
+        exp = be - 1075;
+    } else {
+        exp = -1074;
+    }
+}
+
+// floor(y * 2^sh) for y = +-mant (mant < 2^53, y's sign given by neg); the
+// result is known to fit in int64 when sh >= 0.
+__device__ __forceinline__ int64_t floor_scaled(uint64_t mant, bool neg, int sh) {
+    if (sh >= 0) {
+        const int64_t v = static_cast<int64_t>(mant << sh);
+        return neg ? -v : v;
+    }
+    const int r = -sh;
+    if (r >= 60) return (neg && mant != 0) ? -1 : 0;
+    const uint64_t q = mant >> r;
+    const bool frac = (mant & ((1ull << r) - 1)) != 0;
+    return neg ? -static_cast<int64_t>(q + (frac ? 1 : 0)) : static_cast<int64_t>(q);
+}
+
+// The eight unit-scaled slices of x = hi + lo below exponent E (|x| < 2^E).
+__device__ __forceinline__ void slice_entry(double hi, double lo, int E, double (&out)[kSlices]) {
+    double s, e;
+    two_sum(hi, lo, s, e);  // x = s + e exactly, |e| <= ulp(s)/2
+    if (s == 0.0) {
+#pragma unroll
+        for (int q = 0; q < kSlices; ++q) out[q] = 0.0;
+        return;
+    }
+    const bool neg = s < 0.0;
+    const double ep = neg ? -e : e;  // |x| = |s| + ep
+    uint64_t ms;
+    int es;
+    decompose(s, ms, es);
+    const int W = E - kWindowBits;  // exponent of the window's last unit
+    unsigned __int128 N;
+    if (es >= W) {
+        // |s| 2^-W = ms << (es - W) is an integer below 2^104; add floor(ep 2^-W),
+        // which is below 2^51 in magnitude because |ep| <= ulp(s)/2.
+        N = static_cast<unsigned __int128>(ms) << (es - W);
+        if (ep != 0.0) {
+            uint64_t me;
+            int ee;
+            decompose(ep, me, ee);
+            const int64_t f = floor_scaled(me, ep < 0.0, ee - W);
+            N = static_cast<unsigned __int128>(static_cast<__int128>(N) + f);
+        }
+    } else {
+        // |s| has bits below the window: floor((ms + ep/2^es) / 2^d) with
+        // |ep/2^es| <= 1/2 is floor(ms / 2^d), minus one exactly when ms is a
+        // multiple of 2^d and ep < 0.
+        const int d = W - es;
+        uint64_t q = 0, r = ms;
+        if (d < 64) {
+            q = ms >> d;
+            r = ms & ((1ull << d) - 1);
+        }
+        if (r == 0 && ep < 0.0) q -= 1;
+        N = q;
+    }
+    constexpr double kScale[kSlices] = {0x1p-13, 0x1p-26, 0x1p-39, 0x1p-52,
+                                        0x1p-65, 0x1p-78, 0x1p-91, 0x1p-104};
+#pragma unroll
+    for (int q = 0; q < kSlices; ++q) {
+        const int d = static_cast<int>(static_cast<uint64_t>(N >> (kSliceBits * (kSlices - 1 - q))) & 0x1FFF);
+        out[q] = static_cast<double>(neg ? -d : d) * kScale[q];
+    }
+}
+
+// One wave per row: E[row] = max frexp exponent over the row (axis 0, the A operand).
+__global__ void __launch_bounds__(256) exp_rows_kernel(int64_t rows, int64_t cols,
+                                                       const double* __restrict__ hi,
+                                                       const double* __restrict__ lo, int64_t ld,
+                                                       int32_t* __restrict__ exps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
+    for (int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+         row < rows; row += nwaves) {
+        const double* h = hi + row * ld;
+        const double* l = lo ? lo + row * ld : nullptr;
+        int code = kNoExp;
+        for (int64_t p = lane; p < cols; p += 64) code = max(code, entry_exp_code(h[p], l ? l[p] : 0.0));
+        code = wave_max(code);
+        if (lane == 0) exps[row] = decode_exp(code);
+    }
+}
+
+__global__ void fill_int_kernel(int32_t* __restrict__ p, int64_t count, int32_t v) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = v;
+}
+
+// Column exponents (axis 1, the B operand): each thread takes one column over a
+// chunk of rows and folds its encoded maximum in with a device-memory atomicMax.
+__global__ void __launch_bounds__(256) exp_cols_kernel(int64_t rows, int64_t cols,
+                                                       const double* __restrict__ hi,
+                                                       const double* __restrict__ lo, int64_t ld,
+                                                       int64_t rows_per_chunk,
+                                                       int32_t* __restrict__ codes) {
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (col >= cols) return;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows_per_chunk;
+    const int64_t r1 = min(rows, r0 + rows_per_chunk);
+    int code = kNoExp;
+    for (int64_t r = r0; r < r1; ++r) code = max(code, entry_exp_code(hi[r * ld + col], lo ? lo[r * ld + col] : 0.0));
+    if (code != kNoExp) atomicMax(codes + col, code);
+}
+
+__global__ void decode_exps_kernel(int32_t* __restrict__ exps, int64_t count) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        exps[i] = decode_exp(exps[i]);
+}
+
+// One thread per packed (fragment, lane) position; writes the eight slices of
+// its entry.  AXIS 0: entry (o, p) is X[o][p]; AXIS 1: it is X[p][o].
+template <int AXIS>
+__global__ void __launch_bounds__(256) slice_kernel(int64_t outer, int64_t k, int64_t KB,
+                                                    int64_t total, const double* __restrict__ hi,
+                                                    const double* __restrict__ lo, int64_t ld,
+                                                    const int32_t* __restrict__ exps,
+                                                    double* __restrict__ slices) {
+    for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+         g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int lane = static_cast<int>(g & 63);
+        const int64_t frag = g >> 6;  // (o / 16) * KB + p / 4
+        const int64_t o = (frag / KB) * 16 + (lane & 15);
+        const int64_t p = (frag % KB) * 4 + (lane >> 4);
+        double x_hi = 0.0, x_lo = 0.0;
+        int E = 0;
+        if (o < outer && p < k) {
+            const int64_t idx = AXIS == 0 ? o * ld + p : p * ld + o;
+            x_hi = hi[idx];
+            x_lo = lo ? lo[idx] : 0.0;
+            E = exps[o];
+        }
+        double sl[kSlices];
+        slice_entry(x_hi, x_lo, E, sl);
+        double* dst = slices + frag * kFragSetDoubles + lane;
+#pragma unroll
+        for (int q = 0; q < kSlices; ++q) dst[q * kFragDoubles] = sl[q];
+    }
+}
+
+inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return static_cast<unsigned>(g);
+}
+
+}  // namespace
+
+hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
+                        int64_t ldx, int axis, int32_t* exps, double* slices, hipStream_t stream) {
+    const int64_t outer = axis == 0 ? rows : cols;
+    const int64_t k = axis == 0 ? cols : rows;
+    if (outer == 0) return hipSuccess;
+    if (axis == 0) {
+        exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X_hi, X_lo, ldx, exps);
+    } else {
+        fill_int_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols, kNoExp);
+        if (rows > 0) {
+            int64_t rpc = (rows + 4095) / 4096;
+            if (rpc < 64) rpc = 64;
+            const int64_t chunks = (rows + rpc - 1) / rpc;
+            dim3 grid(static_cast<unsigned>((cols + 255) / 256), static_cast<unsigned>(chunks));
+            exp_cols_kernel<<<grid, 256, 0, stream>>>(rows, cols, X_hi, X_lo, ldx, rpc, exps);
+        }
+        decode_exps_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const PackGeom g(outer, k);
+    if (g.doubles() == 0) return hipSuccess;
+    const int64_t total = g.RB * g.KB * kFragDoubles;
+    const unsigned grid = grid_for(total, 256, 1 << 20);
+    if (axis == 0)
+        slice_kernel<0><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X_hi, X_lo, ldx, exps, slices);
+    else
+        slice_kernel<1><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X_hi, X_lo, ldx, exps, slices);
+    return hipGetLastError();
+}
+
+}  // namespace ddg

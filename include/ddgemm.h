@@ -1,0 +1,190 @@
+/*
+ * ddgemm.h -- double-double matrix product C = A·B on AMD Instinct MI355X
+ * (gfx950) by exact 13-bit slicing on FP64 matrix cores.
+ *
+ * Method: "Multiple Double Arithmetic on NVIDIA Tensor Cores" (arXiv
+ * 2607.06881v1).  §2 cuts every double into 13-bit quarters whose pairwise
+ * products are exact, groups the quarter products by the sum of their indices
+ * (eqs. (1)-(3)), writes the double-double product as one product of double
+ * matrices (eq. (4)) and adds the parts of each output entry in double-double
+ * arithmetic once at the end (the fifth step of the overview).  §3 keeps the
+ * parts on a common exponent grid (balancing).  This library realises that as:
+ *
+ *   1. dd_split_balanced  -- one balancing exponent per row of A / column of B,
+ *                            then eight 13-bit slices of every entry;
+ *   2. dd_sliced_gemm     -- the 36 slice-pair products with s + t <= 7, summed
+ *                            exactly per level l = s + t on FP64 MFMA;
+ *   3. dd_renorm_levels   -- TwoSum cascade of the 8 level sums into (hi, lo);
+ *   dd_sliced_gemm_renorm fuses 2 and 3; dd_gemm / dd_gemm_ws run 1 + 1 + (2+3).
+ *
+ * Conventions for every entry point
+ *   - All matrices are row-major float64 planes in device memory; a
+ *     double-double matrix X is the pair of planes (X_hi, X_lo) with value
+ *     X_hi + X_lo.  Leading dimensions count elements.  A lo pointer may be
+ *     NULL, meaning an all-zero lo plane.
+ *   - Pointers are owned by the caller; the library keeps none after a call
+ *     returns.  Only dd_gemm allocates (stream-ordered, freed on the stream).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work and returns; errors from the execution itself surface at
+ *     the caller's next synchronisation, as with any HIP launch.  Argument
+ *     errors are reported before anything is enqueued.
+ *   - Inputs must be finite; pairs need not be normalised (the exact value
+ *     hi + lo is sliced).  Outputs must not overlap inputs.
+ *   - Calls are reentrant: no global state except a per-device capability
+ *     check cached on first use.
+ */
+#ifndef DDGEMM_H
+#define DDGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DDGEMM_SUCCESS = 0,
+    DDGEMM_ERROR_INVALID_VALUE = 1, /* negative size, short leading dimension, NULL with a
+                                       nonzero extent, bad axis, k > DDGEMM_K_MAX, overlap */
+    DDGEMM_ERROR_WORKSPACE = 2,     /* workspace allocation failed or caller workspace too small */
+    DDGEMM_ERROR_LAUNCH = 3,        /* a HIP launch or runtime call failed while enqueuing */
+    DDGEMM_ERROR_DEVICE = 4         /* no current HIP device, or it is not gfx950 */
+} ddgemm_status_t;
+
+/* Slicing constants ("Multiple Double Arithmetic on NVIDIA Tensor Cores", §2). */
+#define DDGEMM_SLICE_BITS 13 /* significant bits per slice: the pages' quarters   */
+#define DDGEMM_NUM_SLICES 8  /* 104-bit window: four quarters of hi, four of lo    */
+#define DDGEMM_NUM_LEVELS 8  /* levels l = s + t = 0..7; 36 slice pairs            */
+/* Largest k: with every level holding at most 8 pairs, the exact-sum bound of §2
+ * eq. (5) (67,108,865 products of 26-bit quantities) allows 67,108,865 / 8 terms. */
+#define DDGEMM_K_MAX 8388608
+
+/* Packed slice layout (the output of dd_split_balanced, the input of the GEMMs).
+ *
+ * For one operand, "outer" is the row index i of A (axis 0) or the column index
+ * j of B (axis 1) and p is the index along k.  Outer is padded to
+ * Op = roundup(outer, DDGEMM_PACK_OUTER), k to Kp = roundup(k, DDGEMM_PACK_K),
+ * KB = Kp / 4.  Slice s of entry (o, p) is the double at
+ *
+ *     ((((o / 16) * KB + p / 4) * 8 + s) * 64) + (p % 4) * 16 + (o % 16)
+ *
+ * i.e. 16×4 (A) or 4×16 (B) fragments of 64 doubles in the lane order of the
+ * gfx950 FP64 16x16x4 matrix instruction, the eight slices of one fragment
+ * adjacent.  The value stored is sign(x) * d_s * 2^(-13(s+1)) where d_s is the
+ * s-th 13-bit digit of N = floor(|x| * 2^(104-E)), x = hi + lo exactly and E the
+ * balancing exponent of the entry's row (A) or column (B); padding holds +0.0.
+ * Total size: Op * Kp * 8 doubles (dd_split_slices_bytes). */
+#define DDGEMM_PACK_OUTER 128
+#define DDGEMM_PACK_K 16
+
+/* Bytes of packed slices for one operand with `outer` rows (A) / columns (B) and
+ * inner dimension k; 0 for negative sizes. */
+size_t dd_split_slices_bytes(int64_t outer, int64_t k);
+
+/* Workspace bytes dd_gemm_ws needs for an m×k by k×n product (slices of both
+ * operands and both exponent vectors, each region 256-byte aligned); 0 for
+ * negative sizes. */
+size_t dd_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
+
+/*
+ * Balancing exponents and slices of one operand ("Multiple Double Arithmetic on
+ * NVIDIA Tensor Cores", §2 quartering with its worked example, §3 balancing).
+ *
+ *   X_hi, X_lo : rows×cols double-double matrix, row stride ldx >= max(1, cols).
+ *   axis = 0   : X is the A operand (m×k): one exponent per row, outer = rows,
+ *                k = cols; `exps` has rows entries.
+ *   axis = 1   : X is the B operand (k×n): one exponent per column, outer = cols,
+ *                k = rows; `exps` has cols entries.
+ *   exps       : E = the largest frexp exponent of RN(hi + lo) over the nonzero
+ *                entries of the row/column (so |hi + lo| < 2^E), 0 if all are zero.
+ *   slices     : dd_split_slices_bytes(outer, k) bytes, packed as described above.
+ * Errors: DDGEMM_ERROR_INVALID_VALUE for negative sizes, ldx < max(1, cols),
+ * axis not 0/1, k > DDGEMM_K_MAX, or NULL X_hi/exps/slices with a nonzero extent.
+ */
+ddgemm_status_t dd_split_balanced(int64_t rows, int64_t cols,
+                                  const double* X_hi, const double* X_lo, int64_t ldx,
+                                  int axis, int32_t* exps, double* slices, void* stream);
+
+/*
+ * Level sums of the slice-pair products ("Multiple Double Arithmetic on NVIDIA
+ * Tensor Cores", §2 eqs. (3)-(4); exactness: §2 eq. (5)).
+ *
+ *   A_slices : packed A operand (outer = m), B_slices : packed B operand (outer = n),
+ *              both with the same k.
+ *   levels   : 8 planes, plane l at levels + l*m*ldl, each m×n with row stride
+ *              ldl >= max(1, n):  S_l[i][j] = sum_{s+t=l} sum_p A_s[i][p] * B_t[p][j]
+ *              for l = 0..7, computed exactly (every partial sum is an integer
+ *              multiple of 2^(-13(l+2)) below 2^53 units).  k = 0 writes zeros.
+ * Errors: DDGEMM_ERROR_INVALID_VALUE for negative sizes, ldl < max(1, n),
+ * k > DDGEMM_K_MAX, NULL pointers with a nonzero extent.
+ */
+ddgemm_status_t dd_sliced_gemm(int64_t m, int64_t n, int64_t k,
+                               const double* A_slices, const double* B_slices,
+                               double* levels, int64_t ldl, void* stream);
+
+/*
+ * Renormalisation of the level sums ("Multiple Double Arithmetic on NVIDIA
+ * Tensor Cores", §2, the fifth step: the parts of each product entry are added
+ * in double-double arithmetic on the regular cores; Problem 1.1 is why this is
+ * done once per entry and not inside the product).
+ *
+ * Per entry, smallest level first: (h, t) = (S_7, 0); for l = 6..0:
+ * (s, e) = TwoSum(h, S_l); t = t + e; (h, t) = TwoSum(s, t).  Then
+ * C_hi = h * 2^(E[i] + F[j]), C_lo = t * 2^(E[i] + F[j]) (ldexp).
+ *   levels : as written by dd_sliced_gemm (row stride ldl, plane stride m*ldl).
+ *   E, F   : the exponents from dd_split_balanced for A (m) and B (n).
+ *   C_hi, C_lo : m×n, row stride ldc >= max(1, n).
+ */
+ddgemm_status_t dd_renorm_levels(int64_t m, int64_t n, const double* levels, int64_t ldl,
+                                 const int32_t* E, const int32_t* F,
+                                 double* C_hi, double* C_lo, int64_t ldc, void* stream);
+
+/* dd_sliced_gemm followed by dd_renorm_levels in one kernel: the level sums stay
+ * in registers; bit-identical to the two-call sequence. */
+ddgemm_status_t dd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k,
+                                      const double* A_slices, const int32_t* E,
+                                      const double* B_slices, const int32_t* F,
+                                      double* C_hi, double* C_lo, int64_t ldc, void* stream);
+
+/*
+ * C = A·B for double-double A (m×k) and B (k×n) ("Multiple Double Arithmetic on
+ * NVIDIA Tensor Cores", §2 overview, steps 1-5).  Overwrites C (no alpha/beta).
+ * m = 0 or n = 0: no-op.  k = 0: C = 0.  Accuracy: the product of the operands
+ * truncated to 104 bits below their row/column exponents, minus the slice pairs
+ * below the double-double window, renormalised; on inputs whose entries sit
+ * within a few binades of their row/column maximum this is within
+ * 1e-28 * (|A||B|)_ij of the exact product.
+ *   dd_gemm     allocates its workspace with hipMallocAsync/hipFreeAsync on
+ *               `stream` (DDGEMM_ERROR_WORKSPACE if that fails).
+ *   dd_gemm_ws  uses the caller's workspace of ws_bytes >= dd_gemm_workspace_size
+ *               (256-byte aligned), allocates nothing.
+ * Errors: as for the stage calls, plus lda < max(1, k), ldb < max(1, n),
+ * ldc < max(1, n), C overlapping A or B.
+ */
+ddgemm_status_t dd_gemm(int64_t m, int64_t n, int64_t k,
+                        const double* A_hi, const double* A_lo, int64_t lda,
+                        const double* B_hi, const double* B_lo, int64_t ldb,
+                        double* C_hi, double* C_lo, int64_t ldc, void* stream);
+
+ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k,
+                           const double* A_hi, const double* A_lo, int64_t lda,
+                           const double* B_hi, const double* B_lo, int64_t ldb,
+                           double* C_hi, double* C_lo, int64_t ldc,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* ddgemm_status_string(ddgemm_status_t status);
+
+/* Diagnostics: runs one FP64 16x16x4 matrix instruction on one wave with
+ * a-operand lane value (lane + 1) and b-operand lane value 100 * (lane + 1) and
+ * writes the four result doubles of every lane to out[lane * 4 + v]
+ * (256 doubles, device memory).  Used to confirm the operand/result lane layout
+ * the packed format assumes.  Errors: DDGEMM_ERROR_INVALID_VALUE for NULL out. */
+ddgemm_status_t ddgemm_probe_mfma_f64(double* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDGEMM_H */

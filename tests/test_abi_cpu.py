@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes its buffers as documented and rejects bad arguments
+before touching a device.  No GPU needed (no compute call is made)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddgemm.h")
+
+
+@pytest.fixture(scope="module")
+def ddg():
+    import extended_precision_gemm_amd as m
+    return m
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dd\w+|ddgemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("dd_gemm", "dd_gemm_ws", "dd_gemm_workspace_size", "dd_split_balanced",
+                     "dd_sliced_gemm", "dd_renorm_levels", "dd_sliced_gemm_renorm",
+                     "ddgemm_status_string", "dd_split_slices_bytes"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(ddg):
+    raw = ctypes.CDLL(ddg.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+    assert set(_declared_functions()) == set(ddg._SIGNATURES)
+
+
+def test_library_links_no_oracle_code(ddg):
+    raw = ctypes.CDLL(ddg.LIB_PATH)
+    for name in ("oracle_dd_gemm", "oracle_two_sum", "oracle_dd_add"):
+        assert not hasattr(raw, name)
+
+
+def test_packed_sizes(ddg):
+    assert ddg.slices_bytes(0, 10) == 0
+    assert ddg.slices_bytes(10, 0) == 0
+    assert ddg.slices_bytes(1, 1) == 128 * 16 * 8 * 8
+    assert ddg.slices_bytes(129, 17) == 256 * 32 * 8 * 8
+    assert ddg.slices_bytes(4096, 4096) == 4096 * 4096 * 64
+    assert ddg.slices_bytes(-1, 5) == 0
+    m, n, k = 1000, 70, 33
+    ws = ddg.workspace_size(m, n, k)
+    r = lambda x: (x + 255) // 256 * 256
+    assert ws == r(ddg.slices_bytes(m, k)) + r(ddg.slices_bytes(n, k)) + r(4 * m) + r(4 * n)
+    assert ddg.workspace_size(-1, 2, 3) == 0
+    assert ddg.workspace_size(1, 1, ddg.K_MAX + 1) == 0
+
+
+def test_status_strings(ddg):
+    for code in range(5):
+        s = ddg.status_string(code)
+        assert s.startswith("DDGEMM_")
+    assert "unknown" in ddg.status_string(99)
+
+
+# Fake device addresses: never dereferenced, since every call below fails validation.
+P = [0x10000000 * (i + 1) for i in range(8)]
+
+
+def test_gemm_argument_validation(ddg):
+    L = ddg.lib
+    INV, WS = ddg.ERROR_INVALID_VALUE, ddg.ERROR_WORKSPACE
+    ok = dict(m=4, n=5, k=6, A_hi=P[0], A_lo=P[1], lda=6, B_hi=P[2], B_lo=P[3], ldb=5,
+              C_hi=P[4], C_lo=P[5], ldc=5)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.dd_gemm_ws(a["m"], a["n"], a["k"], a["A_hi"], a["A_lo"], a["lda"], a["B_hi"], a["B_lo"],
+                            a["ldb"], a["C_hi"], a["C_lo"], a["ldc"], kw.get("ws", P[6]),
+                            kw.get("ws_bytes", 0), None)
+
+    assert call(m=-1) == INV
+    assert call(n=-1) == INV
+    assert call(k=-1) == INV
+    assert call(k=ddg.K_MAX + 1, lda=ddg.K_MAX + 1) == INV
+    assert call(lda=5) == INV
+    assert call(ldb=4) == INV
+    assert call(ldc=4) == INV
+    assert call(A_hi=None) == INV
+    assert call(B_hi=None) == INV
+    assert call(C_hi=None) == INV
+    assert call(C_lo=None) == INV
+    assert call(C_hi=P[0]) == INV            # C aliases A
+    assert call(C_lo=P[2] + 8) == INV        # C overlaps B
+    assert call(C_lo=P[4] + 16) == INV       # C_hi and C_lo overlap
+    assert call(ws_bytes=10) == WS           # too small
+    need = ddg.workspace_size(4, 5, 6)
+    assert call(ws=P[6] + 8, ws_bytes=need) == WS   # misaligned
+    # m = 0 or n = 0 is a successful no-op that needs no pointers at all
+    assert L.dd_gemm_ws(0, 5, 6, None, None, 6, None, None, 5, None, None, 5, None, 0, None) == 0
+    assert L.dd_gemm_ws(4, 0, 6, None, None, 6, None, None, 1, None, None, 1, None, 0, None) == 0
+    assert L.dd_gemm(0, 0, 0, None, None, 1, None, None, 1, None, None, 1, None) == 0
+    assert L.dd_gemm(3, 3, 3, P[0], None, 2, P[1], None, 3, P[2], P[3], 3, None) == INV
+
+
+def test_stage_argument_validation(ddg):
+    L = ddg.lib
+    INV = ddg.ERROR_INVALID_VALUE
+    assert L.dd_split_balanced(4, 4, P[0], None, 4, 2, P[1], P[2], None) == INV   # bad axis
+    assert L.dd_split_balanced(4, 4, P[0], None, 3, 0, P[1], P[2], None) == INV   # ld < cols
+    assert L.dd_split_balanced(4, 4, None, None, 4, 0, P[1], P[2], None) == INV   # NULL X
+    assert L.dd_split_balanced(4, 4, P[0], None, 4, 1, None, P[2], None) == INV   # NULL exps
+    assert L.dd_split_balanced(4, 4, P[0], None, 4, 1, P[1], None, None) == INV   # NULL slices
+    assert L.dd_split_balanced(ddg.K_MAX + 1, 1, P[0], None, 1, 1, P[1], P[2], None) == INV
+    assert L.dd_split_balanced(0, 4, None, None, 4, 0, None, None, None) == 0      # empty
+    assert L.dd_sliced_gemm(4, 4, 4, P[0], P[1], P[2], 3, None) == INV            # ldl < n
+    assert L.dd_sliced_gemm(4, 4, 4, None, P[1], P[2], 4, None) == INV
+    assert L.dd_sliced_gemm(4, 4, 4, P[0], P[1], None, 4, None) == INV
+    assert L.dd_renorm_levels(4, 4, P[0], 4, P[1], P[2], P[3], P[3], 4, None) == INV  # C_hi == C_lo
+    assert L.dd_renorm_levels(4, 4, P[0], 4, None, P[2], P[3], P[4], 4, None) == INV
+    assert L.dd_sliced_gemm_renorm(4, 4, 4, P[0], P[1], P[2], P[3], P[4], P[5], 3, None) == INV
+    assert L.ddgemm_probe_mfma_f64(None, None) == INV
+
+
+def test_valid_call_without_gpu_reports_device_error(ddg):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = ddg.lib
+    assert L.dd_split_balanced(4, 4, P[0], None, 4, 0, P[1], P[2], None) == ddg.ERROR_DEVICE
+
+
+def test_layout_pack_unpack_roundtrip(ddg):
+    from extended_precision_gemm_amd import layout
+    rng = np.random.default_rng(0)
+    for outer, k in [(1, 1), (17, 5), (130, 33), (128, 16)]:
+        planes = rng.standard_normal((8, outer, k))
+        packed = layout.pack(planes, outer, k)
+        assert packed.size * 8 == ddg.slices_bytes(outer, k)
+        assert np.array_equal(layout.unpack(packed, outer, k), planes)
+        # spot-check the documented index formula
+        KB = layout.padded(outer, k)[1] // 4
+        for (s, o, p) in [(0, 0, 0), (7, outer - 1, k - 1), (3, outer // 2, k // 2)]:
+            idx = (((o // 16) * KB + p // 4) * 8 + s) * 64 + (p % 4) * 16 + (o % 16)
+            assert packed[idx] == planes[s, o, p]

@@ -1,0 +1,391 @@
+"""Parity of the HIP path with the CPU oracle (GPU tests; call through the C ABI).
+
+Bars:
+* slicing (exponents and every slice), level sums, and the whole sliced chain
+  (slices -> level sums -> cascade) are bit-exact against the oracle's exact
+  big-integer implementation of the same steps;
+* the product is within 1e-28 * (|A||B|)_ij of the classical double-double
+  oracle on the five workloads (all entries at 64^3 and 1024^3, sampled entries
+  at the full sizes of the others), in the launch configuration the bench times.
+Every expected value comes from oracle/ on oracle inputs; nothing is read back
+from the GPU and fed to the oracle.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import compare, exact, native
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    import torch
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _bits_equal(a, b):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    return a.shape == b.shape and np.array_equal(a.view(np.int64), b.view(np.int64))
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _gpu_split(ddg, hi, lo, axis):
+    from extended_precision_gemm_amd import layout
+    E, packed = ddg.split_balanced(_dev(hi), _dev(lo), axis)
+    outer = hi.shape[0] if axis == 0 else hi.shape[1]
+    k = hi.shape[1] if axis == 0 else hi.shape[0]
+    return E, packed, outer, k
+
+
+def _unpacked(packed, outer, k, rows=None):
+    """(8, outer, k) host planes (only the selected outer indices when given)."""
+    from extended_precision_gemm_amd import layout
+    import torch
+    planes = layout.unpack(packed, outer, k)
+    if rows is not None:
+        planes = planes[:, torch.as_tensor(np.asarray(rows), device=packed.device), :]
+    return _host(planes.contiguous())
+
+
+# ---------------------------------------------------------------------------
+# device probe
+# ---------------------------------------------------------------------------
+def test_mfma_f64_lane_layout(gpu):
+    """a-operand lane L holds A[L%16][L//16], b-operand lane L holds B[L//16][L%16],
+    result lane L holds D[4*(L//16)+v][L%16]: the layout the packing assumes."""
+    out = _host(gpu.probe_mfma_f64())
+    lanes = np.arange(64)
+    A = np.zeros((16, 4))
+    B = np.zeros((4, 16))
+    A[lanes % 16, lanes // 16] = lanes + 1
+    B[lanes // 16, lanes % 16] = 100.0 * (lanes + 1)
+    D = A @ B
+    expect = np.array([[D[4 * (L // 16) + v, L % 16] for v in range(4)] for L in range(64)])
+    assert np.array_equal(out, expect), out
+
+
+# ---------------------------------------------------------------------------
+# slicing
+# ---------------------------------------------------------------------------
+def test_split_reproduces_the_pages_worked_example(gpu):
+    x = float.fromhex("0x1.234cc9da46998p-1")  # the fraction bits of §2's example, exponent 0
+    hi = np.full((1, 1), x)
+    for axis in (0, 1):
+        E, packed, outer, k = _gpu_split(gpu, hi, np.zeros_like(hi), axis)
+        assert _host(E).tolist() == [0]
+        got = _unpacked(packed, outer, k)[:, 0, 0]
+        digits = [4660, 6547, 5777, 5324, 0, 0, 0, 0]
+        assert got.tolist() == [d * 2.0 ** (-13 * (s + 1)) for s, d in enumerate(digits)]
+
+
+def _edge_matrix(rng, m, k):
+    hi = rng.uniform(-1, 1, (m, k))
+    hi *= np.ldexp(1.0, rng.integers(-12, 3, (m, k)))
+    lo_raw = hi * 2.0 ** -53 * rng.uniform(-1, 1, (m, k))
+    s = hi + lo_raw
+    lo = lo_raw - (s - hi)
+    hi = s
+    if m > 2 and k > 2:
+        hi[1, :] = 0.0
+        lo[1, :] = 0.0                          # all-zero row
+        hi[:, 2] = 0.0
+        lo[:, 2] = 0.0                          # all-zero column
+        hi[0, 0], lo[0, 0] = 1.0, -0.75         # unnormalised: |hi + lo| < |hi|
+        hi[0, 1], lo[0, 1] = 0.5, -2.0 ** -60   # opposite signs (Problem 3.3)
+        hi[2, 0], lo[2, 0] = -0.0, 0.0          # negative zero
+        hi[-1, -1], lo[-1, -1] = 2.0 ** -1074, 0.0  # subnormal
+        hi[-1, 0], lo[-1, 0] = 3 * 2.0 ** -1060, -2.0 ** -1074
+    return hi, lo
+
+
+SMALL_SHAPES = [(1, 1, 1), (3, 5, 7), (16, 16, 4), (17, 33, 5), (64, 64, 64), (130, 65, 33), (1, 300, 200), (200, 1, 300)]
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_SHAPES)
+def test_split_bit_exact_small(gpu, m, n, k):
+    rng = np.random.default_rng(m * 1000 + n * 10 + k)
+    Ah, Al = _edge_matrix(rng, m, k)
+    Bh, Bl = _edge_matrix(rng, k, n)
+    for (hi, lo, axis) in ((Ah, Al, 0), (Bh, Bl, 1)):
+        E, packed, outer, k_ = _gpu_split(gpu, hi, lo, axis)
+        if axis == 0:
+            E_ref, D = exact.slice_rows(hi, lo)
+        else:
+            E_ref, D = exact.slice_cols(hi, lo)
+            D = D.transpose(0, 2, 1)  # (8, outer=n, k)
+        assert np.array_equal(_host(E), E_ref)
+        assert _bits_equal(_unpacked(packed, outer, k_), exact.slice_values(D))
+        # padding holds +0.0
+        from extended_precision_gemm_amd import layout
+        Op, Kp = layout.padded(outer, k_)
+        full = _host(packed).reshape(-1)
+        mask = np.ones(Op * Kp * 8, dtype=bool)
+        mask[layout.pack(np.ones((8, outer, k_)), outer, k_) != 0] = False
+        assert np.all(full[mask].view(np.int64) == 0)
+
+
+def test_split_all_max_digits(gpu):
+    """x = 1 - 2^-104 at E = 0 has every digit 8191 (hi = 1 - 2^-53, lo = 2^-53 - 2^-104)."""
+    hi = np.full((3, 40), 1.0 - 2.0 ** -53)
+    lo = np.full((3, 40), 2.0 ** -53 - 2.0 ** -104)
+    E, packed, outer, k = _gpu_split(gpu, hi, lo, 0)
+    assert _host(E).tolist() == [0, 0, 0]
+    got = _unpacked(packed, outer, k)
+    for s in range(8):
+        assert np.all(got[s] == 8191 * 2.0 ** (-13 * (s + 1)))
+
+
+# ---------------------------------------------------------------------------
+# level sums, cascade, and the whole sliced chain
+# ---------------------------------------------------------------------------
+def _oracle_chain(Ah, Al, Bh, Bl, rows=None, cols=None):
+    E, DA = exact.slice_rows(Ah, Al, rows)
+    F, DB = exact.slice_cols(Bh, Bl, cols)
+    S = exact.level_values(exact.level_sums_units(DA, DB))
+    Ch, Cl = exact.renorm_levels(S, E, F)
+    return S, Ch, Cl
+
+
+def _gpu_chain(gpu, Ah, Al, Bh, Bl):
+    m, k = Ah.shape
+    n = Bh.shape[1]
+    E, As = gpu.split_balanced(_dev(Ah), _dev(Al), 0)
+    F, Bs = gpu.split_balanced(_dev(Bh), _dev(Bl), 1)
+    levels = gpu.sliced_gemm(m, n, k, As, Bs)
+    Ch, Cl = gpu.renorm_levels(levels, E, F)
+    Fh, Fl = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F)
+    return levels, Ch, Cl, Fh, Fl
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_SHAPES + [(128, 128, 16), (96, 160, 100)])
+def test_sliced_chain_bit_exact_small(gpu, m, n, k):
+    rng = np.random.default_rng(7 + m + 3 * n + 5 * k)
+    Ah, Al = _edge_matrix(rng, m, k)
+    Bh, Bl = _edge_matrix(rng, k, n)
+    S, Ch_ref, Cl_ref = _oracle_chain(Ah, Al, Bh, Bl)
+    levels, Ch, Cl, Fh, Fl = _gpu_chain(gpu, Ah, Al, Bh, Bl)
+    assert _bits_equal(_host(levels), S), "level sums"
+    assert _bits_equal(_host(Ch), Ch_ref) and _bits_equal(_host(Cl), Cl_ref), "cascade"
+    assert _bits_equal(_host(Fh), Ch_ref) and _bits_equal(_host(Fl), Cl_ref), "fused epilogue"
+    Gh, Gl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))
+    assert _bits_equal(_host(Gh), Ch_ref) and _bits_equal(_host(Gl), Cl_ref), "dd_gemm_ws"
+    Hh, Hl = gpu.dd_gemm_alloc(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))
+    assert _bits_equal(_host(Hh), Ch_ref) and _bits_equal(_host(Hl), Cl_ref), "dd_gemm"
+
+
+def test_level_sums_exact_at_the_bound(gpu):
+    """Every digit 8191 and k = 8192: level 7 reaches 8 * 8192 * 8191^2 ~ 2^42 units, exactly."""
+    m, n, k = 32, 48, 8192
+    Ah = np.full((m, k), 1.0 - 2.0 ** -53)
+    Al = np.full((m, k), 2.0 ** -53 - 2.0 ** -104)
+    Bh = np.full((k, n), -(1.0 - 2.0 ** -53))
+    Bl = np.full((k, n), -(2.0 ** -53 - 2.0 ** -104))
+    E, As = gpu.split_balanced(_dev(Ah), _dev(Al), 0)
+    F, Bs = gpu.split_balanced(_dev(Bh), _dev(Bl), 1)
+    levels = _host(gpu.sliced_gemm(m, n, k, As, Bs))
+    for l in range(8):
+        expect = -(l + 1) * k * 8191 ** 2
+        assert np.all(levels[l] * 2.0 ** (13 * (l + 2)) == expect)
+
+
+# ---------------------------------------------------------------------------
+# end to end against the classical oracle, edge cases, metamorphic relations
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (17, 33, 5), (130, 65, 33), (64, 200, 300)])
+def test_dd_gemm_within_tolerance_small(gpu, m, n, k):
+    rng = np.random.default_rng(m + n + k)
+    Ah, Al = workloads.random_dd((m, k), rng.integers(1 << 30))
+    Bh, Bl = workloads.random_dd((k, n), rng.integers(1 << 30))
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))
+    Rh, Rl, _ = native.dd_gemm(Ah, Al, Bh, Bl)
+    assert compare.error_ratio(_host(Ch), _host(Cl), Rh, Rl, compare.abs_product(Ah, Bh)) <= compare.TOL
+
+
+def test_k_zero_writes_zeros_and_empty_is_noop(gpu):
+    import torch
+    Ch = torch.full((5, 7), 3.0, dtype=torch.float64, device="cuda")
+    Cl = torch.full((5, 7), 3.0, dtype=torch.float64, device="cuda")
+    A = torch.zeros((5, 0), dtype=torch.float64, device="cuda")
+    B = torch.zeros((0, 7), dtype=torch.float64, device="cuda")
+    gpu.dd_gemm(A, None, B, None, Ch, Cl)
+    assert np.all(_host(Ch) == 0) and np.all(_host(Cl) == 0)
+    E = torch.zeros((0, 4), dtype=torch.float64, device="cuda")
+    out = gpu.dd_gemm(E, None, torch.zeros((4, 3), dtype=torch.float64, device="cuda"), None)
+    assert out[0].shape == (0, 3)
+
+
+def test_strided_operands_and_null_lo(gpu):
+    import torch
+    rng = np.random.default_rng(21)
+    Ah, Al = workloads.random_dd((40, 70), 5)
+    Bh, Bl = workloads.random_dd((70, 90), 6)
+    # operands as column windows of wider matrices (lda > k, ldb > n), C likewise
+    Abig = torch.zeros((40, 100), dtype=torch.float64, device="cuda")
+    Abig[:, 10:80] = _dev(Ah)
+    Bbig = torch.zeros((70, 128), dtype=torch.float64, device="cuda")
+    Bbig[:, 3:93] = _dev(Bh)
+    Cbig = torch.zeros((2, 40, 96), dtype=torch.float64, device="cuda")
+    Ch, Cl = gpu.dd_gemm(Abig[:, 10:80], None, Bbig[:, 3:93], None, Cbig[0, :, :90], Cbig[1, :, :90])
+    ref = gpu.dd_gemm(_dev(Ah), None, _dev(Bh), None)
+    assert _bits_equal(_host(Ch), _host(ref[0])) and _bits_equal(_host(Cl), _host(ref[1]))
+    assert np.all(_host(Cbig[:, :, 90:]) == 0)
+    Rh, Rl, _ = native.dd_gemm(Ah, None, Bh, None)
+    assert compare.error_ratio(_host(Ch), _host(Cl), Rh, Rl, compare.abs_product(Ah, Bh)) <= compare.TOL
+
+
+def test_identity_returns_the_windowed_operand(gpu):
+    rng = np.random.default_rng(22)
+    Bh, Bl = workloads.random_dd((50, 37), 9)
+    I = np.eye(50)
+    Ch, Cl = gpu.dd_gemm(_dev(I), None, _dev(Bh), _dev(Bl))
+    # each column of B is cut at 104 bits below its own exponent: exact when on the grid
+    F, DB = exact.slice_cols(Bh, Bl)
+    for j in (0, 7, 36):
+        for p in (0, 13, 49):
+            got = exact.dd_to_fraction(_host(Ch)[p, j], _host(Cl)[p, j])
+            assert got == exact.reconstruct_entry(DB[:, p, j], int(F[j]))
+
+
+def test_metamorphic_relations_bitwise(gpu):
+    """Exact level sums make these hold bit for bit: power-of-two scaling of A's
+    rows and B's columns, permutation of k, transposition, negation, repetition."""
+    import torch
+    rng = np.random.default_rng(23)
+    m, n, k = 70, 90, 130
+    Ah, Al = workloads.random_dd((m, k), 11)
+    Bh, Bl = workloads.random_dd((k, n), 12)
+    C = [_host(t) for t in gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))]
+    ra = np.ldexp(1.0, rng.integers(-40, 40, m)).reshape(-1, 1)
+    cb = np.ldexp(1.0, rng.integers(-40, 40, n)).reshape(1, -1)
+    S = [_host(t) for t in gpu.dd_gemm(_dev(Ah * ra), _dev(Al * ra), _dev(Bh * cb), _dev(Bl * cb))]
+    assert _bits_equal(S[0], C[0] * ra * cb) and _bits_equal(S[1], C[1] * ra * cb)
+    perm = rng.permutation(k)
+    P = [_host(t) for t in gpu.dd_gemm(_dev(Ah[:, perm]), _dev(Al[:, perm]), _dev(Bh[perm]), _dev(Bl[perm]))]
+    assert _bits_equal(P[0], C[0]) and _bits_equal(P[1], C[1])
+    T = [_host(t) for t in gpu.dd_gemm(_dev(Bh.T), _dev(Bl.T), _dev(Ah.T), _dev(Al.T))]
+    assert _bits_equal(T[0].T, C[0]) and _bits_equal(T[1].T, C[1])
+    N = [_host(t) for t in gpu.dd_gemm(_dev(-Ah), _dev(-Al), _dev(Bh), _dev(Bl))]
+    assert _bits_equal(N[0], -C[0]) and _bits_equal(N[1], -C[1])
+    R = [_host(t) for t in gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))]
+    assert _bits_equal(R[0], C[0]) and _bits_equal(R[1], C[1])
+
+
+def test_nondefault_stream(gpu):
+    import torch
+    Ah, Al = workloads.random_dd((64, 64), 31)
+    Bh, Bl = workloads.random_dd((64, 64), 32)
+    ref = [_host(t) for t in gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))
+    s.synchronize()
+    assert _bits_equal(_host(out[0]), ref[0]) and _bits_equal(_host(out[1]), ref[1])
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+def _sample_indices(rng, size, count):
+    idx = set([0, size - 1]) | set(rng.integers(0, size, count).tolist())
+    return np.array(sorted(idx))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
+def test_workload_parity(gpu, workload_operands, name):
+    import torch
+    w = workloads.by_name(name)
+    _say(f"[parity] {name}: generating operands m={w.m} n={w.n} k={w.k}")
+    Ah, Al, Bh, Bl = workload_operands(name)
+    m, n, k = w.m, w.n, w.k
+    rng = np.random.default_rng(2024 + w.index)
+    dA, dAl, dB, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
+
+    _say(f"[parity] {name}: slicing")
+    E, As = gpu.split_balanced(dA, dAl, 0)
+    F, Bs = gpu.split_balanced(dB, dBl, 1)
+    assert np.array_equal(_host(E), exact.balancing_exponents(Ah, Al, 0)), "row exponents"
+    assert np.array_equal(_host(F), exact.balancing_exponents(Bh, Bl, 1)), "column exponents"
+    rows = _sample_indices(rng, m, 6)
+    cols = _sample_indices(rng, n, 6)
+    if w.cancel_col0:
+        cols = np.union1d(cols, [0])
+    _, DA = exact.slice_rows(Ah, Al, rows)
+    _, DB = exact.slice_cols(Bh, Bl, cols)
+    from extended_precision_gemm_amd import layout
+    gotA = _unpacked(As, m, k, rows)
+    assert _bits_equal(gotA, exact.slice_values(DA)), "A slices"
+    gotB = _unpacked(Bs, n, k, cols)
+    assert _bits_equal(gotB, exact.slice_values(DB.transpose(0, 2, 1))), "B slices"
+
+    _say(f"[parity] {name}: level sums and cascade (sampled {len(rows)}x{len(cols)} block)")
+    levels = gpu.sliced_gemm(m, n, k, As, Bs)
+    S_ref = exact.level_values(exact.level_sums_units(DA, DB))
+    ri = torch.as_tensor(rows, device="cuda")
+    ci = torch.as_tensor(cols, device="cuda")
+    got_levels = _host(levels[:, ri][:, :, ci].contiguous())
+    assert _bits_equal(got_levels, S_ref), "level sums"
+    E_s = exact.balancing_exponents(Ah[rows], Al[rows], 0)
+    F_s = exact.balancing_exponents(Bh[:, cols], Bl[:, cols], 1)
+    Ch_ref, Cl_ref = exact.renorm_levels(S_ref, E_s, F_s)
+    Rh, Rl = gpu.renorm_levels(levels, E, F)
+    del levels
+    Fh, Fl = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F)
+    assert _bits_equal(_host(Fh), _host(Rh)) and _bits_equal(_host(Fl), _host(Rl)), "fused == two-step"
+    del Rh, Rl, As, Bs
+    torch.cuda.empty_cache()
+
+    _say(f"[parity] {name}: dd_gemm end to end")
+    Ch, Cl = gpu.dd_gemm(dA, dAl, dB, dBl)
+    hCh, hCl = _host(Ch), _host(Cl)
+    assert _bits_equal(hCh, _host(Fh)) and _bits_equal(hCl, _host(Fl)), "dd_gemm == stage calls"
+    sub_h = hCh[np.ix_(rows, cols)]
+    sub_l = hCl[np.ix_(rows, cols)]
+    assert _bits_equal(sub_h, Ch_ref) and _bits_equal(sub_l, Cl_ref), "sliced chain vs oracle"
+
+    if m * n * k <= 1024 ** 3:
+        _say(f"[parity] {name}: classical oracle, all {m * n} entries")
+        Rh, Rl, threads = native.dd_gemm(Ah, Al, Bh, Bl)
+        absAB = compare.abs_product(Ah, Bh)
+        ratio = compare.error_ratio(hCh, hCl, Rh, Rl, absAB)
+        eps = compare.eps_max(hCh, hCl, Rh, Rl)
+    else:
+        cnt = 2048
+        qr = rng.integers(0, m, cnt)
+        qc = rng.integers(0, n, cnt)
+        if w.cancel_col0:
+            qc[: cnt // 8] = 0
+        _say(f"[parity] {name}: classical oracle, {cnt} sampled entries")
+        Rh, Rl = native.dd_gemm_entries(Ah, Al, Bh, Bl, qr, qc)
+        absAB = compare.abs_product(Ah, Bh, qr, qc)
+        ratio = compare.error_ratio(hCh[qr, qc], hCl[qr, qc], Rh, Rl, absAB)
+        eps = compare.eps_max(hCh[qr, qc], hCl[qr, qc], Rh, Rl)
+    _say(f"[parity] {name}: max |C-C_ref|/(|A||B|) = {ratio:.3e} (log2 {math.log2(ratio) if ratio > 0 else -math.inf:.1f}), "
+         f"eps_max = {eps:.3e}")
+    assert ratio <= compare.TOL
+    if w.cancel_col0:
+        # row sums of C cancel down to sum_p a_ip * rho_p, rho_p the rounding
+        # residue of row p of B (math.fsum: correctly rounded sums of exact inputs)
+        rho = np.array([math.fsum(Bh[p].tolist() + Bl[p].tolist()) for p in range(k)])
+        for i in rows[:3]:
+            tot = math.fsum(hCh[i].tolist() + hCl[i].tolist())
+            expect = math.fsum((Ah[i] * rho).tolist() + (Al[i] * rho).tolist())
+            bound = compare.TOL * float(compare.abs_product(Ah[i:i + 1], Bh).sum())
+            _say(f"[parity] {name}: row {i}: sum_j C_ij = {tot:.3e}, expected {expect:.3e}, bound {bound:.3e}")
+            assert abs(tot - expect) <= bound
