@@ -78,10 +78,11 @@ def balancing_exponents(hi: np.ndarray, lo: np.ndarray | None, axis: int) -> np.
     lo = np.zeros_like(hi) if lo is None else np.asarray(lo, dtype=np.float64)
     s = hi + lo
     _, ex = np.frexp(s)
-    ex = np.where(s != 0.0, ex, np.iinfo(np.int64).min).astype(np.int64)
-    red = ex.max(axis=1 if axis == 0 else 0) if ex.size else np.zeros(
-        hi.shape[0] if axis == 0 else hi.shape[1], dtype=np.int64)
-    return np.where(red == np.iinfo(np.int64).min, 0, red).astype(np.int32)
+    none = np.int64(np.iinfo(np.int64).min)  # zero entries take no part in the maximum
+    ex = np.where(s != 0.0, ex.astype(np.int64), none)
+    red = ex.max(axis=1 if axis == 0 else 0) if ex.size else np.full(
+        hi.shape[0] if axis == 0 else hi.shape[1], none, dtype=np.int64)
+    return np.where(red == none, 0, red).astype(np.int32)
 
 
 # ---------------------------------------------------------------------------
@@ -133,7 +134,7 @@ def slice_cols(hi, lo, cols=None):
     return F, np.ascontiguousarray(Dt.transpose(0, 2, 1))
 
 
-def slice_values(D: np.ndarray, E) -> np.ndarray:
+def slice_values(D: np.ndarray) -> np.ndarray:
     """Unit-scaled slice values d_s * 2^(-13(s+1)) (the scale 2^E is kept apart)."""
     scale = np.array([2.0 ** (-DIGIT_BITS * (s + 1)) for s in range(N_SLICES)])
     return D.astype(np.float64) * scale.reshape((N_SLICES,) + (1,) * (D.ndim - 1))

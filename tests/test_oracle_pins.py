@@ -287,6 +287,22 @@ def test_balancing_exponents_bound_every_entry_tightly():
         assert all(v < Fraction(2) ** int(F[j]) for v in vals)
 
 
+def test_balancing_exponents_skip_zero_entries():
+    """Zeros take no part in the maximum: a row of small values keeps its own
+    (negative) exponent even next to a zero, and only an all-zero row gets 0."""
+    hi = np.array([[0.0, 0.25, 2.0 ** -40, 0.0],
+                   [0.0, 0.0, 0.0, 0.0],
+                   [-3.0 * 2.0 ** -1070, 0.0, 2.0 ** -1074, -0.0],
+                   [0.0, 0.75, -0.0, 1.0]])
+    lo = np.zeros_like(hi)
+    lo[3, 3] = -2.0 ** -60
+    assert exact.balancing_exponents(hi, lo, axis=0).tolist() == [-1, 0, -1068, 1]  # RN(1 - 2^-60) = 1
+    assert exact.balancing_exponents(hi, lo, axis=1).tolist() == [-1068, 0, -39, 1]
+    for i in range(4):
+        exps = [math.frexp(h + l)[1] for h, l in zip(hi[i], lo[i]) if h + l != 0.0]
+        assert exact.balancing_exponents(hi[i:i + 1], lo[i:i + 1], 0)[0] == (max(exps) if exps else 0)
+
+
 def test_slice_cols_is_slice_rows_of_transpose_with_column_exponents():
     rng = np.random.default_rng(11)
     Bh, Bl = _rand_dd_matrix(rng, (9, 5), "wide")
