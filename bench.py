@@ -176,11 +176,15 @@ def main():
         from oracle import compare, native
         threads = native.max_threads()
         print(f"[bench] cpu baseline: oracle on {threads} threads", file=sys.stderr, flush=True)
-        # calibrate on one row, then take as many leading rows as fit the budget
+        # calibrate on a few rows per thread (rows are the parallel dimension),
+        # then take as many leading rows as fit the time budget
+        native.dd_gemm(Ah[:1, :16], Al[:1, :16], Bh[:16], Bl[:16])  # start the thread pool
+        cal = min(m, 2 * threads)
         t = time.perf_counter()
-        native.dd_gemm(Ah[:1], Al[:1], Bh, Bl)
-        per_row = max(time.perf_counter() - t, 1e-4)
+        native.dd_gemm(Ah[:cal], Al[:cal], Bh, Bl)
+        per_row = max(time.perf_counter() - t, 1e-6) / cal
         rows = int(max(1, min(m, args.cpu_seconds / per_row)))
+        rows = max(threads, rows // threads * threads) if rows >= threads else rows
         t = time.perf_counter()
         Rh, Rl, used = native.dd_gemm(Ah[:rows], Al[:rows], Bh, Bl)
         t_cpu = time.perf_counter() - t

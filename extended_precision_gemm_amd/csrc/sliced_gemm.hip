@@ -23,9 +23,9 @@
 namespace ddg {
 namespace {
 
-// Result layout of the FP64 16x16x4 instruction (confirmed by the probe entry
-// point): lane L holds rows 4*(L/16) + v, v = 0..3, of column L % 16.
-__device__ __forceinline__ int frag_row(int lane, int v) { return 4 * (lane >> 4) + v; }
+// Result layout of the FP64 16x16x4 instruction, as measured with the probe
+// entry point on gfx950: lane L holds rows L/16 + 4v, v = 0..3, of column L % 16.
+__device__ __forceinline__ int frag_row(int lane, int v) { return (lane >> 4) + 4 * v; }
 __device__ __forceinline__ int frag_col(int lane) { return lane & 15; }
 
 template <int WM, int WN>

@@ -68,7 +68,8 @@ def _unpacked(packed, outer, k, rows=None):
 # ---------------------------------------------------------------------------
 def test_mfma_f64_lane_layout(gpu):
     """a-operand lane L holds A[L%16][L//16], b-operand lane L holds B[L//16][L%16],
-    result lane L holds D[4*(L//16)+v][L%16]: the layout the packing assumes."""
+    result lane L holds D[L//16 + 4v][L%16]: the layout the packing and the
+    result stores assume (measured on gfx950)."""
     out = _host(gpu.probe_mfma_f64())
     lanes = np.arange(64)
     A = np.zeros((16, 4))
@@ -76,7 +77,7 @@ def test_mfma_f64_lane_layout(gpu):
     A[lanes % 16, lanes // 16] = lanes + 1
     B[lanes // 16, lanes % 16] = 100.0 * (lanes + 1)
     D = A @ B
-    expect = np.array([[D[4 * (L // 16) + v, L % 16] for v in range(4)] for L in range(64)])
+    expect = np.array([[D[L // 16 + 4 * v, L % 16] for v in range(4)] for L in range(64)])
     assert np.array_equal(out, expect), out
 
 
@@ -140,15 +141,21 @@ def test_split_bit_exact_small(gpu, m, n, k):
         assert np.all(full[mask].view(np.int64) == 0)
 
 
-def test_split_all_max_digits(gpu):
-    """x = 1 - 2^-104 at E = 0 has every digit 8191 (hi = 1 - 2^-53, lo = 2^-53 - 2^-104)."""
-    hi = np.full((3, 40), 1.0 - 2.0 ** -53)
-    lo = np.full((3, 40), 2.0 ** -53 - 2.0 ** -104)
+# The largest window integer any entry can have: RN(hi + lo) < 2^E forces
+# |x| < 2^E (1 - 2^-54), so N <= 2^104 - 2^50 - 1, digits 8191 except 6143 in slice 4.
+MAX_HI, MAX_LO = 1.0 - 2.0 ** -53, 2.0 ** -54 - 2.0 ** -104
+MAX_DIGITS = [8191, 8191, 8191, 8191, 6143, 8191, 8191, 8191]
+
+
+def test_split_largest_digits(gpu):
+    hi = np.full((3, 40), MAX_HI)
+    lo = np.full((3, 40), MAX_LO)
+    assert exact.slice_entry(MAX_HI, MAX_LO, 0) == MAX_DIGITS
     E, packed, outer, k = _gpu_split(gpu, hi, lo, 0)
     assert _host(E).tolist() == [0, 0, 0]
     got = _unpacked(packed, outer, k)
     for s in range(8):
-        assert np.all(got[s] == 8191 * 2.0 ** (-13 * (s + 1)))
+        assert np.all(got[s] == MAX_DIGITS[s] * 2.0 ** (-13 * (s + 1)))
 
 
 # ---------------------------------------------------------------------------
@@ -190,18 +197,16 @@ def test_sliced_chain_bit_exact_small(gpu, m, n, k):
 
 
 def test_level_sums_exact_at_the_bound(gpu):
-    """Every digit 8191 and k = 8192: level 7 reaches 8 * 8192 * 8191^2 ~ 2^42 units, exactly."""
+    """Largest digits everywhere and k = 8192: level sums reach ~2^42 units, exactly."""
     m, n, k = 32, 48, 8192
-    Ah = np.full((m, k), 1.0 - 2.0 ** -53)
-    Al = np.full((m, k), 2.0 ** -53 - 2.0 ** -104)
-    Bh = np.full((k, n), -(1.0 - 2.0 ** -53))
-    Bl = np.full((k, n), -(2.0 ** -53 - 2.0 ** -104))
+    Ah = np.full((m, k), MAX_HI)
+    Al = np.full((m, k), MAX_LO)
     E, As = gpu.split_balanced(_dev(Ah), _dev(Al), 0)
-    F, Bs = gpu.split_balanced(_dev(Bh), _dev(Bl), 1)
+    F, Bs = gpu.split_balanced(_dev(np.full((k, n), -MAX_HI)), _dev(np.full((k, n), -MAX_LO)), 1)
     levels = _host(gpu.sliced_gemm(m, n, k, As, Bs))
     for l in range(8):
-        expect = -(l + 1) * k * 8191 ** 2
-        assert np.all(levels[l] * 2.0 ** (13 * (l + 2)) == expect)
+        expect = -k * sum(MAX_DIGITS[s] * MAX_DIGITS[l - s] for s in range(l + 1))
+        assert np.all(levels[l] * 2.0 ** (13 * (l + 2)) == expect), l
 
 
 # ---------------------------------------------------------------------------
