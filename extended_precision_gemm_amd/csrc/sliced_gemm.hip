@@ -10,15 +10,16 @@
 // is exact and every partial sum is an integer multiple of 2^(-13(l+2)) below
 // 2^53 units: the matrix-core accumulation is exact in any order.
 //
-// Work split: a workgroup of 8 waves (two per SIMD) owns a 64x64 output tile;
-// wave w computes the 32x16 strip at block row 2*(w/4), block column w%4, with
-// eight level accumulators per 16x16 block.  The operand panels move through
-// LDS in stages of one k-block (4 values of k): every (16x4 or 4x16) fragment of
-// one slice is 64 consecutive doubles in the packed planes, so a stage of the
-// tile is 8 contiguous 4 KB runs, copied with 16-byte direct-to-LDS loads and
-// read back by the waves as conflict-free 8-byte-per-lane fragment reads.
-// NBUF stages are in flight; one barrier per stage.  Two waves per SIMD keep the
-// matrix pipe fed while the other waits on LDS or the barrier.
+// Work split: each wave computes a 32x16 strip (two 16x16 blocks stacked) with
+// eight level accumulators per block; a workgroup of WM x WN waves owns a
+// (32 WM) x (16 WN) output tile, and WGS workgroups share a CU (two waves per
+// SIMD in every configuration).  The operand panels move through LDS in stages
+// of KS k-blocks (4 values of k each): every (16x4 or 4x16) fragment of one
+// slice is 64 consecutive doubles in the packed planes, so a stage of one
+// 16-row (16-column) block is a contiguous KS x 4 KB run, copied with 16-byte
+// direct-to-LDS loads and read back by the waves as conflict-free
+// 8-byte-per-lane fragment reads straight into the matrix-instruction operand
+// registers.  NBUF stages are in flight; one workgroup barrier per stage.
 #include "common.hpp"
 #include "eft.hpp"
 
@@ -33,94 +34,117 @@ __device__ __forceinline__ int frag_col(int lane) { return lane & 15; }
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_void_t;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kTileBlocks = 4;                                  // 64x64 tile = 4x4 blocks
-constexpr int kStageDoubles = 2 * kTileBlocks * kFragSetDoubles;  // 4096 doubles = 32 KB
-constexpr int kPiecesPerWave = kStageDoubles / (kWaves * 128);  // 1 KB pieces per wave per stage
-
 // Order the compiler's memory operations around a hardware barrier or wait
 // without adding any instruction.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-template <int NBUF, bool FUSED>
-__global__ void __launch_bounds__(kThreads, 1)
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int WM, int WN, int KS, int NBUF, int WGS>
+struct GemmConfig {
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kNBuf = NBUF;
+    static constexpr int kWGS = WGS;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int kTBM = 2 * WM;                              // 16-row blocks per tile
+    static constexpr int kTBN = WN;                                  // 16-column blocks per tile
+    static constexpr int kBlockStage = KS * kFragSetDoubles;         // one block, one stage
+    static constexpr int kStageDoubles = (kTBM + kTBN) * kBlockStage;
+    static constexpr int kPiecesPerBlock = kBlockStage / 128;        // 1 KB pieces
+    static constexpr int kPieces = (kTBM + kTBN) * kPiecesPerBlock;
+    static constexpr int kPiecesPerWave = kPieces / kWaves;
+    static_assert(kPieces % kWaves == 0, "pieces split evenly over the waves");
+    static_assert(NBUF >= 2 && WGS * NBUF * kStageDoubles * 8 <= 160 * 1024, "LDS budget");
+    static_assert(kPackOuter % (16 * kTBM) == 0 && kPackOuter % (16 * kTBN) == 0, "tile divides the packing");
+    static_assert(kPackK % (4 * KS) == 0, "stage divides the k packing");
+};
+
+template <class C, bool FUSED>
+__global__ void __launch_bounds__(C::kThreads, C::kWGS)
 sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                    const double* __restrict__ Ap, const double* __restrict__ Bp,
                    double* __restrict__ levels, int64_t ldl, int64_t plane,
                    const int32_t* __restrict__ E, const int32_t* __restrict__ F,
                    double* __restrict__ C_hi, double* __restrict__ C_lo, int64_t ldc) {
-    static_assert(NBUF >= 2 && NBUF <= 4, "stages in flight");
-    __shared__ __attribute__((aligned(1024))) double lds[NBUF * kStageDoubles];
+    constexpr int KS = C::kBlockStage / kFragSetDoubles;
+    constexpr int NBUF = C::kNBuf;
+    __shared__ __attribute__((aligned(1024))) double lds[NBUF * C::kStageDoubles];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wr = wave >> 2;  // block rows 2*wr, 2*wr+1 of the tile
-    const int wc = wave & 3;   // block column wc of the tile
+    const int wr = wave / C::kTBN;  // block rows 2*wr, 2*wr+1 of the tile
+    const int wc = wave % C::kTBN;  // block column wc of the tile
     const int64_t tm = static_cast<int64_t>(blockIdx.x) / tiles_n;
     const int64_t tn = static_cast<int64_t>(blockIdx.x) % tiles_n;
-    const int64_t rb0 = tm * kTileBlocks, cb0 = tn * kTileBlocks;
+    const int64_t rb0 = tm * C::kTBM, cb0 = tn * C::kTBN;
+    const int64_t NS = KB / KS;  // KB is a multiple of 4 (k is packed to 16)
 
-    // A stage is 32 pieces of 1 KB: pieces 0-15 are the A panel (block b = q/4,
-    // quarter q%4 of its 4 KB fragment set), 16-31 the B panel.  Wave w copies
-    // pieces w, w+8, w+16, w+24; lane L moves bytes [16L, 16L+16) of a piece.
-    const double* src[kPiecesPerWave];
-    int dst[kPiecesPerWave];
+    // Piece q of a stage: block q / kPiecesPerBlock of the stage (A blocks
+    // first, then B blocks), 1 KB piece q % kPiecesPerBlock of that block's run.
+    // Wave w copies pieces w, w + waves, ...; lane L moves bytes [16L, 16L+16).
+    const double* src[C::kPiecesPerWave];
+    int dst[C::kPiecesPerWave];
 #pragma unroll
-    for (int i = 0; i < kPiecesPerWave; ++i) {
-        const int q = i * kWaves + wave;
-        const int op = q >> 4, blk = (q >> 2) & 3, quarter = q & 3;
-        const double* base = op == 0 ? Ap + (rb0 + blk) * KB * kFragSetDoubles
-                                      : Bp + (cb0 + blk) * KB * kFragSetDoubles;
-        src[i] = base + quarter * 128 + lane * 2;
-        dst[i] = op * (kTileBlocks * kFragSetDoubles) + blk * kFragSetDoubles + quarter * 128;
+    for (int i = 0; i < C::kPiecesPerWave; ++i) {
+        const int q = i * C::kWaves + wave;
+        const int blk = q / C::kPiecesPerBlock, pc = q % C::kPiecesPerBlock;
+        const double* base = blk < C::kTBM ? Ap + (rb0 + blk) * KB * kFragSetDoubles
+                                           : Bp + (cb0 + blk - C::kTBM) * KB * kFragSetDoubles;
+        src[i] = base + pc * 128 + lane * 2;
+        dst[i] = blk * C::kBlockStage + pc * 128;
     }
-    auto issue = [&](int64_t kb, int buf) {
+    auto issue = [&](int64_t st, int buf) {
 #pragma unroll
-        for (int i = 0; i < kPiecesPerWave; ++i)
-            __builtin_amdgcn_global_load_lds(
-                (global_void_t*)(src[i] + kb * kFragSetDoubles),
-                (lds_void_t*)(lds + buf * kStageDoubles + dst[i]), 16, 0, 0);
+        for (int i = 0; i < C::kPiecesPerWave; ++i)
+            __builtin_amdgcn_global_load_lds((global_void_t*)(src[i] + st * C::kBlockStage),
+                                             (lds_void_t*)(lds + buf * C::kStageDoubles + dst[i]), 16, 0, 0);
     };
 
     double4_t acc[kLevels][2];
 #pragma unroll
     for (int l = 0; l < kLevels; ++l) acc[l][0] = acc[l][1] = double4_t{0.0, 0.0, 0.0, 0.0};
 
-    if (KB > 0) {
+    if (NS > 0) {
 #pragma unroll
-        for (int j = 0; j < NBUF - 1; ++j) issue(j < KB ? j : KB - 1, j);
-        for (int64_t kb = 0; kb < KB; ++kb) {
-            // Stage kb has landed once at most NBUF-2 younger stages are pending.
-            if constexpr (NBUF == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            else if constexpr (NBUF == 3) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int j = 0; j < NBUF - 1; ++j) issue(j < NS ? j : NS - 1, j);
+        for (int64_t st = 0; st < NS; ++st) {
+            // Stage st has landed once at most NBUF-2 younger stages are pending.
+            wait_vmcnt<(NBUF - 2) * C::kPiecesPerWave>();
             compiler_fence();
-            __builtin_amdgcn_s_barrier();  // every wave's copy of stage kb is in LDS, and
-            compiler_fence();               // every wave is done reading stage kb-1
-            const int64_t nxt = kb + NBUF - 1;
-            issue(nxt < KB ? nxt : KB - 1, static_cast<int>(nxt % NBUF));
+            __builtin_amdgcn_s_barrier();  // every wave's copy of stage st is in LDS, and
+            compiler_fence();               // every wave is done reading stage st-1
+            const int64_t nxt = st + NBUF - 1;
+            issue(nxt < NS ? nxt : NS - 1, static_cast<int>(nxt % NBUF));
 
-            const double* sa = lds + (kb % NBUF) * kStageDoubles + (2 * wr) * kFragSetDoubles + lane;
-            const double* sb = lds + (kb % NBUF) * kStageDoubles + (kTileBlocks + wc) * kFragSetDoubles + lane;
-            double a[kSlices][2], b[kSlices];
+            const double* stage = lds + (st % NBUF) * C::kStageDoubles + lane;
 #pragma unroll
-            for (int s = 0; s < kSlices; ++s) {
-                a[s][0] = sa[s * kFragDoubles];
-                a[s][1] = sa[kFragSetDoubles + s * kFragDoubles];
-                b[s] = sb[s * kFragDoubles];
+            for (int j = 0; j < KS; ++j) {
+                const double* sa = stage + (2 * wr) * C::kBlockStage + j * kFragSetDoubles;
+                const double* sb = stage + (C::kTBM + wc) * C::kBlockStage + j * kFragSetDoubles;
+                double a[kSlices][2], b[kSlices];
+#pragma unroll
+                for (int s = 0; s < kSlices; ++s) {
+                    a[s][0] = sa[s * kFragDoubles];
+                    a[s][1] = sa[C::kBlockStage + s * kFragDoubles];
+                    b[s] = sb[s * kFragDoubles];
+                }
+                // Triangular schedule: pair (s, t) feeds level s + t.
+#pragma unroll
+                for (int s = 0; s < kSlices; ++s)
+#pragma unroll
+                    for (int t = 0; s + t < kLevels; ++t)
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+                            acc[s + t][r] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s][r], b[t], acc[s + t][r], 0, 0, 0);
             }
-            // Triangular schedule: pair (s, t) feeds level s + t.
-#pragma unroll
-            for (int s = 0; s < kSlices; ++s)
-#pragma unroll
-                for (int t = 0; s + t < kLevels; ++t)
-#pragma unroll
-                    for (int r = 0; r < 2; ++r)
-                        acc[s + t][r] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s][r], b[t], acc[s + t][r], 0, 0, 0);
         }
         // No direct-to-LDS copy may still be in flight when the workgroup ends.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vmcnt<0>();
     }
 
     const int64_t col = (cb0 + wc) * 16 + frag_col(lane);
@@ -176,7 +200,20 @@ __global__ void __launch_bounds__(64) probe_mfma_kernel(double* __restrict__ out
     for (int v = 0; v < 4; ++v) out[lane * 4 + v] = c[v];
 }
 
-constexpr int kNBuf = 4;  // stages in flight
+// Launch configuration: 32x16 wave strips, WM x WN waves per workgroup,
+// KS k-blocks per stage, NBUF stages, WGS workgroups per CU.
+#ifndef DDGEMM_CFG
+#define DDGEMM_CFG 0
+#endif
+#if DDGEMM_CFG == 0
+using Cfg = GemmConfig<2, 4, 2, 2, 1>;  // 64x64 tile, 8 waves, one workgroup per CU
+#elif DDGEMM_CFG == 1
+using Cfg = GemmConfig<2, 2, 1, 3, 2>;  // 64x32 tile, 4 waves, two workgroups per CU
+#elif DDGEMM_CFG == 2
+using Cfg = GemmConfig<1, 4, 1, 3, 2>;  // 32x64 tile, 4 waves, two workgroups per CU
+#elif DDGEMM_CFG == 3
+using Cfg = GemmConfig<2, 2, 2, 2, 1>;  // 64x32 tile, 4 waves, 2 k-blocks per stage (96 KB: one per CU)
+#endif
 
 }  // namespace
 
@@ -186,17 +223,16 @@ hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_s
                               int64_t ldc, bool fused, hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
     const PackGeom ga(m, k);
-    constexpr int BM = kTileBlocks * 16, BN = kTileBlocks * 16;
-    static_assert(kPackOuter % BM == 0 && kPackOuter % BN == 0, "tile must divide the packing");
+    constexpr int BM = Cfg::kTBM * 16, BN = Cfg::kTBN * 16;
     const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
     const int64_t tiles = tiles_m * tiles_n;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int64_t plane = m * ldl;
     if (fused)
-        sliced_gemm_kernel<kNBuf, true><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(
+        sliced_gemm_kernel<Cfg, true><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
             m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, 0, 0, E, F, C_hi, C_lo, ldc);
     else
-        sliced_gemm_kernel<kNBuf, false><<<static_cast<unsigned>(tiles), kThreads, 0, stream>>>(
+        sliced_gemm_kernel<Cfg, false><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
             m, n, ga.KB, tiles_n, A_slices, B_slices, levels, ldl, plane, nullptr, nullptr, nullptr, nullptr, 0);
     return hipGetLastError();
 }
