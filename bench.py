@@ -38,6 +38,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dd4096_exp20")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-epilogue", action="store_true", help="skip the stand-alone renormalisation timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (HBM counter calibration)")
@@ -171,6 +172,30 @@ def main():
             "gemm_ms": round(gemm_ms, 4),
         },
     }
+
+    # The stand-alone renormalisation (dd_renorm_levels, the stage entry point the
+    # fused path does not use), timed on its own outside the timed region:
+    # 64 B of level sums read + 16 B of (hi, lo) written per output.
+    if not args.no_epilogue:
+        levels = ddg.sliced_gemm(m, n, k, As, Bs)
+        R_hi = torch.empty_like(C_hi)
+        R_lo = torch.empty_like(C_lo)
+        ddg.renorm_levels(levels, E, F, R_hi, R_lo, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            ddg.renorm_levels(levels, E, F, R_hi, R_lo, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ren_ms = e0.elapsed_time(e1) / reps
+        same = bool(torch.equal(R_hi.view(torch.int64), C_hi.view(torch.int64)) and
+                    torch.equal(R_lo.view(torch.int64), C_lo.view(torch.int64)))
+        rec["stages"]["renorm_standalone_ms"] = round(ren_ms, 4)
+        rec["stages"]["renorm_GBps"] = round(80.0 * m * n / (ren_ms * 1e-3) / 1e9, 1)
+        rec["stages"]["renorm_frac_hbm"] = round(80.0 * m * n / (ren_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        rec["stages"]["renorm_matches_fused"] = same
+        del levels, R_hi, R_lo
 
     if not args.no_cpu_baseline:
         from oracle import compare, native

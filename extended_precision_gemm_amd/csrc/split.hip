@@ -193,6 +193,110 @@ __global__ void __launch_bounds__(256) slice_kernel(int64_t outer, int64_t k, in
     }
 }
 
+// One workgroup per 16-row (AXIS 0) or 16-column (AXIS 1) block: first the
+// block's balancing exponents, then its slices, so the second read of the
+// block's (hi, lo) comes from cache rather than HBM and no atomics are needed.
+template <int AXIS, int NT>
+__global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t k, int64_t KB,
+                                                         const double* __restrict__ hi,
+                                                         const double* __restrict__ lo, int64_t ld,
+                                                         int32_t* __restrict__ exps,
+                                                         double* __restrict__ slices) {
+    constexpr int kWavesPerBlock = NT / 64;
+    constexpr int kRowsPerWave = 16 / kWavesPerBlock;  // AXIS 0
+    constexpr int kRowGroups = NT / 16;                // AXIS 1
+    __shared__ int codes[NT];
+    __shared__ int block_exp[16];
+    const int t = threadIdx.x;
+    const int64_t o0 = static_cast<int64_t>(blockIdx.x) * 16;
+
+    // Phase 1: exponents of the block's 16 rows/columns.
+    if (AXIS == 0) {
+        // each wave scans kRowsPerWave rows; lane L takes k indices L, L+64, ...
+        const int lane = t & 63, w = t >> 6;
+#pragma unroll 1
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            const int64_t o = o0 + kRowsPerWave * w + i;
+            int c = kNoExp;
+            if (o < outer) {
+                const double* h = hi + o * ld;
+                const double* l = lo ? lo + o * ld : nullptr;
+                int64_t p = lane;
+                for (; p + 192 < k; p += 256) {
+                    double xh[4], xl[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        xh[u] = h[p + 64 * u];
+                        xl[u] = l ? l[p + 64 * u] : 0.0;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) c = max(c, entry_exp_code(xh[u], xl[u]));
+                }
+                for (; p < k; p += 64) c = max(c, entry_exp_code(h[p], l ? l[p] : 0.0));
+            }
+            c = wave_max(c);
+            if (lane == 0) block_exp[kRowsPerWave * w + i] = decode_exp(c);
+        }
+    } else {
+        // thread t takes column o0 + t % 16 over rows t / 16, t / 16 + kRowGroups, ...
+        const int j = t & 15;
+        const int64_t o = o0 + j;
+        int code = kNoExp;
+        if (o < outer) {
+            int64_t p = t >> 4;
+            for (; p + 3 * kRowGroups < k; p += 4 * kRowGroups) {
+                double xh[4], xl[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    xh[u] = hi[(p + kRowGroups * u) * ld + o];
+                    xl[u] = lo ? lo[(p + kRowGroups * u) * ld + o] : 0.0;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) code = max(code, entry_exp_code(xh[u], xl[u]));
+            }
+            for (; p < k; p += kRowGroups) code = max(code, entry_exp_code(hi[p * ld + o], lo ? lo[p * ld + o] : 0.0));
+        }
+        codes[t] = code;
+        __syncthreads();
+        if (t < 16) {
+            int c = kNoExp;
+            for (int g = 0; g < kRowGroups; ++g) c = max(c, codes[g * 16 + t]);
+            block_exp[t] = decode_exp(c);
+        }
+    }
+    __syncthreads();
+    if (t < 16 && o0 + t < outer) exps[o0 + t] = block_exp[t];
+
+    // Phase 2: slices, two neighbouring packed lanes (entries o, o+1 at one p) per
+    // thread and one 16-byte store per slice.
+    const int64_t pairs = KB * 32;
+    for (int64_t q = t; q < pairs; q += NT) {
+        const int64_t kb = q >> 5;
+        const int lane = static_cast<int>(q & 31) * 2;
+        const int oi = lane & 15;
+        const int64_t p = kb * 4 + (lane >> 4);
+        double sl0[kSlices], sl1[kSlices];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int64_t o = o0 + oi + e;
+            double x_hi = 0.0, x_lo = 0.0;
+            if (o < outer && p < k) {
+                const int64_t idx = AXIS == 0 ? o * ld + p : p * ld + o;
+                x_hi = hi[idx];
+                x_lo = lo ? lo[idx] : 0.0;
+            }
+            slice_entry(x_hi, x_lo, block_exp[oi + e], e == 0 ? sl0 : sl1);
+        }
+        double2* dst = reinterpret_cast<double2*>(slices + (static_cast<int64_t>(blockIdx.x) * KB + kb) * kFragSetDoubles + lane);
+#pragma unroll
+        for (int s = 0; s < kSlices; ++s) dst[s * (kFragDoubles / 2)] = make_double2(sl0[s], sl1[s]);
+    }
+}
+
+// Blocks needed before the one-pass block kernel beats two streaming passes
+// (measured: 4096 blocks of k = 512 win, 256 blocks of k = 4096 lose).
+constexpr int64_t kFusedMinBlocks = 1024;
+
 inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap) {
     int64_t g = (work + per_block - 1) / per_block;
     if (g < 1) g = 1;
@@ -207,6 +311,19 @@ hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const do
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     if (outer == 0) return hipSuccess;
+    const PackGeom g(outer, k);
+    constexpr int kBlockThreads = 1024;
+    if (g.doubles() > 0 && g.RB >= kFusedMinBlocks) {
+        // Enough 16-row/16-column blocks to fill the chip: one pass per block.
+        if (axis == 0)
+            split_block_kernel<0, kBlockThreads><<<static_cast<unsigned>(g.RB), kBlockThreads, 0, stream>>>(
+                outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
+        else
+            split_block_kernel<1, kBlockThreads><<<static_cast<unsigned>(g.RB), kBlockThreads, 0, stream>>>(
+                outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
+        return hipGetLastError();
+    }
+    // Otherwise two passes over the operand: exponents, then slices.
     if (axis == 0) {
         exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X_hi, X_lo, ldx, exps);
     } else {
@@ -222,7 +339,6 @@ hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const do
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const PackGeom g(outer, k);
     if (g.doubles() == 0) return hipSuccess;
     const int64_t total = g.RB * g.KB * kFragDoubles;
     const unsigned grid = grid_for(total, 256, 1 << 20);

@@ -141,6 +141,28 @@ def test_split_bit_exact_small(gpu, m, n, k):
         assert np.all(full[mask].view(np.int64) == 0)
 
 
+@pytest.mark.parametrize("axis", [0, 1])
+def test_split_block_path_bit_exact(gpu, axis):
+    """Operands with >= 1024 blocks of 16 rows (columns) take the one-pass block
+    kernel; ragged outer size, short k and the edge values of the small tests."""
+    rng = np.random.default_rng(55 + axis)
+    outer, k = 16500, 37
+    hi, lo = _edge_matrix(rng, outer, k)
+    hi[200:216, :] = 0.0
+    lo[200:216, :] = 0.0                      # a whole all-zero 16-row block
+    if axis == 1:
+        hi, lo = np.ascontiguousarray(hi.T), np.ascontiguousarray(lo.T)
+    E, packed, outer_, k_ = _gpu_split(gpu, hi, lo, axis)
+    assert (outer_, k_) == (outer, k)
+    if axis == 0:
+        E_ref, D = exact.slice_rows(hi, lo)
+    else:
+        E_ref, D = exact.slice_cols(hi, lo)
+        D = D.transpose(0, 2, 1)
+    assert np.array_equal(_host(E), E_ref)
+    assert _bits_equal(_unpacked(packed, outer, k), exact.slice_values(D))
+
+
 # The largest window integer any entry can have: RN(hi + lo) < 2^E forces
 # |x| < 2^E (1 - 2^-54), so N <= 2^104 - 2^50 - 1, digits 8191 except 6143 in slice 4.
 MAX_HI, MAX_LO = 1.0 - 2.0 ** -53, 2.0 ** -54 - 2.0 ** -104
