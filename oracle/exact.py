@@ -15,17 +15,19 @@ Exact references for every intermediate of the sliced double-double product
 
 Readings of points the pages leave open (each one is listed in the design doc):
 
-* A double-double x = hi + lo is cut as a 104-bit fixed-point window below a
-  balancing exponent E with |hi + lo| < 2^E: N = floor(|hi + lo| * 2^(104-E)),
-  digit s = bits [13(7-s), 13(7-s)+13) of N, slice s = sign * digit * 2^(-13(s+1)).
-  Eight slices sit at relative exponents 0, -13, ..., -91 (the pages' quarters at
-  0, -13, -26, -39 for hi, continued for lo).  Truncation toward zero, as the
-  pages' bit fields are.
+* A double-double x = hi + lo is cut as a 13n-bit fixed-point window below a
+  balancing exponent E with |hi + lo| < 2^E: N = floor(|hi + lo| * 2^(13n-E)),
+  digit s = bits [13(n-1-s), 13(n-1-s)+13) of N, slice s = sign * digit *
+  2^(-13(s+1)), for n slices.  n = 8 (a 104-bit window, §2 eq. (4)) is the
+  double-double product; n = 4 is the pages' four quarters of a leading double
+  (§2 eqs. (1)-(3)); the number of slices is a parameter (default 8).  Slices sit
+  at relative exponents 0, -13, ... (the pages' quarters at 0, -13, -26, -39 for
+  hi, continued for lo).  Truncation toward zero, as the pages' bit fields are.
 * E for a row of A (column of B) is the largest frexp exponent of RN(hi + lo)
   over its nonzero entries, 0 when all are zero.
-* Level l collects the pairs s + t = l for l = 0..7 (36 pairs); pairs below the
-  double-double window (s + t >= 8) are not formed.
-* The cascade starts from the smallest level: (h, t) = (S_7, 0); for l = 6..0:
+* Level l collects the pairs s + t = l for l = 0..n-1 (n(n+1)/2 pairs, 36 for
+  n = 8); pairs below the window (s + t >= n) are not formed.
+* The cascade starts from the smallest level: (h, t) = (S_{n-1}, 0); for l = n-2..0:
   (s, e) = TwoSum(h, S_l), t = t + e, (h, t) = TwoSum(s, t); then both words are
   scaled by 2^(E_i + F_j).
 
@@ -88,28 +90,28 @@ def balancing_exponents(hi: np.ndarray, lo: np.ndarray | None, axis: int) -> np.
 # ---------------------------------------------------------------------------
 # slicing
 # ---------------------------------------------------------------------------
-def window_integer(hi: float, lo: float, E: int) -> tuple[int, int]:
-    """(sign, N) with N = floor(|hi + lo| * 2^(104 - E)), sign in {-1, 0, 1}."""
+def window_integer(hi: float, lo: float, E: int, nslices: int = N_SLICES) -> tuple[int, int]:
+    """(sign, N) with N = floor(|hi + lo| * 2^(13 nslices - E)), sign in {-1, 0, 1}."""
     H = double_to_scaled_int(hi)
     L = double_to_scaled_int(lo)
     V = H + L  # (hi + lo) * 2^1074, exact
     sign = (V > 0) - (V < 0)
-    shift = WINDOW_BITS - E - _SCALE_BITS  # N = floor(|V| * 2^shift)
+    shift = DIGIT_BITS * nslices - E - _SCALE_BITS  # N = floor(|V| * 2^shift)
     a = abs(V)
     N = a << shift if shift >= 0 else a >> (-shift)
     return sign, N
 
 
-def slice_entry(hi: float, lo: float, E: int) -> list[int]:
-    """Signed 13-bit digits d_0..d_7 of one entry; slice s = d_s * 2^(E - 13(s+1))."""
-    sign, N = window_integer(hi, lo, E)
-    if N >= 1 << WINDOW_BITS:
+def slice_entry(hi: float, lo: float, E: int, nslices: int = N_SLICES) -> list[int]:
+    """Signed 13-bit digits d_0..d_{n-1} of one entry; slice s = d_s * 2^(E - 13(s+1))."""
+    sign, N = window_integer(hi, lo, E, nslices)
+    if N >= 1 << (DIGIT_BITS * nslices):
         raise ValueError("balancing exponent too small for this entry")
-    return [sign * ((N >> (DIGIT_BITS * (N_SLICES - 1 - s))) & DIGIT_MASK)
-            for s in range(N_SLICES)]
+    return [sign * ((N >> (DIGIT_BITS * (nslices - 1 - s))) & DIGIT_MASK)
+            for s in range(nslices)]
 
 
-def slice_rows(hi, lo, rows=None):
+def slice_rows(hi, lo, rows=None, nslices: int = N_SLICES):
     """Slice the A operand (per-row exponents).
 
     Returns (E, D) with E[r] for the selected rows and D[s, r, k] the signed
@@ -119,25 +121,26 @@ def slice_rows(hi, lo, rows=None):
     lo = np.zeros_like(hi) if lo is None else np.asarray(lo, dtype=np.float64)
     rows = range(hi.shape[0]) if rows is None else list(rows)
     E = balancing_exponents(hi[rows, :], lo[rows, :], axis=0)
-    D = np.zeros((N_SLICES, len(rows), hi.shape[1]), dtype=np.int64)
+    D = np.zeros((nslices, len(rows), hi.shape[1]), dtype=np.int64)
     for r, i in enumerate(rows):
         for p in range(hi.shape[1]):
-            D[:, r, p] = slice_entry(hi[i, p], lo[i, p], int(E[r]))
+            D[:, r, p] = slice_entry(hi[i, p], lo[i, p], int(E[r]), nslices)
     return E, D
 
 
-def slice_cols(hi, lo, cols=None):
+def slice_cols(hi, lo, cols=None, nslices: int = N_SLICES):
     """Slice the B operand (per-column exponents); D[t, k, c] for the selected columns."""
     hi = np.asarray(hi, dtype=np.float64)
     lo = np.zeros_like(hi) if lo is None else np.asarray(lo, dtype=np.float64)
-    F, Dt = slice_rows(hi.T, lo.T, cols)
+    F, Dt = slice_rows(hi.T, lo.T, cols, nslices)
     return F, np.ascontiguousarray(Dt.transpose(0, 2, 1))
 
 
 def slice_values(D: np.ndarray) -> np.ndarray:
     """Unit-scaled slice values d_s * 2^(-13(s+1)) (the scale 2^E is kept apart)."""
-    scale = np.array([2.0 ** (-DIGIT_BITS * (s + 1)) for s in range(N_SLICES)])
-    return D.astype(np.float64) * scale.reshape((N_SLICES,) + (1,) * (D.ndim - 1))
+    n = D.shape[0]
+    scale = np.array([2.0 ** (-DIGIT_BITS * (s + 1)) for s in range(n)])
+    return D.astype(np.float64) * scale.reshape((n,) + (1,) * (D.ndim - 1))
 
 
 def reconstruct_entry(digits, E: int) -> Fraction:
@@ -150,15 +153,17 @@ def reconstruct_entry(digits, E: int) -> Fraction:
 # level sums
 # ---------------------------------------------------------------------------
 def level_sums_units(DA: np.ndarray, DB: np.ndarray) -> np.ndarray:
-    """S[l] = sum_{s+t=l} DA[s] @ DB[t] in integer units, l = 0..7.
+    """S[l] = sum_{s+t=l} DA[s] @ DB[t] in integer units, l = 0..n-1 for n slices.
 
     DA[s] is m×k, DB[t] is k×n (int64 digits).  Level l has weight
     2^(E_i + F_j - 13(l+2)).  Every term fits in int64 for k < 2^21.
     """
+    nl = DA.shape[0]
+    assert DB.shape[0] == nl
     m, k = DA.shape[1], DA.shape[2]
     n = DB.shape[2]
-    S = np.zeros((N_LEVELS, m, n), dtype=np.int64)
-    for l in range(N_LEVELS):
+    S = np.zeros((nl, m, n), dtype=np.int64)
+    for l in range(nl):
         for s in range(l + 1):
             S[l] += DA[s] @ DB[l - s]
     return S
@@ -169,7 +174,7 @@ def level_values(S_units: np.ndarray) -> np.ndarray:
     if np.abs(S_units).max(initial=0) >= 2 ** 53:
         raise ValueError("level sum exceeds 53 bits")
     out = S_units.astype(np.float64)
-    for l in range(N_LEVELS):
+    for l in range(S_units.shape[0]):
         out[l] *= 2.0 ** (-DIGIT_BITS * (l + 2))
     return out
 
@@ -187,15 +192,16 @@ def two_sum(a, b):
 
 
 def renorm_levels(S: np.ndarray, E, F):
-    """Cascade the 8 unit-scaled level planes S[l] (m×n) into (C_hi, C_lo).
+    """Cascade the unit-scaled level planes S[l] (m×n), l = 0..n-1, into (C_hi, C_lo).
 
     E (length m) and F (length n) are the balancing exponents of A's rows and
     B's columns.  Smallest level first, as described in the module docstring.
     """
     S = np.asarray(S, dtype=np.float64)
-    h = S[N_LEVELS - 1].copy()
+    nl = S.shape[0]
+    h = S[nl - 1].copy()
     t = np.zeros_like(h)
-    for l in range(N_LEVELS - 2, -1, -1):
+    for l in range(nl - 2, -1, -1):
         s, e = two_sum(h, S[l])
         t = t + e
         h, t = two_sum(s, t)
@@ -206,7 +212,7 @@ def renorm_levels(S: np.ndarray, E, F):
 def level_target(S_units: np.ndarray, E: int, F: int, i: int, j: int) -> Fraction:
     """Exact value sum_l S_units[l][i,j] * 2^(E + F - 13(l+2)) of one output entry."""
     return sum((Fraction(int(S_units[l, i, j])) * Fraction(2) ** (E + F - DIGIT_BITS * (l + 2))
-                for l in range(N_LEVELS)), Fraction(0))
+                for l in range(S_units.shape[0])), Fraction(0))
 
 
 # ---------------------------------------------------------------------------
@@ -226,3 +232,35 @@ def exact_entries(A_hi, A_lo, B_hi, B_lo, rows, cols) -> list[Fraction]:
     A_lo = np.zeros_like(A_hi) if A_lo is None else A_lo
     B_lo = np.zeros_like(B_hi) if B_lo is None else B_lo
     return [exact_dot(A_hi[i, :], A_lo[i, :], B_hi[:, j], B_lo[:, j]) for i, j in zip(rows, cols)]
+
+
+def error_bound(A_hi, B_hi, E, F, nslices: int, rows=None, cols=None):
+    """Upper bound on |C - A·B| for the sliced product with n slices, per entry.
+
+    Cutting each entry below 2^E_i (2^F_j) loses less than 2^(E_i - 13n)
+    (2^(F_j - 13n)), so one product term is off by less than
+    2^(-13n) (|a| 2^F_j + |b| 2^E_i); the pairs with s + t >= n that are not formed
+    add at most (n-1) 2^(E_i + F_j - 13n) per term; the final cascade adds at most
+    2^-104 of the level magnitudes, and a classical double-double reference to
+    compare with is itself off by well under 2^-90 (|A||B|)_ij.  With the lo words
+    below 2^-52 of hi, |a| and |b| are bounded by 1.000001 |a_hi|, |b_hi|:
+        bound_ij = 2^(-13n) (2^F_j S_a[i] + 2^E_i S_b[j] + n k 2^(E_i+F_j))
+                   + 2^-90 (|A||B|)_ij
+    with S_a[i] = sum_p |a_ip|, S_b[j] = sum_p |b_pj| (times 1.000001).
+    """
+    A = np.abs(np.asarray(A_hi, dtype=np.float64)) * 1.000001
+    B = np.abs(np.asarray(B_hi, dtype=np.float64)) * 1.000001
+    k = A.shape[1]
+    Sa = A.sum(axis=1)
+    Sb = B.sum(axis=0)
+    w = np.ldexp(1.0, np.asarray(E, dtype=np.int64))
+    v = np.ldexp(1.0, np.asarray(F, dtype=np.int64))
+    if rows is None:
+        absAB = A @ B
+        return 2.0 ** (-DIGIT_BITS * nslices) * (np.outer(Sa, v) + np.outer(w, Sb) + nslices * k * np.outer(w, v)) \
+            + 2.0 ** -90 * absAB
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    absAB = np.einsum("qk,kq->q", A[rows, :], B[:, cols])
+    return 2.0 ** (-DIGIT_BITS * nslices) * (Sa[rows] * v[cols] + w[rows] * Sb[cols]
+                                             + nslices * k * w[rows] * v[cols]) + 2.0 ** -90 * absAB

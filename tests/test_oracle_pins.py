@@ -435,3 +435,84 @@ def test_error_ratio_detects_a_planted_error():
     bad = Cl.copy()
     bad[2, 3] += 1e-25 * absAB[2, 3]
     assert compare.error_ratio(Ch, bad, Ch, Cl, absAB) > 1e-28
+
+
+# ---------------------------------------------------------------------------
+# fewer slices per operand (n = 4: the pages' quarters of a leading double)
+# ---------------------------------------------------------------------------
+def test_four_slices_are_the_pages_quarters():
+    """With n = 4 the window is the 52-bit fraction of the worked example: the four
+    slices are exactly the fields f0..f3 the page prints."""
+    g = _golden_rows("quartering_example.txt")
+    f = _bits(g["f"])
+    x = int(f, 2) * 2.0 ** -52
+    fields = [int(f[13 * i: 13 * (i + 1)], 2) for i in range(4)]
+    assert exact.slice_entry(x, 0.0, 0, nslices=4) == fields
+    # and the product of two such quarters-vectors follows eq. (3) level by level
+    y = float.fromhex("0x1.9e0a3c2b5d1f8p-1")
+    dy = exact.slice_entry(y, 0.0, 0, nslices=4)
+    S = exact.level_sums_units(np.array(fields).reshape(4, 1, 1), np.array(dy).reshape(4, 1, 1))
+    for l in range(4):
+        assert S[l, 0, 0] == sum(fields[s] * dy[l - s] for s in range(l + 1))
+
+
+@pytest.mark.parametrize("n", [4, 5, 6, 7])
+def test_slicing_with_n_slices_reconstructs_the_window(n):
+    rng = np.random.default_rng(100 + n)
+    for hi, lo in _edge_pairs(rng)[:150]:
+        E = exact.entry_exponent(hi, lo)
+        E = 0 if E is None else E + int(rng.integers(0, 3))
+        v = Fraction(hi) + Fraction(lo)
+        d = exact.slice_entry(hi, lo, E, nslices=n)
+        assert len(d) == n and all(abs(x) <= 8191 for x in d)
+        r = exact.reconstruct_entry(d, E)
+        unit = Fraction(2) ** (E - 13 * n)
+        assert abs(r) <= abs(v) < abs(r) + unit
+        # the n-slice digits are the leading n of the 8-slice digits
+        assert d == exact.slice_entry(hi, lo, E)[:n]
+
+
+@pytest.mark.parametrize("n", [4, 5])
+def test_n_slice_levels_plus_dropped_pairs_equal_windowed_product(n):
+    rng = np.random.default_rng(200 + n)
+    m, k, c = 4, 6, 3
+    Ah, Al = _rand_dd_matrix(rng, (m, k), "wide")
+    Bh, Bl = _rand_dd_matrix(rng, (k, c), "wide")
+    E, DA = exact.slice_rows(Ah, Al, nslices=n)
+    F, DB = exact.slice_cols(Bh, Bl, nslices=n)
+    S = exact.level_sums_units(DA, DB)
+    assert S.shape == (n, m, c)
+    for i in range(m):
+        for j in range(c):
+            kept = exact.level_target(S, int(E[i]), int(F[j]), i, j)
+            dropped = Fraction(0)
+            for s in range(n):
+                for t in range(n - s, n):
+                    dd = sum(int(DA[s, i, p]) * int(DB[t, p, j]) for p in range(k))
+                    dropped += Fraction(dd) * Fraction(2) ** (int(E[i]) + int(F[j]) - 13 * (s + t + 2))
+            win = sum((exact.reconstruct_entry(DA[:, i, p], int(E[i])) *
+                       exact.reconstruct_entry(DB[:, p, j], int(F[j])) for p in range(k)), Fraction(0))
+            assert kept + dropped == win
+
+
+@pytest.mark.parametrize("n", [4, 5, 6, 7, 8])
+@pytest.mark.parametrize("kind", ["uniform", "wide"])
+def test_error_bound_holds_for_the_exact_sliced_chain(n, kind):
+    """The per-entry bound of exact.error_bound against exact rational products."""
+    rng = np.random.default_rng(300 + n + (kind == "wide"))
+    m, k, c = 5, 17, 4
+    Ah, Al = _rand_dd_matrix(rng, (m, k), kind)
+    Bh, Bl = _rand_dd_matrix(rng, (k, c), kind)
+    E, DA = exact.slice_rows(Ah, Al, nslices=n)
+    F, DB = exact.slice_cols(Bh, Bl, nslices=n)
+    Ch, Cl = exact.renorm_levels(exact.level_values(exact.level_sums_units(DA, DB)), E, F)
+    bound = exact.error_bound(Ah, Bh, E, F, n)
+    rows, cols = np.meshgrid(np.arange(m), np.arange(c), indexing="ij")
+    ex = exact.exact_entries(Ah, Al, Bh, Bl, rows.ravel(), cols.ravel())
+    worst = 0.0
+    for q, (i, j) in enumerate(zip(rows.ravel(), cols.ravel())):
+        err = abs(exact.dd_to_fraction(Ch[i, j], Cl[i, j]) - ex[q])
+        assert err <= Fraction(float(bound[i, j])), (n, kind, i, j)
+        worst = max(worst, float(err / Fraction(float(bound[i, j]))))
+    # the bound is not vacuous: the error comes within 2^14 of it
+    assert n == 8 or worst > 2.0 ** -14
