@@ -23,7 +23,8 @@ from . import layout  # noqa: F401  (host-side description of the packed slice l
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libddgemm.so")
 
-NUM_SLICES = 8
+NUM_SLICES = 8          # the double-double product
+MIN_SLICES = 4          # the pages' four quarters of a leading double
 NUM_LEVELS = 8
 SLICE_BITS = 13
 K_MAX = 8388608
@@ -56,6 +57,12 @@ _SIGNATURES = {
     "dd_sliced_gemm_renorm": (_st, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
     "dd_gemm": (_st, [_i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp]),
     "dd_gemm_ws": (_st, [_i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _sz, _vp]),
+    "dd_split_slices_bytes_ns": (_sz, [_i64, _i64, ctypes.c_int]),
+    "dd_gemm_workspace_size_ns": (_sz, [_i64, _i64, _i64, ctypes.c_int]),
+    "dd_split_balanced_ns": (_st, [_i64, _i64, _vp, _vp, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
+    "dd_sliced_gemm_renorm_ns": (_st, [_i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "dd_gemm_ws_ns": (_st, [_i64, _i64, _i64, ctypes.c_int, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
+                            _vp, _sz, _vp]),
     "ddgemm_status_string": (ctypes.c_char_p, [_st]),
     "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
 }
@@ -118,16 +125,21 @@ def _check_lo(lo, hi, name):
         raise ValueError(f"{name} must have the same strides as its hi plane")
 
 
-def slices_bytes(outer: int, k: int) -> int:
-    return lib.dd_split_slices_bytes(outer, k)
+def slices_bytes(outer: int, k: int, nslices: int = NUM_SLICES) -> int:
+    if nslices == NUM_SLICES:
+        return lib.dd_split_slices_bytes(outer, k)
+    return lib.dd_split_slices_bytes_ns(outer, k, nslices)
 
 
-def workspace_size(m: int, n: int, k: int) -> int:
-    return lib.dd_gemm_workspace_size(m, n, k)
+def workspace_size(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:
+    if nslices == NUM_SLICES:
+        return lib.dd_gemm_workspace_size(m, n, k)
+    return lib.dd_gemm_workspace_size_ns(m, n, k, nslices)
 
 
-def split_balanced(X_hi, X_lo, axis: int, exps=None, slices=None, stream=None):
-    """Balancing exponents and packed slices of one operand (axis 0: A, axis 1: B)."""
+def split_balanced(X_hi, X_lo, axis: int, exps=None, slices=None, stream=None, nslices: int = NUM_SLICES):
+    """Balancing exponents and packed slices of one operand (axis 0: A, axis 1: B),
+    with ``nslices`` 13-bit slices per entry (8: double-double)."""
     ldx = _matrix(X_hi, "X_hi")
     _check_lo(X_lo, X_hi, "X_lo")
     rows, cols = X_hi.shape
@@ -137,9 +149,13 @@ def split_balanced(X_hi, X_lo, axis: int, exps=None, slices=None, stream=None):
     if exps is None:
         exps = torch.empty(outer, dtype=torch.int32, device=dev)
     if slices is None:
-        slices = torch.empty(slices_bytes(outer, k) // 8, dtype=torch.float64, device=dev)
-    _check(lib.dd_split_balanced(rows, cols, _ptr(X_hi), _ptr(X_lo), ldx, axis, _ptr(exps), _ptr(slices),
-                                 _stream(stream)))
+        slices = torch.empty(slices_bytes(outer, k, nslices) // 8, dtype=torch.float64, device=dev)
+    if nslices == NUM_SLICES:
+        _check(lib.dd_split_balanced(rows, cols, _ptr(X_hi), _ptr(X_lo), ldx, axis, _ptr(exps), _ptr(slices),
+                                     _stream(stream)))
+    else:
+        _check(lib.dd_split_balanced_ns(rows, cols, _ptr(X_hi), _ptr(X_lo), ldx, axis, nslices, _ptr(exps),
+                                        _ptr(slices), _stream(stream)))
     return exps, slices
 
 
@@ -167,14 +183,19 @@ def renorm_levels(levels, E, F, C_hi=None, C_lo=None, stream=None):
     return C_hi, C_lo
 
 
-def sliced_gemm_renorm(m, n, k, A_slices, E, B_slices, F, C_hi=None, C_lo=None, stream=None):
+def sliced_gemm_renorm(m, n, k, A_slices, E, B_slices, F, C_hi=None, C_lo=None, stream=None,
+                       nslices: int = NUM_SLICES):
     dev = A_slices.device
     C_hi = torch.empty((m, n), dtype=torch.float64, device=dev) if C_hi is None else C_hi
     C_lo = torch.empty((m, n), dtype=torch.float64, device=dev) if C_lo is None else C_lo
     ldc = _matrix(C_hi, "C_hi", (m, n))
     _check_lo(C_lo, C_hi, "C_lo")
-    _check(lib.dd_sliced_gemm_renorm(m, n, k, _ptr(A_slices), _ptr(E), _ptr(B_slices), _ptr(F),
-                                     _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
+    if nslices == NUM_SLICES:
+        _check(lib.dd_sliced_gemm_renorm(m, n, k, _ptr(A_slices), _ptr(E), _ptr(B_slices), _ptr(F),
+                                         _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
+    else:
+        _check(lib.dd_sliced_gemm_renorm_ns(m, n, k, nslices, _ptr(A_slices), _ptr(E), _ptr(B_slices), _ptr(F),
+                                            _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
     return C_hi, C_lo
 
 
@@ -195,15 +216,22 @@ def _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo):
     return m, n, k, lda, ldb, ldc, C_hi, C_lo
 
 
-def dd_gemm(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, workspace=None, stream=None):
-    """C = A·B; returns (C_hi, C_lo).  The workspace comes from PyTorch's allocator
-    unless a uint8 device tensor of at least workspace_size(m, n, k) bytes is given."""
+def dd_gemm(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, workspace=None, stream=None,
+            nslices: int = NUM_SLICES):
+    """C = A·B; returns (C_hi, C_lo).  ``nslices`` = 8 is the double-double
+    product; 4..7 keep fewer slices (n(n+1)/2 pairs) for less accuracy and time.
+    The workspace comes from PyTorch's allocator unless a uint8 device tensor of
+    at least workspace_size(m, n, k, nslices) bytes is given."""
     m, n, k, lda, ldb, ldc, C_hi, C_lo = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
-    need = workspace_size(m, n, k)
+    need = workspace_size(m, n, k, nslices)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=A_hi.device)
-    _check(lib.dd_gemm_ws(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
-                          _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(), _stream(stream)))
+    if nslices == NUM_SLICES:
+        _check(lib.dd_gemm_ws(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
+                              _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(), _stream(stream)))
+    else:
+        _check(lib.dd_gemm_ws_ns(m, n, k, nslices, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
+                                 _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(), _stream(stream)))
     return C_hi, C_lo
 
 

@@ -52,15 +52,18 @@ ddgemm_status_t check_device() {
 
 inline ddgemm_status_t launched(hipError_t e) { return e == hipSuccess ? DDGEMM_SUCCESS : DDGEMM_ERROR_LAUNCH; }
 
-ddgemm_status_t validate_split(int64_t rows, int64_t cols, const double* X_hi, int64_t ldx, int axis,
+inline bool ns_ok(int ns) { return ns >= kMinSlices && ns <= kSlices; }
+
+ddgemm_status_t validate_split(int64_t rows, int64_t cols, const double* X_hi, int64_t ldx, int axis, int ns,
                                const int32_t* exps, const double* slices) {
-    if (!size_ok(rows, cols) || !ld_ok(ldx, cols) || (axis != 0 && axis != 1)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!size_ok(rows, cols) || !ld_ok(ldx, cols) || (axis != 0 && axis != 1) || !ns_ok(ns))
+        return DDGEMM_ERROR_INVALID_VALUE;
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     if (k > DDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
     if (rows * cols > 0 && !X_hi) return DDGEMM_ERROR_INVALID_VALUE;
     if (outer > 0 && !exps) return DDGEMM_ERROR_INVALID_VALUE;
-    if (dd_split_slices_bytes(outer, k) > 0 && !slices) return DDGEMM_ERROR_INVALID_VALUE;
+    if (dd_split_slices_bytes_ns(outer, k, ns) > 0 && !slices) return DDGEMM_ERROR_INVALID_VALUE;
     return DDGEMM_SUCCESS;
 }
 
@@ -74,25 +77,35 @@ ddgemm_status_t validate_gemm_dims(int64_t m, int64_t n, int64_t k) {
 
 extern "C" {
 
-size_t dd_split_slices_bytes(int64_t outer, int64_t k) {
-    if (!size_ok(outer, k)) return 0;
-    return static_cast<size_t>(PackGeom(outer, k).doubles()) * sizeof(double);
+size_t dd_split_slices_bytes_ns(int64_t outer, int64_t k, int nslices) {
+    if (!size_ok(outer, k) || !ns_ok(nslices)) return 0;
+    return static_cast<size_t>(PackGeom(outer, k).doubles(nslices)) * sizeof(double);
 }
 
-size_t dd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
-    if (validate_gemm_dims(m, n, k) != DDGEMM_SUCCESS) return 0;
-    return align_up(dd_split_slices_bytes(m, k)) + align_up(dd_split_slices_bytes(n, k)) +
+size_t dd_split_slices_bytes(int64_t outer, int64_t k) { return dd_split_slices_bytes_ns(outer, k, kSlices); }
+
+size_t dd_gemm_workspace_size_ns(int64_t m, int64_t n, int64_t k, int nslices) {
+    if (validate_gemm_dims(m, n, k) != DDGEMM_SUCCESS || !ns_ok(nslices)) return 0;
+    return align_up(dd_split_slices_bytes_ns(m, k, nslices)) + align_up(dd_split_slices_bytes_ns(n, k, nslices)) +
            align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4);
+}
+
+size_t dd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) { return dd_gemm_workspace_size_ns(m, n, k, kSlices); }
+
+ddgemm_status_t dd_split_balanced_ns(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
+                                     int64_t ldx, int axis, int nslices, int32_t* exps, double* slices,
+                                     void* stream) {
+    ddgemm_status_t st = validate_split(rows, cols, X_hi, ldx, axis, nslices, exps, slices);
+    if (st != DDGEMM_SUCCESS) return st;
+    if ((axis == 0 ? rows : cols) == 0) return DDGEMM_SUCCESS;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+    return launched(launch_split(rows, cols, X_hi, X_lo, ldx, axis, nslices, exps, slices,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 ddgemm_status_t dd_split_balanced(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
                                   int64_t ldx, int axis, int32_t* exps, double* slices, void* stream) {
-    ddgemm_status_t st = validate_split(rows, cols, X_hi, ldx, axis, exps, slices);
-    if (st != DDGEMM_SUCCESS) return st;
-    if ((axis == 0 ? rows : cols) == 0) return DDGEMM_SUCCESS;
-    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
-    return launched(launch_split(rows, cols, X_hi, X_lo, ldx, axis, exps, slices,
-                                 static_cast<hipStream_t>(stream)));
+    return dd_split_balanced_ns(rows, cols, X_hi, X_lo, ldx, axis, kSlices, exps, slices, stream);
 }
 
 ddgemm_status_t dd_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices,
@@ -103,7 +116,7 @@ ddgemm_status_t dd_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_
     if (!levels || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
     if (!size_ok(m * ldl, DDGEMM_NUM_LEVELS)) return DDGEMM_ERROR_INVALID_VALUE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
-    return launched(launch_sliced_gemm(m, n, k, A_slices, B_slices, levels, ldl, nullptr, nullptr,
+    return launched(launch_sliced_gemm(m, n, k, kSlices, A_slices, B_slices, levels, ldl, nullptr, nullptr,
                                        nullptr, nullptr, 0, false, static_cast<hipStream_t>(stream)));
 }
 
@@ -122,26 +135,33 @@ ddgemm_status_t dd_renorm_levels(int64_t m, int64_t n, const double* levels, int
     return launched(launch_renorm(m, n, levels, ldl, E, F, C_hi, C_lo, ldc, static_cast<hipStream_t>(stream)));
 }
 
-ddgemm_status_t dd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k, const double* A_slices,
-                                      const int32_t* E, const double* B_slices, const int32_t* F,
-                                      double* C_hi, double* C_lo, int64_t ldc, void* stream) {
+ddgemm_status_t dd_sliced_gemm_renorm_ns(int64_t m, int64_t n, int64_t k, int nslices, const double* A_slices,
+                                         const int32_t* E, const double* B_slices, const int32_t* F,
+                                         double* C_hi, double* C_lo, int64_t ldc, void* stream) {
     ddgemm_status_t st = validate_gemm_dims(m, n, k);
-    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, n) || !ns_ok(nslices)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!E || !F || !C_hi || !C_lo || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
     const int64_t ce = extent(m, n, ldc);
     if (overlaps(C_hi, ce, C_lo, ce)) return DDGEMM_ERROR_INVALID_VALUE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
-    return launched(launch_sliced_gemm(m, n, k, A_slices, B_slices, nullptr, 0, E, F, C_hi, C_lo, ldc,
+    return launched(launch_sliced_gemm(m, n, k, nslices, A_slices, B_slices, nullptr, 0, E, F, C_hi, C_lo, ldc,
                                        true, static_cast<hipStream_t>(stream)));
 }
 
-ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* A_hi, const double* A_lo,
-                           int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb,
-                           double* C_hi, double* C_lo, int64_t ldc, void* workspace, size_t ws_bytes,
-                           void* stream) {
+ddgemm_status_t dd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k, const double* A_slices,
+                                      const int32_t* E, const double* B_slices, const int32_t* F,
+                                      double* C_hi, double* C_lo, int64_t ldc, void* stream) {
+    return dd_sliced_gemm_renorm_ns(m, n, k, kSlices, A_slices, E, B_slices, F, C_hi, C_lo, ldc, stream);
+}
+
+ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices, const double* A_hi,
+                              const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo,
+                              int64_t ldb, double* C_hi, double* C_lo, int64_t ldc, void* workspace,
+                              size_t ws_bytes, void* stream) {
     ddgemm_status_t st = validate_gemm_dims(m, n, k);
     if (st != DDGEMM_SUCCESS) return st;
+    if (!ns_ok(nslices)) return DDGEMM_ERROR_INVALID_VALUE;
     if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return DDGEMM_ERROR_INVALID_VALUE;
@@ -151,25 +171,34 @@ ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* A_hi, 
             overlaps(C, ce, B_lo, be))
             return DDGEMM_ERROR_INVALID_VALUE;
     if (overlaps(C_hi, ce, C_lo, ce)) return DDGEMM_ERROR_INVALID_VALUE;
-    const size_t need = dd_gemm_workspace_size(m, n, k);
+    const size_t need = dd_gemm_workspace_size_ns(m, n, k, nslices);
     if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return DDGEMM_ERROR_WORKSPACE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
 
     char* w = static_cast<char*>(workspace);
     double* A_sl = reinterpret_cast<double*>(w);
-    w += align_up(dd_split_slices_bytes(m, k));
+    w += align_up(dd_split_slices_bytes_ns(m, k, nslices));
     double* B_sl = reinterpret_cast<double*>(w);
-    w += align_up(dd_split_slices_bytes(n, k));
+    w += align_up(dd_split_slices_bytes_ns(n, k, nslices));
     int32_t* E = reinterpret_cast<int32_t*>(w);
     w += align_up(static_cast<size_t>(m) * 4);
     int32_t* F = reinterpret_cast<int32_t*>(w);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_split(m, k, A_hi, A_lo, lda, 0, E, A_sl, s);
-    if (e == hipSuccess) e = launch_split(k, n, B_hi, B_lo, ldb, 1, F, B_sl, s);
-    if (e == hipSuccess) e = launch_sliced_gemm(m, n, k, A_sl, B_sl, nullptr, 0, E, F, C_hi, C_lo, ldc, true, s);
+    hipError_t e = launch_split(m, k, A_hi, A_lo, lda, 0, nslices, E, A_sl, s);
+    if (e == hipSuccess) e = launch_split(k, n, B_hi, B_lo, ldb, 1, nslices, F, B_sl, s);
+    if (e == hipSuccess)
+        e = launch_sliced_gemm(m, n, k, nslices, A_sl, B_sl, nullptr, 0, E, F, C_hi, C_lo, ldc, true, s);
     return launched(e);
+}
+
+ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* A_hi, const double* A_lo,
+                           int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb,
+                           double* C_hi, double* C_lo, int64_t ldc, void* workspace, size_t ws_bytes,
+                           void* stream) {
+    return dd_gemm_ws_ns(m, n, k, kSlices, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc, workspace,
+                         ws_bytes, stream);
 }
 
 ddgemm_status_t dd_gemm(int64_t m, int64_t n, int64_t k, const double* A_hi, const double* A_lo,

@@ -10,7 +10,8 @@
 namespace ddg {
 
 constexpr int kSliceBits = DDGEMM_SLICE_BITS;
-constexpr int kSlices = DDGEMM_NUM_SLICES;
+constexpr int kSlices = DDGEMM_NUM_SLICES;  // slices of the double-double product
+constexpr int kMinSlices = DDGEMM_MIN_SLICES;
 constexpr int kLevels = DDGEMM_NUM_LEVELS;
 constexpr int kWindowBits = kSliceBits * kSlices;  // 104
 constexpr int kPackOuter = DDGEMM_PACK_OUTER;
@@ -28,13 +29,13 @@ struct PackGeom {
     PackGeom(int64_t outer_, int64_t k_)
         : outer(outer_), k(k_), Op(round_up(outer_, kPackOuter)), Kp(round_up(k_, kPackK)),
           KB(round_up(k_, kPackK) / 4), RB(round_up(outer_, kPackOuter) / 16) {}
-    int64_t doubles() const { return Op * Kp * kSlices; }
+    int64_t doubles(int ns = kSlices) const { return Op * Kp * ns; }
 };
 
 // Host-side launch helpers implemented next to their kernels.
 hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
-                        int64_t ldx, int axis, int32_t* exps, double* slices, hipStream_t stream);
-hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices,
+                        int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream);
+hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                               const double* B_slices, double* levels, int64_t ldl,
                               const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
                               int64_t ldc, bool fused, hipStream_t stream);

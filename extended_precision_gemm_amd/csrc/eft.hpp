@@ -19,16 +19,16 @@ __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e
 }
 
 // Level renormalisation ("Multiple Double Arithmetic on NVIDIA Tensor Cores",
-// §2, fifth step): add the 8 exact level sums of one output entry into a
+// §2, fifth step): add the NL exact level sums of one output entry into a
 // double-double, smallest level first, then apply the entry's scale 2^sc.
 // TwoSum is used for the renormalising step too (FastTwoSum gives the same bits
 // whenever its precondition holds, and TwoSum needs no branch when it does not).
-__device__ __forceinline__ void renorm_levels(const double (&S)[kLevels], int sc, double& c_hi,
-                                              double& c_lo) {
-    double h = S[kLevels - 1];
+template <int NL>
+__device__ __forceinline__ void renorm_levels(const double (&S)[NL], int sc, double& c_hi, double& c_lo) {
+    double h = S[NL - 1];
     double t = 0.0;
 #pragma unroll
-    for (int l = kLevels - 2; l >= 0; --l) {
+    for (int l = NL - 2; l >= 0; --l) {
         double s, e;
         two_sum(h, S[l], s, e);
         t = t + e;

@@ -45,15 +45,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int WM, int WN, int KS, int NBUF, int WGS>
+template <int WM, int WN, int KS, int NBUF, int WGS, int NS>
 struct GemmConfig {
     static constexpr int kWaves = WM * WN;
     static constexpr int kNBuf = NBUF;
     static constexpr int kWGS = WGS;
+    static constexpr int kNS = NS;                                   // slices per operand entry
+    static constexpr int kSetDoubles = NS * kFragDoubles;            // one fragment, all slices
     static constexpr int kThreads = kWaves * 64;
     static constexpr int kTBM = 2 * WM;                              // 16-row blocks per tile
     static constexpr int kTBN = WN;                                  // 16-column blocks per tile
-    static constexpr int kBlockStage = KS * kFragSetDoubles;         // one block, one stage
+    static constexpr int kKS = KS;
+    static constexpr int kBlockStage = KS * kSetDoubles;             // one block, one stage
     static constexpr int kStageDoubles = (kTBM + kTBN) * kBlockStage;
     static constexpr int kPiecesPerBlock = kBlockStage / 128;        // 1 KB pieces
     static constexpr int kPieces = (kTBM + kTBN) * kPiecesPerBlock;
@@ -71,8 +74,9 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                    double* __restrict__ levels, int64_t ldl, int64_t plane,
                    const int32_t* __restrict__ E, const int32_t* __restrict__ F,
                    double* __restrict__ C_hi, double* __restrict__ C_lo, int64_t ldc) {
-    constexpr int KS = C::kBlockStage / kFragSetDoubles;
+    constexpr int KS = C::kKS;
     constexpr int NBUF = C::kNBuf;
+    constexpr int NS = C::kNS;
     __shared__ __attribute__((aligned(1024))) double lds[NBUF * C::kStageDoubles];
 
     const int lane = threadIdx.x & 63;
@@ -82,7 +86,7 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
     const int64_t tm = static_cast<int64_t>(blockIdx.x) / tiles_n;
     const int64_t tn = static_cast<int64_t>(blockIdx.x) % tiles_n;
     const int64_t rb0 = tm * C::kTBM, cb0 = tn * C::kTBN;
-    const int64_t NS = KB / KS;  // KB is a multiple of 4 (k is packed to 16)
+    const int64_t nstages = KB / KS;  // KB is a multiple of 4 (k is packed to 16)
 
     // Piece q of a stage: block q / kPiecesPerBlock of the stage (A blocks
     // first, then B blocks), 1 KB piece q % kPiecesPerBlock of that block's run.
@@ -93,8 +97,8 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
     for (int i = 0; i < C::kPiecesPerWave; ++i) {
         const int q = i * C::kWaves + wave;
         const int blk = q / C::kPiecesPerBlock, pc = q % C::kPiecesPerBlock;
-        const double* base = blk < C::kTBM ? Ap + (rb0 + blk) * KB * kFragSetDoubles
-                                           : Bp + (cb0 + blk - C::kTBM) * KB * kFragSetDoubles;
+        const double* base = blk < C::kTBM ? Ap + (rb0 + blk) * KB * C::kSetDoubles
+                                           : Bp + (cb0 + blk - C::kTBM) * KB * C::kSetDoubles;
         src[i] = base + pc * 128 + lane * 2;
         dst[i] = blk * C::kBlockStage + pc * 128;
     }
@@ -105,39 +109,39 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                                              (lds_void_t*)(lds + buf * C::kStageDoubles + dst[i]), 16, 0, 0);
     };
 
-    double4_t acc[kLevels][2];
+    double4_t acc[NS][2];
 #pragma unroll
-    for (int l = 0; l < kLevels; ++l) acc[l][0] = acc[l][1] = double4_t{0.0, 0.0, 0.0, 0.0};
+    for (int l = 0; l < NS; ++l) acc[l][0] = acc[l][1] = double4_t{0.0, 0.0, 0.0, 0.0};
 
-    if (NS > 0) {
+    if (nstages > 0) {
 #pragma unroll
-        for (int j = 0; j < NBUF - 1; ++j) issue(j < NS ? j : NS - 1, j);
-        for (int64_t st = 0; st < NS; ++st) {
+        for (int j = 0; j < NBUF - 1; ++j) issue(j < nstages ? j : nstages - 1, j);
+        for (int64_t st = 0; st < nstages; ++st) {
             // Stage st has landed once at most NBUF-2 younger stages are pending.
             wait_vmcnt<(NBUF - 2) * C::kPiecesPerWave>();
             compiler_fence();
             __builtin_amdgcn_s_barrier();  // every wave's copy of stage st is in LDS, and
             compiler_fence();               // every wave is done reading stage st-1
             const int64_t nxt = st + NBUF - 1;
-            issue(nxt < NS ? nxt : NS - 1, static_cast<int>(nxt % NBUF));
+            issue(nxt < nstages ? nxt : nstages - 1, static_cast<int>(nxt % NBUF));
 
             const double* stage = lds + (st % NBUF) * C::kStageDoubles + lane;
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
-                const double* sa = stage + (2 * wr) * C::kBlockStage + j * kFragSetDoubles;
-                const double* sb = stage + (C::kTBM + wc) * C::kBlockStage + j * kFragSetDoubles;
-                double a[kSlices][2], b[kSlices];
+                const double* sa = stage + (2 * wr) * C::kBlockStage + j * C::kSetDoubles;
+                const double* sb = stage + (C::kTBM + wc) * C::kBlockStage + j * C::kSetDoubles;
+                double a[NS][2], b[NS];
 #pragma unroll
-                for (int s = 0; s < kSlices; ++s) {
+                for (int s = 0; s < NS; ++s) {
                     a[s][0] = sa[s * kFragDoubles];
                     a[s][1] = sa[C::kBlockStage + s * kFragDoubles];
                     b[s] = sb[s * kFragDoubles];
                 }
-                // Triangular schedule: pair (s, t) feeds level s + t.
+                // Triangular schedule: pair (s, t) feeds level s + t < NS.
 #pragma unroll
-                for (int s = 0; s < kSlices; ++s)
+                for (int s = 0; s < NS; ++s)
 #pragma unroll
-                    for (int t = 0; s + t < kLevels; ++t)
+                    for (int t = 0; s + t < NS; ++t)
 #pragma unroll
                         for (int r = 0; r < 2; ++r)
                             acc[s + t][r] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s][r], b[t], acc[s + t][r], 0, 0, 0);
@@ -155,16 +159,16 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
             const int64_t row = (rb0 + 2 * wr + r) * 16 + frag_row(lane, v);
             if (row < m && col < n) {
                 if constexpr (FUSED) {
-                    double S[kLevels];
+                    double S[NS];
 #pragma unroll
-                    for (int l = 0; l < kLevels; ++l) S[l] = acc[l][r][v];
+                    for (int l = 0; l < NS; ++l) S[l] = acc[l][r][v];
                     double hi, lo;
-                    renorm_levels(S, E[row] + F[col], hi, lo);
+                    renorm_levels<NS>(S, E[row] + F[col], hi, lo);
                     C_hi[row * ldc + col] = hi;
                     C_lo[row * ldc + col] = lo;
                 } else {
 #pragma unroll
-                    for (int l = 0; l < kLevels; ++l) levels[l * plane + row * ldl + col] = acc[l][r][v];
+                    for (int l = 0; l < NS; ++l) levels[l * plane + row * ldl + col] = acc[l][r][v];
                 }
             }
         }
@@ -184,7 +188,7 @@ __global__ void __launch_bounds__(256) renorm_kernel(int64_t m, int64_t n, const
 #pragma unroll
         for (int l = 0; l < kLevels; ++l) S[l] = levels[l * plane + row * ldl + col];
         double hi, lo;
-        renorm_levels(S, E[row] + f, hi, lo);
+        renorm_levels<kLevels>(S, E[row] + f, hi, lo);
         C_hi[row * ldc + col] = hi;
         C_lo[row * ldc + col] = lo;
     }
@@ -200,28 +204,21 @@ __global__ void __launch_bounds__(64) probe_mfma_kernel(double* __restrict__ out
     for (int v = 0; v < 4; ++v) out[lane * 4 + v] = c[v];
 }
 
-// Launch configuration: 32x16 wave strips, WM x WN waves per workgroup,
-// KS k-blocks per stage, NBUF stages, WGS workgroups per CU.
-#ifndef DDGEMM_CFG
-#define DDGEMM_CFG 0
-#endif
-#if DDGEMM_CFG == 0
-using Cfg = GemmConfig<2, 4, 2, 2, 1>;  // 64x64 tile, 8 waves, one workgroup per CU
-#elif DDGEMM_CFG == 1
-using Cfg = GemmConfig<2, 2, 1, 3, 2>;  // 64x32 tile, 4 waves, two workgroups per CU
-#elif DDGEMM_CFG == 2
-using Cfg = GemmConfig<1, 4, 1, 3, 2>;  // 32x64 tile, 4 waves, two workgroups per CU
-#elif DDGEMM_CFG == 3
-using Cfg = GemmConfig<2, 2, 2, 2, 1>;  // 64x32 tile, 4 waves, 2 k-blocks per stage (96 KB: one per CU)
-#endif
+// Launch configuration per slice count: 32x16 wave strips, 2 x 4 waves per
+// workgroup (64x64 tile, one workgroup per CU), KS k-blocks per LDS stage so that
+// a stage stays at or below 64 KB, two stages.
+template <int NS> struct ConfigFor;
+template <> struct ConfigFor<4> { using type = GemmConfig<2, 4, 4, 2, 1, 4>; };
+template <> struct ConfigFor<5> { using type = GemmConfig<2, 4, 2, 2, 1, 5>; };
+template <> struct ConfigFor<6> { using type = GemmConfig<2, 4, 2, 2, 1, 6>; };
+template <> struct ConfigFor<7> { using type = GemmConfig<2, 4, 2, 2, 1, 7>; };
+template <> struct ConfigFor<8> { using type = GemmConfig<2, 4, 2, 2, 1, 8>; };
 
-}  // namespace
-
-hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices,
-                              const double* B_slices, double* levels, int64_t ldl,
-                              const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
-                              int64_t ldc, bool fused, hipStream_t stream) {
-    if (m == 0 || n == 0) return hipSuccess;
+template <int NS>
+hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
+                          double* levels, int64_t ldl, const int32_t* E, const int32_t* F, double* C_hi,
+                          double* C_lo, int64_t ldc, bool fused, hipStream_t stream) {
+    using Cfg = typename ConfigFor<NS>::type;
     const PackGeom ga(m, k);
     constexpr int BM = Cfg::kTBM * 16, BN = Cfg::kTBN * 16;
     const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
@@ -231,10 +228,29 @@ hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_s
     if (fused)
         sliced_gemm_kernel<Cfg, true><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
             m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, 0, 0, E, F, C_hi, C_lo, ldc);
-    else
+    else if constexpr (NS == kSlices)
         sliced_gemm_kernel<Cfg, false><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
             m, n, ga.KB, tiles_n, A_slices, B_slices, levels, ldl, plane, nullptr, nullptr, nullptr, nullptr, 0);
+    else
+        return hipErrorInvalidValue;  // level planes are offered for the double-double product only
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
+                              const double* B_slices, double* levels, int64_t ldl,
+                              const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
+                              int64_t ldc, bool fused, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    switch (ns) {
+        case 4: return launch_gemm_ns<4>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 5: return launch_gemm_ns<5>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 6: return launch_gemm_ns<6>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 7: return launch_gemm_ns<7>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 8: return launch_gemm_ns<8>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,

@@ -68,13 +68,15 @@ __device__ __forceinline__ int64_t floor_scaled(uint64_t mant, bool neg, int sh)
     return neg ? -static_cast<int64_t>(q + (frac ? 1 : 0)) : static_cast<int64_t>(q);
 }
 
-// The eight unit-scaled slices of x = hi + lo below exponent E (|x| < 2^E).
-__device__ __forceinline__ void slice_entry(double hi, double lo, int E, double (&out)[kSlices]) {
+// The NS unit-scaled slices of x = hi + lo in the 13 NS-bit window below
+// exponent E (|x| < 2^E).
+template <int NS>
+__device__ __forceinline__ void slice_entry(double hi, double lo, int E, double (&out)[NS]) {
     double s, e;
     two_sum(hi, lo, s, e);  // x = s + e exactly, |e| <= ulp(s)/2
     if (s == 0.0) {
 #pragma unroll
-        for (int q = 0; q < kSlices; ++q) out[q] = 0.0;
+        for (int q = 0; q < NS; ++q) out[q] = 0.0;
         return;
     }
     const bool neg = s < 0.0;
@@ -82,10 +84,10 @@ __device__ __forceinline__ void slice_entry(double hi, double lo, int E, double 
     uint64_t ms;
     int es;
     decompose(s, ms, es);
-    const int W = E - kWindowBits;  // exponent of the window's last unit
+    const int W = E - kSliceBits * NS;  // exponent of the window's last unit
     unsigned __int128 N;
     if (es >= W) {
-        // |s| 2^-W = ms << (es - W) is an integer below 2^104; add floor(ep 2^-W),
+        // |s| 2^-W = ms << (es - W) is an integer below 2^(13 NS); add floor(ep 2^-W),
         // which is below 2^51 in magnitude because |ep| <= ulp(s)/2.
         N = static_cast<unsigned __int128>(ms) << (es - W);
         if (ep != 0.0) {
@@ -111,8 +113,8 @@ __device__ __forceinline__ void slice_entry(double hi, double lo, int E, double 
     constexpr double kScale[kSlices] = {0x1p-13, 0x1p-26, 0x1p-39, 0x1p-52,
                                         0x1p-65, 0x1p-78, 0x1p-91, 0x1p-104};
 #pragma unroll
-    for (int q = 0; q < kSlices; ++q) {
-        const int d = static_cast<int>(static_cast<uint64_t>(N >> (kSliceBits * (kSlices - 1 - q))) & 0x1FFF);
+    for (int q = 0; q < NS; ++q) {
+        const int d = static_cast<int>(static_cast<uint64_t>(N >> (kSliceBits * (NS - 1 - q))) & 0x1FFF);
         out[q] = static_cast<double>(neg ? -d : d) * kScale[q];
     }
 }
@@ -163,9 +165,9 @@ __global__ void decode_exps_kernel(int32_t* __restrict__ exps, int64_t count) {
         exps[i] = decode_exp(exps[i]);
 }
 
-// One thread per packed (fragment, lane) position; writes the eight slices of
+// One thread per packed (fragment, lane) position; writes the NS slices of
 // its entry.  AXIS 0: entry (o, p) is X[o][p]; AXIS 1: it is X[p][o].
-template <int AXIS>
+template <int AXIS, int NS>
 __global__ void __launch_bounds__(256) slice_kernel(int64_t outer, int64_t k, int64_t KB,
                                                     int64_t total, const double* __restrict__ hi,
                                                     const double* __restrict__ lo, int64_t ld,
@@ -185,18 +187,18 @@ __global__ void __launch_bounds__(256) slice_kernel(int64_t outer, int64_t k, in
             x_lo = lo ? lo[idx] : 0.0;
             E = exps[o];
         }
-        double sl[kSlices];
-        slice_entry(x_hi, x_lo, E, sl);
-        double* dst = slices + frag * kFragSetDoubles + lane;
+        double sl[NS];
+        slice_entry<NS>(x_hi, x_lo, E, sl);
+        double* dst = slices + frag * (NS * kFragDoubles) + lane;
 #pragma unroll
-        for (int q = 0; q < kSlices; ++q) dst[q * kFragDoubles] = sl[q];
+        for (int q = 0; q < NS; ++q) dst[q * kFragDoubles] = sl[q];
     }
 }
 
 // One workgroup per 16-row (AXIS 0) or 16-column (AXIS 1) block: first the
 // block's balancing exponents, then its slices, so the second read of the
 // block's (hi, lo) comes from cache rather than HBM and no atomics are needed.
-template <int AXIS, int NT>
+template <int AXIS, int NT, int NS>
 __global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t k, int64_t KB,
                                                          const double* __restrict__ hi,
                                                          const double* __restrict__ lo, int64_t ld,
@@ -275,7 +277,7 @@ __global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t 
         const int lane = static_cast<int>(q & 31) * 2;
         const int oi = lane & 15;
         const int64_t p = kb * 4 + (lane >> 4);
-        double sl0[kSlices], sl1[kSlices];
+        double sl0[NS], sl1[NS];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int64_t o = o0 + oi + e;
@@ -285,11 +287,11 @@ __global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t 
                 x_hi = hi[idx];
                 x_lo = lo ? lo[idx] : 0.0;
             }
-            slice_entry(x_hi, x_lo, block_exp[oi + e], e == 0 ? sl0 : sl1);
+            slice_entry<NS>(x_hi, x_lo, block_exp[oi + e], e == 0 ? sl0 : sl1);
         }
-        double2* dst = reinterpret_cast<double2*>(slices + (static_cast<int64_t>(blockIdx.x) * KB + kb) * kFragSetDoubles + lane);
+        double2* dst = reinterpret_cast<double2*>(slices + (static_cast<int64_t>(blockIdx.x) * KB + kb) * (NS * kFragDoubles) + lane);
 #pragma unroll
-        for (int s = 0; s < kSlices; ++s) dst[s * (kFragDoubles / 2)] = make_double2(sl0[s], sl1[s]);
+        for (int s = 0; s < NS; ++s) dst[s * (kFragDoubles / 2)] = make_double2(sl0[s], sl1[s]);
     }
 }
 
@@ -304,22 +306,21 @@ inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap) {
     return static_cast<unsigned>(g);
 }
 
-}  // namespace
-
-hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
-                        int64_t ldx, int axis, int32_t* exps, double* slices, hipStream_t stream) {
+template <int NS>
+hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
+                           int64_t ldx, int axis, int32_t* exps, double* slices, hipStream_t stream) {
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     if (outer == 0) return hipSuccess;
     const PackGeom g(outer, k);
     constexpr int kBlockThreads = 1024;
-    if (g.doubles() > 0 && g.RB >= kFusedMinBlocks) {
+    if (g.doubles(NS) > 0 && g.RB >= kFusedMinBlocks) {
         // Enough 16-row/16-column blocks to fill the chip: one pass per block.
         if (axis == 0)
-            split_block_kernel<0, kBlockThreads><<<static_cast<unsigned>(g.RB), kBlockThreads, 0, stream>>>(
+            split_block_kernel<0, kBlockThreads, NS><<<static_cast<unsigned>(g.RB), kBlockThreads, 0, stream>>>(
                 outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
         else
-            split_block_kernel<1, kBlockThreads><<<static_cast<unsigned>(g.RB), kBlockThreads, 0, stream>>>(
+            split_block_kernel<1, kBlockThreads, NS><<<static_cast<unsigned>(g.RB), kBlockThreads, 0, stream>>>(
                 outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
         return hipGetLastError();
     }
@@ -339,14 +340,28 @@ hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const do
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (g.doubles() == 0) return hipSuccess;
+    if (g.doubles(NS) == 0) return hipSuccess;
     const int64_t total = g.RB * g.KB * kFragDoubles;
     const unsigned grid = grid_for(total, 256, 1 << 20);
     if (axis == 0)
-        slice_kernel<0><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X_hi, X_lo, ldx, exps, slices);
+        slice_kernel<0, NS><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X_hi, X_lo, ldx, exps, slices);
     else
-        slice_kernel<1><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X_hi, X_lo, ldx, exps, slices);
+        slice_kernel<1, NS><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X_hi, X_lo, ldx, exps, slices);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
+                        int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream) {
+    switch (ns) {
+        case 4: return launch_split_ns<4>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 5: return launch_split_ns<5>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 6: return launch_split_ns<6>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 7: return launch_split_ns<7>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 8: return launch_split_ns<8>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace ddg

@@ -56,6 +56,12 @@ typedef enum {
 #define DDGEMM_SLICE_BITS 13 /* significant bits per slice: the pages' quarters   */
 #define DDGEMM_NUM_SLICES 8  /* 104-bit window: four quarters of hi, four of lo    */
 #define DDGEMM_NUM_LEVELS 8  /* levels l = s + t = 0..7; 36 slice pairs            */
+/* The *_ns entry points take the number of slices n per operand entry instead:
+ * a 13n-bit window, n levels, n(n+1)/2 slice pairs, DDGEMM_MIN_SLICES <= n <=
+ * DDGEMM_NUM_SLICES.  n = 4 is §2 eqs. (1)-(3): the four quarters of a leading
+ * double; n = 8 is the double-double product.  Fewer slices trade accuracy
+ * (about 13n - 7 bits relative to the row/column maxima) for speed. */
+#define DDGEMM_MIN_SLICES 4
 /* Largest k: with every level holding at most 8 pairs, the exact-sum bound of §2
  * eq. (5) (67,108,865 products of 26-bit quantities) allows 67,108,865 / 8 terms. */
 #define DDGEMM_K_MAX 8388608
@@ -172,6 +178,33 @@ ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k,
                            const double* B_hi, const double* B_lo, int64_t ldb,
                            double* C_hi, double* C_lo, int64_t ldc,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The same operations with n slices per entry (see DDGEMM_MIN_SLICES).  The
+ * packed layout is the one described above with n slices per fragment in place
+ * of 8 (slice s of entry (o, p) at ((((o/16)*KB + p/4)*n + s)*64) + (p%4)*16 +
+ * o%16); for n = 8 every call equals its counterpart without the suffix.  The
+ * product C is the renormalised sum of the n level sums; per entry it is
+ * within 2^(-13n) (2^F_j sum_p |a_ip| + 2^E_i sum_p |b_pj| + n k 2^(E_i+F_j))
+ * + 2^-90 (|A||B|)_ij of the exact product, E_i and F_j the row/column
+ * exponents.  Errors: as for the counterparts, plus DDGEMM_ERROR_INVALID_VALUE
+ * for n outside [DDGEMM_MIN_SLICES, DDGEMM_NUM_SLICES].
+ */
+size_t dd_split_slices_bytes_ns(int64_t outer, int64_t k, int nslices);
+size_t dd_gemm_workspace_size_ns(int64_t m, int64_t n, int64_t k, int nslices);
+ddgemm_status_t dd_split_balanced_ns(int64_t rows, int64_t cols,
+                                     const double* X_hi, const double* X_lo, int64_t ldx,
+                                     int axis, int nslices, int32_t* exps, double* slices,
+                                     void* stream);
+ddgemm_status_t dd_sliced_gemm_renorm_ns(int64_t m, int64_t n, int64_t k, int nslices,
+                                         const double* A_slices, const int32_t* E,
+                                         const double* B_slices, const int32_t* F,
+                                         double* C_hi, double* C_lo, int64_t ldc, void* stream);
+ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices,
+                              const double* A_hi, const double* A_lo, int64_t lda,
+                              const double* B_hi, const double* B_lo, int64_t ldb,
+                              double* C_hi, double* C_lo, int64_t ldc,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* ddgemm_status_string(ddgemm_status_t status);

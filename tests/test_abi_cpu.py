@@ -147,3 +147,25 @@ def test_layout_pack_unpack_roundtrip(ddg):
         for (s, o, p) in [(0, 0, 0), (7, outer - 1, k - 1), (3, outer // 2, k // 2)]:
             idx = (((o // 16) * KB + p // 4) * 8 + s) * 64 + (p % 4) * 16 + (o % 16)
             assert packed[idx] == planes[s, o, p]
+
+
+def test_n_slice_sizes_and_validation(ddg):
+    L = ddg.lib
+    INV = ddg.ERROR_INVALID_VALUE
+    for n in range(ddg.MIN_SLICES, ddg.NUM_SLICES + 1):
+        assert L.dd_split_slices_bytes_ns(130, 33, n) == 256 * 48 * n * 8
+    assert L.dd_split_slices_bytes_ns(130, 33, 8) == ddg.slices_bytes(130, 33)
+    assert L.dd_gemm_workspace_size_ns(100, 70, 33, 8) == ddg.workspace_size(100, 70, 33)
+    assert L.dd_gemm_workspace_size_ns(100, 70, 33, 4) < ddg.workspace_size(100, 70, 33)
+    for bad in (0, 3, 9, -1):
+        assert L.dd_split_slices_bytes_ns(10, 10, bad) == 0
+        assert L.dd_gemm_workspace_size_ns(10, 10, 10, bad) == 0
+        assert L.dd_split_balanced_ns(4, 4, P[0], None, 4, 0, bad, P[1], P[2], None) == INV
+        assert L.dd_sliced_gemm_renorm_ns(4, 4, 4, bad, P[0], P[1], P[2], P[3], P[4], P[5], 4, None) == INV
+        assert L.dd_gemm_ws_ns(4, 5, 6, bad, P[0], P[1], 6, P[2], P[3], 5, P[4], P[5], 5, P[6], 1 << 20,
+                               None) == INV
+    # the suffixed entry points validate like their counterparts
+    assert L.dd_gemm_ws_ns(4, 5, 6, 4, P[0], P[1], 5, P[2], P[3], 5, P[4], P[5], 5, P[6], 1 << 20, None) == INV
+    assert L.dd_gemm_ws_ns(4, 5, 6, 4, P[0], P[1], 6, P[2], P[3], 5, P[4], P[5], 5, P[6], 10, None) == \
+        ddg.ERROR_WORKSPACE
+    assert L.dd_gemm_ws_ns(0, 5, 6, 4, None, None, 6, None, None, 5, None, None, 5, None, 0, None) == 0

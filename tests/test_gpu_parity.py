@@ -416,3 +416,65 @@ def test_workload_parity(gpu, workload_operands, name):
             bound = compare.TOL * float(compare.abs_product(Ah[i:i + 1], Bh).sum())
             _say(f"[parity] {name}: row {i}: sum_j C_ij = {tot:.3e}, expected {expect:.3e}, bound {bound:.3e}")
             assert abs(tot - expect) <= bound
+
+
+# ---------------------------------------------------------------------------
+# fewer slices per entry (n = 4: the pages' quarters of a leading double)
+# ---------------------------------------------------------------------------
+def test_four_slices_split_is_the_pages_quarters(gpu):
+    x = float.fromhex("0x1.234cc9da46998p-1")
+    hi = np.full((1, 1), x)
+    E, packed = gpu.split_balanced(_dev(hi), None, 0, nslices=4)
+    from extended_precision_gemm_amd import layout
+    got = _host(layout.unpack(packed, 1, 1, nslices=4).contiguous())[:, 0, 0]
+    assert _host(E).tolist() == [0]
+    assert got.tolist() == [d * 2.0 ** (-13 * (s + 1)) for s, d in enumerate([4660, 6547, 5777, 5324])]
+
+
+@pytest.mark.parametrize("nslices", [4, 5, 6, 7])
+@pytest.mark.parametrize("m,n,k", [(17, 33, 5), (130, 65, 33), (96, 160, 100)])
+def test_n_slice_chain_bit_exact(gpu, nslices, m, n, k):
+    rng = np.random.default_rng(nslices * 1000 + m + n + k)
+    Ah, Al = _edge_matrix(rng, m, k)
+    Bh, Bl = _edge_matrix(rng, k, n)
+    E, DA = exact.slice_rows(Ah, Al, nslices=nslices)
+    F, DB = exact.slice_cols(Bh, Bl, nslices=nslices)
+    S = exact.level_values(exact.level_sums_units(DA, DB))
+    Ch_ref, Cl_ref = exact.renorm_levels(S, E, F)
+    from extended_precision_gemm_amd import layout
+    gE, gA = gpu.split_balanced(_dev(Ah), _dev(Al), 0, nslices=nslices)
+    gF, gB = gpu.split_balanced(_dev(Bh), _dev(Bl), 1, nslices=nslices)
+    assert np.array_equal(_host(gE), E) and np.array_equal(_host(gF), F)
+    assert _bits_equal(_host(layout.unpack(gA, m, k, nslices).contiguous()), exact.slice_values(DA))
+    assert _bits_equal(_host(layout.unpack(gB, n, k, nslices).contiguous()),
+                       exact.slice_values(DB).transpose(0, 2, 1))
+    Fh, Fl = gpu.sliced_gemm_renorm(m, n, k, gA, gE, gB, gF, nslices=nslices)
+    assert _bits_equal(_host(Fh), Ch_ref) and _bits_equal(_host(Fl), Cl_ref)
+    Gh, Gl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl), nslices=nslices)
+    assert _bits_equal(_host(Gh), Ch_ref) and _bits_equal(_host(Gl), Cl_ref)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["dd1024", "dd4096_exp20"])
+def test_n_slice_products_within_their_error_bound(gpu, workload_operands, name):
+    """Against the classical oracle: every n stays inside the per-entry bound of
+    window truncation plus pairs not formed (oracle.exact.error_bound)."""
+    Ah, Al, Bh, Bl = workload_operands(name)
+    m, k = Ah.shape
+    n = Bh.shape[1]
+    rng = np.random.default_rng(7)
+    qr = rng.integers(0, m, 1024)
+    qc = rng.integers(0, n, 1024)
+    Rh, Rl = native.dd_gemm_entries(Ah, Al, Bh, Bl, qr, qc)
+    E = exact.balancing_exponents(Ah, Al, 0)
+    F = exact.balancing_exponents(Bh, Bl, 1)
+    dA, dAl, dB, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
+    for nslices in (4, 5, 6, 7, 8):
+        Ch, Cl = gpu.dd_gemm(dA, dAl, dB, dBl, nslices=nslices)
+        hCh, hCl = _host(Ch), _host(Cl)
+        err = np.abs((hCh[qr, qc] - Rh) + (hCl[qr, qc] - Rl))
+        bound = exact.error_bound(Ah, Bh, E, F, nslices, qr, qc)
+        ratio = float((err / bound).max())
+        _say(f"[parity] {name} n={nslices}: max |C-C_ref| / bound = {ratio:.3e}")
+        assert ratio <= 1.0
+        del Ch, Cl
