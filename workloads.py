@@ -17,6 +17,14 @@ then ``u``.
 The pages ("Multiple Double Arithmetic on NVIDIA Tensor Cores", §4.1) say only
 that random numbers were used; the five workloads below fix the shapes and
 value distributions.
+
+A quad-double matrix is four float64 planes (x0, x1, x2, x3).  Entry recipe:
+draw x0 from the distribution, then for c = 0, 1, 2 draw u_c ~ U(-1/2, 1/2) and
+set x_{c+1} = RN(x_c * 2**-53 * u_c), so every component is at most half an
+ulp of the one before it (the normalisation of the quad-double library the
+pages cite, [3]).  Seeds ``default_rng(2000 + 10*c)`` (A) and ``+ 1`` (B) for
+quad-double workload ``c``; draws in order: x0's variates, then u_0, u_1, u_2.
+The sizes follow the pages' quad-double runs (§4.2, Table 1: n = 1024, 2048).
 """
 from __future__ import annotations
 
@@ -25,7 +33,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "by_name", "make_operands", "dd_pair_from_hi"]
+__all__ = ["Workload", "WORKLOADS", "QD_WORKLOADS", "by_name", "make_operands", "dd_pair_from_hi",
+           "qd_from_x0", "random_qd", "make_qd_operands"]
 
 
 @dataclass(frozen=True)
@@ -60,7 +69,22 @@ WORKLOADS: tuple[Workload, ...] = (
 )
 
 
+QD_WORKLOADS: tuple[Workload, ...] = (
+    Workload(0, "qd64", 64, 64, 64, "uniform", "uniform",
+             description="quad-double m=n=k=64, x0 ~ U(-1,1)"),
+    Workload(1, "qd1024", 1024, 1024, 1024, "uniform", "uniform",
+             description="quad-double m=n=k=1024, x0 ~ U(-1,1)"),
+    Workload(2, "qd2048", 2048, 2048, 2048, "uniform", "uniform",
+             description="quad-double m=n=k=2048, x0 ~ U(-1,1)"),
+    Workload(3, "qd4096_exp20", 4096, 4096, 4096, "signed_exp20", "signed_exp20",
+             description="quad-double m=n=k=4096, x0 = sign*U(0.5,1)*2^e, e in [-20,20]"),
+)
+
+
 def by_name(name: str) -> Workload:
+    for w in QD_WORKLOADS:
+        if w.name == name:
+            return w
     for w in WORKLOADS:
         if w.name == name or str(w.index) == str(name):
             return w
@@ -125,3 +149,32 @@ def random_dd(shape, seed: int, dist: str = "uniform"):
     """A small seeded (hi, lo) matrix with a workload distribution (edge-case tests)."""
     rng = np.random.default_rng(seed)
     return dd_pair_from_hi(rng, _draw_hi(rng, dist, shape))
+
+
+def qd_from_x0(rng: np.random.Generator, x0: np.ndarray) -> np.ndarray:
+    """Stack (x0, x1, x2, x3) with x_{c+1} = RN(x_c * 2^-53 * u_c), u_c ~ U(-1/2, 1/2)."""
+    out = np.empty((4,) + x0.shape, dtype=np.float64)
+    out[0] = x0
+    for c in range(3):
+        u = rng.uniform(-0.5, 0.5, size=x0.shape)
+        out[c + 1] = out[c] * (2.0 ** -53) * u
+    return out
+
+
+def random_qd(shape, seed: int, dist: str = "uniform") -> np.ndarray:
+    """A small seeded quad-double matrix, shape (4, *shape) (edge-case tests)."""
+    rng = np.random.default_rng(seed)
+    return qd_from_x0(rng, _draw_hi(rng, dist, shape))
+
+
+def make_qd_operands(w: Workload | str):
+    """Return (A, B): float64 arrays of shape (4, m, k) and (4, k, n)."""
+    if not isinstance(w, Workload):
+        w = by_name(str(w))
+    if w not in QD_WORKLOADS:
+        raise KeyError(f"{w.name} is not a quad-double workload")
+    ra = np.random.default_rng(2000 + 10 * w.index)
+    A = qd_from_x0(ra, _draw_hi(ra, w.a_dist, (w.m, w.k)))
+    rb = np.random.default_rng(2000 + 10 * w.index + 1)
+    B = qd_from_x0(rb, _draw_hi(rb, w.b_dist, (w.k, w.n)))
+    return A, B
