@@ -1,6 +1,7 @@
-"""Double-double matrix product C = A·B on AMD Instinct MI355X (gfx950).
+"""Double-double and quad-double matrix products C = A·B on AMD Instinct MI355X (gfx950).
 
-Thin ctypes binding of ``libddgemm.so`` (C ABI in ``include/ddgemm.h``).  It
+Thin ctypes binding of ``libddgemm.so`` (C ABI in ``include/ddgemm.h`` and
+``include/qdgemm.h``).  It
 only marshals arguments: every step of the product runs in the library's HIP
 kernels; PyTorch supplies device memory and the current stream.  Importing
 this module fails loudly when the library has not been built.
@@ -10,6 +11,8 @@ double-double entry is cut into eight 13-bit slices below a per-row (A) or
 per-column (B) balancing exponent, the 36 slice pairs inside the double-double
 window are multiplied exactly on FP64 matrix cores and summed per level, and
 the eight level sums of every output entry are renormalised into (hi, lo) once.
+The quad-double product (``qd_*``) takes sixteen slices, 136 pairs and sixteen
+levels, whose exact total is rounded to the nearest four-double result.
 """
 from __future__ import annotations
 
@@ -28,6 +31,8 @@ MIN_SLICES = 4          # the pages' four quarters of a leading double
 NUM_LEVELS = 8
 SLICE_BITS = 13
 K_MAX = 8388608
+QD_NUM_SLICES = 16      # the quad-double product
+QD_K_MAX = 4194304
 
 SUCCESS = 0
 ERROR_INVALID_VALUE = 1
@@ -46,6 +51,7 @@ _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t
 _st = ctypes.c_int
+_pp = ctypes.POINTER(ctypes.c_void_p)   # a host array of four device pointers (qd planes)
 
 # name -> (restype, argtypes); mirrors include/ddgemm.h
 _SIGNATURES = {
@@ -63,6 +69,12 @@ _SIGNATURES = {
     "dd_sliced_gemm_renorm_ns": (_st, [_i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
     "dd_gemm_ws_ns": (_st, [_i64, _i64, _i64, ctypes.c_int, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                             _vp, _sz, _vp]),
+    "qd_split_slices_bytes": (_sz, [_i64, _i64]),
+    "qd_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "qd_split_balanced": (_st, [_i64, _i64, _pp, _i64, ctypes.c_int, _vp, _vp, _vp]),
+    "qd_sliced_gemm_renorm": (_st, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _pp, _i64, _vp]),
+    "qd_gemm": (_st, [_i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp]),
+    "qd_gemm_ws": (_st, [_i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp, _sz, _vp]),
     "ddgemm_status_string": (ctypes.c_char_p, [_st]),
     "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
 }
@@ -241,6 +253,101 @@ def dd_gemm_alloc(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, stream=None):
     _check(lib.dd_gemm(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
                        _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
     return C_hi, C_lo
+
+
+# ---------------------------------------------------------------------------
+# quad-double product
+# ---------------------------------------------------------------------------
+def _qd_planes(X, name, shape=None):
+    """Components of a quad-double matrix: a (4, rows, cols) tensor or a sequence
+    of up to four (rows, cols) tensors (None after the first = zero plane).
+    Returns (components, leading dimension, ctypes array of four pointers)."""
+    comps = [X[c] for c in range(X.shape[0])] if isinstance(X, torch.Tensor) else list(X)
+    if not 1 <= len(comps) <= 4 or comps[0] is None:
+        raise ValueError(f"{name} needs one to four component planes, the first present")
+    ld = _matrix(comps[0], f"{name}[0]", shape)
+    for c, t in enumerate(comps[1:], 1):
+        if t is not None:
+            _matrix(t, f"{name}[{c}]", comps[0].shape)
+            if t.stride() != comps[0].stride():
+                raise ValueError(f"{name}[{c}] must have the strides of {name}[0]")
+    comps = comps + [None] * (4 - len(comps))
+    return comps, ld, (ctypes.c_void_p * 4)(*[_ptr(t) for t in comps])
+
+
+def _qd_out(C, m, n, device):
+    if C is None:
+        C = torch.empty((4, m, n), dtype=torch.float64, device=device)
+    comps = [C[c] for c in range(4)] if isinstance(C, torch.Tensor) else list(C)
+    if len(comps) != 4 or any(t is None for t in comps):
+        raise ValueError("C needs four component planes")
+    ldc = _matrix(comps[0], "C[0]", (m, n))
+    for c in range(1, 4):
+        _matrix(comps[c], f"C[{c}]", (m, n))
+        if comps[c].stride() != comps[0].stride():
+            raise ValueError(f"C[{c}] must have the strides of C[0]")
+    return C, ldc, (ctypes.c_void_p * 4)(*[_ptr(t) for t in comps])
+
+
+def qd_slices_bytes(outer: int, k: int) -> int:
+    return lib.qd_split_slices_bytes(outer, k)
+
+
+def qd_workspace_size(m: int, n: int, k: int) -> int:
+    return lib.qd_gemm_workspace_size(m, n, k)
+
+
+def qd_split_balanced(X, axis: int, exps=None, slices=None, stream=None):
+    """Balancing exponents and the sixteen packed slices of one quad-double operand."""
+    comps, ldx, arr = _qd_planes(X, "X")
+    rows, cols = comps[0].shape
+    outer = rows if axis == 0 else cols
+    k = cols if axis == 0 else rows
+    dev = comps[0].device
+    if exps is None:
+        exps = torch.empty(outer, dtype=torch.int32, device=dev)
+    if slices is None:
+        slices = torch.empty(qd_slices_bytes(outer, k) // 8, dtype=torch.float64, device=dev)
+    _check(lib.qd_split_balanced(rows, cols, arr, ldx, axis, _ptr(exps), _ptr(slices), _stream(stream)))
+    return exps, slices
+
+
+def qd_sliced_gemm_renorm(m, n, k, A_slices, E, B_slices, F, C=None, stream=None):
+    """Level sums of the 136 slice pairs and the exact four-double epilogue; returns C."""
+    C, ldc, arr = _qd_out(C, m, n, A_slices.device)
+    _check(lib.qd_sliced_gemm_renorm(m, n, k, _ptr(A_slices), _ptr(E), _ptr(B_slices), _ptr(F), arr, ldc,
+                                     _stream(stream)))
+    return C
+
+
+def _qd_gemm_args(A, B, C):
+    a, lda, pa = _qd_planes(A, "A")
+    b, ldb, pb = _qd_planes(B, "B")
+    m, k = a[0].shape
+    k2, n = b[0].shape
+    if k != k2:
+        raise ValueError(f"inner dimensions differ: {k} vs {k2}")
+    C, ldc, pc = _qd_out(C, m, n, a[0].device)
+    return m, n, k, pa, lda, pb, ldb, C, pc, ldc
+
+
+def qd_gemm(A, B, C=None, workspace=None, stream=None):
+    """C = A·B for quad-double A (m×k) and B (k×n); returns C as a (4, m, n) tensor
+    (or the given planes).  The workspace comes from PyTorch's allocator unless a
+    uint8 device tensor of at least qd_workspace_size(m, n, k) bytes is given."""
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _qd_gemm_args(A, B, C)
+    need = qd_workspace_size(m, n, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    _check(lib.qd_gemm_ws(m, n, k, pa, lda, pb, ldb, pc, ldc, _ptr(workspace), workspace.numel(), _stream(stream)))
+    return C
+
+
+def qd_gemm_alloc(A, B, C=None, stream=None):
+    """C = A·B through the entry point that allocates its own (stream-ordered) workspace."""
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _qd_gemm_args(A, B, C)
+    _check(lib.qd_gemm(m, n, k, pa, lda, pb, ldb, pc, ldc, _stream(stream)))
+    return C
 
 
 def probe_mfma_f64(device="cuda", stream=None):

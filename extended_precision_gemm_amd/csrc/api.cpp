@@ -73,6 +73,36 @@ ddgemm_status_t validate_gemm_dims(int64_t m, int64_t n, int64_t k) {
     return DDGEMM_SUCCESS;
 }
 
+// Quad-double operands: a host array of four device pointers per matrix.
+ddgemm_status_t read_qd_planes(const double* const X[4], int64_t extent_elems, QdPlanes& out) {
+    if (extent_elems == 0) {
+        for (int c = 0; c < 4; ++c) out.x[c] = X ? X[c] : nullptr;
+        return DDGEMM_SUCCESS;
+    }
+    if (!X || !X[0]) return DDGEMM_ERROR_INVALID_VALUE;
+    for (int c = 0; c < 4; ++c) out.x[c] = X[c];
+    return DDGEMM_SUCCESS;
+}
+
+// Four output planes: all present, pairwise disjoint.
+ddgemm_status_t read_out_planes(double* const C[4], int64_t ce, OutPlanes& out) {
+    if (!C) return DDGEMM_ERROR_INVALID_VALUE;
+    for (int c = 0; c < 4; ++c) {
+        if (!C[c]) return DDGEMM_ERROR_INVALID_VALUE;
+        out.c[c] = C[c];
+    }
+    for (int a = 0; a < 4; ++a)
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(C[a], ce, C[b], ce)) return DDGEMM_ERROR_INVALID_VALUE;
+    return DDGEMM_SUCCESS;
+}
+
+ddgemm_status_t validate_qd_gemm_dims(int64_t m, int64_t n, int64_t k) {
+    if (!size_ok(m, k) || !size_ok(k, n) || !size_ok(m, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (k > QDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
+    return DDGEMM_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,6 +245,105 @@ ddgemm_status_t dd_gemm(int64_t m, int64_t n, int64_t k, const double* A_hi, con
     void* ws = nullptr;
     if (hipMallocAsync(&ws, need, s) != hipSuccess || !ws) return DDGEMM_ERROR_WORKSPACE;
     st = dd_gemm_ws(m, n, k, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc, ws, need, stream);
+    if (hipFreeAsync(ws, s) != hipSuccess && st == DDGEMM_SUCCESS) st = DDGEMM_ERROR_LAUNCH;
+    return st;
+}
+
+size_t qd_split_slices_bytes(int64_t outer, int64_t k) {
+    if (!size_ok(outer, k) || !size_ok(outer, k * kQdSlices)) return 0;
+    return static_cast<size_t>(PackGeom(outer, k).doubles(kQdSlices)) * sizeof(double);
+}
+
+size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
+    if (validate_qd_gemm_dims(m, n, k) != DDGEMM_SUCCESS) return 0;
+    return align_up(qd_split_slices_bytes(m, k)) + align_up(qd_split_slices_bytes(n, k)) +
+           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4);
+}
+
+ddgemm_status_t qd_split_balanced(int64_t rows, int64_t cols, const double* const X[4], int64_t ldx, int axis,
+                                  int32_t* exps, double* slices, void* stream) {
+    if (!size_ok(rows, cols) || !ld_ok(ldx, cols) || (axis != 0 && axis != 1)) return DDGEMM_ERROR_INVALID_VALUE;
+    const int64_t outer = axis == 0 ? rows : cols;
+    const int64_t k = axis == 0 ? cols : rows;
+    if (k > QDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
+    QdPlanes planes;
+    ddgemm_status_t st = read_qd_planes(X, rows * cols, planes);
+    if (st != DDGEMM_SUCCESS) return st;
+    if (outer > 0 && !exps) return DDGEMM_ERROR_INVALID_VALUE;
+    if (qd_split_slices_bytes(outer, k) > 0 && !slices) return DDGEMM_ERROR_INVALID_VALUE;
+    if (outer == 0) return DDGEMM_SUCCESS;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+    return launched(launch_qd_split(rows, cols, planes, ldx, axis, exps, slices, static_cast<hipStream_t>(stream)));
+}
+
+ddgemm_status_t qd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k, const double* A_slices, const int32_t* E,
+                                      const double* B_slices, const int32_t* F, double* const C[4], int64_t ldc,
+                                      void* stream) {
+    ddgemm_status_t st = validate_qd_gemm_dims(m, n, k);
+    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
+    OutPlanes out;
+    if ((st = read_out_planes(C, extent(m, n, ldc), out)) != DDGEMM_SUCCESS) return st;
+    if (!E || !F || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+    return launched(launch_qd_gemm(m, n, k, A_slices, B_slices, E, F, out, ldc, static_cast<hipStream_t>(stream)));
+}
+
+ddgemm_status_t qd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* const A[4], int64_t lda,
+                           const double* const B[4], int64_t ldb, double* const C[4], int64_t ldc,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    ddgemm_status_t st = validate_qd_gemm_dims(m, n, k);
+    if (st != DDGEMM_SUCCESS) return st;
+    if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
+    const int64_t ae = extent(m, k, lda), be = extent(k, n, ldb), ce = extent(m, n, ldc);
+    QdPlanes pa, pb;
+    OutPlanes out;
+    if ((st = read_qd_planes(A, m * k, pa)) != DDGEMM_SUCCESS) return st;
+    if ((st = read_qd_planes(B, k * n, pb)) != DDGEMM_SUCCESS) return st;
+    if ((st = read_out_planes(C, ce, out)) != DDGEMM_SUCCESS) return st;
+    for (int c = 0; c < 4; ++c)
+        for (int q = 0; q < 4; ++q)
+            if (overlaps(out.c[c], ce, pa.x[q], ae) || overlaps(out.c[c], ce, pb.x[q], be))
+                return DDGEMM_ERROR_INVALID_VALUE;
+    const size_t need = qd_gemm_workspace_size(m, n, k);
+    if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return DDGEMM_ERROR_WORKSPACE;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+
+    char* w = static_cast<char*>(workspace);
+    double* A_sl = reinterpret_cast<double*>(w);
+    w += align_up(qd_split_slices_bytes(m, k));
+    double* B_sl = reinterpret_cast<double*>(w);
+    w += align_up(qd_split_slices_bytes(n, k));
+    int32_t* E = reinterpret_cast<int32_t*>(w);
+    w += align_up(static_cast<size_t>(m) * 4);
+    int32_t* F = reinterpret_cast<int32_t*>(w);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s);
+    if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s);
+    if (e == hipSuccess) e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s);
+    return launched(e);
+}
+
+ddgemm_status_t qd_gemm(int64_t m, int64_t n, int64_t k, const double* const A[4], int64_t lda,
+                        const double* const B[4], int64_t ldb, double* const C[4], int64_t ldc, void* stream) {
+    ddgemm_status_t st = validate_qd_gemm_dims(m, n, k);
+    if (st != DDGEMM_SUCCESS) return st;
+    if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
+    QdPlanes pa, pb;
+    OutPlanes out;
+    if ((st = read_qd_planes(A, m * k, pa)) != DDGEMM_SUCCESS) return st;
+    if ((st = read_qd_planes(B, k * n, pb)) != DDGEMM_SUCCESS) return st;
+    if ((st = read_out_planes(C, extent(m, n, ldc), out)) != DDGEMM_SUCCESS) return st;
+    if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t need = qd_gemm_workspace_size(m, n, k);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, need, s) != hipSuccess || !ws) return DDGEMM_ERROR_WORKSPACE;
+    st = qd_gemm_ws(m, n, k, A, lda, B, ldb, C, ldc, ws, need, stream);
     if (hipFreeAsync(ws, s) != hipSuccess && st == DDGEMM_SUCCESS) st = DDGEMM_ERROR_LAUNCH;
     return st;
 }

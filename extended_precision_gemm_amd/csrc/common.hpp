@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "ddgemm.h"
+#include "qdgemm.h"
 
 namespace ddg {
 
@@ -18,6 +19,7 @@ constexpr int kPackOuter = DDGEMM_PACK_OUTER;
 constexpr int kPackK = DDGEMM_PACK_K;
 constexpr int kFragDoubles = 64;                    // one 16x4 / 4x16 FP64 MFMA operand
 constexpr int kFragSetDoubles = kFragDoubles * kSlices;  // all 8 slices of one fragment
+constexpr int kQdSlices = QDGEMM_NUM_SLICES;         // slices of the quad-double product
 
 typedef double double4_t __attribute__((ext_vector_type(4)));
 
@@ -32,6 +34,17 @@ struct PackGeom {
     int64_t doubles(int ns = kSlices) const { return Op * Kp * ns; }
 };
 
+// The component planes of one quad-double operand (x[1..3] may be null: zero).
+struct QdPlanes {
+    const double* x[4];
+};
+
+// Output planes of the fused product: c[0], c[1] = (hi, lo) for a double-double
+// result; c[0..3] for a quad-double result.
+struct OutPlanes {
+    double* c[4];
+};
+
 // Host-side launch helpers implemented next to their kernels.
 hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
                         int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream);
@@ -43,5 +56,10 @@ hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl
                          const int32_t* F, double* C_hi, double* C_lo, int64_t ldc,
                          hipStream_t stream);
 hipError_t launch_probe_mfma(double* out, hipStream_t stream);
+hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
+                           double* slices, hipStream_t stream);
+hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
+                          const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
+                          hipStream_t stream);
 
 }  // namespace ddg

@@ -1,0 +1,188 @@
+// Balancing exponents and 13-bit slicing of one quad-double operand
+// ("Multiple Double Arithmetic on NVIDIA Tensor Cores": §2 quartering, and its
+// remark that a quartered quad-double matrix is sixteen times the size of a
+// matrix of doubles; §3 balancing).
+//
+// An entry x = x0 + x1 + x2 + x3 is normalised: every component is at most half
+// an ulp of the one before it (the convention of the quad-double library the
+// pages build on).  It is cut as the 208-bit fixed-point window below the
+// balancing exponent E of its row (A) or column (B): N = floor(|x| 2^(208-E)),
+// slice s = sign(x) * ((N >> 13(15-s)) & 8191) * 2^(-13(s+1)), s = 0..15.  N is
+// formed exactly in 256-bit register integers from the components' integer
+// mantissas; E is the largest frexp exponent of RN(x) over the row or column.
+#include "common.hpp"
+#include "split_common.hpp"
+#include "wide_int.hpp"
+
+namespace ddg {
+namespace {
+
+constexpr int kQdWindowBits = kSliceBits * kQdSlices;  // 208
+
+__device__ __forceinline__ void load_qd(const QdPlanes& X, int64_t idx, double (&x)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = X.x[c] ? X.x[c][idx] : 0.0;
+}
+
+// floor(|x| 2^-u) for a normalised quad double x, as an L-limb integer (the
+// caller picks u so the result fits).  The components' integer parts are summed
+// with their signs; the part below the unit is, by the normalisation, smaller in
+// magnitude than one unit and has the sign of the first component that reaches
+// below the unit, so it lowers the floor by one exactly when that sign is
+// negative.
+template <int L>
+__device__ __forceinline__ WideInt<L> qd_floor_abs(const double (&x)[4], int u) {
+    WideInt<L> acc;
+    wide_zero(acc);
+    const bool neg = x[0] < 0.0;
+    bool decided = false, borrow = false;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const double y = neg ? -x[c] : x[c];
+        if (y != 0.0) {
+            uint64_t mant;
+            int e;
+            decompose(y, mant, e);  // |y| = mant 2^e
+            const bool yneg = y < 0.0;
+            const int sh = e - u;
+            if (sh >= 0) {
+                const int64_t v = static_cast<int64_t>(mant);
+                wide_add_shifted(acc, yneg ? -v : v, sh);
+            } else {
+                const int d = -sh;
+                const uint64_t t = d < 64 ? mant >> d : 0;
+                const bool frac = d < 64 ? (mant & ((1ull << d) - 1)) != 0 : true;
+                if (t != 0) wide_add_shifted(acc, yneg ? -static_cast<int64_t>(t) : static_cast<int64_t>(t), 0);
+                if (!decided && frac) {
+                    decided = true;
+                    borrow = yneg;
+                }
+            }
+        }
+    }
+    if (borrow) wide_add_shifted(acc, -1, 0);
+    return acc;
+}
+
+// Encoded frexp exponent of RN(x), kNoExp for zero.  With e = frexp exponent of
+// x0, |x| < 2^e, and M = floor(|x| 2^(55-e)) < 2^55 decides the rounding:
+// RN(x) = 2^e from M >= 2^55 - 2 (|x| >= 2^e - 2^(e-54), ties to even), RN(x)
+// >= 2^(e-1) from M >= 2^54 - 1, and RN(x) < 2^(e-1) below that.
+__device__ __forceinline__ int qd_entry_code(const double (&x)[4]) {
+    if (x[0] == 0.0) return kNoExp;
+    const int e = frexp_exponent(x[0]);
+    const uint64_t M = qd_floor_abs<1>(x, e - 55).w[0];
+    const int ex = M >= (1ull << 55) - 2 ? e + 1 : (M >= (1ull << 54) - 1 ? e : e - 1);
+    return ex + kExpBias;
+}
+
+__device__ __forceinline__ void qd_slice_entry(const double (&x)[4], int E, double (&out)[kQdSlices]) {
+    if (x[0] == 0.0) {
+#pragma unroll
+        for (int s = 0; s < kQdSlices; ++s) out[s] = 0.0;
+        return;
+    }
+    const bool neg = x[0] < 0.0;
+    const WideInt<4> N = qd_floor_abs<4>(x, E - kQdWindowBits);
+#pragma unroll
+    for (int s = 0; s < kQdSlices; ++s) {
+        const int d = static_cast<int>(wide_bits64(N, kSliceBits * (kQdSlices - 1 - s)) & 0x1FFF);
+        out[s] = ldexp(static_cast<double>(neg ? -d : d), -kSliceBits * (s + 1));
+    }
+}
+
+// One wave per row: E[row] = max exponent over the row (axis 0, the A operand).
+__global__ void __launch_bounds__(256) qd_exp_rows_kernel(int64_t rows, int64_t cols, QdPlanes X, int64_t ld,
+                                                          int32_t* __restrict__ exps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
+    for (int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+         row < rows; row += nwaves) {
+        int code = kNoExp;
+        for (int64_t p = lane; p < cols; p += 64) {
+            double x[4];
+            load_qd(X, row * ld + p, x);
+            code = max(code, qd_entry_code(x));
+        }
+        code = wave_max(code);
+        if (lane == 0) exps[row] = decode_exp(code);
+    }
+}
+
+// Column exponents (axis 1, the B operand): one thread per column over a chunk
+// of rows, folded in with a device-memory atomicMax on the encoded exponent.
+__global__ void __launch_bounds__(256) qd_exp_cols_kernel(int64_t rows, int64_t cols, QdPlanes X, int64_t ld,
+                                                          int64_t rows_per_chunk, int32_t* __restrict__ codes) {
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (col >= cols) return;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows_per_chunk;
+    const int64_t r1 = min(rows, r0 + rows_per_chunk);
+    int code = kNoExp;
+    for (int64_t r = r0; r < r1; ++r) {
+        double x[4];
+        load_qd(X, r * ld + col, x);
+        code = max(code, qd_entry_code(x));
+    }
+    if (code != kNoExp) atomicMax(codes + col, code);
+}
+
+// One thread per packed (fragment, lane) position; writes the 16 slices of its
+// entry.  AXIS 0: entry (o, p) is X[o][p]; AXIS 1: it is X[p][o].
+template <int AXIS>
+__global__ void __launch_bounds__(256) qd_slice_kernel(int64_t outer, int64_t k, int64_t KB, int64_t total,
+                                                       QdPlanes X, int64_t ld, const int32_t* __restrict__ exps,
+                                                       double* __restrict__ slices) {
+    for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
+         g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int lane = static_cast<int>(g & 63);
+        const int64_t frag = g >> 6;
+        const int64_t o = (frag / KB) * 16 + (lane & 15);
+        const int64_t p = (frag % KB) * 4 + (lane >> 4);
+        double x[4] = {0.0, 0.0, 0.0, 0.0};
+        int E = 0;
+        if (o < outer && p < k) {
+            load_qd(X, AXIS == 0 ? o * ld + p : p * ld + o, x);
+            E = exps[o];
+        }
+        double sl[kQdSlices];
+        qd_slice_entry(x, E, sl);
+        double* dst = slices + frag * (kQdSlices * kFragDoubles) + lane;
+#pragma unroll
+        for (int s = 0; s < kQdSlices; ++s) dst[s * kFragDoubles] = sl[s];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
+                           double* slices, hipStream_t stream) {
+    const int64_t outer = axis == 0 ? rows : cols;
+    const int64_t k = axis == 0 ? cols : rows;
+    if (outer == 0) return hipSuccess;
+    if (axis == 0) {
+        qd_exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X, ldx, exps);
+    } else {
+        fill_int_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols, kNoExp);
+        if (rows > 0) {
+            int64_t rpc = (rows + 4095) / 4096;
+            if (rpc < 64) rpc = 64;
+            const int64_t chunks = (rows + rpc - 1) / rpc;
+            dim3 grid(static_cast<unsigned>((cols + 255) / 256), static_cast<unsigned>(chunks));
+            qd_exp_cols_kernel<<<grid, 256, 0, stream>>>(rows, cols, X, ldx, rpc, exps);
+        }
+        decode_exps_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const PackGeom g(outer, k);
+    if (g.doubles(kQdSlices) == 0) return hipSuccess;
+    const int64_t total = g.RB * g.KB * kFragDoubles;
+    const unsigned grid = grid_for(total, 256, 1 << 20);
+    if (axis == 0)
+        qd_slice_kernel<0><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X, ldx, exps, slices);
+    else
+        qd_slice_kernel<1><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X, ldx, exps, slices);
+    return hipGetLastError();
+}
+
+}  // namespace ddg

@@ -10,10 +10,12 @@
 // is exact and every partial sum is an integer multiple of 2^(-13(l+2)) below
 // 2^53 units: the matrix-core accumulation is exact in any order.
 //
-// Work split: each wave computes a 32x16 strip (two 16x16 blocks stacked) with
-// eight level accumulators per block; a workgroup of WM x WN waves owns a
-// (32 WM) x (16 WN) output tile, and WGS workgroups share a CU (two waves per
-// SIMD in every configuration).  The operand panels move through LDS in stages
+// Work split: each wave computes a (16 RPW)x16 strip (RPW 16x16 blocks stacked;
+// RPW = 2 for up to eight slices, 1 for sixteen) with one accumulator per level
+// and block; a workgroup of WM x WN waves owns a (16 RPW WM) x (16 WN) output
+// tile, and WGS workgroups share a CU (two waves per SIMD in every
+// configuration).  The same kernel serves the quad-double product: sixteen
+// slices, 136 pairs, sixteen levels, and the exact four-double epilogue.  The operand panels move through LDS in stages
 // of KS k-blocks (4 values of k each): every (16x4 or 4x16) fragment of one
 // slice is 64 consecutive doubles in the packed planes, so a stage of one
 // 16-row (16-column) block is a contiguous KS x 4 KB run, copied with 16-byte
@@ -22,6 +24,7 @@
 // registers.  NBUF stages are in flight; one workgroup barrier per stage.
 #include "common.hpp"
 #include "eft.hpp"
+#include "qd_levels.hpp"
 
 namespace ddg {
 namespace {
@@ -45,15 +48,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int WM, int WN, int KS, int NBUF, int WGS, int NS>
+template <int WM, int WN, int KS, int NBUF, int WGS, int NS, int RPW = 2>
 struct GemmConfig {
     static constexpr int kWaves = WM * WN;
+    static constexpr int kRPW = RPW;                                 // 16-row blocks per wave
     static constexpr int kNBuf = NBUF;
     static constexpr int kWGS = WGS;
     static constexpr int kNS = NS;                                   // slices per operand entry
     static constexpr int kSetDoubles = NS * kFragDoubles;            // one fragment, all slices
     static constexpr int kThreads = kWaves * 64;
-    static constexpr int kTBM = 2 * WM;                              // 16-row blocks per tile
+    static constexpr int kTBM = RPW * WM;                            // 16-row blocks per tile
     static constexpr int kTBN = WN;                                  // 16-column blocks per tile
     static constexpr int kKS = KS;
     static constexpr int kBlockStage = KS * kSetDoubles;             // one block, one stage
@@ -73,15 +77,16 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                    const double* __restrict__ Ap, const double* __restrict__ Bp,
                    double* __restrict__ levels, int64_t ldl, int64_t plane,
                    const int32_t* __restrict__ E, const int32_t* __restrict__ F,
-                   double* __restrict__ C_hi, double* __restrict__ C_lo, int64_t ldc) {
+                   OutPlanes out, int64_t ldc) {
     constexpr int KS = C::kKS;
+    constexpr int RPW = C::kRPW;
     constexpr int NBUF = C::kNBuf;
     constexpr int NS = C::kNS;
     __shared__ __attribute__((aligned(1024))) double lds[NBUF * C::kStageDoubles];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wr = wave / C::kTBN;  // block rows 2*wr, 2*wr+1 of the tile
+    const int wr = wave / C::kTBN;  // block rows RPW*wr .. RPW*wr+RPW-1 of the tile
     const int wc = wave % C::kTBN;  // block column wc of the tile
     const int64_t tm = static_cast<int64_t>(blockIdx.x) / tiles_n;
     const int64_t tn = static_cast<int64_t>(blockIdx.x) % tiles_n;
@@ -109,9 +114,11 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                                              (lds_void_t*)(lds + buf * C::kStageDoubles + dst[i]), 16, 0, 0);
     };
 
-    double4_t acc[NS][2];
+    double4_t acc[NS][RPW];
 #pragma unroll
-    for (int l = 0; l < NS; ++l) acc[l][0] = acc[l][1] = double4_t{0.0, 0.0, 0.0, 0.0};
+    for (int l = 0; l < NS; ++l)
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) acc[l][r] = double4_t{0.0, 0.0, 0.0, 0.0};
 
     if (nstages > 0) {
 #pragma unroll
@@ -128,13 +135,13 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
             const double* stage = lds + (st % NBUF) * C::kStageDoubles + lane;
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
-                const double* sa = stage + (2 * wr) * C::kBlockStage + j * C::kSetDoubles;
+                const double* sa = stage + (RPW * wr) * C::kBlockStage + j * C::kSetDoubles;
                 const double* sb = stage + (C::kTBM + wc) * C::kBlockStage + j * C::kSetDoubles;
-                double a[NS][2], b[NS];
+                double a[NS][RPW], b[NS];
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    a[s][0] = sa[s * kFragDoubles];
-                    a[s][1] = sa[C::kBlockStage + s * kFragDoubles];
+#pragma unroll
+                    for (int r = 0; r < RPW; ++r) a[s][r] = sa[r * C::kBlockStage + s * kFragDoubles];
                     b[s] = sb[s * kFragDoubles];
                 }
                 // Triangular schedule: pair (s, t) feeds level s + t < NS.
@@ -143,7 +150,7 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
 #pragma unroll
                     for (int t = 0; s + t < NS; ++t)
 #pragma unroll
-                        for (int r = 0; r < 2; ++r)
+                        for (int r = 0; r < RPW; ++r)
                             acc[s + t][r] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s][r], b[t], acc[s + t][r], 0, 0, 0);
             }
         }
@@ -153,19 +160,28 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
 
     const int64_t col = (cb0 + wc) * 16 + frag_col(lane);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < RPW; ++r) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int64_t row = (rb0 + 2 * wr + r) * 16 + frag_row(lane, v);
+            const int64_t row = (rb0 + RPW * wr + r) * 16 + frag_row(lane, v);
             if (row < m && col < n) {
                 if constexpr (FUSED) {
                     double S[NS];
 #pragma unroll
                     for (int l = 0; l < NS; ++l) S[l] = acc[l][r][v];
-                    double hi, lo;
-                    renorm_levels<NS>(S, E[row] + F[col], hi, lo);
-                    C_hi[row * ldc + col] = hi;
-                    C_lo[row * ldc + col] = lo;
+                    const int sc = E[row] + F[col];
+                    const int64_t idx = row * ldc + col;
+                    if constexpr (NS <= kSlices) {
+                        double hi, lo;
+                        renorm_levels<NS>(S, sc, hi, lo);
+                        out.c[0][idx] = hi;
+                        out.c[1][idx] = lo;
+                    } else {
+                        double c[4];
+                        qd_from_levels<NS>(S, sc, c);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) out.c[q][idx] = c[q];
+                    }
                 } else {
 #pragma unroll
                     for (int l = 0; l < NS; ++l) levels[l * plane + row * ldl + col] = acc[l][r][v];
@@ -213,6 +229,9 @@ template <> struct ConfigFor<5> { using type = GemmConfig<2, 4, 2, 2, 1, 5>; };
 template <> struct ConfigFor<6> { using type = GemmConfig<2, 4, 2, 2, 1, 6>; };
 template <> struct ConfigFor<7> { using type = GemmConfig<2, 4, 2, 2, 1, 7>; };
 template <> struct ConfigFor<8> { using type = GemmConfig<2, 4, 2, 2, 1, 8>; };
+// Sixteen slices (quad double): 16 level accumulators of one 16x16 block per
+// wave (128 registers), a 32x64 tile, one k-block per 48 KB stage.
+template <> struct ConfigFor<16> { using type = GemmConfig<2, 4, 1, 2, 1, 16, 1>; };
 
 template <int NS>
 hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
@@ -227,10 +246,12 @@ hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slice
     const int64_t plane = m * ldl;
     if (fused)
         sliced_gemm_kernel<Cfg, true><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, 0, 0, E, F, C_hi, C_lo, ldc);
+            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, 0, 0, E, F, OutPlanes{{C_hi, C_lo, nullptr, nullptr}},
+            ldc);
     else if constexpr (NS == kSlices)
         sliced_gemm_kernel<Cfg, false><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, A_slices, B_slices, levels, ldl, plane, nullptr, nullptr, nullptr, nullptr, 0);
+            m, n, ga.KB, tiles_n, A_slices, B_slices, levels, ldl, plane, nullptr, nullptr,
+            OutPlanes{{nullptr, nullptr, nullptr, nullptr}}, 0);
     else
         return hipErrorInvalidValue;  // level planes are offered for the double-double product only
     return hipGetLastError();
@@ -251,6 +272,21 @@ hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const dou
         case 8: return launch_gemm_ns<8>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
+                          const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
+                          hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    using Cfg = ConfigFor<kQdSlices>::type;
+    const PackGeom ga(m, k);
+    constexpr int BM = Cfg::kTBM * 16, BN = Cfg::kTBN * 16;
+    const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
+    const int64_t tiles = tiles_m * tiles_n;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    sliced_gemm_kernel<Cfg, true><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
+        m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, 0, 0, E, F, C, ldc);
+    return hipGetLastError();
 }
 
 hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,

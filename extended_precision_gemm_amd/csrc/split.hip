@@ -11,47 +11,15 @@
 // (which overflows for E < -919) is ever formed in floating point.
 #include "common.hpp"
 #include "eft.hpp"
+#include "split_common.hpp"
 
 namespace ddg {
 namespace {
-
-constexpr int kNoExp = 0;          // encoded "no nonzero entry seen"
-constexpr int kExpBias = 4096;     // encoded exponent = frexp exponent + bias (>= 1)
-constexpr uint64_t kMant = (1ull << 52) - 1;
-
-// frexp exponent of a nonzero finite double: smallest e with |x| < 2^e.
-__device__ __forceinline__ int frexp_exponent(double x) {
-    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x)) & 0x7FFFFFFFFFFFFFFFull;
-    const int be = static_cast<int>(b >> 52);
-    if (be != 0) return be - 1022;
-    return (64 - __clzll(static_cast<long long>(b & kMant))) - 1074;
-}
 
 // Encoded exponent of RN(hi + lo), kNoExp for zero.
 __device__ __forceinline__ int entry_exp_code(double hi, double lo) {
     const double s = hi + lo;
     return s == 0.0 ? kNoExp : frexp_exponent(s) + kExpBias;
-}
-
-__device__ __forceinline__ int decode_exp(int code) { return code == kNoExp ? 0 : code - kExpBias; }
-
-__device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-// |x| = mant * 2^exp for a finite double (sign ignored); mant < 2^53.
-__device__ __forceinline__ void decompose(double x, uint64_t& mant, int& exp) {
-    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x)) & 0x7FFFFFFFFFFFFFFFull;
-    const int be = static_cast<int>(b >> 52);
-    mant = b & kMant;
-    if (be != 0) {
-        mant |= 1ull << 52;
-        exp = be - 1075;
-    } else {
-        exp = -1074;
-    }
 }
 
 // floor(y * 2^sh) for y = +-mant (mant < 2^53, y's sign given by neg); the
@@ -137,12 +105,6 @@ __global__ void __launch_bounds__(256) exp_rows_kernel(int64_t rows, int64_t col
     }
 }
 
-__global__ void fill_int_kernel(int32_t* __restrict__ p, int64_t count, int32_t v) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        p[i] = v;
-}
-
 // Column exponents (axis 1, the B operand): each thread takes one column over a
 // chunk of rows and folds its encoded maximum in with a device-memory atomicMax.
 __global__ void __launch_bounds__(256) exp_cols_kernel(int64_t rows, int64_t cols,
@@ -157,12 +119,6 @@ __global__ void __launch_bounds__(256) exp_cols_kernel(int64_t rows, int64_t col
     int code = kNoExp;
     for (int64_t r = r0; r < r1; ++r) code = max(code, entry_exp_code(hi[r * ld + col], lo ? lo[r * ld + col] : 0.0));
     if (code != kNoExp) atomicMax(codes + col, code);
-}
-
-__global__ void decode_exps_kernel(int32_t* __restrict__ exps, int64_t count) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        exps[i] = decode_exp(exps[i]);
 }
 
 // One thread per packed (fragment, lane) position; writes the NS slices of
@@ -298,13 +254,6 @@ __global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t 
 // Blocks needed before the one-pass block kernel beats two streaming passes
 // (measured: 4096 blocks of k = 512 win, 256 blocks of k = 4096 lose).
 constexpr int64_t kFusedMinBlocks = 1024;
-
-inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap) {
-    int64_t g = (work + per_block - 1) / per_block;
-    if (g < 1) g = 1;
-    if (g > cap) g = cap;
-    return static_cast<unsigned>(g);
-}
 
 template <int NS>
 hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,

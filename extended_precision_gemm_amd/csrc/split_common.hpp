@@ -1,0 +1,64 @@
+// Helpers shared by the double-double and quad-double slicers: exponent
+// encoding for max-reductions, exact decomposition of a double, and two small
+// utility kernels.
+#pragma once
+
+#include "common.hpp"
+
+namespace ddg {
+namespace {
+
+constexpr int kNoExp = 0;          // encoded "no nonzero entry seen"
+constexpr int kExpBias = 4096;     // encoded exponent = frexp exponent + bias (>= 1)
+constexpr uint64_t kMant = (1ull << 52) - 1;
+
+// frexp exponent of a nonzero finite double: smallest e with |x| < 2^e.
+__device__ __forceinline__ int frexp_exponent(double x) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x)) & 0x7FFFFFFFFFFFFFFFull;
+    const int be = static_cast<int>(b >> 52);
+    if (be != 0) return be - 1022;
+    return (64 - __clzll(static_cast<long long>(b & kMant))) - 1074;
+}
+
+__device__ __forceinline__ int decode_exp(int code) { return code == kNoExp ? 0 : code - kExpBias; }
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// |x| = mant * 2^exp for a finite double (sign ignored); mant < 2^53.
+__device__ __forceinline__ void decompose(double x, uint64_t& mant, int& exp) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(x)) & 0x7FFFFFFFFFFFFFFFull;
+    const int be = static_cast<int>(b >> 52);
+    mant = b & kMant;
+    if (be != 0) {
+        mant |= 1ull << 52;
+        exp = be - 1075;
+    } else {
+        exp = -1074;
+    }
+}
+
+__global__ void fill_int_kernel(int32_t* __restrict__ p, int64_t count, int32_t v) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = v;
+}
+
+__global__ void decode_exps_kernel(int32_t* __restrict__ exps, int64_t count) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        exps[i] = decode_exp(exps[i]);
+}
+
+inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap) {
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return static_cast<unsigned>(g);
+}
+
+}  // namespace
+}  // namespace ddg

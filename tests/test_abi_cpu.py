@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ddgemm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -19,16 +20,20 @@ def ddg():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dd\w+|ddgemm_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:dd|qd)\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for required in ("dd_gemm", "dd_gemm_ws", "dd_gemm_workspace_size", "dd_split_balanced",
                      "dd_sliced_gemm", "dd_renorm_levels", "dd_sliced_gemm_renorm",
-                     "ddgemm_status_string", "dd_split_slices_bytes"):
+                     "ddgemm_status_string", "dd_split_slices_bytes", "qd_gemm", "qd_gemm_ws",
+                     "qd_split_balanced", "qd_sliced_gemm_renorm", "qd_split_slices_bytes",
+                     "qd_gemm_workspace_size"):
         assert required in names
 
 
@@ -169,3 +174,66 @@ def test_n_slice_sizes_and_validation(ddg):
     assert L.dd_gemm_ws_ns(4, 5, 6, 4, P[0], P[1], 6, P[2], P[3], 5, P[4], P[5], 5, P[6], 10, None) == \
         ddg.ERROR_WORKSPACE
     assert L.dd_gemm_ws_ns(0, 5, 6, 4, None, None, 6, None, None, 5, None, None, 5, None, 0, None) == 0
+
+
+def _arr(*ptrs):
+    return (ctypes.c_void_p * 4)(*(list(ptrs) + [None] * (4 - len(ptrs))))
+
+
+def test_qd_sizes(ddg):
+    L = ddg.lib
+    assert L.qd_split_slices_bytes(130, 33) == 256 * 48 * 16 * 8
+    assert L.qd_split_slices_bytes(0, 33) == 0
+    assert L.qd_split_slices_bytes(-1, 33) == 0
+    r = lambda x: (x + 255) // 256 * 256
+    m, n, k = 100, 70, 33
+    assert L.qd_gemm_workspace_size(m, n, k) == (r(L.qd_split_slices_bytes(m, k)) + r(L.qd_split_slices_bytes(n, k))
+                                                  + r(4 * m) + r(4 * n))
+    assert L.qd_gemm_workspace_size(4, 4, ddg.QD_K_MAX) > 0
+    assert L.qd_gemm_workspace_size(4, 4, ddg.QD_K_MAX + 1) == 0
+    assert ddg.QD_K_MAX == 67108865 // 16
+
+
+def test_qd_argument_validation(ddg):
+    L = ddg.lib
+    INV, WS = ddg.ERROR_INVALID_VALUE, ddg.ERROR_WORKSPACE
+    A, B, C = _arr(P[0], P[1]), _arr(P[2]), _arr(P[3], P[3] + 4096, P[3] + 8192, P[3] + 12288)
+    need = L.qd_gemm_workspace_size(4, 5, 6)
+
+    def gemm(m=4, n=5, k=6, A=A, lda=6, B=B, ldb=5, C=C, ldc=5, ws=P[6], ws_bytes=need):
+        return L.qd_gemm_ws(m, n, k, A, lda, B, ldb, C, ldc, ws, ws_bytes, None)
+
+    assert gemm(m=-1) == INV
+    assert gemm(k=ddg.QD_K_MAX + 1, lda=ddg.QD_K_MAX + 1) == INV
+    assert gemm(lda=5) == INV
+    assert gemm(ldb=4) == INV
+    assert gemm(ldc=4) == INV
+    assert gemm(A=None) == INV
+    assert gemm(A=_arr(None, P[1])) == INV                                 # first component missing
+    assert gemm(C=_arr(P[3], P[3] + 4096, None, P[3] + 12288)) == INV       # an output plane missing
+    assert gemm(C=_arr(P[3], P[3] + 64, P[3] + 8192, P[3] + 12288)) == INV  # output planes overlap
+    assert gemm(C=_arr(P[0], P[3] + 4096, P[3] + 8192, P[3] + 12288)) == INV  # C aliases A
+    assert gemm(C=_arr(P[3], P[3] + 4096, P[3] + 8192, P[1] + 8)) == INV     # C overlaps A's x1
+    assert gemm(ws_bytes=10) == WS
+    assert gemm(ws=P[6] + 8) == WS
+    assert gemm(m=0, A=None, B=None, C=None) == 0                           # empty: no-op
+    assert L.qd_gemm(0, 5, 6, None, 6, None, 5, None, 5, None) == 0
+    assert L.qd_gemm(3, 3, 3, A, 3, B, 3, None, 3, None) == INV
+    # stage calls
+    assert L.qd_split_balanced(4, 4, A, 4, 2, P[4], P[5], None) == INV          # bad axis
+    assert L.qd_split_balanced(4, 4, A, 3, 0, P[4], P[5], None) == INV          # ld < cols
+    assert L.qd_split_balanced(4, 4, _arr(None), 4, 0, P[4], P[5], None) == INV
+    assert L.qd_split_balanced(4, 4, A, 4, 0, None, P[5], None) == INV
+    assert L.qd_split_balanced(4, 4, A, 4, 0, P[4], None, None) == INV
+    assert L.qd_split_balanced(ddg.QD_K_MAX + 1, 1, A, 1, 1, P[4], P[5], None) == INV
+    assert L.qd_split_balanced(0, 4, None, 4, 0, None, None, None) == 0
+    assert L.qd_sliced_gemm_renorm(4, 4, 4, P[0], P[1], P[2], P[3], C, 3, None) == INV   # ldc < n
+    assert L.qd_sliced_gemm_renorm(4, 4, 4, P[0], None, P[2], P[3], C, 4, None) == INV
+    assert L.qd_sliced_gemm_renorm(4, 4, 4, P[0], P[1], P[2], P[3], None, 4, None) == INV
+
+
+def test_qd_valid_call_without_gpu_reports_device_error(ddg):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert ddg.lib.qd_split_balanced(4, 4, _arr(P[0]), 4, 0, P[1], P[2], None) == ddg.ERROR_DEVICE

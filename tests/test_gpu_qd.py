@@ -1,0 +1,268 @@
+"""Parity of the quad-double HIP path with the CPU oracle (GPU tests; C ABI).
+
+Bars:
+* exponents, every one of the sixteen slices, and the whole chain (slices ->
+  level sums -> exact total -> nearest four-double result) are bit-exact
+  against oracle/qd.py, on small shapes spanning several tiles with ragged
+  edges, on edge-case entries, and on sampled outputs of the full workloads in
+  the configuration the bench times;
+* the product is within oracle/qd.py's error bound of the exact product
+  (Python integers), all entries at 64^3 and sampled entries at full size.
+Every expected value comes from oracle/ on the same seeded inputs.
+"""
+import sys
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import exact, qd
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    import torch
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _bits_equal(a, b):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    return a.shape == b.shape and np.array_equal(a.view(np.int64), b.view(np.int64))
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _unpack(packed, outer, k, nslices=16):
+    from extended_precision_gemm_amd import layout
+    return _host(layout.unpack(packed, outer, k, nslices).contiguous())
+
+
+# Entries whose rounding decides the exponent, or whose lower components reach
+# far below the window with either sign (all normalised quad doubles).
+_SPECIAL = [
+    (1.0, -(2.0 ** -54), 0.0, 0.0),                    # RN = 1 (tie to even)
+    (1.0, -(2.0 ** -53), 0.0, 0.0),                    # 1 - 2^-53 exactly
+    (1.0, -(2.0 ** -54), -(2.0 ** -110), 0.0),         # just below the tie
+    (2.0 - 2.0 ** -52, 2.0 ** -53, 0.0, 0.0),          # tie rounds up to 2
+    (2.0 - 2.0 ** -52, 2.0 ** -53, -(2.0 ** -120), 0.0),
+    (-(2.0 - 2.0 ** -52), -(2.0 ** -53), 0.0, 0.0),
+    (1.0, 2.0 ** -60, -(2.0 ** -300), 0.0),            # negative tail far below: floor borrows
+    (-1.0, -(2.0 ** -60), 2.0 ** -300, 0.0),
+    (0.75, 2.0 ** -56, -(2.0 ** -112), 2.0 ** -170),
+    (5e-324, 0.0, 0.0, 0.0),
+    (3 * 5e-324, 0.0, 0.0, 0.0),
+    (2.0 ** -1022, 0.0, 0.0, 0.0),
+    (2.0 ** 900 * 1.25, 2.0 ** 840, -(2.0 ** 780), 2.0 ** 700),
+    (0.0, 0.0, 0.0, 0.0),
+]
+
+
+def _edge_matrix(rows, cols, seed):
+    """Random normalised quad doubles with the special entries planted, a zero row."""
+    X = workloads.random_qd((rows, cols), seed, "signed_exp30")
+    rng = np.random.default_rng(seed)
+    for q, e in enumerate(_SPECIAL):
+        i, j = int(rng.integers(rows)), int(rng.integers(cols))
+        X[:, i, j] = e
+        if q % 3 == 0 and rows > 4:
+            X[:, (i + 1) % rows, :] *= 2.0 ** -200  # a row far below its neighbours
+    if rows > 2:
+        X[:, rows // 2, :] = 0.0
+    for i in range(rows):
+        for j in range(cols):
+            assert qd.is_normalized(X[:, i, j])
+    return X
+
+
+def _oracle_slice_values(D):
+    return exact.slice_values(D)
+
+
+# ---------------------------------------------------------------------------
+# slicing
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,cols", [(1, 1), (17, 5), (40, 33), (130, 21), (5, 140)])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_qd_split_bit_exact(gpu, rows, cols, axis):
+    _say(f"[qd split] {rows}x{cols} axis={axis}")
+    X = _edge_matrix(rows, cols, 100 + rows + cols + axis)
+    E, packed = gpu.qd_split_balanced(_dev(X), axis)
+    if axis == 0:
+        E_ref, D = qd.slice_rows(X)
+        outer, k = rows, cols
+    else:
+        E_ref, D = qd.slice_cols(X)
+        D = D.transpose(0, 2, 1)
+        outer, k = cols, rows
+    assert np.array_equal(_host(E), E_ref)
+    assert _bits_equal(_unpack(packed, outer, k), _oracle_slice_values(D))
+
+
+def test_qd_split_null_components_and_stride(gpu):
+    import torch
+    X = workloads.random_qd((37, 29), 7, "uniform")
+    X[2:] = 0.0
+    big = torch.zeros((2, 37, 40), dtype=torch.float64, device="cuda")
+    big[0, :, :29] = _dev(X[0])
+    big[1, :, :29] = _dev(X[1])
+    E, packed = gpu.qd_split_balanced([big[0, :, :29], big[1, :, :29], None, None], 0)
+    E_ref, D = qd.slice_rows(X)
+    assert np.array_equal(_host(E), E_ref)
+    assert _bits_equal(_unpack(packed, 37, 29), _oracle_slice_values(D))
+
+
+def test_qd_split_of_double_double_matches_dd_slicer(gpu):
+    """Top eight of the sixteen slices of (hi, lo, 0, 0) are the double-double slices."""
+    hi, lo = workloads.random_dd((70, 45), 12, "signed_exp30")
+    for axis in (0, 1):
+        Eq, pq = gpu.qd_split_balanced([_dev(hi), _dev(lo)], axis)
+        Ed, pd = gpu.split_balanced(_dev(hi), _dev(lo), axis)
+        outer, k = (70, 45) if axis == 0 else (45, 70)
+        assert np.array_equal(_host(Eq), _host(Ed))
+        assert _bits_equal(_unpack(pq, outer, k)[:8], _unpack(pd, outer, k, 8))
+
+
+# ---------------------------------------------------------------------------
+# the chain
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,n,k", [(1, 1, 1), (64, 64, 64), (100, 70, 33), (33, 130, 17), (130, 65, 200)])
+def test_qd_chain_bit_exact(gpu, m, n, k):
+    _say(f"[qd chain] {m}x{n}x{k}")
+    A = workloads.random_qd((m, k), 200 + m, "uniform")
+    B = workloads.random_qd((k, n), 300 + n, "signed_exp20")
+    C = gpu.qd_gemm(_dev(A), _dev(B))
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert _bits_equal(_host(C), C_ref)
+
+
+def test_qd_chain_edge_entries_bit_exact(gpu):
+    A = _edge_matrix(40, 36, 401)
+    B = _edge_matrix(36, 23, 402)
+    # keep the products finite: scale the huge planted entries down
+    A[:, np.abs(A[0]) > 2.0 ** 500] *= 2.0 ** -800
+    B[:, np.abs(B[0]) > 2.0 ** 500] *= 2.0 ** -800
+    C = gpu.qd_gemm(_dev(A), _dev(B))
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert _bits_equal(_host(C), C_ref)
+
+
+def test_qd_subnormal_and_zero_outputs_bit_exact(gpu):
+    A = workloads.random_qd((20, 30), 501, "uniform") * 2.0 ** -560
+    B = workloads.random_qd((30, 25), 502, "uniform") * 2.0 ** -520
+    A[:, 3, :] = 0.0
+    B[:, :, 4] = 0.0
+    C = gpu.qd_gemm(_dev(A), _dev(B))
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    got = _host(C)
+    assert _bits_equal(got, C_ref)
+    assert (np.abs(got[0]) < 2.0 ** -1022).any()          # subnormal results occur
+
+
+def test_qd_identity_returns_truncated_operand(gpu):
+    B = workloads.random_qd((48, 37), 601, "signed_exp20")
+    A = np.zeros((4, 48, 48))
+    A[0] = np.eye(48)
+    C = _host(gpu.qd_gemm(_dev(A), _dev(B)))
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert _bits_equal(C, C_ref)
+
+
+def test_qd_entry_points_agree(gpu):
+    import torch
+    m, n, k = 90, 77, 51
+    A = workloads.random_qd((m, k), 701, "normal")
+    B = workloads.random_qd((k, n), 702, "uniform")
+    dA, dB = _dev(A), _dev(B)
+    C1 = _host(gpu.qd_gemm(dA, dB))
+    C2 = _host(gpu.qd_gemm_alloc(dA, dB))
+    E, As = gpu.qd_split_balanced(dA, 0)
+    F, Bs = gpu.qd_split_balanced(dB, 1)
+    C3 = _host(gpu.qd_sliced_gemm_renorm(m, n, k, As, E, Bs, F))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C4 = gpu.qd_gemm(dA, dB, stream=s)
+    s.synchronize()
+    # strided output planes
+    out = torch.full((4, m, n + 9), 7.0, dtype=torch.float64, device="cuda")
+    gpu.qd_gemm(dA, dB, C=[out[c, :, :n] for c in range(4)])
+    C5 = _host(out[:, :, :n].contiguous())
+    assert (_host(out[:, :, n:]) == 7.0).all()
+    for Cx in (C2, C3, _host(C4), C5):
+        assert _bits_equal(Cx, C1)
+
+
+def test_qd_k_zero_and_empty(gpu):
+    import torch
+    A = torch.zeros((4, 5, 0), dtype=torch.float64, device="cuda")
+    B = torch.zeros((4, 0, 6), dtype=torch.float64, device="cuda")
+    C = torch.full((4, 5, 6), 3.0, dtype=torch.float64, device="cuda")
+    gpu.qd_gemm(A, B, C=C)
+    assert _bits_equal(_host(C), np.zeros((4, 5, 6)))
+    E = gpu.qd_gemm(torch.zeros((4, 0, 3), dtype=torch.float64, device="cuda"),
+                    torch.zeros((4, 3, 4), dtype=torch.float64, device="cuda"))
+    assert tuple(E.shape) == (4, 0, 4)
+
+
+# ---------------------------------------------------------------------------
+# workloads: accuracy against the exact product, bit-exact sampled outputs
+# ---------------------------------------------------------------------------
+def _oracle_entry(A, B, i, j):
+    """The oracle's chain for one output entry: its row of A, its column of B."""
+    E, DA = qd.slice_rows(A, rows=[i])
+    F, DB = qd.slice_cols(B, cols=[j])
+    S = qd.level_sums(DA, DB)
+    return int(E[0]), int(F[0]), qd.renorm_levels(S, E, F)[:, 0, 0]
+
+
+@pytest.mark.parametrize("name,samples", [("qd64", None), ("qd1024", 24), ("qd2048", 12), ("qd4096_exp20", 6)])
+def test_qd_workload_parity(gpu, name, samples):
+    w = workloads.by_name(name)
+    _say(f"[qd workload] {name} m={w.m} n={w.n} k={w.k}")
+    A, B = workloads.make_qd_operands(w)
+    dA, dB = _dev(A), _dev(B)
+    E, As = gpu.qd_split_balanced(dA, 0)
+    F, Bs = gpu.qd_split_balanced(dB, 1)
+    C = gpu.qd_sliced_gemm_renorm(w.m, w.n, w.k, As, E, Bs, F)
+    Eh, Fh = _host(E), _host(F)
+    del As, Bs
+    if samples is None:
+        rows = [i for i in range(w.m) for _ in range(w.n)]
+        cols = [j for _ in range(w.m) for j in range(w.n)]
+        got = _host(C)
+        E_ref, F_ref, _, C_ref = qd.sliced_product(A, B)
+        assert np.array_equal(Eh, E_ref) and np.array_equal(Fh, F_ref)
+        assert _bits_equal(got, C_ref)
+        vals = [got[:, i, j] for i, j in zip(rows, cols)]
+    else:
+        rng = np.random.default_rng(w.m + samples)
+        rows = [int(x) for x in rng.integers(0, w.m, samples)] + [0, w.m - 1]
+        cols = [int(x) for x in rng.integers(0, w.n, samples)] + [w.n - 1, 0]
+        import torch
+        ri = torch.as_tensor(rows, device="cuda")
+        ci = torch.as_tensor(cols, device="cuda")
+        got = _host(C[:, ri, ci])
+        vals = [got[:, q] for q in range(len(rows))]
+        for q, (i, j) in enumerate(zip(rows, cols)):
+            Ei, Fj, ref = _oracle_entry(A, B, i, j)
+            assert Ei == Eh[i] and Fj == Fh[j]
+            assert _bits_equal(got[:, q], ref), (i, j)
+    exact_vals = qd.exact_entries(A, B, rows, cols)
+    err = np.array([float(abs(sum(Fraction(float(c)) for c in v) - e)) for v, e in zip(vals, exact_vals)])
+    bound = qd.error_bound(A[0], B[0], Eh, Fh, rows, cols)
+    ratio = float((err / bound).max())
+    absAB = np.einsum("qk,kq->q", np.abs(A[0])[rows, :], np.abs(B[0])[:, cols])
+    rel = float((err / absAB).max())
+    _say(f"[qd parity] {name}: max err/bound = {ratio:.3e}, max err/(|A||B|) = {rel:.3e}")
+    assert ratio <= 1.0
