@@ -6,6 +6,10 @@ slice A (row exponents), slice B (column exponents), fused sliced GEMM +
 renormalisation epilogue.  HIP events on the same stream bracket each stage, so
 the dominant kernel's launch duration is measured live inside the timed region.
 
+With a quad-double workload (``--workload qd1024``, ``qd2048``, ``qd4096_exp20``)
+the step is the quad-double product: slice A and B into sixteen slices, then
+the fused 136-pair GEMM with the exact four-double epilogue.
+
 Prints ONE JSON line.  Default workload: the 4096^3 product with per-entry
 exponents in [-20, 20].
 """
@@ -29,6 +33,10 @@ PAIRS = 36                     # slice pairs with s + t <= 7
 # sliced operands, tensor-core product, assemble; unstated NVIDIA GPU): 7.93621 s
 # ("Multiple Double Arithmetic on NVIDIA Tensor Cores", §4.2, Table 1, t_TC).
 PAGES_TTC_4096_S = 7.93621
+# The pages' quad-double full-path times (same table): n = 1024 and n = 2048.
+PAGES_QD_TTC_S = {1024: 0.752966, 2048: 4.23463}
+QD_METRIC = "effective quad-double GFLOP/s (2mnk/t); % of sliced FP64-MFMA roof (peak / 136 pairs)"
+QD_PAIRS = 136
 
 
 def _parse():
@@ -87,6 +95,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     w = workloads.by_name(args.workload)
+    if w in workloads.QD_WORKLOADS:
+        return _run_qd(args, w)
     m, n, k = w.m, w.n, w.k
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.name} (m={m} n={n} k={k})", file=sys.stderr, flush=True)
@@ -234,6 +244,123 @@ def main():
                                       exact.balancing_exponents(Bh, Bl, 1), ns)
             ratio = float((np.abs((gh - Rh) + (gl - Rl)) / bound).max())
             rec["parity_sample"] = {"rows": rows, "max_err_over_bound": ratio, "ok": bool(ratio <= 1.0)}
+    print(json.dumps(rec), flush=True)
+
+
+def _run_qd(args, w):
+    """The quad-double product: slice A, slice B, fused sliced GEMM + exact epilogue."""
+    import numpy as np
+    import torch
+
+    import extended_precision_gemm_amd as ddg
+    import workloads
+
+    m, n, k = w.m, w.n, w.k
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.name} (m={m} n={n} k={k})", file=sys.stderr, flush=True)
+    A, B = workloads.make_qd_operands(w)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    C = torch.empty((4, m, n), dtype=torch.float64, device=dev)
+    E = torch.empty(m, dtype=torch.int32, device=dev)
+    F = torch.empty(n, dtype=torch.int32, device=dev)
+    As = torch.empty(ddg.qd_slices_bytes(m, k) // 8, dtype=torch.float64, device=dev)
+    Bs = torch.empty(ddg.qd_slices_bytes(n, k) // 8, dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(events=None):
+        if events:
+            events[0].record(stream)
+        ddg.qd_split_balanced(dA, 0, E, As, stream)
+        ddg.qd_split_balanced(dB, 1, F, Bs, stream)
+        if events:
+            events[1].record(stream)
+        ddg.qd_sliced_gemm_renorm(m, n, k, As, E, Bs, F, C, stream)
+        if events:
+            events[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    value = 2.0 * m * n * k / (elapsed / args.steps) / 1e9
+    gemm_tflops = QD_PAIRS * 2.0 * m * n * k / (gemm_ms * 1e-3) / 1e12
+    split_bytes = (32.0 + 128.0) * (m * k + k * n)  # four components read, sixteen slices written
+    ttc = PAGES_QD_TTC_S.get(m) if m == n == k else None
+    rec = {
+        "metric": QD_METRIC,
+        "value": round(value, 3),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (2.0 * m ** 3 / ttc / 1e9), 3) if ttc else None,
+        "vs_baseline_ref": ("pages' quad-double t_TC = %g s at n = %d (unstated NVIDIA GPU)" % (ttc, m)) if ttc
+        else None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "m": m, "n": n, "k": k, "description": w.description,
+                   "slices": 16, "slice_bits": 13, "pairs": QD_PAIRS},
+        "pct_sliced_roof": round(100.0 * value / (PEAK_FP64_MFMA_TFLOPS * 1e3 / QD_PAIRS), 2),
+        "roofline": {
+            "kernel": "sliced_gemm_kernel, 16 slices (fused exact four-double epilogue)",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 3),
+            "peak": PEAK_FP64_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP64_MFMA_TFLOPS, 4),
+            "traffic": _traffic_from_profile(w.name),
+            "flops_per_launch": QD_PAIRS * 2.0 * m * n * k,
+            "launch_ms": round(gemm_ms, 4),
+        },
+        "stages": {
+            "split_ms": round(split_ms, 4),
+            "split_GBps": round(split_bytes / (split_ms * 1e-3) / 1e9, 1),
+            "split_frac_hbm": round(split_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gemm_ms": round(gemm_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        from fractions import Fraction
+
+        from oracle import qd
+        # the exact-integer oracle, one entry at a time, for about cpu_seconds
+        rng = np.random.default_rng(7)
+        rows, cols = [], []
+        t = time.perf_counter()
+        exact_vals = []
+        while time.perf_counter() - t < args.cpu_seconds and len(rows) < m * n:
+            i, j = int(rng.integers(m)), int(rng.integers(n))
+            exact_vals += qd.exact_entries(A, B, [i], [j])
+            rows.append(i)
+            cols.append(j)
+        t_cpu = time.perf_counter() - t
+        rec["cpu_baseline"] = {
+            "value": round(2.0 * k * len(rows) / t_cpu / 1e9, 6), "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(rows)} random entries of C by the exact-integer oracle ({t_cpu:.1f} s, one thread)",
+        }
+        ri = torch.as_tensor(rows, device=dev)
+        ci = torch.as_tensor(cols, device=dev)
+        got = C[:, ri, ci].cpu().numpy()
+        err = np.array([float(abs(sum(Fraction(float(c)) for c in got[:, q]) - e))
+                        for q, e in enumerate(exact_vals)])
+        Eh, Fh = E.cpu().numpy(), F.cpu().numpy()
+        bound = qd.error_bound(A[0], B[0], Eh, Fh, rows, cols)
+        absAB = np.einsum("qk,kq->q", np.abs(A[0])[rows, :], np.abs(B[0])[:, cols])
+        ratio = float((err / bound).max())
+        rec["parity_sample"] = {"entries": len(rows), "max_err_over_bound": ratio,
+                                "max_err_over_absAB": float((err / absAB).max()), "ok": bool(ratio <= 1.0)}
     print(json.dumps(rec), flush=True)
 
 
