@@ -77,6 +77,17 @@ def _traffic_from_profile(workload: str):
         return None
 
 
+def _calibration_copy(args, dev):
+    """One device copy of known size first, so HBM counters can be scaled by it."""
+    import torch
+    if args.calib_copy_mib > 0:
+        x = torch.ones(args.calib_copy_mib * (1 << 20) // 8, dtype=torch.float64, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -111,12 +122,7 @@ def main():
     As = torch.empty(ddg.slices_bytes(m, k, ns) // 8, dtype=torch.float64, device=dev)
     Bs = torch.empty(ddg.slices_bytes(n, k, ns) // 8, dtype=torch.float64, device=dev)
 
-    if args.calib_copy_mib > 0:
-        x = torch.ones(args.calib_copy_mib * (1 << 20) // 8, dtype=torch.float64, device=dev)
-        y = torch.empty_like(x)
-        y.copy_(x)
-        torch.cuda.synchronize()
-        del x, y
+    _calibration_copy(args, dev)
 
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -266,6 +272,7 @@ def _run_qd(args, w):
     F = torch.empty(n, dtype=torch.int32, device=dev)
     As = torch.empty(ddg.qd_slices_bytes(m, k) // 8, dtype=torch.float64, device=dev)
     Bs = torch.empty(ddg.qd_slices_bytes(n, k) // 8, dtype=torch.float64, device=dev)
+    _calibration_copy(args, dev)
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
 
