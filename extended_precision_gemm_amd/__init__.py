@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libddgemm.so")
 
 NUM_SLICES = 8          # the double-double product
 MIN_SLICES = 4          # the pages' four quarters of a leading double
+MAX_SLICES = 16         # double-double inputs with windows 13 * (n - 8) bits deeper
 NUM_LEVELS = 8
 SLICE_BITS = 13
 K_MAX = 8388608
@@ -137,6 +138,11 @@ def _check_lo(lo, hi, name):
         raise ValueError(f"{name} must have the same strides as its hi plane")
 
 
+def k_max(nslices: int = NUM_SLICES) -> int:
+    """Largest k for n slices (§2 eq. (5): at most 67,108,865 exact terms per level sum)."""
+    return K_MAX if nslices <= NUM_SLICES else 67108865 // nslices
+
+
 def slices_bytes(outer: int, k: int, nslices: int = NUM_SLICES) -> int:
     if nslices == NUM_SLICES:
         return lib.dd_split_slices_bytes(outer, k)
@@ -231,7 +237,8 @@ def _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo):
 def dd_gemm(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, workspace=None, stream=None,
             nslices: int = NUM_SLICES):
     """C = A·B; returns (C_hi, C_lo).  ``nslices`` = 8 is the double-double
-    product; 4..7 keep fewer slices (n(n+1)/2 pairs) for less accuracy and time.
+    product; 4..7 keep fewer slices (n(n+1)/2 pairs) for less accuracy and time,
+    9..16 more, for entries far below their row's (column's) largest.
     The workspace comes from PyTorch's allocator unless a uint8 device tensor of
     at least workspace_size(m, n, k, nslices) bytes is given."""
     m, n, k, lda, ldb, ldc, C_hi, C_lo = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)

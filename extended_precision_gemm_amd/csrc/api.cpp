@@ -52,7 +52,9 @@ ddgemm_status_t check_device() {
 
 inline ddgemm_status_t launched(hipError_t e) { return e == hipSuccess ? DDGEMM_SUCCESS : DDGEMM_ERROR_LAUNCH; }
 
-inline bool ns_ok(int ns) { return ns >= kMinSlices && ns <= kSlices; }
+inline bool ns_ok(int ns) { return ns >= kMinSlices && ns <= kMaxSlices; }
+
+inline int64_t k_max(int ns) { return DDGEMM_K_MAX_NS(ns); }
 
 ddgemm_status_t validate_split(int64_t rows, int64_t cols, const double* X_hi, int64_t ldx, int axis, int ns,
                                const int32_t* exps, const double* slices) {
@@ -60,7 +62,7 @@ ddgemm_status_t validate_split(int64_t rows, int64_t cols, const double* X_hi, i
         return DDGEMM_ERROR_INVALID_VALUE;
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
-    if (k > DDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
+    if (k > k_max(ns)) return DDGEMM_ERROR_INVALID_VALUE;
     if (rows * cols > 0 && !X_hi) return DDGEMM_ERROR_INVALID_VALUE;
     if (outer > 0 && !exps) return DDGEMM_ERROR_INVALID_VALUE;
     if (dd_split_slices_bytes_ns(outer, k, ns) > 0 && !slices) return DDGEMM_ERROR_INVALID_VALUE;
@@ -108,14 +110,14 @@ ddgemm_status_t validate_qd_gemm_dims(int64_t m, int64_t n, int64_t k) {
 extern "C" {
 
 size_t dd_split_slices_bytes_ns(int64_t outer, int64_t k, int nslices) {
-    if (!size_ok(outer, k) || !ns_ok(nslices)) return 0;
+    if (!ns_ok(nslices) || !size_ok(outer, k) || !size_ok(outer, k * nslices)) return 0;
     return static_cast<size_t>(PackGeom(outer, k).doubles(nslices)) * sizeof(double);
 }
 
 size_t dd_split_slices_bytes(int64_t outer, int64_t k) { return dd_split_slices_bytes_ns(outer, k, kSlices); }
 
 size_t dd_gemm_workspace_size_ns(int64_t m, int64_t n, int64_t k, int nslices) {
-    if (validate_gemm_dims(m, n, k) != DDGEMM_SUCCESS || !ns_ok(nslices)) return 0;
+    if (validate_gemm_dims(m, n, k) != DDGEMM_SUCCESS || !ns_ok(nslices) || k > k_max(nslices)) return 0;
     return align_up(dd_split_slices_bytes_ns(m, k, nslices)) + align_up(dd_split_slices_bytes_ns(n, k, nslices)) +
            align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4);
 }
@@ -169,7 +171,8 @@ ddgemm_status_t dd_sliced_gemm_renorm_ns(int64_t m, int64_t n, int64_t k, int ns
                                          const int32_t* E, const double* B_slices, const int32_t* F,
                                          double* C_hi, double* C_lo, int64_t ldc, void* stream) {
     ddgemm_status_t st = validate_gemm_dims(m, n, k);
-    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, n) || !ns_ok(nslices)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, n) || !ns_ok(nslices) || k > k_max(nslices))
+        return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!E || !F || !C_hi || !C_lo || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
     const int64_t ce = extent(m, n, ldc);
@@ -191,7 +194,7 @@ ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices, cons
                               size_t ws_bytes, void* stream) {
     ddgemm_status_t st = validate_gemm_dims(m, n, k);
     if (st != DDGEMM_SUCCESS) return st;
-    if (!ns_ok(nslices)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!ns_ok(nslices) || k > k_max(nslices)) return DDGEMM_ERROR_INVALID_VALUE;
     if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return DDGEMM_ERROR_INVALID_VALUE;

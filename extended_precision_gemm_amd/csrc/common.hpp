@@ -13,6 +13,7 @@ namespace ddg {
 constexpr int kSliceBits = DDGEMM_SLICE_BITS;
 constexpr int kSlices = DDGEMM_NUM_SLICES;  // slices of the double-double product
 constexpr int kMinSlices = DDGEMM_MIN_SLICES;
+constexpr int kMaxSlices = DDGEMM_MAX_SLICES;
 constexpr int kLevels = DDGEMM_NUM_LEVELS;
 constexpr int kWindowBits = kSliceBits * kSlices;  // 104
 constexpr int kPackOuter = DDGEMM_PACK_OUTER;

@@ -12,7 +12,7 @@
 // mantissas; E is the largest frexp exponent of RN(x) over the row or column.
 #include "common.hpp"
 #include "split_common.hpp"
-#include "wide_int.hpp"
+#include "window.hpp"
 
 namespace ddg {
 namespace {
@@ -24,46 +24,6 @@ __device__ __forceinline__ void load_qd(const QdPlanes& X, int64_t idx, double (
     for (int c = 0; c < 4; ++c) x[c] = X.x[c] ? X.x[c][idx] : 0.0;
 }
 
-// floor(|x| 2^-u) for a normalised quad double x, as an L-limb integer (the
-// caller picks u so the result fits).  The components' integer parts are summed
-// with their signs; the part below the unit is, by the normalisation, smaller in
-// magnitude than one unit and has the sign of the first component that reaches
-// below the unit, so it lowers the floor by one exactly when that sign is
-// negative.
-template <int L>
-__device__ __forceinline__ WideInt<L> qd_floor_abs(const double (&x)[4], int u) {
-    WideInt<L> acc;
-    wide_zero(acc);
-    const bool neg = x[0] < 0.0;
-    bool decided = false, borrow = false;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const double y = neg ? -x[c] : x[c];
-        if (y != 0.0) {
-            uint64_t mant;
-            int e;
-            decompose(y, mant, e);  // |y| = mant 2^e
-            const bool yneg = y < 0.0;
-            const int sh = e - u;
-            if (sh >= 0) {
-                const int64_t v = static_cast<int64_t>(mant);
-                wide_add_shifted(acc, yneg ? -v : v, sh);
-            } else {
-                const int d = -sh;
-                const uint64_t t = d < 64 ? mant >> d : 0;
-                const bool frac = d < 64 ? (mant & ((1ull << d) - 1)) != 0 : true;
-                if (t != 0) wide_add_shifted(acc, yneg ? -static_cast<int64_t>(t) : static_cast<int64_t>(t), 0);
-                if (!decided && frac) {
-                    decided = true;
-                    borrow = yneg;
-                }
-            }
-        }
-    }
-    if (borrow) wide_add_shifted(acc, -1, 0);
-    return acc;
-}
-
 // Encoded frexp exponent of RN(x), kNoExp for zero.  With e = frexp exponent of
 // x0, |x| < 2^e, and M = floor(|x| 2^(55-e)) < 2^55 decides the rounding:
 // RN(x) = 2^e from M >= 2^55 - 2 (|x| >= 2^e - 2^(e-54), ties to even), RN(x)
@@ -71,7 +31,7 @@ __device__ __forceinline__ WideInt<L> qd_floor_abs(const double (&x)[4], int u) 
 __device__ __forceinline__ int qd_entry_code(const double (&x)[4]) {
     if (x[0] == 0.0) return kNoExp;
     const int e = frexp_exponent(x[0]);
-    const uint64_t M = qd_floor_abs<1>(x, e - 55).w[0];
+    const uint64_t M = floor_abs_window<1>(x, e - 55).w[0];
     const int ex = M >= (1ull << 55) - 2 ? e + 1 : (M >= (1ull << 54) - 1 ? e : e - 1);
     return ex + kExpBias;
 }
@@ -83,7 +43,7 @@ __device__ __forceinline__ void qd_slice_entry(const double (&x)[4], int E, doub
         return;
     }
     const bool neg = x[0] < 0.0;
-    const WideInt<4> N = qd_floor_abs<4>(x, E - kQdWindowBits);
+    const WideInt<4> N = floor_abs_window<4>(x, E - kQdWindowBits);
 #pragma unroll
     for (int s = 0; s < kQdSlices; ++s) {
         const int d = static_cast<int>(wide_bits64(N, kSliceBits * (kQdSlices - 1 - s)) & 0x1FFF);

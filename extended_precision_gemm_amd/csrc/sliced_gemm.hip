@@ -11,11 +11,12 @@
 // 2^53 units: the matrix-core accumulation is exact in any order.
 //
 // Work split: each wave computes a (16 RPW)x16 strip (RPW 16x16 blocks stacked;
-// RPW = 2 for up to eight slices, 1 for sixteen) with one accumulator per level
-// and block; a workgroup of WM x WN waves owns a (16 RPW WM) x (16 WN) output
-// tile, and WGS workgroups share a CU (two waves per SIMD in every
-// configuration).  The same kernel serves the quad-double product: sixteen
-// slices, 136 pairs, sixteen levels, and the exact four-double epilogue.  The operand panels move through LDS in stages
+// RPW = 2 for up to eight slices, 1 for nine to sixteen) with one accumulator
+// per level and block; a workgroup of WM x WN waves owns a (16 RPW WM) x (16 WN)
+// output tile, and WGS workgroups share a CU (two waves per SIMD in every
+// configuration).  The same kernel serves the quad-double product (QD_OUT):
+// sixteen slices, 136 pairs, sixteen levels, and the exact four-double
+// epilogue.  The operand panels move through LDS in stages
 // of KS k-blocks (4 values of k each): every (16x4 or 4x16) fragment of one
 // slice is 64 consecutive doubles in the packed planes, so a stage of one
 // 16-row (16-column) block is a contiguous KS x 4 KB run, copied with 16-byte
@@ -62,16 +63,17 @@ struct GemmConfig {
     static constexpr int kKS = KS;
     static constexpr int kBlockStage = KS * kSetDoubles;             // one block, one stage
     static constexpr int kStageDoubles = (kTBM + kTBN) * kBlockStage;
-    static constexpr int kPiecesPerBlock = kBlockStage / 128;        // 1 KB pieces
-    static constexpr int kPieces = (kTBM + kTBN) * kPiecesPerBlock;
-    static constexpr int kPiecesPerWave = kPieces / kWaves;
-    static_assert(kPieces % kWaves == 0, "pieces split evenly over the waves");
+    static constexpr int kPieces = kStageDoubles / 128;               // 1 KB pieces per stage
+    static constexpr int kPiecesPerWave = (kPieces + kWaves - 1) / kWaves;
+    static constexpr bool kEvenPieces = kPieces % kWaves == 0;
+    static_assert(kStageDoubles % 128 == 0, "a stage is whole 1 KB pieces");
+    static_assert(kEvenPieces || NBUF == 2, "uneven copies rely on the full wait of two stages");
     static_assert(NBUF >= 2 && WGS * NBUF * kStageDoubles * 8 <= 160 * 1024, "LDS budget");
     static_assert(kPackOuter % (16 * kTBM) == 0 && kPackOuter % (16 * kTBN) == 0, "tile divides the packing");
     static_assert(kPackK % (4 * KS) == 0, "stage divides the k packing");
 };
 
-template <class C, bool FUSED>
+template <class C, bool FUSED, bool QD_OUT = false>
 __global__ void __launch_bounds__(C::kThreads, C::kWGS)
 sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                    const double* __restrict__ Ap, const double* __restrict__ Bp,
@@ -93,25 +95,42 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
     const int64_t rb0 = tm * C::kTBM, cb0 = tn * C::kTBN;
     const int64_t nstages = KB / KS;  // KB is a multiple of 4 (k is packed to 16)
 
-    // Piece q of a stage: block q / kPiecesPerBlock of the stage (A blocks
-    // first, then B blocks), 1 KB piece q % kPiecesPerBlock of that block's run.
-    // Wave w copies pieces w, w + waves, ...; lane L moves bytes [16L, 16L+16).
+    // A stage in LDS is the runs of its blocks back to back (A blocks first,
+    // then B blocks), kBlockStage doubles each.  1 KB piece q of it is copied by
+    // wave q % waves; lane L moves the 16 bytes at stage offset 1024 q + 16 L,
+    // which lie in block (128 q + 2 L) / kBlockStage (a piece may straddle two
+    // runs).  When the pieces do not split evenly the last round is issued by
+    // the first kPieces % waves waves only.
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
     const double* src[C::kPiecesPerWave];
     int dst[C::kPiecesPerWave];
 #pragma unroll
     for (int i = 0; i < C::kPiecesPerWave; ++i) {
-        const int q = i * C::kWaves + wave;
-        const int blk = q / C::kPiecesPerBlock, pc = q % C::kPiecesPerBlock;
-        const double* base = blk < C::kTBM ? Ap + (rb0 + blk) * KB * C::kSetDoubles
-                                           : Bp + (cb0 + blk - C::kTBM) * KB * C::kSetDoubles;
-        src[i] = base + pc * 128 + lane * 2;
-        dst[i] = blk * C::kBlockStage + pc * 128;
+        if constexpr (C::kEvenPieces && C::kBlockStage % 128 == 0) {
+            // every piece inside one block's run: the block is uniform per piece
+            const int q = i * C::kWaves + wave;
+            const int blk = q / (C::kBlockStage / 128), pc = q % (C::kBlockStage / 128);
+            const double* base = blk < C::kTBM ? Ap + (rb0 + blk) * KB * C::kSetDoubles
+                                               : Bp + (cb0 + blk - C::kTBM) * KB * C::kSetDoubles;
+            src[i] = base + pc * 128 + lane * 2;
+            dst[i] = blk * C::kBlockStage + pc * 128;
+        } else {
+            int q = i * C::kWaves + uwave;
+            if (q >= C::kPieces) q = 0;  // not issued; keeps the address in range
+            const int g = q * 128 + lane * 2;
+            const int blk = g / C::kBlockStage, off = g % C::kBlockStage;
+            const double* base = blk < C::kTBM ? Ap + (rb0 + blk) * KB * C::kSetDoubles
+                                               : Bp + (cb0 + blk - C::kTBM) * KB * C::kSetDoubles;
+            src[i] = base + off;
+            dst[i] = q * 128;
+        }
     }
     auto issue = [&](int64_t st, int buf) {
 #pragma unroll
         for (int i = 0; i < C::kPiecesPerWave; ++i)
-            __builtin_amdgcn_global_load_lds((global_void_t*)(src[i] + st * C::kBlockStage),
-                                             (lds_void_t*)(lds + buf * C::kStageDoubles + dst[i]), 16, 0, 0);
+            if (C::kEvenPieces || i + 1 < C::kPiecesPerWave || i * C::kWaves + uwave < C::kPieces)
+                __builtin_amdgcn_global_load_lds((global_void_t*)(src[i] + st * C::kBlockStage),
+                                                 (lds_void_t*)(lds + buf * C::kStageDoubles + dst[i]), 16, 0, 0);
     };
 
     double4_t acc[NS][RPW];
@@ -171,7 +190,7 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                     for (int l = 0; l < NS; ++l) S[l] = acc[l][r][v];
                     const int sc = E[row] + F[col];
                     const int64_t idx = row * ldc + col;
-                    if constexpr (NS <= kSlices) {
+                    if constexpr (!QD_OUT) {
                         double hi, lo;
                         renorm_levels<NS>(S, sc, hi, lo);
                         out.c[0][idx] = hi;
@@ -229,8 +248,16 @@ template <> struct ConfigFor<5> { using type = GemmConfig<2, 4, 2, 2, 1, 5>; };
 template <> struct ConfigFor<6> { using type = GemmConfig<2, 4, 2, 2, 1, 6>; };
 template <> struct ConfigFor<7> { using type = GemmConfig<2, 4, 2, 2, 1, 7>; };
 template <> struct ConfigFor<8> { using type = GemmConfig<2, 4, 2, 2, 1, 8>; };
-// Sixteen slices (quad double): 16 level accumulators of one 16x16 block per
-// wave (128 registers), a 32x64 tile, one k-block per 48 KB stage.
+// Nine to sixteen slices (wide double-double windows, the quad-double product):
+// up to 16 level accumulators of one 16x16 block per wave (at most 128
+// registers), a 32x64 tile, one k-block per stage of at most 48 KB.
+template <> struct ConfigFor<9> { using type = GemmConfig<2, 4, 1, 2, 1, 9, 1>; };
+template <> struct ConfigFor<10> { using type = GemmConfig<2, 4, 1, 2, 1, 10, 1>; };
+template <> struct ConfigFor<11> { using type = GemmConfig<2, 4, 1, 2, 1, 11, 1>; };
+template <> struct ConfigFor<12> { using type = GemmConfig<2, 4, 1, 2, 1, 12, 1>; };
+template <> struct ConfigFor<13> { using type = GemmConfig<2, 4, 1, 2, 1, 13, 1>; };
+template <> struct ConfigFor<14> { using type = GemmConfig<2, 4, 1, 2, 1, 14, 1>; };
+template <> struct ConfigFor<15> { using type = GemmConfig<2, 4, 1, 2, 1, 15, 1>; };
 template <> struct ConfigFor<16> { using type = GemmConfig<2, 4, 1, 2, 1, 16, 1>; };
 
 template <int NS>
@@ -270,6 +297,14 @@ hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const dou
         case 6: return launch_gemm_ns<6>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
         case 7: return launch_gemm_ns<7>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
         case 8: return launch_gemm_ns<8>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 9: return launch_gemm_ns<9>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 10: return launch_gemm_ns<10>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 11: return launch_gemm_ns<11>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 12: return launch_gemm_ns<12>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 13: return launch_gemm_ns<13>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 14: return launch_gemm_ns<14>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 15: return launch_gemm_ns<15>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
+        case 16: return launch_gemm_ns<16>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -284,7 +319,7 @@ hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slice
     const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
     const int64_t tiles = tiles_m * tiles_n;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-    sliced_gemm_kernel<Cfg, true><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
+    sliced_gemm_kernel<Cfg, true, true><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
         m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, 0, 0, E, F, C, ldc);
     return hipGetLastError();
 }

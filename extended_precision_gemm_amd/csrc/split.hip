@@ -12,6 +12,7 @@
 #include "common.hpp"
 #include "eft.hpp"
 #include "split_common.hpp"
+#include "window.hpp"
 
 namespace ddg {
 namespace {
@@ -48,42 +49,54 @@ __device__ __forceinline__ void slice_entry(double hi, double lo, int E, double 
         return;
     }
     const bool neg = s < 0.0;
-    const double ep = neg ? -e : e;  // |x| = |s| + ep
-    uint64_t ms;
-    int es;
-    decompose(s, ms, es);
-    const int W = E - kSliceBits * NS;  // exponent of the window's last unit
-    unsigned __int128 N;
-    if (es >= W) {
-        // |s| 2^-W = ms << (es - W) is an integer below 2^(13 NS); add floor(ep 2^-W),
-        // which is below 2^51 in magnitude because |ep| <= ulp(s)/2.
-        N = static_cast<unsigned __int128>(ms) << (es - W);
-        if (ep != 0.0) {
-            uint64_t me;
-            int ee;
-            decompose(ep, me, ee);
-            const int64_t f = floor_scaled(me, ep < 0.0, ee - W);
-            N = static_cast<unsigned __int128>(static_cast<__int128>(N) + f);
+    if constexpr (NS > kSlices) {
+        // Windows wider than 128 bits: (s, e) is a normalised pair, so the exact
+        // floor comes from the 256-bit window of (s, e, 0, 0).
+        const double x[4] = {s, e, 0.0, 0.0};
+        const WideInt<4> N = floor_abs_window<4>(x, E - kSliceBits * NS);
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            const int d = static_cast<int>(wide_bits64(N, kSliceBits * (NS - 1 - q)) & 0x1FFF);
+            out[q] = ldexp(static_cast<double>(neg ? -d : d), -kSliceBits * (q + 1));
         }
     } else {
-        // |s| has bits below the window: floor((ms + ep/2^es) / 2^d) with
-        // |ep/2^es| <= 1/2 is floor(ms / 2^d), minus one exactly when ms is a
-        // multiple of 2^d and ep < 0.
-        const int d = W - es;
-        uint64_t q = 0, r = ms;
-        if (d < 64) {
-            q = ms >> d;
-            r = ms & ((1ull << d) - 1);
+        const double ep = neg ? -e : e;  // |x| = |s| + ep
+        uint64_t ms;
+        int es;
+        decompose(s, ms, es);
+        const int W = E - kSliceBits * NS;  // exponent of the window's last unit
+        unsigned __int128 N;
+        if (es >= W) {
+            // |s| 2^-W = ms << (es - W) is an integer below 2^(13 NS); add floor(ep 2^-W),
+            // which is below 2^51 in magnitude because |ep| <= ulp(s)/2.
+            N = static_cast<unsigned __int128>(ms) << (es - W);
+            if (ep != 0.0) {
+                uint64_t me;
+                int ee;
+                decompose(ep, me, ee);
+                const int64_t f = floor_scaled(me, ep < 0.0, ee - W);
+                N = static_cast<unsigned __int128>(static_cast<__int128>(N) + f);
+            }
+        } else {
+            // |s| has bits below the window: floor((ms + ep/2^es) / 2^d) with
+            // |ep/2^es| <= 1/2 is floor(ms / 2^d), minus one exactly when ms is a
+            // multiple of 2^d and ep < 0.
+            const int d = W - es;
+            uint64_t q = 0, r = ms;
+            if (d < 64) {
+                q = ms >> d;
+                r = ms & ((1ull << d) - 1);
+            }
+            if (r == 0 && ep < 0.0) q -= 1;
+            N = q;
         }
-        if (r == 0 && ep < 0.0) q -= 1;
-        N = q;
-    }
-    constexpr double kScale[kSlices] = {0x1p-13, 0x1p-26, 0x1p-39, 0x1p-52,
-                                        0x1p-65, 0x1p-78, 0x1p-91, 0x1p-104};
+        constexpr double kScale[kSlices] = {0x1p-13, 0x1p-26, 0x1p-39, 0x1p-52,
+                                            0x1p-65, 0x1p-78, 0x1p-91, 0x1p-104};
 #pragma unroll
-    for (int q = 0; q < NS; ++q) {
-        const int d = static_cast<int>(static_cast<uint64_t>(N >> (kSliceBits * (NS - 1 - q))) & 0x1FFF);
-        out[q] = static_cast<double>(neg ? -d : d) * kScale[q];
+        for (int q = 0; q < NS; ++q) {
+            const int d = static_cast<int>(static_cast<uint64_t>(N >> (kSliceBits * (NS - 1 - q))) & 0x1FFF);
+            out[q] = static_cast<double>(neg ? -d : d) * kScale[q];
+        }
     }
 }
 
@@ -309,6 +322,14 @@ hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const do
         case 6: return launch_split_ns<6>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
         case 7: return launch_split_ns<7>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
         case 8: return launch_split_ns<8>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 9: return launch_split_ns<9>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 10: return launch_split_ns<10>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 11: return launch_split_ns<11>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 12: return launch_split_ns<12>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 13: return launch_split_ns<13>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 14: return launch_split_ns<14>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 15: return launch_split_ns<15>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 16: return launch_split_ns<16>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
         default: return hipErrorInvalidValue;
     }
 }

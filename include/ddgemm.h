@@ -58,13 +58,21 @@ typedef enum {
 #define DDGEMM_NUM_LEVELS 8  /* levels l = s + t = 0..7; 36 slice pairs            */
 /* The *_ns entry points take the number of slices n per operand entry instead:
  * a 13n-bit window, n levels, n(n+1)/2 slice pairs, DDGEMM_MIN_SLICES <= n <=
- * DDGEMM_NUM_SLICES.  n = 4 is §2 eqs. (1)-(3): the four quarters of a leading
+ * DDGEMM_MAX_SLICES.  n = 4 is §2 eqs. (1)-(3): the four quarters of a leading
  * double; n = 8 is the double-double product.  Fewer slices trade accuracy
- * (about 13n - 7 bits relative to the row/column maxima) for speed. */
+ * (about 13n - 7 bits relative to the row/column maxima) for speed; more than
+ * eight keep entries that lie up to 13(n - 8) bits below their row's (column's)
+ * largest at full double-double precision -- the purpose of §3 Problem 3.2's
+ * exponent classes, a class 13c bits down being the same digits c places
+ * deeper -- for n(n+1)/2 pairs. */
 #define DDGEMM_MIN_SLICES 4
+#define DDGEMM_MAX_SLICES 16
 /* Largest k: with every level holding at most 8 pairs, the exact-sum bound of §2
- * eq. (5) (67,108,865 products of 26-bit quantities) allows 67,108,865 / 8 terms. */
+ * eq. (5) (67,108,865 products of 26-bit quantities) allows 67,108,865 / 8 terms.
+ * With n > 8 slices the deepest level holds n pairs: k <= floor(67,108,865 / n)
+ * (DDGEMM_K_MAX_NS(n)). */
 #define DDGEMM_K_MAX 8388608
+#define DDGEMM_K_MAX_NS(n) ((n) <= 8 ? DDGEMM_K_MAX : 67108865 / (n))
 
 /* Packed slice layout (the output of dd_split_balanced, the input of the GEMMs).
  *
@@ -187,8 +195,10 @@ ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k,
  * product C is the renormalised sum of the n level sums; per entry it is
  * within 2^(-13n) (2^F_j sum_p |a_ip| + 2^E_i sum_p |b_pj| + n k 2^(E_i+F_j))
  * + 2^-90 (|A||B|)_ij of the exact product, E_i and F_j the row/column
- * exponents.  Errors: as for the counterparts, plus DDGEMM_ERROR_INVALID_VALUE
- * for n outside [DDGEMM_MIN_SLICES, DDGEMM_NUM_SLICES].
+ * exponents (for n > 8 the last term covers the cascade alone, and a larger n
+ * shrinks the rest).  Errors: as for the counterparts, plus
+ * DDGEMM_ERROR_INVALID_VALUE for n outside [DDGEMM_MIN_SLICES, DDGEMM_MAX_SLICES]
+ * and k > DDGEMM_K_MAX_NS(n).
  */
 size_t dd_split_slices_bytes_ns(int64_t outer, int64_t k, int nslices);
 size_t dd_gemm_workspace_size_ns(int64_t m, int64_t n, int64_t k, int nslices);

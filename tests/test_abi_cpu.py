@@ -157,12 +157,19 @@ def test_layout_pack_unpack_roundtrip(ddg):
 def test_n_slice_sizes_and_validation(ddg):
     L = ddg.lib
     INV = ddg.ERROR_INVALID_VALUE
-    for n in range(ddg.MIN_SLICES, ddg.NUM_SLICES + 1):
+    for n in range(ddg.MIN_SLICES, ddg.MAX_SLICES + 1):
         assert L.dd_split_slices_bytes_ns(130, 33, n) == 256 * 48 * n * 8
+        kmax = ddg.k_max(n)
+        assert kmax == (8388608 if n <= 8 else 67108865 // n)
+        assert L.dd_gemm_workspace_size_ns(4, 4, kmax, n) > 0
+        assert L.dd_gemm_workspace_size_ns(4, 4, kmax + 1, n) == 0
+        assert L.dd_split_balanced_ns(4, kmax + 1, P[0], None, kmax + 1, 0, n, P[1], P[2], None) == INV
+        assert L.dd_sliced_gemm_renorm_ns(4, 4, kmax + 1, n, P[0], P[1], P[2], P[3], P[4], P[5], 4, None) == INV
     assert L.dd_split_slices_bytes_ns(130, 33, 8) == ddg.slices_bytes(130, 33)
     assert L.dd_gemm_workspace_size_ns(100, 70, 33, 8) == ddg.workspace_size(100, 70, 33)
     assert L.dd_gemm_workspace_size_ns(100, 70, 33, 4) < ddg.workspace_size(100, 70, 33)
-    for bad in (0, 3, 9, -1):
+    assert L.dd_gemm_workspace_size_ns(100, 70, 33, 16) > ddg.workspace_size(100, 70, 33)
+    for bad in (0, 3, 17, -1):
         assert L.dd_split_slices_bytes_ns(10, 10, bad) == 0
         assert L.dd_gemm_workspace_size_ns(10, 10, 10, bad) == 0
         assert L.dd_split_balanced_ns(4, 4, P[0], None, 4, 0, bad, P[1], P[2], None) == INV
