@@ -209,6 +209,39 @@ def renorm_levels(S: np.ndarray, E, F):
     return np.ldexp(h, sc), np.ldexp(t, sc)
 
 
+def sliced_product(A_hi, A_lo, B_hi, B_lo, nslices: int = N_SLICES):
+    """The whole chain on one block: (C_hi, C_lo) of the sliced product."""
+    E, DA = slice_rows(A_hi, A_lo, nslices=nslices)
+    F, DB = slice_cols(B_hi, B_lo, nslices=nslices)
+    return renorm_levels(level_values(level_sums_units(DA, DB)), E, F)
+
+
+def sliced_product_kblocks(A_hi, A_lo, B_hi, B_lo, kblock: int, nslices: int = N_SLICES):
+    """k split into consecutive blocks of kblock columns of A (rows of B); each
+    block is an independent sliced product (its own balancing exponents, so the
+    exact-sum bound of §2 eq. (5) holds per block), and the block results are
+    added into the running (C_hi, C_lo), first block first, with the oracle's
+    accurate double-word addition."""
+    from . import native
+    A_hi = np.asarray(A_hi, dtype=np.float64)
+    B_hi = np.asarray(B_hi, dtype=np.float64)
+    A_lo = np.zeros_like(A_hi) if A_lo is None else np.asarray(A_lo, dtype=np.float64)
+    B_lo = np.zeros_like(B_hi) if B_lo is None else np.asarray(B_lo, dtype=np.float64)
+    k = A_hi.shape[1]
+    starts = list(range(0, k, kblock)) if k > 0 else [0]
+    C_hi = C_lo = None
+    for p0 in starts:
+        p1 = min(k, p0 + kblock)
+        Th, Tl = sliced_product(A_hi[:, p0:p1], A_lo[:, p0:p1], B_hi[p0:p1, :], B_lo[p0:p1, :], nslices)
+        if C_hi is None:
+            C_hi, C_lo = Th, Tl
+            continue
+        for i in range(C_hi.shape[0]):
+            for j in range(C_hi.shape[1]):
+                C_hi[i, j], C_lo[i, j] = native.dd_add(C_hi[i, j], C_lo[i, j], Th[i, j], Tl[i, j])
+    return C_hi, C_lo
+
+
 def level_target(S_units: np.ndarray, E: int, F: int, i: int, j: int) -> Fraction:
     """Exact value sum_l S_units[l][i,j] * 2^(E + F - 13(l+2)) of one output entry."""
     return sum((Fraction(int(S_units[l, i, j])) * Fraction(2) ** (E + F - DIGIT_BITS * (l + 2))

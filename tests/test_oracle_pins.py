@@ -548,3 +548,42 @@ def test_more_slices_recover_entries_far_below_the_row_maximum():
     assert worst(8) > compare.TOL
     assert worst(13) <= compare.TOL
     assert worst(16) <= compare.TOL
+
+
+def test_kblocked_chain_with_one_block_is_the_plain_chain():
+    rng = np.random.default_rng(41)
+    Ah, Al = _rand_dd_matrix(rng, (6, 23), "wide")
+    Bh, Bl = _rand_dd_matrix(rng, (23, 5), "wide")
+    Ch, Cl = exact.sliced_product(Ah, Al, Bh, Bl)
+    for kb in (23, 24, 1000):
+        Kh, Kl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kb)
+        assert np.array_equal(Kh.view(np.int64), Ch.view(np.int64))
+        assert np.array_equal(Kl.view(np.int64), Cl.view(np.int64))
+
+
+@pytest.mark.parametrize("kblock", [1, 5, 8, 16])
+def test_kblocked_chain_within_the_summed_bound(kblock):
+    """Each block obeys its own error bound (its own exponents); the accurate
+    double-word additions add at most 3u^2 of the running sum each (u = 2^-53)."""
+    rng = np.random.default_rng(50 + kblock)
+    m, k, c = 4, 37, 3
+    Ah, Al = _rand_dd_matrix(rng, (m, k), "wide")
+    Bh, Bl = _rand_dd_matrix(rng, (k, c), "wide")
+    Ch, Cl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kblock)
+    bound = np.zeros((m, c))
+    for p0 in range(0, k, kblock):
+        p1 = min(k, p0 + kblock)
+        E = exact.balancing_exponents(Ah[:, p0:p1], Al[:, p0:p1], 0)
+        F = exact.balancing_exponents(Bh[p0:p1], Bl[p0:p1], 1)
+        bound += exact.error_bound(Ah[:, p0:p1], Bh[p0:p1], E, F, 8)
+    nblocks = -(-k // kblock)
+    bound += (nblocks - 1) * 3 * 2.0 ** -106 * compare.abs_product(Ah, Bh) * 1.000001
+    rows, cols = np.meshgrid(np.arange(m), np.arange(c), indexing="ij")
+    ex = exact.exact_entries(Ah, Al, Bh, Bl, rows.ravel(), cols.ravel())
+    for q, (i, j) in enumerate(zip(rows.ravel(), cols.ravel())):
+        err = abs(exact.dd_to_fraction(Ch[i, j], Cl[i, j]) - ex[q])
+        assert err <= Fraction(float(bound[i, j])), (kblock, i, j)
+    # blocks really are separate: block-local exponents change the low bits
+    Ph, Pl = exact.sliced_product(Ah, Al, Bh, Bl)
+    assert not (np.array_equal(Ph.view(np.int64), Ch.view(np.int64))
+                and np.array_equal(Pl.view(np.int64), Cl.view(np.int64)))
