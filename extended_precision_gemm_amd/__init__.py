@@ -76,6 +76,9 @@ _SIGNATURES = {
     "qd_sliced_gemm_renorm": (_st, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _pp, _i64, _vp]),
     "qd_gemm": (_st, [_i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp]),
     "qd_gemm_ws": (_st, [_i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp, _sz, _vp]),
+    "dd_gemm_workspace_size_kb": (_sz, [_i64, _i64, _i64, ctypes.c_int, _i64]),
+    "dd_gemm_ws_kb": (_st, [_i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
+                            _vp, _sz, _vp]),
     "ddgemm_status_string": (ctypes.c_char_p, [_st]),
     "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
 }
@@ -149,7 +152,9 @@ def slices_bytes(outer: int, k: int, nslices: int = NUM_SLICES) -> int:
     return lib.dd_split_slices_bytes_ns(outer, k, nslices)
 
 
-def workspace_size(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:
+def workspace_size(m: int, n: int, k: int, nslices: int = NUM_SLICES, kblock: int | None = None) -> int:
+    if kblock is not None:
+        return lib.dd_gemm_workspace_size_kb(m, n, k, nslices, kblock)
     if nslices == NUM_SLICES:
         return lib.dd_gemm_workspace_size(m, n, k)
     return lib.dd_gemm_workspace_size_ns(m, n, k, nslices)
@@ -235,17 +240,23 @@ def _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo):
 
 
 def dd_gemm(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, workspace=None, stream=None,
-            nslices: int = NUM_SLICES):
+            nslices: int = NUM_SLICES, kblock: int | None = None):
     """C = A·B; returns (C_hi, C_lo).  ``nslices`` = 8 is the double-double
     product; 4..7 keep fewer slices (n(n+1)/2 pairs) for less accuracy and time,
-    9..16 more, for entries far below their row's (column's) largest.
+    9..16 more, for entries far below their row's (column's) largest.  ``kblock``
+    cuts k into blocks summed in double-double arithmetic (k beyond k_max(n) is
+    blocked automatically).
     The workspace comes from PyTorch's allocator unless a uint8 device tensor of
     at least workspace_size(m, n, k, nslices) bytes is given."""
     m, n, k, lda, ldb, ldc, C_hi, C_lo = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
-    need = workspace_size(m, n, k, nslices)
+    need = workspace_size(m, n, k, nslices, kblock)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=A_hi.device)
-    if nslices == NUM_SLICES:
+    if kblock is not None:
+        _check(lib.dd_gemm_ws_kb(m, n, k, nslices, kblock, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo),
+                                 ldb, _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
+    elif nslices == NUM_SLICES:
         _check(lib.dd_gemm_ws(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
                               _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(), _stream(stream)))
     else:

@@ -69,11 +69,29 @@ ddgemm_status_t validate_split(int64_t rows, int64_t cols, const double* X_hi, i
     return DDGEMM_SUCCESS;
 }
 
-ddgemm_status_t validate_gemm_dims(int64_t m, int64_t n, int64_t k) {
+ddgemm_status_t validate_sizes(int64_t m, int64_t n, int64_t k) {
     if (!size_ok(m, k) || !size_ok(k, n) || !size_ok(m, n)) return DDGEMM_ERROR_INVALID_VALUE;
-    if (k > DDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
     return DDGEMM_SUCCESS;
 }
+
+// One sliced product: k within the exact-sum bound.
+ddgemm_status_t validate_gemm_dims(int64_t m, int64_t n, int64_t k) {
+    if (validate_sizes(m, n, k) != DDGEMM_SUCCESS || k > DDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
+    return DDGEMM_SUCCESS;
+}
+
+// The k-block dd_gemm uses when none is given: all of k when it fits the
+// exact-sum bound, else the fewest equal blocks that do.
+int64_t default_kblock(int64_t k, int ns) {
+    const int64_t km = k_max(ns);
+    if (k <= km) return k;
+    const int64_t blocks = (k + km - 1) / km;
+    return (k + blocks - 1) / blocks;
+}
+
+bool kblock_ok(int64_t k, int ns, int64_t kblock) { return k == 0 || (kblock >= 1 && kblock <= k_max(ns)); }
+
+int64_t block_count(int64_t k, int64_t kblock) { return k == 0 ? 1 : (k + kblock - 1) / kblock; }
 
 // Quad-double operands: a host array of four device pointers per matrix.
 ddgemm_status_t read_qd_planes(const double* const X[4], int64_t extent_elems, QdPlanes& out) {
@@ -116,10 +134,19 @@ size_t dd_split_slices_bytes_ns(int64_t outer, int64_t k, int nslices) {
 
 size_t dd_split_slices_bytes(int64_t outer, int64_t k) { return dd_split_slices_bytes_ns(outer, k, kSlices); }
 
+size_t dd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock) {
+    if (validate_sizes(m, n, k) != DDGEMM_SUCCESS || !ns_ok(nslices) || !kblock_ok(k, nslices, kblock)) return 0;
+    const int64_t kb = k < kblock ? k : kblock;
+    size_t bytes = align_up(dd_split_slices_bytes_ns(m, kb, nslices)) +
+                   align_up(dd_split_slices_bytes_ns(n, kb, nslices)) + align_up(static_cast<size_t>(m) * 4) +
+                   align_up(static_cast<size_t>(n) * 4);
+    if (block_count(k, kblock) > 1) bytes += 2 * align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
+    return bytes;
+}
+
 size_t dd_gemm_workspace_size_ns(int64_t m, int64_t n, int64_t k, int nslices) {
-    if (validate_gemm_dims(m, n, k) != DDGEMM_SUCCESS || !ns_ok(nslices) || k > k_max(nslices)) return 0;
-    return align_up(dd_split_slices_bytes_ns(m, k, nslices)) + align_up(dd_split_slices_bytes_ns(n, k, nslices)) +
-           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4);
+    if (!ns_ok(nslices) || k < 0) return 0;
+    return dd_gemm_workspace_size_kb(m, n, k, nslices, default_kblock(k, nslices));
 }
 
 size_t dd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) { return dd_gemm_workspace_size_ns(m, n, k, kSlices); }
@@ -188,13 +215,13 @@ ddgemm_status_t dd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k, const dou
     return dd_sliced_gemm_renorm_ns(m, n, k, kSlices, A_slices, E, B_slices, F, C_hi, C_lo, ldc, stream);
 }
 
-ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices, const double* A_hi,
+ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock, const double* A_hi,
                               const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo,
                               int64_t ldb, double* C_hi, double* C_lo, int64_t ldc, void* workspace,
                               size_t ws_bytes, void* stream) {
-    ddgemm_status_t st = validate_gemm_dims(m, n, k);
+    ddgemm_status_t st = validate_sizes(m, n, k);
     if (st != DDGEMM_SUCCESS) return st;
-    if (!ns_ok(nslices) || k > k_max(nslices)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!ns_ok(nslices) || !kblock_ok(k, nslices, kblock)) return DDGEMM_ERROR_INVALID_VALUE;
     if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return DDGEMM_ERROR_INVALID_VALUE;
@@ -204,26 +231,57 @@ ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices, cons
             overlaps(C, ce, B_lo, be))
             return DDGEMM_ERROR_INVALID_VALUE;
     if (overlaps(C_hi, ce, C_lo, ce)) return DDGEMM_ERROR_INVALID_VALUE;
-    const size_t need = dd_gemm_workspace_size_ns(m, n, k, nslices);
+    const size_t need = dd_gemm_workspace_size_kb(m, n, k, nslices, kblock);
     if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return DDGEMM_ERROR_WORKSPACE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
 
+    const int64_t kb = k < kblock ? k : kblock;
+    const int64_t blocks = block_count(k, kb);
     char* w = static_cast<char*>(workspace);
     double* A_sl = reinterpret_cast<double*>(w);
-    w += align_up(dd_split_slices_bytes_ns(m, k, nslices));
+    w += align_up(dd_split_slices_bytes_ns(m, kb, nslices));
     double* B_sl = reinterpret_cast<double*>(w);
-    w += align_up(dd_split_slices_bytes_ns(n, k, nslices));
+    w += align_up(dd_split_slices_bytes_ns(n, kb, nslices));
     int32_t* E = reinterpret_cast<int32_t*>(w);
     w += align_up(static_cast<size_t>(m) * 4);
     int32_t* F = reinterpret_cast<int32_t*>(w);
+    w += align_up(static_cast<size_t>(n) * 4);
+    double* T_hi = reinterpret_cast<double*>(w);  // block results after the first (blocks > 1)
+    double* T_lo = T_hi + (blocks > 1 ? align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8) / 8 : 0);
 
+    // Block b covers k indices [b kb, min(k, (b+1) kb)): a separate sliced product
+    // with its own exponents; blocks after the first are added into C in
+    // double-double arithmetic, in order, on the caller's stream.
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_split(m, k, A_hi, A_lo, lda, 0, nslices, E, A_sl, s);
-    if (e == hipSuccess) e = launch_split(k, n, B_hi, B_lo, ldb, 1, nslices, F, B_sl, s);
-    if (e == hipSuccess)
-        e = launch_sliced_gemm(m, n, k, nslices, A_sl, B_sl, nullptr, 0, E, F, C_hi, C_lo, ldc, true, s);
+    hipError_t e = hipSuccess;
+    for (int64_t b = 0; b < blocks && e == hipSuccess; ++b) {
+        const int64_t p0 = b * kb;
+        const int64_t kc = k - p0 < kb ? k - p0 : kb;
+        const double* a_hi = A_hi ? A_hi + p0 : nullptr;
+        const double* a_lo = A_lo ? A_lo + p0 : nullptr;
+        const double* b_hi = B_hi ? B_hi + p0 * ldb : nullptr;
+        const double* b_lo = B_lo ? B_lo + p0 * ldb : nullptr;
+        e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s);
+        if (e == hipSuccess) e = launch_split(kc, n, b_hi, b_lo, ldb, 1, nslices, F, B_sl, s);
+        if (e != hipSuccess) break;
+        if (b == 0) {
+            e = launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, C_hi, C_lo, ldc, true, s);
+        } else {
+            e = launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, T_hi, T_lo, n, true, s);
+            if (e == hipSuccess) e = launch_dd_accumulate(m, n, C_hi, C_lo, ldc, T_hi, T_lo, n, s);
+        }
+    }
     return launched(e);
+}
+
+ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices, const double* A_hi,
+                              const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo,
+                              int64_t ldb, double* C_hi, double* C_lo, int64_t ldc, void* workspace,
+                              size_t ws_bytes, void* stream) {
+    if (!ns_ok(nslices) || k < 0) return DDGEMM_ERROR_INVALID_VALUE;
+    return dd_gemm_ws_kb(m, n, k, nslices, default_kblock(k, nslices), A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi,
+                         C_lo, ldc, workspace, ws_bytes, stream);
 }
 
 ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* A_hi, const double* A_lo,
@@ -237,7 +295,7 @@ ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* A_hi, 
 ddgemm_status_t dd_gemm(int64_t m, int64_t n, int64_t k, const double* A_hi, const double* A_lo,
                         int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb, double* C_hi,
                         double* C_lo, int64_t ldc, void* stream) {
-    ddgemm_status_t st = validate_gemm_dims(m, n, k);
+    ddgemm_status_t st = validate_sizes(m, n, k);
     if (st != DDGEMM_SUCCESS) return st;
     if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;

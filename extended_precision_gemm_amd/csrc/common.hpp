@@ -57,6 +57,8 @@ hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl
                          const int32_t* F, double* C_hi, double* C_lo, int64_t ldc,
                          hipStream_t stream);
 hipError_t launch_probe_mfma(double* out, hipStream_t stream);
+hipError_t launch_dd_accumulate(int64_t m, int64_t n, double* C_hi, double* C_lo, int64_t ldc, const double* T_hi,
+                                const double* T_lo, int64_t ldt, hipStream_t stream);
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
                            double* slices, hipStream_t stream);
 hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,

@@ -18,6 +18,26 @@ __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e
     e = (a - av) + (b - bv);
 }
 
+// Dekker's FastTwoSum: s = RN(a + b), e = (a + b) - s exactly when |a| >= |b|
+// (or a = 0).
+__device__ __forceinline__ void fast_two_sum(double a, double b, double& s, double& e) {
+    s = a + b;
+    e = b - (s - a);
+}
+
+// Accurate double-word addition (Joldes, Muller and Popescu, "Tight and rigorous
+// error bounds for basic building blocks of double-word arithmetic", ACM TOMS
+// 2017): relative error below 3u^2 for u = 2^-53.
+__device__ __forceinline__ void dd_add(double ah, double al, double bh, double bl, double& zh, double& zl) {
+    double sh, sl, th, tl, vh, vl;
+    two_sum(ah, bh, sh, sl);
+    two_sum(al, bl, th, tl);
+    sl = sl + th;
+    fast_two_sum(sh, sl, vh, vl);
+    vl = vl + tl;
+    fast_two_sum(vh, vl, zh, zl);
+}
+
 // Level renormalisation ("Multiple Double Arithmetic on NVIDIA Tensor Cores",
 // §2, fifth step): add the NL exact level sums of one output entry into a
 // double-double, smallest level first, then apply the entry's scale 2^sc.

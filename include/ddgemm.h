@@ -164,7 +164,8 @@ ddgemm_status_t dd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k,
 /*
  * C = A·B for double-double A (m×k) and B (k×n) ("Multiple Double Arithmetic on
  * NVIDIA Tensor Cores", §2 overview, steps 1-5).  Overwrites C (no alpha/beta).
- * m = 0 or n = 0: no-op.  k = 0: C = 0.  Accuracy: the product of the operands
+ * m = 0 or n = 0: no-op.  k = 0: C = 0.  k beyond DDGEMM_K_MAX is processed in
+ * the fewest equal k-blocks within it, as dd_gemm_ws_kb describes.  Accuracy: the product of the operands
  * truncated to 104 bits below their row/column exponents, minus the slice pairs
  * below the double-double window, renormalised; on inputs whose entries sit
  * within a few binades of their row/column maximum this is within
@@ -173,8 +174,8 @@ ddgemm_status_t dd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k,
  *               `stream` (DDGEMM_ERROR_WORKSPACE if that fails).
  *   dd_gemm_ws  uses the caller's workspace of ws_bytes >= dd_gemm_workspace_size
  *               (256-byte aligned), allocates nothing.
- * Errors: as for the stage calls, plus lda < max(1, k), ldb < max(1, n),
- * ldc < max(1, n), C overlapping A or B.
+ * Errors: as for the stage calls (except the k limit), plus lda < max(1, k),
+ * ldb < max(1, n), ldc < max(1, n), C overlapping A or B.
  */
 ddgemm_status_t dd_gemm(int64_t m, int64_t n, int64_t k,
                         const double* A_hi, const double* A_lo, int64_t lda,
@@ -211,6 +212,26 @@ ddgemm_status_t dd_sliced_gemm_renorm_ns(int64_t m, int64_t n, int64_t k, int ns
                                          const double* B_slices, const int32_t* F,
                                          double* C_hi, double* C_lo, int64_t ldc, void* stream);
 ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices,
+                              const double* A_hi, const double* A_lo, int64_t lda,
+                              const double* B_hi, const double* B_lo, int64_t ldb,
+                              double* C_hi, double* C_lo, int64_t ldc,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * k-blocked product (§2 eq. (5) bounds how many slice products one level sum
+ * holds exactly).  k is cut into consecutive blocks of kblock indices (the last
+ * one shorter); block b is the sliced product of A[:, b kblock ...] and the
+ * matching rows of B with its own balancing exponents, and the block results
+ * are added into C in block order with the accurate double-word addition of
+ * Joldes, Muller and Popescu (relative error < 3·2^-106 per addition).  With
+ * kblock >= k this is dd_gemm_ws_ns bit for bit.  Smaller blocks also shrink the
+ * workspace: slices are sized by kblock, plus two m×n planes when there is more
+ * than one block (dd_gemm_workspace_size_kb).
+ * Errors: as for dd_gemm_ws_ns, plus DDGEMM_ERROR_INVALID_VALUE for k > 0 and
+ * kblock outside [1, DDGEMM_K_MAX_NS(n)].
+ */
+size_t dd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock);
+ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock,
                               const double* A_hi, const double* A_lo, int64_t lda,
                               const double* B_hi, const double* B_lo, int64_t ldb,
                               double* C_hi, double* C_lo, int64_t ldc,

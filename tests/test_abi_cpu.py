@@ -62,7 +62,18 @@ def test_packed_sizes(ddg):
     r = lambda x: (x + 255) // 256 * 256
     assert ws == r(ddg.slices_bytes(m, k)) + r(ddg.slices_bytes(n, k)) + r(4 * m) + r(4 * n)
     assert ddg.workspace_size(-1, 2, 3) == 0
-    assert ddg.workspace_size(1, 1, ddg.K_MAX + 1) == 0
+    # beyond the exact-sum bound k is cut into the fewest equal blocks: slices
+    # for one block plus two m×n planes for the block results
+    k2 = ddg.K_MAX + 1
+    kb = (k2 + 1) // 2
+    assert ddg.workspace_size(3, 5, k2) == (r(ddg.slices_bytes(3, kb)) + r(ddg.slices_bytes(5, kb)) + r(12) + r(20)
+                                            + 2 * r(3 * 5 * 8))
+    assert ddg.workspace_size(3, 5, 100, kblock=100) == ddg.workspace_size(3, 5, 100)
+    assert ddg.workspace_size(3, 5, 100, kblock=30) == (r(ddg.slices_bytes(3, 30)) + r(ddg.slices_bytes(5, 30))
+                                                        + r(12) + r(20) + 2 * r(3 * 5 * 8))
+    assert ddg.workspace_size(3, 5, 100, kblock=0) == 0
+    assert ddg.workspace_size(3, 5, 100, kblock=ddg.K_MAX + 1) == 0
+    assert ddg.workspace_size(3, 5, 0, kblock=0) > 0
 
 
 def test_status_strings(ddg):
@@ -91,7 +102,9 @@ def test_gemm_argument_validation(ddg):
     assert call(m=-1) == INV
     assert call(n=-1) == INV
     assert call(k=-1) == INV
-    assert call(k=ddg.K_MAX + 1, lda=ddg.K_MAX + 1) == INV
+    far = [(1 << 40) * (i + 1) for i in range(7)]             # extents of gigabytes must not overlap
+    assert call(k=ddg.K_MAX + 1, lda=ddg.K_MAX + 1, A_hi=far[0], A_lo=far[1], B_hi=far[2], B_lo=far[3],
+                C_hi=far[4], C_lo=far[5], ws=far[6]) == WS         # blocked: needs its workspace
     assert call(lda=5) == INV
     assert call(ldb=4) == INV
     assert call(ldc=4) == INV
@@ -162,7 +175,13 @@ def test_n_slice_sizes_and_validation(ddg):
         kmax = ddg.k_max(n)
         assert kmax == (8388608 if n <= 8 else 67108865 // n)
         assert L.dd_gemm_workspace_size_ns(4, 4, kmax, n) > 0
-        assert L.dd_gemm_workspace_size_ns(4, 4, kmax + 1, n) == 0
+        assert L.dd_gemm_workspace_size_ns(4, 4, kmax + 1, n) == L.dd_gemm_workspace_size_kb(4, 4, kmax + 1, n,
+                                                                                             (kmax + 2) // 2)
+        assert L.dd_gemm_workspace_size_kb(4, 4, 10, n, kmax + 1) == 0
+        assert L.dd_gemm_ws_kb(4, 4, 10, n, kmax + 1, P[0], None, 10, P[1], None, 4, P[2], P[3], 4, P[4], 1 << 30,
+                               None) == INV
+        assert L.dd_gemm_ws_kb(4, 4, 10, n, 0, P[0], None, 10, P[1], None, 4, P[2], P[3], 4, P[4], 1 << 30,
+                               None) == INV
         assert L.dd_split_balanced_ns(4, kmax + 1, P[0], None, kmax + 1, 0, n, P[1], P[2], None) == INV
         assert L.dd_sliced_gemm_renorm_ns(4, 4, kmax + 1, n, P[0], P[1], P[2], P[3], P[4], P[5], 4, None) == INV
     assert L.dd_split_slices_bytes_ns(130, 33, 8) == ddg.slices_bytes(130, 33)

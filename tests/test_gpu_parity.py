@@ -507,3 +507,35 @@ def test_more_slices_recover_entries_far_below_the_row_maximum(gpu):
     _say(f"[parity] wide-range rows: n=8 {worst[8]:.3e}, n=13 {worst[13]:.3e} (tolerance {compare.TOL})")
     assert worst[8] > compare.TOL
     assert worst[13] <= compare.TOL
+
+
+# ---------------------------------------------------------------------------
+# k-blocked products (block results added in double-double arithmetic)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("nslices", [8, 12])
+@pytest.mark.parametrize("m,n,k", [(40, 30, 250), (130, 65, 97)])
+def test_kblocked_chain_bit_exact(gpu, nslices, m, n, k):
+    rng = np.random.default_rng(k + m + nslices)
+    Ah, Al = _edge_matrix(rng, m, k)
+    Bh, Bl = _edge_matrix(rng, k, n)
+    dA, dAl, dB, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
+    for kblock in (16, 33, 100, k, k + 5):
+        Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kblock, nslices)
+        Ch, Cl = gpu.dd_gemm(dA, dAl, dB, dBl, nslices=nslices, kblock=kblock)
+        assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl), kblock
+
+
+def test_kblocked_workload_within_tolerance(gpu, workload_operands):
+    """dd4096_exp20 cut into four k-blocks of 1024: within the dd tolerance of the
+    classical oracle on sampled entries."""
+    Ah, Al, Bh, Bl = workload_operands("dd4096_exp20")
+    rng = np.random.default_rng(11)
+    qr = rng.integers(0, Ah.shape[0], 512)
+    qc = rng.integers(0, Bh.shape[1], 512)
+    Rh, Rl = native.dd_gemm_entries(Ah, Al, Bh, Bl, qr, qc)
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl), kblock=1024)
+    hCh, hCl = _host(Ch), _host(Cl)
+    err = np.abs((hCh[qr, qc] - Rh) + (hCl[qr, qc] - Rl))
+    ratio = float((err / np.einsum("qk,kq->q", np.abs(Ah[qr]), np.abs(Bh[:, qc]))).max())
+    _say(f"[parity] dd4096_exp20 in 4 k-blocks: max |C-C_ref|/(|A||B|) = {ratio:.3e}")
+    assert ratio <= compare.TOL
