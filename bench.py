@@ -77,6 +77,30 @@ def _traffic_from_profile(workload: str):
         return None
 
 
+def _timing(ev):
+    """Median and minimum over the timed steps of the per-step GPU times (HIP
+    events on the bench stream): the whole step and its GEMM launch."""
+    import statistics
+    step = [e[0].elapsed_time(e[2]) for e in ev]
+    gemm = [e[1].elapsed_time(e[2]) for e in ev]
+    return {"step_ms_median": round(statistics.median(step), 4), "step_ms_min": round(min(step), 4),
+            "gemm_ms_median": round(statistics.median(gemm), 4), "gemm_ms_min": round(min(gemm), 4)}
+
+
+def _host_info(threads_used):
+    """CPU model, logical CPUs and the OpenMP thread setting of the host running the oracle."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "threads_used": threads_used}
+
+
 def _calibration_copy(args, dev):
     """One device copy of known size first, so HBM counters can be scaled by it."""
     import torch
@@ -192,6 +216,7 @@ def main():
             "split_frac_hbm": round(split_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "gemm_ms": round(gemm_ms, 4),
         },
+        "timing": _timing(ev),
     }
 
     # The stand-alone renormalisation (dd_renorm_levels, the stage entry point the
@@ -239,6 +264,7 @@ def main():
         rec["cpu_baseline"] = {
             "value": round(cpu_gflops, 3), "unit": "GFLOP/s", "cores": used, "kind": "oracle",
             "sample": f"first {rows} rows of C ({rows}x{n}x{k}, classical dd GEMM, {t_cpu:.1f} s)",
+            "host": _host_info(used),
         }
         if ns == 8:
             ratio = compare.error_ratio(gh, gl, Rh, Rl, compare.abs_product(Ah[:rows], Bh))
@@ -337,6 +363,7 @@ def _run_qd(args, w):
             "split_frac_hbm": round(split_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "gemm_ms": round(gemm_ms, 4),
         },
+        "timing": _timing(ev),
     }
     if not args.no_cpu_baseline:
         from fractions import Fraction
@@ -356,6 +383,7 @@ def _run_qd(args, w):
         rec["cpu_baseline"] = {
             "value": round(2.0 * k * len(rows) / t_cpu / 1e9, 6), "unit": "GFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(rows)} random entries of C by the exact-integer oracle ({t_cpu:.1f} s, one thread)",
+            "host": _host_info(1),
         }
         ri = torch.as_tensor(rows, device=dev)
         ci = torch.as_tensor(cols, device=dev)
