@@ -266,3 +266,30 @@ def test_qd_workload_parity(gpu, name, samples):
     rel = float((err / absAB).max())
     _say(f"[qd parity] {name}: max err/bound = {ratio:.3e}, max err/(|A||B|) = {rel:.3e}")
     assert ratio <= 1.0
+
+
+# ---------------------------------------------------------------------------
+# metamorphic relations (exact level sums make these hold bit for bit)
+# ---------------------------------------------------------------------------
+def test_qd_metamorphic_relations(gpu):
+    m, n, k = 70, 45, 90
+    A = workloads.random_qd((m, k), 801, "signed_exp20")
+    B = workloads.random_qd((k, n), 802, "uniform")
+    C = _host(gpu.qd_gemm(_dev(A), _dev(B)))
+    # k permutation: the same products summed in another order
+    perm = np.random.default_rng(3).permutation(k)
+    Cp = _host(gpu.qd_gemm(_dev(A[:, :, perm]), _dev(B[:, perm, :])))
+    assert _bits_equal(Cp, C)
+    # power-of-two scaling of A's rows and B's columns scales C exactly
+    er = np.random.default_rng(4).integers(-40, 41, m)
+    ec = np.random.default_rng(5).integers(-40, 41, n)
+    As = A * np.ldexp(1.0, er)[None, :, None]
+    Bs = B * np.ldexp(1.0, ec)[None, None, :]
+    Cs = _host(gpu.qd_gemm(_dev(As), _dev(Bs)))
+    assert _bits_equal(Cs, C * np.ldexp(1.0, er[:, None] + ec[None, :])[None])
+    # negation of A negates C (compared as values: an exact zero stays +0)
+    Cn = _host(gpu.qd_gemm(_dev(-A), _dev(B)))
+    assert np.array_equal(Cn, -C)
+    # transposition: (A B)^T = B^T A^T, the operands swapping roles
+    Ct = _host(gpu.qd_gemm(_dev(B.transpose(0, 2, 1)), _dev(A.transpose(0, 2, 1))))
+    assert _bits_equal(Ct, C.transpose(0, 2, 1))
