@@ -115,8 +115,8 @@ def _calibration_copy(args, dev):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
-              "the product shards by output tiles with no exchange, but multi-GPU runs are not part of it.",
+        print(f"bench.py: the library runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              "the product shards by output tiles with no exchange, but runs across GPUs are not implemented.",
               file=sys.stderr)
         sys.exit(2)
 

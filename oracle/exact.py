@@ -13,7 +13,7 @@ Exact references for every intermediate of the sliced double-double product
   fifth step: sum the parts of each product entry in double-double arithmetic),
 * the exact rational value of a double-double inner product.
 
-Readings of points the pages leave open (each one is listed in the design doc):
+Readings of points the pages leave open:
 
 * A double-double x = hi + lo is cut as a 13n-bit fixed-point window below a
   balancing exponent E with |hi + lo| < 2^E: N = floor(|hi + lo| * 2^(13n-E)),
