@@ -273,11 +273,14 @@ __global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t 
 // Blocks needed before the one-pass block kernel beats two streaming passes
 // (measured: 4096 blocks of k = 512 win, 256 blocks of k = 4096 lose).
 constexpr int64_t kFusedMinBlocks = 1024;
-// A B operand (column exponents: two passes take four launches) of at most this
-// many bytes of (hi, lo) is sliced in one pass with its k-blocks shared among
-// enough workgroups; the parts' exponent re-reads then hit the cache (measured
-// on gfx950: 1024^2 29 vs 44 us, 1536^2 61 vs 59 us, 4096^2 483 vs 339 us).
+// A B operand (column exponents: two passes take four launches) of at most
+// kSmallColsBytes of (hi, lo) is sliced in one pass with its k-blocks shared
+// among enough workgroups, as long as the parts' exponent re-reads (every part
+// re-reads its block) stay within kSmallColsReread bytes and so hit the cache
+// (measured on gfx950: 1024^2 29 vs 44 us with 256 MB re-read, 1536^2 61 vs
+// 59 us with 396 MB, 4096^2 483 vs 339 us).
 constexpr int64_t kSmallColsBytes = 24ll << 20;
+constexpr int64_t kSmallColsReread = 320ll << 20;
 
 template <int NS>
 hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
@@ -287,11 +290,12 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
     if (outer == 0) return hipSuccess;
     const PackGeom g(outer, k);
     constexpr int kBlockThreads = 1024;
-    const bool small_cols = axis == 1 && rows * cols * 16 <= kSmallColsBytes;
+    int64_t kparts = (kFusedMinBlocks + g.RB - 1) / g.RB;
+    if (kparts > g.KB) kparts = g.KB;
+    const int64_t bytes = rows * cols * 16;
+    const bool small_cols = axis == 1 && bytes <= kSmallColsBytes && bytes * kparts <= kSmallColsReread;
     if (g.doubles(NS) > 0 && (g.RB >= kFusedMinBlocks || small_cols)) {
         // One pass per block; k-blocks shared among parts when blocks are few.
-        int64_t kparts = (kFusedMinBlocks + g.RB - 1) / g.RB;
-        if (kparts > g.KB) kparts = g.KB;
         const dim3 grid(static_cast<unsigned>(g.RB), static_cast<unsigned>(kparts));
         if (axis == 0)
             split_block_kernel<0, kBlockThreads, NS><<<grid, kBlockThreads, 0, stream>>>(
