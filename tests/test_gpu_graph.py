@@ -1,4 +1,5 @@
-"""The workspace entry points inside a captured HIP graph (GPU tests).
+"""The workspace entry points inside a captured HIP graph, and concurrent calls
+from several host threads (GPU tests).
 
 dd_gemm_ws and qd_gemm_ws allocate nothing and clear memory with a kernel, not
 a memset, so a caller can capture them once and replay them with new operands
@@ -88,3 +89,46 @@ def test_qd_gemm_ws_replays_in_a_graph(gpu):
         graph.replay()
         R = gpu.qd_gemm(dA, dB)
         assert np.array_equal(_bits(C), _bits(R)), rep
+
+
+def test_concurrent_calls_from_threads_on_their_own_streams(gpu):
+    """The entry points keep no per-call state in the library: products issued
+    at the same time from several host threads, each on its own stream, equal
+    the same products issued one after another."""
+    import threading
+    import torch
+    jobs = []
+    for t in range(4):
+        m, n, k = 60 + 17 * t, 50 + 9 * t, 40 + 23 * t
+        ah, al = workloads.random_dd((m, k), 900 + t, "signed_exp20")
+        bh, bl = workloads.random_dd((k, n), 950 + t, "uniform")
+        jobs.append(tuple(_dev(x) for x in (ah, al, bh, bl)))
+    qa = _dev(workloads.random_qd((33, 70), 990, "uniform"))
+    qb = _dev(workloads.random_qd((70, 41), 991, "uniform"))
+    serial = [gpu.dd_gemm(*j) for j in jobs]
+    serial_q = gpu.qd_gemm(qa, qb)
+    torch.cuda.synchronize()
+    results = [None] * (len(jobs) + 1)
+    errors = []
+
+    def run(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    out = gpu.dd_gemm(*jobs[i], stream=s) if i < len(jobs) else gpu.qd_gemm(qa, qb, stream=s)
+            s.synchronize()
+            results[i] = out
+        except Exception as exc:  # reported below
+            errors.append(exc)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(jobs) + 1)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for i, (Sh, Sl) in enumerate(serial):
+        Ch, Cl = results[i]
+        assert np.array_equal(_bits(Ch), _bits(Sh)) and np.array_equal(_bits(Cl), _bits(Sl)), i
+    assert np.array_equal(_bits(results[-1]), _bits(serial_q))
