@@ -148,12 +148,17 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
             compiler_fence();
             __builtin_amdgcn_s_barrier();  // every wave's copy of stage st is in LDS, and
             compiler_fence();               // every wave is done reading stage st-1
+            // The copy of stage st + NBUF - 1 goes into the buffer every wave has
+            // finished reading (certified by the barrier above); it is issued
+            // after the first fragment reads of this stage rather than before
+            // them, so the matrix instructions start sooner (measured: +2-3 %).
             const int64_t nxt = st + NBUF - 1;
-            issue(nxt < nstages ? nxt : nstages - 1, static_cast<int>(nxt % NBUF));
+            const int64_t nxt_c = nxt < nstages ? nxt : nstages - 1;
 
             const double* stage = lds + (st % NBUF) * C::kStageDoubles + lane;
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
+                if (KS > 1 && j == KS / 2) issue(nxt_c, static_cast<int>(nxt % NBUF));
                 const double* sa = stage + (RPW * wr) * C::kBlockStage + j * C::kSetDoubles;
                 const double* sb = stage + (C::kTBM + wc) * C::kBlockStage + j * C::kSetDoubles;
                 double a[NS][RPW], b[NS];
@@ -163,6 +168,7 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                     for (int r = 0; r < RPW; ++r) a[s][r] = sa[r * C::kBlockStage + s * kFragDoubles];
                     b[s] = sb[s * kFragDoubles];
                 }
+                if (KS == 1) issue(nxt_c, static_cast<int>(nxt % NBUF));
                 // Triangular schedule: pair (s, t) feeds level s + t < NS.
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
