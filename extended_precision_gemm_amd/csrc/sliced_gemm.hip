@@ -246,10 +246,11 @@ __global__ void __launch_bounds__(64) probe_mfma_kernel(double* __restrict__ out
 }
 
 // Launch configuration per slice count: 32x16 wave strips, 2 x 4 waves per
-// workgroup (64x64 tile, one workgroup per CU), KS k-blocks per LDS stage so that
-// a stage stays at or below 64 KB, two stages.
+// workgroup (64x64 tile, one workgroup per CU), two k-blocks per LDS stage (at
+// most 64 KB), two stages; measured best among the stage depths and strip
+// shapes that fit.
 template <int NS> struct ConfigFor;
-template <> struct ConfigFor<4> { using type = GemmConfig<2, 4, 4, 2, 1, 4>; };
+template <> struct ConfigFor<4> { using type = GemmConfig<2, 4, 2, 2, 1, 4>; };
 template <> struct ConfigFor<5> { using type = GemmConfig<2, 4, 2, 2, 1, 5>; };
 template <> struct ConfigFor<6> { using type = GemmConfig<2, 4, 2, 2, 1, 6>; };
 template <> struct ConfigFor<7> { using type = GemmConfig<2, 4, 2, 2, 1, 7>; };
