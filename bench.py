@@ -269,6 +269,7 @@ def main():
         if ns == 8:
             ratio = compare.error_ratio(gh, gl, Rh, Rl, compare.abs_product(Ah[:rows], Bh))
             rec["parity_sample"] = {"rows": rows, "max_err_over_absAB": ratio, "tol": compare.TOL,
+                                    "eps_max": compare.eps_max(gh, gl, Rh, Rl),
                                     "ok": bool(ratio <= compare.TOL)}
         else:
             from oracle import exact
