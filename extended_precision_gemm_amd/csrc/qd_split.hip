@@ -112,6 +112,66 @@ __global__ void __launch_bounds__(256) qd_slice_kernel(int64_t outer, int64_t k,
     }
 }
 
+// One pass over a small B operand (column exponents otherwise take four
+// launches): workgroup (b, c) finds the exponents of 16-column block b -- every
+// part c re-reads the block, from cache at the sizes this is used for -- and
+// slices the part's share of the block's k-blocks; part 0 stores the exponents.
+template <int NT>
+__global__ void __launch_bounds__(NT) qd_split_cols_block_kernel(int64_t outer, int64_t k, int64_t KB, QdPlanes X,
+                                                                 int64_t ld, int32_t* __restrict__ exps,
+                                                                 double* __restrict__ slices) {
+    constexpr int kRowGroups = NT / 16;
+    __shared__ int codes[NT];
+    __shared__ int block_exp[16];
+    const int t = threadIdx.x;
+    const int64_t blk = blockIdx.x;
+    const int64_t o0 = blk * 16;
+    const int64_t kparts = gridDim.y;
+    const int64_t kb_begin = KB * blockIdx.y / kparts, kb_end = KB * (blockIdx.y + 1) / kparts;
+
+    // thread t takes column o0 + t % 16 over rows t / 16, t / 16 + kRowGroups, ...
+    int code = kNoExp;
+    const int64_t oc = o0 + (t & 15);
+    if (oc < outer) {
+        for (int64_t p = t >> 4; p < k; p += kRowGroups) {
+            double x[4];
+            load_qd(X, p * ld + oc, x);
+            code = max(code, qd_entry_code(x));
+        }
+    }
+    codes[t] = code;
+    __syncthreads();
+    if (t < 16) {
+        int c = kNoExp;
+        for (int g = 0; g < kRowGroups; ++g) c = max(c, codes[g * 16 + t]);
+        block_exp[t] = decode_exp(c);
+    }
+    __syncthreads();
+    if (blockIdx.y == 0 && t < 16 && o0 + t < outer) exps[o0 + t] = block_exp[t];
+
+    // one thread per packed (fragment, lane) position of the part's k-blocks
+    const int64_t total = (kb_end - kb_begin) * kFragDoubles;
+    for (int64_t q = t; q < total; q += NT) {
+        const int64_t kb = kb_begin + q / kFragDoubles;
+        const int lane = static_cast<int>(q % kFragDoubles);
+        const int64_t o = o0 + (lane & 15);
+        const int64_t p = kb * 4 + (lane >> 4);
+        double x[4] = {0.0, 0.0, 0.0, 0.0};
+        if (o < outer && p < k) load_qd(X, p * ld + o, x);
+        double sl[kQdSlices];
+        qd_slice_entry(x, block_exp[lane & 15], sl);
+        double* dst = slices + (blk * KB + kb) * (kQdSlices * kFragDoubles) + lane;
+#pragma unroll
+        for (int s = 0; s < kQdSlices; ++s) dst[s * kFragDoubles] = sl[s];
+    }
+}
+
+// Limits of the one-pass path: operand bytes (four planes) and the parts'
+// exponent re-reads (measured on gfx950, B operand: 256^2 45 -> 18 us, 512^2
+// 62 -> 32 us, 1024^2 76 -> 65 us; from 1536^2 up the two passes are as fast).
+constexpr int64_t kQdSmallColsBytes = 32ll << 20;
+constexpr int64_t kQdSmallColsReread = 512ll << 20;
+
 }  // namespace
 
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
@@ -119,6 +179,18 @@ hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     if (outer == 0) return hipSuccess;
+    if (axis == 1 && rows > 0) {
+        const PackGeom gb(outer, k);
+        constexpr int64_t kMinWorkgroups = 1024;
+        int64_t kparts = (kMinWorkgroups + gb.RB - 1) / gb.RB;
+        if (kparts > gb.KB) kparts = gb.KB;
+        const int64_t bytes = rows * cols * 32;
+        if (bytes <= kQdSmallColsBytes && bytes * kparts <= kQdSmallColsReread) {
+            const dim3 grid(static_cast<unsigned>(gb.RB), static_cast<unsigned>(kparts));
+            qd_split_cols_block_kernel<1024><<<grid, 1024, 0, stream>>>(outer, k, gb.KB, X, ldx, exps, slices);
+            return hipGetLastError();
+        }
+    }
     if (axis == 0) {
         qd_exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X, ldx, exps);
     } else {
