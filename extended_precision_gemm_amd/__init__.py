@@ -34,6 +34,7 @@ SLICE_BITS = 13
 K_MAX = 8388608
 QD_NUM_SLICES = 16      # the quad-double product
 QD_K_MAX = 4194304
+QD_K_MAX_BLOCKED = 4294967296   # longer qd products run in k-blocks sharing their exponents
 
 SUCCESS = 0
 ERROR_INVALID_VALUE = 1
@@ -76,6 +77,8 @@ _SIGNATURES = {
     "qd_sliced_gemm_renorm": (_st, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _pp, _i64, _vp]),
     "qd_gemm": (_st, [_i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp]),
     "qd_gemm_ws": (_st, [_i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp, _sz, _vp]),
+    "qd_gemm_workspace_size_kb": (_sz, [_i64, _i64, _i64, _i64]),
+    "qd_gemm_ws_kb": (_st, [_i64, _i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp, _sz, _vp]),
     "dd_gemm_workspace_size_kb": (_sz, [_i64, _i64, _i64, ctypes.c_int, _i64]),
     "dd_gemm_ws_kb": (_st, [_i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                             _vp, _sz, _vp]),
@@ -311,7 +314,9 @@ def qd_slices_bytes(outer: int, k: int) -> int:
     return lib.qd_split_slices_bytes(outer, k)
 
 
-def qd_workspace_size(m: int, n: int, k: int) -> int:
+def qd_workspace_size(m: int, n: int, k: int, kblock: int | None = None) -> int:
+    if kblock is not None:
+        return lib.qd_gemm_workspace_size_kb(m, n, k, kblock)
     return lib.qd_gemm_workspace_size(m, n, k)
 
 
@@ -349,15 +354,22 @@ def _qd_gemm_args(A, B, C):
     return m, n, k, pa, lda, pb, ldb, C, pc, ldc
 
 
-def qd_gemm(A, B, C=None, workspace=None, stream=None):
+def qd_gemm(A, B, C=None, workspace=None, stream=None, kblock: int | None = None):
     """C = A·B for quad-double A (m×k) and B (k×n); returns C as a (4, m, n) tensor
     (or the given planes).  The workspace comes from PyTorch's allocator unless a
-    uint8 device tensor of at least qd_workspace_size(m, n, k) bytes is given."""
+    uint8 device tensor of at least qd_workspace_size(m, n, k, kblock) bytes is
+    given.  ``kblock`` runs the product in k-blocks of that many terms (the
+    result does not depend on it); by default k is split only beyond QD_K_MAX."""
     m, n, k, pa, lda, pb, ldb, C, pc, ldc = _qd_gemm_args(A, B, C)
-    need = qd_workspace_size(m, n, k)
+    need = qd_workspace_size(m, n, k, kblock)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
-    _check(lib.qd_gemm_ws(m, n, k, pa, lda, pb, ldb, pc, ldc, _ptr(workspace), workspace.numel(), _stream(stream)))
+    if kblock is None:
+        _check(lib.qd_gemm_ws(m, n, k, pa, lda, pb, ldb, pc, ldc, _ptr(workspace), workspace.numel(),
+                              _stream(stream)))
+    else:
+        _check(lib.qd_gemm_ws_kb(m, n, k, kblock, pa, lda, pb, ldb, pc, ldc, _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
     return C
 
 

@@ -123,6 +123,28 @@ ddgemm_status_t validate_qd_gemm_dims(int64_t m, int64_t n, int64_t k) {
     return DDGEMM_SUCCESS;
 }
 
+// The quad-double product in k-blocks: k up to QDGEMM_K_MAX_BLOCKED.
+ddgemm_status_t validate_qd_blocked_dims(int64_t m, int64_t n, int64_t k, int64_t kblock) {
+    if (!size_ok(m, k) || !size_ok(k, n) || !size_ok(m, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (k > QDGEMM_K_MAX_BLOCKED) return DDGEMM_ERROR_INVALID_VALUE;
+    if (k > 0 && (kblock < 1 || kblock > QDGEMM_K_MAX)) return DDGEMM_ERROR_INVALID_VALUE;
+    return DDGEMM_SUCCESS;
+}
+
+// All of k when it fits one sliced product, else the fewest equal blocks that do.
+int64_t qd_default_kblock(int64_t k) {
+    if (k <= QDGEMM_K_MAX) return k;
+    const int64_t blocks = (k + QDGEMM_K_MAX - 1) / QDGEMM_K_MAX;
+    return (k + blocks - 1) / blocks;
+}
+
+// Plane c of X advanced by `off` entries (a missing plane stays missing).
+QdPlanes offset_planes(const QdPlanes& X, int64_t off) {
+    QdPlanes r;
+    for (int c = 0; c < 4; ++c) r.x[c] = X.x[c] ? X.x[c] + off : nullptr;
+    return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -315,10 +337,18 @@ size_t qd_split_slices_bytes(int64_t outer, int64_t k) {
     return static_cast<size_t>(PackGeom(outer, k).doubles(kQdSlices)) * sizeof(double);
 }
 
+size_t qd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int64_t kblock) {
+    if (validate_qd_blocked_dims(m, n, k, kblock) != DDGEMM_SUCCESS) return 0;
+    const int64_t kb = k < kblock ? k : kblock;
+    const size_t units = block_count(k, kb) > 1 ? static_cast<size_t>(m) * static_cast<size_t>(n) * 8 : 0;
+    return align_up(qd_split_slices_bytes(m, kb)) + align_up(qd_split_slices_bytes(n, kb)) +
+           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4) +
+           align_up(units * QDGEMM_NUM_LEVELS);
+}
+
 size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
-    if (validate_qd_gemm_dims(m, n, k) != DDGEMM_SUCCESS) return 0;
-    return align_up(qd_split_slices_bytes(m, k)) + align_up(qd_split_slices_bytes(n, k)) +
-           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4);
+    if (k < 0) return 0;
+    return qd_gemm_workspace_size_kb(m, n, k, qd_default_kblock(k));
 }
 
 ddgemm_status_t qd_split_balanced(int64_t rows, int64_t cols, const double* const X[4], int64_t ldx, int axis,
@@ -350,10 +380,10 @@ ddgemm_status_t qd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k, const dou
     return launched(launch_qd_gemm(m, n, k, A_slices, B_slices, E, F, out, ldc, static_cast<hipStream_t>(stream)));
 }
 
-ddgemm_status_t qd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* const A[4], int64_t lda,
-                           const double* const B[4], int64_t ldb, double* const C[4], int64_t ldc,
-                           void* workspace, size_t ws_bytes, void* stream) {
-    ddgemm_status_t st = validate_qd_gemm_dims(m, n, k);
+ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, const double* const A[4],
+                              int64_t lda, const double* const B[4], int64_t ldb, double* const C[4], int64_t ldc,
+                              void* workspace, size_t ws_bytes, void* stream) {
+    ddgemm_status_t st = validate_qd_blocked_dims(m, n, k, kblock);
     if (st != DDGEMM_SUCCESS) return st;
     if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
@@ -367,30 +397,59 @@ ddgemm_status_t qd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* const 
         for (int q = 0; q < 4; ++q)
             if (overlaps(out.c[c], ce, pa.x[q], ae) || overlaps(out.c[c], ce, pb.x[q], be))
                 return DDGEMM_ERROR_INVALID_VALUE;
-    const size_t need = qd_gemm_workspace_size(m, n, k);
+    const size_t need = qd_gemm_workspace_size_kb(m, n, k, kblock);
     if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return DDGEMM_ERROR_WORKSPACE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
 
+    const int64_t kb = k < kblock ? k : kblock;
+    const int64_t blocks = block_count(k, kb);
     char* w = static_cast<char*>(workspace);
     double* A_sl = reinterpret_cast<double*>(w);
-    w += align_up(qd_split_slices_bytes(m, k));
+    w += align_up(qd_split_slices_bytes(m, kb));
     double* B_sl = reinterpret_cast<double*>(w);
-    w += align_up(qd_split_slices_bytes(n, k));
+    w += align_up(qd_split_slices_bytes(n, kb));
     int32_t* E = reinterpret_cast<int32_t*>(w);
     w += align_up(static_cast<size_t>(m) * 4);
     int32_t* F = reinterpret_cast<int32_t*>(w);
+    w += align_up(static_cast<size_t>(n) * 4);
+    int64_t* units = reinterpret_cast<int64_t*>(w);  // [16][m][n] level sums (blocks > 1)
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s);
-    if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s);
-    if (e == hipSuccess) e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s);
+    if (blocks == 1) {
+        hipError_t e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s);
+        if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s);
+        if (e == hipSuccess) e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s);
+        return launched(e);
+    }
+    // Exponents of the whole rows of A / columns of B; block b covers k indices
+    // [b kb, min(k, (b+1) kb)) and is sliced below them, so the blocks' level
+    // sums add exactly; the last block rounds the total.
+    hipError_t e = launch_qd_exps(m, k, pa, lda, 0, E, s);
+    if (e == hipSuccess) e = launch_qd_exps(k, n, pb, ldb, 1, F, s);
+    for (int64_t b = 0; b < blocks && e == hipSuccess; ++b) {
+        const int64_t p0 = b * kb;
+        const int64_t kc = k - p0 < kb ? k - p0 : kb;
+        e = launch_qd_slices(m, kc, offset_planes(pa, p0), lda, 0, E, A_sl, s);
+        if (e == hipSuccess) e = launch_qd_slices(kc, n, offset_planes(pb, p0 * ldb), ldb, 1, F, B_sl, s);
+        if (e != hipSuccess) break;
+        const QdBlockStep step = b == 0 ? kQdFirstBlock : (b + 1 == blocks ? kQdLastBlock : kQdMiddleBlock);
+        e = launch_qd_gemm_block(m, n, kc, A_sl, B_sl, units, step, E, F, out, ldc, s);
+    }
     return launched(e);
+}
+
+ddgemm_status_t qd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* const A[4], int64_t lda,
+                           const double* const B[4], int64_t ldb, double* const C[4], int64_t ldc,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    if (k < 0) return DDGEMM_ERROR_INVALID_VALUE;
+    return qd_gemm_ws_kb(m, n, k, qd_default_kblock(k), A, lda, B, ldb, C, ldc, workspace, ws_bytes, stream);
 }
 
 ddgemm_status_t qd_gemm(int64_t m, int64_t n, int64_t k, const double* const A[4], int64_t lda,
                         const double* const B[4], int64_t ldb, double* const C[4], int64_t ldc, void* stream) {
-    ddgemm_status_t st = validate_qd_gemm_dims(m, n, k);
+    if (k < 0) return DDGEMM_ERROR_INVALID_VALUE;
+    ddgemm_status_t st = validate_qd_blocked_dims(m, n, k, qd_default_kblock(k));
     if (st != DDGEMM_SUCCESS) return st;
     if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;

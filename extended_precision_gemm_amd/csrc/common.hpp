@@ -61,6 +61,18 @@ hipError_t launch_dd_accumulate(int64_t m, int64_t n, double* C_hi, double* C_lo
                                 const double* T_lo, int64_t ldt, hipStream_t stream);
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
                            double* slices, hipStream_t stream);
+hipError_t launch_qd_exps(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
+                          hipStream_t stream);
+hipError_t launch_qd_slices(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis,
+                            const int32_t* exps, double* slices, hipStream_t stream);
+// Quad-double k-blocks that share their balancing exponents: the 16 level sums
+// of a block, in integer units, are stored into (first block) or added to
+// (later blocks) int64 level planes [16][m][n]; the last block adds its own and
+// rounds the exact total to C.
+enum QdBlockStep { kQdFirstBlock = 0, kQdMiddleBlock = 1, kQdLastBlock = 2 };
+hipError_t launch_qd_gemm_block(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
+                                int64_t* units, QdBlockStep step, const int32_t* E, const int32_t* F,
+                                const OutPlanes& C, int64_t ldc, hipStream_t stream);
 hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
                           const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
                           hipStream_t stream);

@@ -17,18 +17,12 @@
 
 namespace ddg {
 
-template <int NL>
-__device__ __forceinline__ void qd_from_levels(const double (&S)[NL], int sc, double (&c)[4]) {
-    WideInt<4> T;
-    wide_zero(T);
-#pragma unroll
-    for (int l = 0; l < NL; ++l) {
-        const int64_t units = static_cast<int64_t>(ldexp(S[l], kSliceBits * (l + 2)));  // exact integer
-        wide_add_shifted(T, units, kSliceBits * (NL - 1 - l));
-    }
+// c[0..3] = the nearest quad double of T * 2^base, T an L-limb two's-complement
+// integer (greedy: each word the nearest double of what is left).
+template <int L>
+__device__ __forceinline__ void qd_round_total(WideInt<L> T, int base, double (&c)[4]) {
     bool neg = wide_is_neg(T);
     if (neg) wide_negate(T);
-    const int base = sc - kSliceBits * (NL + 1);  // exponent of one unit of T
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int b = wide_bit_length(T);
@@ -57,6 +51,29 @@ __device__ __forceinline__ void qd_from_levels(const double (&S)[NL], int sc, do
         c[i] = (b > 0 && neg) ? -v : v;  // an exact zero remainder gives +0
         if (up) neg = !neg;
     }
+}
+
+template <int NL>
+__device__ __forceinline__ void qd_from_levels(const double (&S)[NL], int sc, double (&c)[4]) {
+    WideInt<4> T;
+    wide_zero(T);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        const int64_t units = static_cast<int64_t>(ldexp(S[l], kSliceBits * (l + 2)));  // exact integer
+        wide_add_shifted(T, units, kSliceBits * (NL - 1 - l));
+    }
+    qd_round_total(T, sc - kSliceBits * (NL + 1), c);  // one unit of T is 2^(sc - 13(NL+1))
+}
+
+// The same from level sums already in integer units (summed over k-blocks that
+// share their exponents): |N_l| < 2^63, so the total needs five limbs.
+template <int NL>
+__device__ __forceinline__ void qd_from_level_units(const int64_t (&N)[NL], int sc, double (&c)[4]) {
+    WideInt<5> T;
+    wide_zero(T);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) wide_add_shifted(T, N[l], kSliceBits * (NL - 1 - l));
+    qd_round_total(T, sc - kSliceBits * (NL + 1), c);
 }
 
 }  // namespace ddg

@@ -174,6 +174,40 @@ constexpr int64_t kQdSmallColsReread = 512ll << 20;
 
 }  // namespace
 
+hipError_t launch_qd_exps(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
+                          hipStream_t stream) {
+    if ((axis == 0 ? rows : cols) == 0) return hipSuccess;
+    if (axis == 0) {
+        qd_exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X, ldx, exps);
+    } else {
+        fill_int_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols, kNoExp);
+        if (rows > 0) {
+            int64_t rpc = (rows + 4095) / 4096;
+            if (rpc < 64) rpc = 64;
+            const int64_t chunks = (rows + rpc - 1) / rpc;
+            dim3 grid(static_cast<unsigned>((cols + 255) / 256), static_cast<unsigned>(chunks));
+            qd_exp_cols_kernel<<<grid, 256, 0, stream>>>(rows, cols, X, ldx, rpc, exps);
+        }
+        decode_exps_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_qd_slices(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis,
+                            const int32_t* exps, double* slices, hipStream_t stream) {
+    const int64_t outer = axis == 0 ? rows : cols;
+    const int64_t k = axis == 0 ? cols : rows;
+    const PackGeom g(outer, k);
+    if (outer == 0 || g.doubles(kQdSlices) == 0) return hipSuccess;
+    const int64_t total = g.RB * g.KB * kFragDoubles;
+    const unsigned grid = grid_for(total, 256, 1 << 20);
+    if (axis == 0)
+        qd_slice_kernel<0><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X, ldx, exps, slices);
+    else
+        qd_slice_kernel<1><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X, ldx, exps, slices);
+    return hipGetLastError();
+}
+
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
                            double* slices, hipStream_t stream) {
     const int64_t outer = axis == 0 ? rows : cols;
@@ -191,30 +225,9 @@ hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_
             return hipGetLastError();
         }
     }
-    if (axis == 0) {
-        qd_exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X, ldx, exps);
-    } else {
-        fill_int_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols, kNoExp);
-        if (rows > 0) {
-            int64_t rpc = (rows + 4095) / 4096;
-            if (rpc < 64) rpc = 64;
-            const int64_t chunks = (rows + rpc - 1) / rpc;
-            dim3 grid(static_cast<unsigned>((cols + 255) / 256), static_cast<unsigned>(chunks));
-            qd_exp_cols_kernel<<<grid, 256, 0, stream>>>(rows, cols, X, ldx, rpc, exps);
-        }
-        decode_exps_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols);
-    }
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_qd_exps(rows, cols, X, ldx, axis, exps, stream);
     if (err != hipSuccess) return err;
-    const PackGeom g(outer, k);
-    if (g.doubles(kQdSlices) == 0) return hipSuccess;
-    const int64_t total = g.RB * g.KB * kFragDoubles;
-    const unsigned grid = grid_for(total, 256, 1 << 20);
-    if (axis == 0)
-        qd_slice_kernel<0><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X, ldx, exps, slices);
-    else
-        qd_slice_kernel<1><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X, ldx, exps, slices);
-    return hipGetLastError();
+    return launch_qd_slices(rows, cols, X, ldx, axis, exps, slices, stream);
 }
 
 }  // namespace ddg

@@ -14,9 +14,10 @@
 // RPW = 2 for up to eight slices, 1 for nine to sixteen) with one accumulator
 // per level and block; a workgroup of WM x WN waves owns a (16 RPW WM) x (16 WN)
 // output tile, and WGS workgroups share a CU (two waves per SIMD in every
-// configuration).  The same kernel serves the quad-double product (QD_OUT):
+// configuration).  The same kernel serves the quad-double product:
 // sixteen slices, 136 pairs, sixteen levels, and the exact four-double
-// epilogue.  The operand panels move through LDS in stages
+// epilogue (or, for a k-block of a longer product, the level sums in integer
+// units added into int64 planes).  The operand panels move through LDS in stages
 // of KS k-blocks (4 values of k each): every (16x4 or 4x16) fragment of one
 // slice is 64 consecutive doubles in the packed planes, so a stage of one
 // 16-row (16-column) block is a contiguous KS x 4 KB run, copied with 16-byte
@@ -73,11 +74,21 @@ struct GemmConfig {
     static_assert(kPackK % (4 * KS) == 0, "stage divides the k packing");
 };
 
-template <class C, bool FUSED, bool QD_OUT = false>
+// What the epilogue does with the NS level sums of an output entry.
+enum Epilogue : int {
+    kEpiLevels = 0,    // store them as doubles to level planes
+    kEpiDD = 1,        // cascade them into (hi, lo)
+    kEpiQD = 2,        // round their exact total to four doubles
+    kEpiUnitsSet = 3,  // store them in integer units to int64 planes
+    kEpiUnitsAdd = 4,  // add them in integer units to the int64 planes
+    kEpiUnitsQD = 5,   // add them to the int64 planes' values and round that total
+};
+
+template <class C, int EPI>
 __global__ void __launch_bounds__(C::kThreads, C::kWGS)
 sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                    const double* __restrict__ Ap, const double* __restrict__ Bp,
-                   double* __restrict__ levels, int64_t ldl, int64_t plane,
+                   double* __restrict__ levels, int64_t* __restrict__ units, int64_t ldl, int64_t plane,
                    const int32_t* __restrict__ E, const int32_t* __restrict__ F,
                    OutPlanes out, int64_t ldc) {
     constexpr int KS = C::kKS;
@@ -190,13 +201,16 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
         for (int v = 0; v < 4; ++v) {
             const int64_t row = (rb0 + RPW * wr + r) * 16 + frag_row(lane, v);
             if (row < m && col < n) {
-                if constexpr (FUSED) {
-                    double S[NS];
+                double S[NS];
 #pragma unroll
-                    for (int l = 0; l < NS; ++l) S[l] = acc[l][r][v];
+                for (int l = 0; l < NS; ++l) S[l] = acc[l][r][v];
+                if constexpr (EPI == kEpiLevels) {
+#pragma unroll
+                    for (int l = 0; l < NS; ++l) levels[l * plane + row * ldl + col] = S[l];
+                } else if constexpr (EPI == kEpiDD || EPI == kEpiQD) {
                     const int sc = E[row] + F[col];
                     const int64_t idx = row * ldc + col;
-                    if constexpr (!QD_OUT) {
+                    if constexpr (EPI == kEpiDD) {
                         double hi, lo;
                         renorm_levels<NS>(S, sc, hi, lo);
                         out.c[0][idx] = hi;
@@ -208,8 +222,23 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                         for (int q = 0; q < 4; ++q) out.c[q][idx] = c[q];
                     }
                 } else {
+                    // Level l is an integer number of units 2^(-13(l+2)) below
+                    // 2^53 per block, so int64 holds the sum of up to 1023 blocks.
+                    int64_t N[NS];
 #pragma unroll
-                    for (int l = 0; l < NS; ++l) levels[l * plane + row * ldl + col] = acc[l][r][v];
+                    for (int l = 0; l < NS; ++l) {
+                        N[l] = static_cast<int64_t>(ldexp(S[l], kSliceBits * (l + 2)));
+                        int64_t* u = units + l * plane + row * ldl + col;
+                        if constexpr (EPI != kEpiUnitsSet) N[l] += *u;
+                        if constexpr (EPI != kEpiUnitsQD) *u = N[l];
+                    }
+                    if constexpr (EPI == kEpiUnitsQD) {
+                        double c[4];
+                        qd_from_level_units<NS>(N, E[row] + F[col], c);
+                        const int64_t idx = row * ldc + col;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) out.c[q][idx] = c[q];
+                    }
                 }
             }
         }
@@ -279,12 +308,12 @@ hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slice
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int64_t plane = m * ldl;
     if (fused)
-        sliced_gemm_kernel<Cfg, true><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, 0, 0, E, F, OutPlanes{{C_hi, C_lo, nullptr, nullptr}},
-            ldc);
+        sliced_gemm_kernel<Cfg, kEpiDD><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
+            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, nullptr, 0, 0, E, F,
+            OutPlanes{{C_hi, C_lo, nullptr, nullptr}}, ldc);
     else if constexpr (NS == kSlices)
-        sliced_gemm_kernel<Cfg, false><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, A_slices, B_slices, levels, ldl, plane, nullptr, nullptr,
+        sliced_gemm_kernel<Cfg, kEpiLevels><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
+            m, n, ga.KB, tiles_n, A_slices, B_slices, levels, nullptr, ldl, plane, nullptr, nullptr,
             OutPlanes{{nullptr, nullptr, nullptr, nullptr}}, 0);
     else
         return hipErrorInvalidValue;  // level planes are offered for the double-double product only
@@ -322,12 +351,34 @@ hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slice
     if (m == 0 || n == 0) return hipSuccess;
     using Cfg = ConfigFor<kQdSlices>::type;
     const PackGeom ga(m, k);
-    constexpr int BM = Cfg::kTBM * 16, BN = Cfg::kTBN * 16;
-    const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
-    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t tiles_n = (n + Cfg::kTBN * 16 - 1) / (Cfg::kTBN * 16);
+    const int64_t tiles = (m + Cfg::kTBM * 16 - 1) / (Cfg::kTBM * 16) * tiles_n;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-    sliced_gemm_kernel<Cfg, true, true><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
-        m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, 0, 0, E, F, C, ldc);
+    sliced_gemm_kernel<Cfg, kEpiQD><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
+        m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, nullptr, 0, 0, E, F, C, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_qd_gemm_block(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
+                                int64_t* units, QdBlockStep step, const int32_t* E, const int32_t* F,
+                                const OutPlanes& C, int64_t ldc, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    using Cfg = ConfigFor<kQdSlices>::type;
+    const PackGeom ga(m, k);
+    const int64_t tiles_n = (n + Cfg::kTBN * 16 - 1) / (Cfg::kTBN * 16);
+    const int64_t tiles = (m + Cfg::kTBM * 16 - 1) / (Cfg::kTBM * 16) * tiles_n;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const unsigned g = static_cast<unsigned>(tiles);
+    const int64_t plane = m * n;  // level plane l of the int64 sums: units[l][row][col], row stride n
+    if (step == kQdFirstBlock)
+        sliced_gemm_kernel<Cfg, kEpiUnitsSet><<<g, Cfg::kThreads, 0, stream>>>(
+            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0);
+    else if (step == kQdMiddleBlock)
+        sliced_gemm_kernel<Cfg, kEpiUnitsAdd><<<g, Cfg::kThreads, 0, stream>>>(
+            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0);
+    else
+        sliced_gemm_kernel<Cfg, kEpiUnitsQD><<<g, Cfg::kThreads, 0, stream>>>(
+            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, units, n, plane, E, F, C, ldc);
     return hipGetLastError();
 }
 

@@ -15,7 +15,8 @@
  *                               summed exactly per level l = s + t on FP64 MFMA,
  *                               and per output the exact total of the sixteen
  *                               level sums rounded to the nearest quad double;
- *   qd_gemm / qd_gemm_ws run 1 + 1 + (2+3).
+ *   qd_gemm / qd_gemm_ws run 1 + 1 + (2+3); for k > QDGEMM_K_MAX they run
+ *   the product in k-blocks that share the exponents of the whole k (below).
  *
  * Conventions (as in ddgemm.h, whose status codes these calls return)
  *   - A quad-double matrix X is four row-major float64 planes X[0..3] in device
@@ -47,6 +48,13 @@ extern "C" {
 /* Largest k: level 15 holds 16 pairs per k, and the exact-sum bound of §2 eq. (5)
  * (67,108,865 products of 26-bit quantities) allows 67,108,865 / 16 terms. */
 #define QDGEMM_K_MAX 4194304
+/* Largest k of qd_gemm, qd_gemm_ws and qd_gemm_ws_kb.  Longer products run in
+ * k-blocks of at most QDGEMM_K_MAX terms.  Every block slices its entries below
+ * the exponents of the whole row of A / column of B, so all blocks' level sums
+ * are integers on the same grids; they are added exactly in 64-bit integers
+ * (|level sum| <= 16 k (2^13 - 1)^2 < 2^62 units for k <= 2^32), and the total
+ * is rounded once: the result equals that of one unblocked product, bit for bit. */
+#define QDGEMM_K_MAX_BLOCKED 4294967296LL
 
 /* Packed slices: the layout of ddgemm.h with 16 slices per fragment, slice s of
  * entry (o, p) at ((((o/16)*KB + p/4)*16 + s)*64) + (p%4)*16 + o%16, value
@@ -55,9 +63,13 @@ extern "C" {
  * 0 for negative sizes. */
 size_t qd_split_slices_bytes(int64_t outer, int64_t k);
 
-/* Workspace bytes qd_gemm_ws needs (slices of both operands and both exponent
- * vectors, 256-byte aligned regions); 0 for negative sizes or k > QDGEMM_K_MAX. */
+/* Workspace bytes qd_gemm_ws needs (slices of both operands for one k-block,
+ * both exponent vectors and, when k needs more than one block, sixteen int64
+ * m×n level planes; 256-byte aligned regions); 0 for negative sizes or
+ * k > QDGEMM_K_MAX_BLOCKED.  The _kb form is for qd_gemm_ws_kb with k-blocks of
+ * kblock terms (0 for kblock outside [1, QDGEMM_K_MAX] when k > 0). */
 size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
+size_t qd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int64_t kblock);
 
 /*
  * Balancing exponents and slices of one quad-double operand.
@@ -100,12 +112,19 @@ ddgemm_status_t qd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k,
  * of the exact product (E_i, F_j the row/column exponents): the truncation of
  * the operands to 208 bits below their exponents, the slice pairs below the
  * window, and the final rounding.
- *   qd_gemm     allocates its workspace with hipMallocAsync/hipFreeAsync on
- *               `stream` (DDGEMM_ERROR_WORKSPACE if that fails).
- *   qd_gemm_ws  uses the caller's workspace of ws_bytes >= qd_gemm_workspace_size
- *               (256-byte aligned), allocates nothing.
+ * k up to QDGEMM_K_MAX_BLOCKED: beyond QDGEMM_K_MAX the product runs in the
+ * fewest equal k-blocks within it, with the same result (see that constant).
+ *   qd_gemm       allocates its workspace with hipMallocAsync/hipFreeAsync on
+ *                 `stream` (DDGEMM_ERROR_WORKSPACE if that fails).
+ *   qd_gemm_ws    uses the caller's workspace of ws_bytes >= qd_gemm_workspace_size
+ *                 (256-byte aligned), allocates nothing.
+ *   qd_gemm_ws_kb the same with k-blocks of kblock terms (1 <= kblock <=
+ *                 QDGEMM_K_MAX; any k > 0) and ws_bytes >= qd_gemm_workspace_size_kb:
+ *                 block b covers k indices [b kblock, min(k, (b+1) kblock)).
+ *                 The result does not depend on kblock.
  * Errors: as for the stage calls, plus lda < max(1, k), ldb < max(1, n), a C
- * plane overlapping A, B or another C plane.
+ * plane overlapping A, B or another C plane, k > QDGEMM_K_MAX_BLOCKED, kblock
+ * out of range.
  */
 ddgemm_status_t qd_gemm(int64_t m, int64_t n, int64_t k,
                         const double* const A[4], int64_t lda,
@@ -117,6 +136,12 @@ ddgemm_status_t qd_gemm_ws(int64_t m, int64_t n, int64_t k,
                            const double* const B[4], int64_t ldb,
                            double* const C[4], int64_t ldc,
                            void* workspace, size_t ws_bytes, void* stream);
+
+ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock,
+                              const double* const A[4], int64_t lda,
+                              const double* const B[4], int64_t ldb,
+                              double* const C[4], int64_t ldc,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

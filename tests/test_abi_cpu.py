@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
                      "dd_sliced_gemm", "dd_renorm_levels", "dd_sliced_gemm_renorm",
                      "ddgemm_status_string", "dd_split_slices_bytes", "qd_gemm", "qd_gemm_ws",
                      "qd_split_balanced", "qd_sliced_gemm_renorm", "qd_split_slices_bytes",
-                     "qd_gemm_workspace_size"):
+                     "qd_gemm_workspace_size", "qd_gemm_workspace_size_kb", "qd_gemm_ws_kb"):
         assert required in names
 
 
@@ -216,8 +216,27 @@ def test_qd_sizes(ddg):
     assert L.qd_gemm_workspace_size(m, n, k) == (r(L.qd_split_slices_bytes(m, k)) + r(L.qd_split_slices_bytes(n, k))
                                                   + r(4 * m) + r(4 * n))
     assert L.qd_gemm_workspace_size(4, 4, ddg.QD_K_MAX) > 0
-    assert L.qd_gemm_workspace_size(4, 4, ddg.QD_K_MAX + 1) == 0
     assert ddg.QD_K_MAX == 67108865 // 16
+    # k-blocks: slices of one block, and sixteen int64 m x n level planes when k needs two or more
+    for kb in (1, 7, 32, 33):
+        blocked = 16 * 8 * m * n if kb < k else 0
+        assert L.qd_gemm_workspace_size_kb(m, n, k, kb) == (r(L.qd_split_slices_bytes(m, min(k, kb)))
+                                                            + r(L.qd_split_slices_bytes(n, min(k, kb)))
+                                                            + r(4 * m) + r(4 * n) + r(blocked))
+    assert L.qd_gemm_workspace_size_kb(m, n, k, k) == L.qd_gemm_workspace_size(m, n, k)
+    # beyond QD_K_MAX the default is the fewest equal blocks within it
+    big = ddg.QD_K_MAX + 1
+    assert L.qd_gemm_workspace_size(4, 4, big) == L.qd_gemm_workspace_size_kb(4, 4, big, (big + 1) // 2)
+    assert L.qd_gemm_workspace_size(4, 4, 3 * ddg.QD_K_MAX) == \
+        L.qd_gemm_workspace_size_kb(4, 4, 3 * ddg.QD_K_MAX, ddg.QD_K_MAX)
+    assert L.qd_gemm_workspace_size(1, 1, ddg.QD_K_MAX_BLOCKED) > 0
+    assert L.qd_gemm_workspace_size(1, 1, ddg.QD_K_MAX_BLOCKED + 1) == 0
+    assert ddg.QD_K_MAX_BLOCKED == 1 << 32
+    # the int64 level sums cannot overflow: |S_l| <= 16 k (2^13 - 1)^2 < 2^62 for k <= 2^32
+    assert 16 * ddg.QD_K_MAX_BLOCKED * (2 ** 13 - 1) ** 2 < 2 ** 62
+    for bad in (0, -1, ddg.QD_K_MAX + 1):
+        assert L.qd_gemm_workspace_size_kb(m, n, k, bad) == 0
+    assert L.qd_gemm_workspace_size_kb(m, n, 0, 0) > 0            # k = 0 takes no block size
 
 
 def test_qd_argument_validation(ddg):
@@ -230,7 +249,8 @@ def test_qd_argument_validation(ddg):
         return L.qd_gemm_ws(m, n, k, A, lda, B, ldb, C, ldc, ws, ws_bytes, None)
 
     assert gemm(m=-1) == INV
-    assert gemm(k=ddg.QD_K_MAX + 1, lda=ddg.QD_K_MAX + 1) == INV
+    assert gemm(k=ddg.QD_K_MAX_BLOCKED + 1, lda=ddg.QD_K_MAX_BLOCKED + 1) == INV
+    assert gemm(k=ddg.QD_K_MAX + 1, lda=ddg.QD_K_MAX + 1) == WS           # blocked: a bigger workspace
     assert gemm(lda=5) == INV
     assert gemm(ldb=4) == INV
     assert gemm(ldc=4) == INV
@@ -244,6 +264,16 @@ def test_qd_argument_validation(ddg):
     assert gemm(ws=P[6] + 8) == WS
     assert gemm(m=0, A=None, B=None, C=None) == 0                           # empty: no-op
     assert L.qd_gemm(0, 5, 6, None, 6, None, 5, None, 5, None) == 0
+
+    def gemm_kb(kb, m=4, n=5, k=6, ws_bytes=1 << 30):
+        return L.qd_gemm_ws_kb(m, n, k, kb, A, max(k, 1), B, n, C, n, P[6], ws_bytes, None)
+
+    assert gemm_kb(0) == INV
+    assert gemm_kb(-3) == INV
+    assert gemm_kb(ddg.QD_K_MAX + 1) == INV
+    assert gemm_kb(2, ws_bytes=L.qd_gemm_workspace_size_kb(4, 5, 6, 2) - 1) == WS
+    assert gemm_kb(0, m=0) == INV                                        # kblock is checked first
+    assert gemm_kb(0, k=0, ws_bytes=0) == WS                             # k = 0: no block size needed
     assert L.qd_gemm(3, 3, 3, A, 3, B, 3, None, 3, None) == INV
     # stage calls
     assert L.qd_split_balanced(4, 4, A, 4, 2, P[4], P[5], None) == INV          # bad axis
@@ -263,3 +293,7 @@ def test_qd_valid_call_without_gpu_reports_device_error(ddg):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert ddg.lib.qd_split_balanced(4, 4, _arr(P[0]), 4, 0, P[1], P[2], None) == ddg.ERROR_DEVICE
+    L = ddg.lib
+    C = _arr(P[3], P[3] + 4096, P[3] + 8192, P[3] + 12288)
+    assert L.qd_gemm_ws_kb(4, 5, 6, 2, _arr(P[0]), 6, _arr(P[2]), 5, C, 5, P[6],
+                           L.qd_gemm_workspace_size_kb(4, 5, 6, 2), None) == ddg.ERROR_DEVICE

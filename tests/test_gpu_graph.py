@@ -91,6 +91,38 @@ def test_qd_gemm_ws_replays_in_a_graph(gpu):
         assert np.array_equal(_bits(C), _bits(R)), rep
 
 
+def test_qd_gemm_ws_kb_replays_in_a_graph(gpu):
+    """The k-blocked product: its int64 level planes are written by the first
+    block's kernel (no clearing pass), so replays start from a clean state."""
+    import torch
+    m, n, k, kb = 70, 90, 100, 30
+    dA = torch.empty((4, m, k), dtype=torch.float64, device="cuda")
+    dB = torch.empty((4, k, n), dtype=torch.float64, device="cuda")
+    C = torch.empty((4, m, n), dtype=torch.float64, device="cuda")
+    ws = torch.empty(gpu.qd_workspace_size(m, n, k, kblock=kb), dtype=torch.uint8, device="cuda")
+
+    def load(seed):
+        dA.copy_(_dev(workloads.random_qd((m, k), seed, "signed_exp20")))
+        dB.copy_(_dev(workloads.random_qd((k, n), seed + 1, "uniform")))
+
+    load(70)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gpu.qd_gemm(dA, dB, C=C, workspace=ws, kblock=kb)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gpu.qd_gemm(dA, dB, C=C, workspace=ws, kblock=kb)
+    for rep, seed in enumerate((70, 80, 80, 90)):
+        load(seed)
+        C.fill_(float("nan"))
+        ws.fill_(0xA5)                     # stale level planes must not leak into a replay
+        graph.replay()
+        R = gpu.qd_gemm(dA, dB)            # eager, one block
+        assert np.array_equal(_bits(C), _bits(R)), rep
+
+
 def test_concurrent_calls_from_threads_on_their_own_streams(gpu):
     """The entry points keep no per-call state in the library: products issued
     at the same time from several host threads, each on its own stream, equal

@@ -216,6 +216,91 @@ def test_qd_k_zero_and_empty(gpu):
 
 
 # ---------------------------------------------------------------------------
+# k-blocks: every block sliced below the exponents of the whole k, level sums
+# added exactly in int64, one rounding -- the unblocked result, bit for bit
+# ---------------------------------------------------------------------------
+def _two_scale_operands(m, n, k, seed):
+    """Operands whose second half of k is far smaller, so a block's own
+    exponents would differ from those of the whole row / column."""
+    A = workloads.random_qd((m, k), seed, "uniform")
+    B = workloads.random_qd((k, n), seed + 1, "signed_exp20")
+    A[:, :, k // 2:] *= 2.0 ** -60
+    B[:, k // 2:, :] *= 2.0 ** -40
+    return A, B
+
+
+def _local_exponent_blocks(A, B, kblock):
+    """Oracle only: the result if each k-block were sliced below its own
+    exponents and the blocks' exact totals added (the design not taken)."""
+    m, k, n = A.shape[1], A.shape[2], B.shape[2]
+    unit = 2 ** (-13 * (qd.QD_SLICES + 1))
+    total = [[Fraction(0)] * n for _ in range(m)]
+    for p0 in range(0, k, kblock):
+        E, F, S, _ = qd.sliced_product(A[:, :, p0:p0 + kblock], B[:, p0:p0 + kblock, :])
+        for i in range(m):
+            for j in range(n):
+                total[i][j] += qd.level_total(S, i, j) * Fraction(2) ** int(E[i] + F[j]) * Fraction(unit)
+    out = np.zeros((4, m, n))
+    for i in range(m):
+        for j in range(n):
+            out[:, i, j] = qd.greedy_qd(total[i][j])
+    return out
+
+
+@pytest.mark.parametrize("m,n,k,kblock", [(100, 70, 130, 33), (33, 130, 200, 64), (64, 64, 64, 1),
+                                          (40, 50, 97, 96), (17, 18, 45, 45), (130, 65, 200, 7)])
+def test_qd_kblocked_chain_equals_unblocked_oracle(gpu, m, n, k, kblock):
+    _say(f"[qd k-blocks] {m}x{n}x{k} kblock={kblock}")
+    A, B = _two_scale_operands(m, n, k, 1000 + k + kblock)
+    C = _host(gpu.qd_gemm(_dev(A), _dev(B), kblock=kblock))
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert _bits_equal(C, C_ref)
+
+
+def test_qd_kblocked_inputs_distinguish_local_exponents(gpu):
+    """The operands above make block-local exponents give another result, so
+    the bit-exact comparison checks that the whole k's exponents are used."""
+    m, n, k, kblock = 12, 10, 40, 16
+    A, B = _two_scale_operands(m, n, k, 77)
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert not _bits_equal(_local_exponent_blocks(A, B, kblock), C_ref)
+    assert _bits_equal(_host(gpu.qd_gemm(_dev(A), _dev(B), kblock=kblock)), C_ref)
+
+
+def test_qd_kblocked_strided_and_null_planes(gpu):
+    import torch
+    m, n, k = 50, 41, 90
+    A, B = _two_scale_operands(m, n, k, 88)
+    A[2:] = 0.0                                       # double-double A: two planes given
+    bigA = torch.zeros((2, m, k + 5), dtype=torch.float64, device="cuda")
+    bigA[:, :, :k] = _dev(A[:2])
+    bigB = torch.zeros((4, k, n + 3), dtype=torch.float64, device="cuda")
+    bigB[:, :, :n] = _dev(B)
+    out = torch.full((4, m, n + 2), 5.0, dtype=torch.float64, device="cuda")
+    gpu.qd_gemm([bigA[0, :, :k], bigA[1, :, :k], None, None], [bigB[c, :, :n] for c in range(4)],
+                C=[out[c, :, :n] for c in range(4)], kblock=25)
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert _bits_equal(_host(out[:, :, :n].contiguous()), C_ref)
+    assert (_host(out[:, :, n:]) == 5.0).all()
+
+
+def test_qd_kblocked_workload_matches_unblocked(gpu):
+    """qd1024 in blocks of 256 (four blocks: first, two middle, last) equals the
+    one-block product everywhere and the oracle on sampled entries."""
+    import torch
+    w = workloads.by_name("qd1024")
+    A, B = workloads.make_qd_operands(w)
+    dA, dB = _dev(A), _dev(B)
+    C1 = gpu.qd_gemm(dA, dB)
+    C4 = gpu.qd_gemm(dA, dB, kblock=256)
+    assert torch.equal(C1.view(torch.int64), C4.view(torch.int64))
+    rng = np.random.default_rng(31)
+    for i, j in zip(rng.integers(0, w.m, 6), rng.integers(0, w.n, 6)):
+        _, _, ref = _oracle_entry(A, B, int(i), int(j))
+        assert _bits_equal(_host(C4[:, int(i), int(j)]), ref)
+
+
+# ---------------------------------------------------------------------------
 # workloads: accuracy against the exact product, bit-exact sampled outputs
 # ---------------------------------------------------------------------------
 def _oracle_entry(A, B, i, j):

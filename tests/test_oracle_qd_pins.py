@@ -124,6 +124,27 @@ def test_level_sums_brute_force():
     assert qd.QD_K_MAX == 4194304
 
 
+def test_level_sums_add_over_k_blocks_under_shared_exponents():
+    """Integer level sums are sums over k: with the digits taken below the
+    exponents of whole rows / columns, blocks of k add up to the full sums
+    exactly, whatever the blocks' own exponents would be."""
+    A = workloads.random_qd((6, 30), 12, "uniform")
+    B = workloads.random_qd((30, 5), 13, "normal")
+    A[:, :, 15:] *= 2.0 ** -50
+    E, DA = qd.slice_rows(A)
+    F, DB = qd.slice_cols(B)
+    S = qd.level_sums(DA, DB)
+    parts = sum(qd.level_sums(DA[:, :, p0:p0 + 7], DB[:, p0:p0 + 7, :]) for p0 in range(0, 30, 7))
+    assert np.array_equal(parts, S)
+    # digits of one entry depend only on it and its row's exponent
+    i, p = 2, 20
+    assert [int(d) for d in DA[:, i, p]] == qd.slice_entry(A[:, i, p], int(E[i]))
+    # the second half's own exponents are smaller: its digits would differ
+    E_local, DA_local = qd.slice_rows(A[:, :, 15:])
+    assert (E_local < E).all()
+    assert not np.array_equal(DA_local, DA[:, :, 15:])
+
+
 def test_greedy_closed_forms_and_properties():
     assert qd.greedy_qd(1 + P ** -60) == [1.0, 2.0 ** -60, 0.0, 0.0]
     assert qd.greedy_qd(3 * P ** -1074) == [3 * 5e-324, 0.0, 0.0, 0.0]
