@@ -118,20 +118,51 @@ __global__ void __launch_bounds__(256) exp_rows_kernel(int64_t rows, int64_t col
     }
 }
 
-// Column exponents (axis 1, the B operand): each thread takes one column over a
-// chunk of rows and folds its encoded maximum in with a device-memory atomicMax.
-__global__ void __launch_bounds__(256) exp_cols_kernel(int64_t rows, int64_t cols,
-                                                       const double* __restrict__ hi,
-                                                       const double* __restrict__ lo, int64_t ld,
-                                                       int64_t rows_per_chunk,
-                                                       int32_t* __restrict__ codes) {
-    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (col >= cols) return;
-    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * rows_per_chunk;
-    const int64_t r1 = min(rows, r0 + rows_per_chunk);
-    int code = kNoExp;
-    for (int64_t r = r0; r < r1; ++r) code = max(code, entry_exp_code(hi[r * ld + col], lo ? lo[r * ld + col] : 0.0));
-    if (code != kNoExp) atomicMax(codes + col, code);
+// Column exponents (axis 1, the B operand): workgroup (b, c) reduces columns
+// 16b .. 16b+15 over row part c of gridDim.y; thread t takes column 16b + t % 16
+// and rows t / 16, t / 16 + NT / 16, ..., four rows in flight per plane.  With
+// one part the decoded exponents are stored; with several the encoded maxima
+// are folded into `out` (cleared to kNoExp) with atomicMax and decoded after.
+template <int NT>
+__global__ void __launch_bounds__(NT) exp_cols_block_kernel(int64_t rows, int64_t cols,
+                                                            const double* __restrict__ hi,
+                                                            const double* __restrict__ lo, int64_t ld,
+                                                            int32_t* __restrict__ out) {
+    constexpr int kRowGroups = NT / 16;
+    __shared__ int codes[NT];
+    const int t = threadIdx.x;
+    const int64_t parts = gridDim.y;
+    const int64_t r0 = rows * blockIdx.y / parts, r1 = rows * (blockIdx.y + 1) / parts;
+    const int64_t nblocks = (cols + 15) / 16;
+    for (int64_t b = blockIdx.x; b < nblocks; b += gridDim.x) {  // uniform per workgroup
+        const int64_t o = b * 16 + (t & 15);
+        int code = kNoExp;
+        if (o < cols) {
+            int64_t p = r0 + (t >> 4);
+            for (; p + 3 * kRowGroups < r1; p += 4 * kRowGroups) {
+                double xh[4], xl[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    xh[u] = hi[(p + kRowGroups * u) * ld + o];
+                    xl[u] = lo ? lo[(p + kRowGroups * u) * ld + o] : 0.0;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) code = max(code, entry_exp_code(xh[u], xl[u]));
+            }
+            for (; p < r1; p += kRowGroups) code = max(code, entry_exp_code(hi[p * ld + o], lo ? lo[p * ld + o] : 0.0));
+        }
+        codes[t] = code;
+        __syncthreads();
+        if (t < 16 && o < cols) {
+            int c = kNoExp;
+            for (int g = 0; g < kRowGroups; ++g) c = max(c, codes[g * 16 + t]);
+            if (parts == 1)
+                out[o] = decode_exp(c);
+            else if (c != kNoExp)
+                atomicMax(out + o, c);
+        }
+        __syncthreads();  // codes[] is rewritten by the next column block
+    }
 }
 
 // One thread per packed (fragment, lane) position; writes the NS slices of
@@ -309,15 +340,11 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
     if (axis == 0) {
         exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X_hi, X_lo, ldx, exps);
     } else {
-        fill_int_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols, kNoExp);
-        if (rows > 0) {
-            int64_t rpc = (rows + 4095) / 4096;
-            if (rpc < 64) rpc = 64;
-            const int64_t chunks = (rows + rpc - 1) / rpc;
-            dim3 grid(static_cast<unsigned>((cols + 255) / 256), static_cast<unsigned>(chunks));
-            exp_cols_kernel<<<grid, 256, 0, stream>>>(rows, cols, X_hi, X_lo, ldx, rpc, exps);
-        }
-        decode_exps_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols);
+        const int64_t parts = exp_col_parts(rows, cols);
+        const dim3 grid(grid_for(cols, 16, 1 << 20), static_cast<unsigned>(parts));
+        if (parts > 1) fill_int_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols, kNoExp);
+        exp_cols_block_kernel<1024><<<grid, 1024, 0, stream>>>(rows, cols, X_hi, X_lo, ldx, exps);
+        if (parts > 1) decode_exps_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

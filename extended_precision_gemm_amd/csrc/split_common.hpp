@@ -53,6 +53,21 @@ __global__ void decode_exps_kernel(int32_t* __restrict__ exps, int64_t count) {
         exps[i] = decode_exp(exps[i]);
 }
 
+// Row parts for the column-exponent kernels: enough workgroups of 16 columns
+// to fill the chip, each part at least kMinRowsPerPart rows long (one part,
+// and so no clearing and decoding launches, from kExpColMinWorkgroups column
+// blocks up).
+constexpr int64_t kExpColMinWorkgroups = 256;
+constexpr int64_t kMinRowsPerPart = 256;
+inline int64_t exp_col_parts(int64_t rows, int64_t cols) {
+    const int64_t blocks = (cols + 15) / 16;
+    int64_t parts = (kExpColMinWorkgroups + blocks - 1) / blocks;
+    const int64_t most = rows / kMinRowsPerPart > 1 ? rows / kMinRowsPerPart : 1;
+    if (parts > most) parts = most;
+    if (parts > 65535) parts = 65535;
+    return parts;
+}
+
 inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap) {
     int64_t g = (work + per_block - 1) / per_block;
     if (g < 1) g = 1;
