@@ -1,0 +1,119 @@
+"""Operands whose packed slices pass 2^31 values (GPU tests).
+
+A tall double-double A (65536 x 8192), a wide double-double B (8192 x 65536)
+and a tall quad-double A (36864 x 4096): each packed slice buffer holds more
+than 2^31 doubles, so a 32-bit index anywhere on the path (slicer, GEMM stage
+copies, epilogue) would read or write the wrong place.  The large operand is a
+seeded block repeated along its long side on the device, which keeps input
+generation cheap; outputs of the last repeat must equal those of the first,
+and sampled outputs there are compared bit for bit with the oracle's chain on
+the same rows and columns of the seeded block.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import exact, qd
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _bits_equal(a, b):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    return a.shape == b.shape and np.array_equal(a.view(np.int64), b.view(np.int64))
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _free():
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _dd_chain(ah, al, bh, bl, rows, cols):
+    E, DA = exact.slice_rows(ah, al, rows)
+    F, DB = exact.slice_cols(bh, bl, cols)
+    return exact.renorm_levels(exact.level_values(exact.level_sums_units(DA, DB)), E, F)
+
+
+@pytest.mark.timeout(600)
+def test_dd_tall_A_past_2_31_slice_values(gpu):
+    base, reps, k, n = 1024, 64, 8192, 64
+    m = base * reps
+    assert gpu.slices_bytes(m, k) // 8 > 2 ** 31
+    _say(f"[large] dd tall A {m}x{k} (block of {base} rows x {reps}), n={n}")
+    ah, al = workloads.random_dd((base, k), 5151, "signed_exp20")
+    bh, bl = workloads.random_dd((k, n), 5152, "normal")
+    dAh, dAl = _dev(ah).repeat(reps, 1), _dev(al).repeat(reps, 1)
+    Ch, Cl = gpu.dd_gemm(dAh, dAl, _dev(bh), _dev(bl))
+    del dAh, dAl
+    hCh, hCl = _host(Ch), _host(Cl)
+    del Ch, Cl
+    _free()
+    assert _bits_equal(hCh[-base:], hCh[:base]) and _bits_equal(hCl[-base:], hCl[:base])
+    rows, cols = [0, 517, base - 1], [0, 31, n - 1]
+    Rh, Rl = _dd_chain(ah, al, bh, bl, rows, cols)
+    last = [(reps - 1) * base + r for r in rows]
+    assert _bits_equal(hCh[np.ix_(last, cols)], Rh) and _bits_equal(hCl[np.ix_(last, cols)], Rl)
+
+
+@pytest.mark.timeout(600)
+def test_dd_wide_B_past_2_31_slice_values(gpu):
+    base, reps, k, m = 1024, 64, 8192, 64
+    n = base * reps
+    assert gpu.slices_bytes(n, k) // 8 > 2 ** 31
+    _say(f"[large] dd wide B {k}x{n} (block of {base} columns x {reps}), m={m}")
+    ah, al = workloads.random_dd((m, k), 5161, "uniform")
+    bh, bl = workloads.random_dd((k, base), 5162, "signed_exp20")
+    dBh, dBl = _dev(bh).repeat(1, reps), _dev(bl).repeat(1, reps)
+    Ch, Cl = gpu.dd_gemm(_dev(ah), _dev(al), dBh, dBl)
+    del dBh, dBl
+    hCh, hCl = _host(Ch), _host(Cl)
+    del Ch, Cl
+    _free()
+    assert _bits_equal(hCh[:, -base:], hCh[:, :base]) and _bits_equal(hCl[:, -base:], hCl[:, :base])
+    rows, cols = [0, 40, m - 1], [0, 700, base - 1]
+    Rh, Rl = _dd_chain(ah, al, bh, bl, rows, cols)
+    last = [(reps - 1) * base + c for c in cols]
+    assert _bits_equal(hCh[np.ix_(rows, last)], Rh) and _bits_equal(hCl[np.ix_(rows, last)], Rl)
+
+
+@pytest.mark.timeout(600)
+def test_qd_tall_A_past_2_31_slice_values(gpu):
+    base, reps, k, n = 512, 72, 4096, 64
+    m = base * reps
+    assert gpu.qd_slices_bytes(m, k) // 8 > 2 ** 31
+    _say(f"[large] qd tall A {m}x{k} (block of {base} rows x {reps}), n={n}")
+    A = workloads.random_qd((base, k), 5171, "signed_exp20")
+    B = workloads.random_qd((k, n), 5172, "uniform")
+    dA = _dev(A).repeat(1, reps, 1)
+    C = gpu.qd_gemm(dA, _dev(B))
+    del dA
+    hC = _host(C)
+    del C
+    _free()
+    assert _bits_equal(hC[:, -base:], hC[:, :base])
+    rows, cols = [0, 300, base - 1], [0, n - 1]
+    E, DA = qd.slice_rows(A, rows=rows)
+    F, DB = qd.slice_cols(B, cols=cols)
+    ref = qd.renorm_levels(qd.level_sums(DA, DB), E, F)
+    last = [(reps - 1) * base + r for r in rows]
+    assert _bits_equal(hC[:, last][:, :, cols], ref)
