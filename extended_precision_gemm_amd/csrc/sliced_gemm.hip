@@ -11,10 +11,10 @@
 // 2^53 units: the matrix-core accumulation is exact in any order.
 //
 // Work split: each wave computes a (16 RPW)x16 strip (RPW 16x16 blocks stacked;
-// RPW = 2 for up to eight slices, 1 for nine to sixteen) with one accumulator
+// RPW = 2 for 4, 5, 7 and 8 slices, 1 for 6 and for 9 to 16) with one accumulator
 // per level and block; a workgroup of WM x WN waves owns a (16 RPW WM) x (16 WN)
-// output tile, and WGS workgroups share a CU (two waves per SIMD in every
-// configuration).  The same kernel serves the quad-double product:
+// output tile; at least two waves share each SIMD (with six slices a workgroup
+// takes 72 KB of LDS and two fit a CU, four waves per SIMD).  The same kernel serves the quad-double product:
 // sixteen slices, 136 pairs, sixteen levels, and the exact four-double
 // epilogue (or, for a k-block of a longer product, the level sums in integer
 // units added into int64 planes).  The operand panels move through LDS in stages
@@ -281,7 +281,9 @@ __global__ void __launch_bounds__(64) probe_mfma_kernel(double* __restrict__ out
 template <int NS> struct ConfigFor;
 template <> struct ConfigFor<4> { using type = GemmConfig<2, 4, 2, 2, 1, 4>; };
 template <> struct ConfigFor<5> { using type = GemmConfig<2, 4, 2, 2, 1, 5>; };
-template <> struct ConfigFor<6> { using type = GemmConfig<2, 4, 2, 2, 1, 6>; };
+// Six slices: one 16x16 block per wave (32x64 tile) measured faster than two
+// (73.2 vs 71.6 TFLOP/s at 4096^3; slower for 4, 5 and 7 slices).
+template <> struct ConfigFor<6> { using type = GemmConfig<2, 4, 2, 2, 1, 6, 1>; };
 template <> struct ConfigFor<7> { using type = GemmConfig<2, 4, 2, 2, 1, 7>; };
 template <> struct ConfigFor<8> { using type = GemmConfig<2, 4, 2, 2, 1, 8>; };
 // Nine to sixteen slices (wide double-double windows, the quad-double product):
