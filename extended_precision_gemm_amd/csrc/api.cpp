@@ -27,11 +27,15 @@ inline bool overlaps(const void* a, int64_t a_elems, const void* b, int64_t b_el
     return pa < pb + b_elems * 8 && pb < pa + a_elems * 8;
 }
 
-inline bool ld_ok(int64_t ld, int64_t cols) { return ld >= (cols > 1 ? cols : 1); }
-
 // Sizes beyond this would overflow the 64-bit byte counts below.
 inline bool size_ok(int64_t a, int64_t b) {
     return a >= 0 && b >= 0 && (a == 0 || b <= (int64_t(1) << 58) / (a > 0 ? a : 1));
+}
+
+// A row stride for a rows×cols matrix: at least max(1, cols), and small enough
+// that the extent rows·ld (and its bytes) cannot overflow.
+inline bool ld_ok(int64_t ld, int64_t rows, int64_t cols) {
+    return ld >= (cols > 1 ? cols : 1) && size_ok(rows, ld);
 }
 
 std::atomic<int> g_device_state[256];  // 0 unknown, 1 gfx950, 2 unsupported
@@ -58,7 +62,7 @@ inline int64_t k_max(int ns) { return DDGEMM_K_MAX_NS(ns); }
 
 ddgemm_status_t validate_split(int64_t rows, int64_t cols, const double* X_hi, int64_t ldx, int axis, int ns,
                                const int32_t* exps, const double* slices) {
-    if (!size_ok(rows, cols) || !ld_ok(ldx, cols) || (axis != 0 && axis != 1) || !ns_ok(ns))
+    if (!size_ok(rows, cols) || !ld_ok(ldx, rows, cols) || (axis != 0 && axis != 1) || !ns_ok(ns))
         return DDGEMM_ERROR_INVALID_VALUE;
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
@@ -192,7 +196,7 @@ ddgemm_status_t dd_split_balanced(int64_t rows, int64_t cols, const double* X_hi
 ddgemm_status_t dd_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices,
                                const double* B_slices, double* levels, int64_t ldl, void* stream) {
     ddgemm_status_t st = validate_gemm_dims(m, n, k);
-    if (st != DDGEMM_SUCCESS || !ld_ok(ldl, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (st != DDGEMM_SUCCESS || !ld_ok(ldl, m, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!levels || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
     if (!size_ok(m * ldl, DDGEMM_NUM_LEVELS)) return DDGEMM_ERROR_INVALID_VALUE;
@@ -204,7 +208,8 @@ ddgemm_status_t dd_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_
 ddgemm_status_t dd_renorm_levels(int64_t m, int64_t n, const double* levels, int64_t ldl,
                                  const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
                                  int64_t ldc, void* stream) {
-    if (!size_ok(m, n) || !ld_ok(ldl, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!size_ok(m, n) || !ld_ok(ldl, m, n) || !ld_ok(ldc, m, n) || !size_ok(m * ldl, DDGEMM_NUM_LEVELS))
+        return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!levels || !E || !F || !C_hi || !C_lo) return DDGEMM_ERROR_INVALID_VALUE;
     const int64_t ce = extent(m, n, ldc);
@@ -220,7 +225,7 @@ ddgemm_status_t dd_sliced_gemm_renorm_ns(int64_t m, int64_t n, int64_t k, int ns
                                          const int32_t* E, const double* B_slices, const int32_t* F,
                                          double* C_hi, double* C_lo, int64_t ldc, void* stream) {
     ddgemm_status_t st = validate_gemm_dims(m, n, k);
-    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, n) || !ns_ok(nslices) || k > k_max(nslices))
+    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, m, n) || !ns_ok(nslices) || k > k_max(nslices))
         return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!E || !F || !C_hi || !C_lo || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
@@ -244,7 +249,7 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
     ddgemm_status_t st = validate_sizes(m, n, k);
     if (st != DDGEMM_SUCCESS) return st;
     if (!ns_ok(nslices) || !kblock_ok(k, nslices, kblock)) return DDGEMM_ERROR_INVALID_VALUE;
-    if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!ld_ok(lda, m, k) || !ld_ok(ldb, k, n) || !ld_ok(ldc, m, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return DDGEMM_ERROR_INVALID_VALUE;
     const int64_t ae = extent(m, k, lda), be = extent(k, n, ldb), ce = extent(m, n, ldc);
@@ -319,7 +324,7 @@ ddgemm_status_t dd_gemm(int64_t m, int64_t n, int64_t k, const double* A_hi, con
                         double* C_lo, int64_t ldc, void* stream) {
     ddgemm_status_t st = validate_sizes(m, n, k);
     if (st != DDGEMM_SUCCESS) return st;
-    if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!ld_ok(lda, m, k) || !ld_ok(ldb, k, n) || !ld_ok(ldc, m, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return DDGEMM_ERROR_INVALID_VALUE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
@@ -353,7 +358,7 @@ size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
 
 ddgemm_status_t qd_split_balanced(int64_t rows, int64_t cols, const double* const X[4], int64_t ldx, int axis,
                                   int32_t* exps, double* slices, void* stream) {
-    if (!size_ok(rows, cols) || !ld_ok(ldx, cols) || (axis != 0 && axis != 1)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!size_ok(rows, cols) || !ld_ok(ldx, rows, cols) || (axis != 0 && axis != 1)) return DDGEMM_ERROR_INVALID_VALUE;
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     if (k > QDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
@@ -371,7 +376,7 @@ ddgemm_status_t qd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k, const dou
                                       const double* B_slices, const int32_t* F, double* const C[4], int64_t ldc,
                                       void* stream) {
     ddgemm_status_t st = validate_qd_gemm_dims(m, n, k);
-    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (st != DDGEMM_SUCCESS || !ld_ok(ldc, m, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     OutPlanes out;
     if ((st = read_out_planes(C, extent(m, n, ldc), out)) != DDGEMM_SUCCESS) return st;
@@ -385,7 +390,7 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
                               void* workspace, size_t ws_bytes, void* stream) {
     ddgemm_status_t st = validate_qd_blocked_dims(m, n, k, kblock);
     if (st != DDGEMM_SUCCESS) return st;
-    if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!ld_ok(lda, m, k) || !ld_ok(ldb, k, n) || !ld_ok(ldc, m, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     const int64_t ae = extent(m, k, lda), be = extent(k, n, ldb), ce = extent(m, n, ldc);
     QdPlanes pa, pb;
@@ -451,7 +456,7 @@ ddgemm_status_t qd_gemm(int64_t m, int64_t n, int64_t k, const double* const A[4
     if (k < 0) return DDGEMM_ERROR_INVALID_VALUE;
     ddgemm_status_t st = validate_qd_blocked_dims(m, n, k, qd_default_kblock(k));
     if (st != DDGEMM_SUCCESS) return st;
-    if (!ld_ok(lda, k) || !ld_ok(ldb, n) || !ld_ok(ldc, n)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (!ld_ok(lda, m, k) || !ld_ok(ldb, k, n) || !ld_ok(ldc, m, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     QdPlanes pa, pb;
     OutPlanes out;

@@ -20,7 +20,9 @@
  * Conventions for every entry point
  *   - All matrices are row-major float64 planes in device memory; a
  *     double-double matrix X is the pair of planes (X_hi, X_lo) with value
- *     X_hi + X_lo.  Leading dimensions count elements.  A lo pointer may be
+ *     X_hi + X_lo.  Leading dimensions count elements; a rows×cols matrix
+ *     needs max(1, cols) <= ld and rows·ld <= 2^58 (so that no extent or byte
+ *     count overflows), else DDGEMM_ERROR_INVALID_VALUE.  A lo pointer may be
  *     NULL, meaning an all-zero lo plane.
  *   - Pointers are owned by the caller; the library keeps none after a call
  *     returns.  Only dd_gemm allocates (stream-ordered, freed on the stream).

@@ -152,6 +152,31 @@ def test_valid_call_without_gpu_reports_device_error(ddg):
     assert L.dd_split_balanced(4, 4, P[0], None, 4, 0, P[1], P[2], None) == ddg.ERROR_DEVICE
 
 
+def test_leading_dimensions_whose_extent_would_overflow_are_rejected(ddg):
+    """rows x ld must stay within the 2^58-element size bound, so the extent and
+    byte arithmetic behind the overlap checks cannot overflow."""
+    L = ddg.lib
+    INV = ddg.ERROR_INVALID_VALUE
+    huge = 1 << 62
+    assert L.dd_gemm_ws(3, 4, 5, P[0], None, huge, P[1], None, 4, P[2], P[3], 4, P[4], 1 << 30, None) == INV
+    assert L.dd_gemm_ws(3, 4, 5, P[0], None, 5, P[1], None, huge, P[2], P[3], 4, P[4], 1 << 30, None) == INV
+    assert L.dd_gemm_ws(3, 4, 5, P[0], None, 5, P[1], None, 4, P[2], P[3], huge, P[4], 1 << 30, None) == INV
+    assert L.dd_gemm(3, 4, 5, P[0], None, huge, P[1], None, 4, P[2], P[3], 4, None) == INV
+    assert L.dd_split_balanced(3, 4, P[0], None, huge, 0, P[1], P[2], None) == INV
+    assert L.dd_sliced_gemm(3, 4, 5, P[0], P[1], P[2], huge, None) == INV
+    assert L.dd_renorm_levels(3, 4, P[0], huge, P[1], P[2], P[3], P[4], 4, None) == INV
+    assert L.dd_renorm_levels(3, 4, P[0], 4, P[1], P[2], P[3], P[4], huge, None) == INV
+    assert L.dd_sliced_gemm_renorm(3, 4, 5, P[0], P[1], P[2], P[3], P[4], P[5], huge, None) == INV
+    A, B = _arr(P[0]), _arr(P[1])
+    C = _arr(P[2], P[2] + 4096, P[2] + 8192, P[2] + 12288)
+    assert L.qd_gemm_ws(3, 4, 5, A, 5, B, huge, C, 4, P[4], 1 << 30, None) == INV
+    assert L.qd_gemm_ws_kb(3, 4, 5, 2, A, huge, B, 4, C, 4, P[4], 1 << 30, None) == INV
+    assert L.qd_split_balanced(3, 4, A, huge, 0, P[1], P[2], None) == INV
+    # the bound is rows x ld <= 2^58, whatever the row count
+    assert L.dd_split_balanced(1, 4, P[0], None, huge, 0, P[1], P[2], None) == INV
+    assert L.dd_split_balanced(1, 4, P[0], None, 1 << 58, 0, P[1], P[2], None) in (ddg.ERROR_DEVICE, 0)
+
+
 def test_layout_pack_unpack_roundtrip(ddg):
     from extended_precision_gemm_amd import layout
     rng = np.random.default_rng(0)
