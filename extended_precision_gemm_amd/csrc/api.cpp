@@ -289,8 +289,11 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
         const double* a_lo = A_lo ? A_lo + p0 : nullptr;
         const double* b_hi = B_hi ? B_hi + p0 * ldb : nullptr;
         const double* b_lo = B_lo ? B_lo + p0 * ldb : nullptr;
-        e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s);
-        if (e == hipSuccess) e = launch_split(kc, n, b_hi, b_lo, ldb, 1, nslices, F, B_sl, s);
+        // Both exponent passes first: one right behind a slice pass's writes runs at half speed.
+        e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s, kSplitExps);
+        if (e == hipSuccess) e = launch_split(kc, n, b_hi, b_lo, ldb, 1, nslices, F, B_sl, s, kSplitExps);
+        if (e == hipSuccess) e = launch_split(kc, n, b_hi, b_lo, ldb, 1, nslices, F, B_sl, s, kSplitSlices);
+        if (e == hipSuccess) e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s, kSplitSlices);
         if (e != hipSuccess) break;
         if (b == 0) {
             e = launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, C_hi, C_lo, ldc, true, s);
@@ -422,8 +425,10 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (blocks == 1) {
-        hipError_t e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s);
-        if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s);
+        hipError_t e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitExps);  // both exponent passes first
+        if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitExps);
+        if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitSlices);
+        if (e == hipSuccess) e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitSlices);
         if (e == hipSuccess) e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s);
         return launched(e);
     }

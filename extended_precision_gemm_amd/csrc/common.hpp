@@ -46,9 +46,17 @@ struct OutPlanes {
     double* c[4];
 };
 
+// Phases of an operand's split: the exponent pass and the slice pass, so that a
+// product can run both operands' exponent passes before either slice pass
+// (measured: an exponent pass right behind a slice pass's gigabyte of writes
+// runs at half speed).  An operand sliced in one pass does it all in the slice
+// phase.
+enum SplitPhase { kSplitExps = 1, kSplitSlices = 2, kSplitAll = 3 };
+
 // Host-side launch helpers implemented next to their kernels.
 hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
-                        int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream);
+                        int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream,
+                        int phases = kSplitAll);
 hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                               const double* B_slices, double* levels, int64_t ldl,
                               const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
@@ -60,7 +68,7 @@ hipError_t launch_probe_mfma(double* out, hipStream_t stream);
 hipError_t launch_dd_accumulate(int64_t m, int64_t n, double* C_hi, double* C_lo, int64_t ldc, const double* T_hi,
                                 const double* T_lo, int64_t ldt, hipStream_t stream);
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
-                           double* slices, hipStream_t stream);
+                           double* slices, hipStream_t stream, int phases = kSplitAll);
 hipError_t launch_qd_exps(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
                           hipStream_t stream);
 hipError_t launch_qd_slices(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis,

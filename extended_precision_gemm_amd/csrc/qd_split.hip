@@ -233,7 +233,7 @@ hipError_t launch_qd_slices(int64_t rows, int64_t cols, const QdPlanes& X, int64
 }
 
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
-                           double* slices, hipStream_t stream) {
+                           double* slices, hipStream_t stream, int phases) {
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     if (outer == 0) return hipSuccess;
@@ -244,13 +244,17 @@ hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_
         if (kparts > gb.KB) kparts = gb.KB;
         const int64_t bytes = rows * cols * 32;
         if (bytes <= kQdSmallColsBytes && bytes * kparts <= kQdSmallColsReread) {
+            if (!(phases & kSplitSlices)) return hipSuccess;  // one pass: all of it in the slice phase
             const dim3 grid(static_cast<unsigned>(gb.RB), static_cast<unsigned>(kparts));
             qd_split_cols_block_kernel<1024><<<grid, 1024, 0, stream>>>(outer, k, gb.KB, X, ldx, exps, slices);
             return hipGetLastError();
         }
     }
-    hipError_t err = launch_qd_exps(rows, cols, X, ldx, axis, exps, stream);
-    if (err != hipSuccess) return err;
+    if (phases & kSplitExps) {
+        hipError_t err = launch_qd_exps(rows, cols, X, ldx, axis, exps, stream);
+        if (err != hipSuccess) return err;
+    }
+    if (!(phases & kSplitSlices)) return hipSuccess;
     return launch_qd_slices(rows, cols, X, ldx, axis, exps, slices, stream);
 }
 

@@ -315,7 +315,8 @@ constexpr int64_t kSmallColsReread = 320ll << 20;
 
 template <int NS>
 hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
-                           int64_t ldx, int axis, int32_t* exps, double* slices, hipStream_t stream) {
+                           int64_t ldx, int axis, int32_t* exps, double* slices, hipStream_t stream,
+                           int phases) {
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     if (outer == 0) return hipSuccess;
@@ -327,6 +328,8 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
     const bool small_cols = axis == 1 && bytes <= kSmallColsBytes && bytes * kparts <= kSmallColsReread;
     if (g.doubles(NS) > 0 && (g.RB >= kFusedMinBlocks || small_cols)) {
         // One pass per block; k-blocks shared among parts when blocks are few.
+        // All of it belongs to the slice phase.
+        if (!(phases & kSplitSlices)) return hipSuccess;
         const dim3 grid(static_cast<unsigned>(g.RB), static_cast<unsigned>(kparts));
         if (axis == 0)
             split_block_kernel<0, kBlockThreads, NS><<<grid, kBlockThreads, 0, stream>>>(
@@ -337,9 +340,9 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
         return hipGetLastError();
     }
     // Otherwise two passes over the operand: exponents, then slices.
-    if (axis == 0) {
+    if ((phases & kSplitExps) && axis == 0) {
         exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X_hi, X_lo, ldx, exps);
-    } else {
+    } else if (phases & kSplitExps) {
         const int64_t parts = exp_col_parts(rows, cols);
         const dim3 grid(grid_for(cols, 16, 1 << 20), static_cast<unsigned>(parts));
         if (parts > 1) fill_int_kernel<<<grid_for(cols, 256, 4096), 256, 0, stream>>>(exps, cols, kNoExp);
@@ -348,7 +351,7 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (g.doubles(NS) == 0) return hipSuccess;
+    if (!(phases & kSplitSlices) || g.doubles(NS) == 0) return hipSuccess;
     const int64_t total = g.RB * g.KB * kFragDoubles;
     const unsigned grid = grid_for(total, 256, 1 << 20);
     if (axis == 0)
@@ -361,21 +364,22 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
 }  // namespace
 
 hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
-                        int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream) {
+                        int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream,
+                        int phases) {
     switch (ns) {
-        case 4: return launch_split_ns<4>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 5: return launch_split_ns<5>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 6: return launch_split_ns<6>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 7: return launch_split_ns<7>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 8: return launch_split_ns<8>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 9: return launch_split_ns<9>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 10: return launch_split_ns<10>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 11: return launch_split_ns<11>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 12: return launch_split_ns<12>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 13: return launch_split_ns<13>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 14: return launch_split_ns<14>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 15: return launch_split_ns<15>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
-        case 16: return launch_split_ns<16>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream);
+        case 4: return launch_split_ns<4>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 5: return launch_split_ns<5>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 6: return launch_split_ns<6>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 7: return launch_split_ns<7>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 8: return launch_split_ns<8>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 9: return launch_split_ns<9>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 10: return launch_split_ns<10>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 11: return launch_split_ns<11>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 12: return launch_split_ns<12>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 13: return launch_split_ns<13>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 14: return launch_split_ns<14>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 15: return launch_split_ns<15>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 16: return launch_split_ns<16>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
         default: return hipErrorInvalidValue;
     }
 }

@@ -163,6 +163,41 @@ def test_split_block_path_bit_exact(gpu, axis):
     assert _bits_equal(_unpacked(packed, outer, k), exact.slice_values(D))
 
 
+@pytest.mark.parametrize("rows,cols", [(3000, 2500), (64, 30000), (1500, 4100)])
+def test_split_large_B_two_pass_bit_exact(gpu, rows, cols):
+    """B operands above the one-pass size (24 MiB) take the two-pass split
+    (column-block exponents, then slices): ragged column blocks, the edge values
+    of the small tests, a column whose only nonzero entry is in the last row, an
+    entry whose RN(hi + lo) rounds up to the next binade; then NULL lo and a
+    strided view."""
+    import torch
+    assert rows * cols * 16 > 24 << 20
+    rng = np.random.default_rng(rows + cols)
+    hi, lo = _edge_matrix(rng, rows, cols)
+    hi[:, cols - 3] = 0.0
+    lo[:, cols - 3] = 0.0
+    hi[rows - 1, cols - 3] = 2.0 ** 30                      # last row decides the column
+    hi[rows // 2, cols - 5], lo[rows // 2, cols - 5] = 2.0 ** 40 - 2.0 ** -13, 2.0 ** -14  # tie: RN -> 2^40
+    hi[:, 1030] *= 2.0 ** 200                                # a column far above the others
+    E, packed, outer, k = _gpu_split(gpu, hi, lo, 1)
+    F_ref = exact.balancing_exponents(hi, lo, 1)
+    assert np.array_equal(_host(E), F_ref)
+    cols_s = sorted({0, 2, 1023, 1024, 1030, cols - 5, cols - 3, cols - 1})
+    _, D = exact.slice_cols(hi, lo, cols_s)
+    assert _bits_equal(_unpacked(packed, outer, k, cols_s), exact.slice_values(D.transpose(0, 2, 1)))
+    # NULL lo
+    E0, _ = gpu.split_balanced(_dev(hi), None, 1)
+    assert np.array_equal(_host(E0), exact.balancing_exponents(hi, np.zeros_like(lo), 1))
+    # a strided view: columns of a wider matrix
+    wide_h = torch.zeros((rows, cols + 40), dtype=torch.float64, device="cuda")
+    wide_l = torch.zeros_like(wide_h)
+    wide_h[:, 7:7 + cols] = _dev(hi)
+    wide_l[:, 7:7 + cols] = _dev(lo)
+    Es, Ps = gpu.split_balanced(wide_h[:, 7:7 + cols], wide_l[:, 7:7 + cols], 1)
+    assert np.array_equal(_host(Es), F_ref)
+    assert torch.equal(Ps.view(torch.int64), packed.view(torch.int64))
+
+
 # The largest window integer any entry can have: RN(hi + lo) < 2^E forces
 # |x| < 2^E (1 - 2^-54), so N <= 2^104 - 2^50 - 1, digits 8191 except 6143 in slice 4.
 MAX_HI, MAX_LO = 1.0 - 2.0 ** -53, 2.0 ** -54 - 2.0 ** -104

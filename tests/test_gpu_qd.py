@@ -110,6 +110,27 @@ def test_qd_split_bit_exact(gpu, rows, cols, axis):
     assert _bits_equal(_unpack(packed, outer, k), _oracle_slice_values(D))
 
 
+def test_qd_split_large_B_two_pass_bit_exact(gpu):
+    """A quad-double B above the one-pass size (32 MiB) takes the two-pass split
+    (column-block exponents, then slices): ragged column blocks, special
+    entries, a column decided by its last row."""
+    rows, cols = 1100, 1100
+    assert rows * cols * 32 > 32 << 20
+    X = workloads.random_qd((rows, cols), 4321, "signed_exp30")
+    X[:, :, 17] *= 2.0 ** 300
+    rng = np.random.default_rng(4321)
+    for e in _SPECIAL:
+        X[:, int(rng.integers(rows)), int(rng.integers(cols))] = e
+    X[:, :, 1050] = 0.0
+    X[:, rows - 1, 1050] = (2.0 ** -700, 2.0 ** -760, 0.0, 0.0)
+    E, packed = gpu.qd_split_balanced(_dev(X), 1)
+    assert np.array_equal(_host(E), qd.balancing_exponents(X, 1))
+    cols_s = [0, 17, 1023, 1024, 1050, cols - 1]
+    E_s, D = qd.slice_cols(X, cols=cols_s)
+    got = _unpack(packed, cols, rows)
+    assert _bits_equal(got[:, cols_s, :], _oracle_slice_values(D.transpose(0, 2, 1)))
+
+
 def test_qd_split_null_components_and_stride(gpu):
     import torch
     X = workloads.random_qd((37, 29), 7, "uniform")
