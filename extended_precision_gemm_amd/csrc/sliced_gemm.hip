@@ -84,8 +84,10 @@ enum Epilogue : int {
     kEpiUnitsQD = 5,   // add them to the int64 planes' values and round that total
 };
 
+// The second launch bound is the minimum number of waves per SIMD (four SIMDs
+// per CU): kWGS workgroups of kWaves waves.
 template <class C, int EPI>
-__global__ void __launch_bounds__(C::kThreads, C::kWGS)
+__global__ void __launch_bounds__(C::kThreads, C::kWGS * C::kWaves / 4)
 sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                    const double* __restrict__ Ap, const double* __restrict__ Bp,
                    double* __restrict__ levels, int64_t* __restrict__ units, int64_t ldl, int64_t plane,
