@@ -348,6 +348,34 @@ def test_metamorphic_relations_bitwise(gpu):
     assert _bits_equal(R[0], C[0]) and _bits_equal(R[1], C[1])
 
 
+def test_level_planes_with_a_wider_stride(gpu):
+    """dd_sliced_gemm / dd_renorm_levels with ldl > n and ldc > n, through the C
+    ABI: the level sums and the cascade match the packed-stride calls, and the
+    padding columns are left untouched."""
+    import torch
+    m, n, k, pad = 70, 45, 33, 7
+    Ah, Al = workloads.random_dd((m, k), 61, "signed_exp20")
+    Bh, Bl = workloads.random_dd((k, n), 62, "uniform")
+    E, As = gpu.split_balanced(_dev(Ah), _dev(Al), 0)
+    F, Bs = gpu.split_balanced(_dev(Bh), _dev(Bl), 1)
+    ref = gpu.sliced_gemm(m, n, k, As, Bs)
+    Rh, Rl = gpu.renorm_levels(ref, E, F)
+    ldl = n + pad
+    wide = torch.full((8, m, ldl), 3.0, dtype=torch.float64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    L = gpu.lib
+    assert L.dd_sliced_gemm(m, n, k, As.data_ptr(), Bs.data_ptr(), wide.data_ptr(), ldl, s) == 0
+    assert _bits_equal(_host(wide[:, :, :n].contiguous()), _host(ref))
+    assert (_host(wide[:, :, n:]) == 3.0).all()
+    Ch = torch.full((m, ldl + 2), 5.0, dtype=torch.float64, device="cuda")
+    Cl = torch.full((m, ldl + 2), 5.0, dtype=torch.float64, device="cuda")
+    assert L.dd_renorm_levels(m, n, wide.data_ptr(), ldl, E.data_ptr(), F.data_ptr(), Ch.data_ptr(),
+                              Cl.data_ptr(), ldl + 2, s) == 0
+    assert _bits_equal(_host(Ch[:, :n].contiguous()), _host(Rh))
+    assert _bits_equal(_host(Cl[:, :n].contiguous()), _host(Rl))
+    assert (_host(Ch[:, n:]) == 5.0).all() and (_host(Cl[:, n:]) == 5.0).all()
+
+
 def test_nondefault_stream(gpu):
     import torch
     Ah, Al = workloads.random_dd((64, 64), 31)
@@ -558,6 +586,32 @@ def test_kblocked_chain_bit_exact(gpu, nslices, m, n, k):
         Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kblock, nslices)
         Ch, Cl = gpu.dd_gemm(dA, dAl, dB, dBl, nslices=nslices, kblock=kblock)
         assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl), kblock
+
+
+def test_kblocked_strided_operands_and_null_lo(gpu):
+    """k-blocks step through strided operands (lda > k, ldb > n) by pointer
+    offsets; the result equals the oracle's blocked chain bit for bit, with and
+    without lo planes, and the output's padding stays untouched."""
+    import torch
+    rng = np.random.default_rng(808)
+    m, n, k, kblock = 50, 41, 97, 30
+    Ah, Al = _edge_matrix(rng, m, k)
+    Bh, Bl = _edge_matrix(rng, k, n)
+    wideA = torch.zeros((2, m, k + 9), dtype=torch.float64, device="cuda")
+    wideB = torch.zeros((2, k, n + 4), dtype=torch.float64, device="cuda")
+    wideA[0, :, 3:3 + k], wideA[1, :, 3:3 + k] = _dev(Ah), _dev(Al)
+    wideB[0, :, 1:1 + n], wideB[1, :, 1:1 + n] = _dev(Bh), _dev(Bl)
+    vA = [wideA[c, :, 3:3 + k] for c in range(2)]
+    vB = [wideB[c, :, 1:1 + n] for c in range(2)]
+    out = torch.full((2, m, n + 6), 9.0, dtype=torch.float64, device="cuda")
+    Ch, Cl = out[0, :, :n], out[1, :, :n]
+    gpu.dd_gemm(vA[0], vA[1], vB[0], vB[1], C_hi=Ch, C_lo=Cl, kblock=kblock)
+    Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kblock, 8)
+    assert _bits_equal(_host(Ch.contiguous()), Rh) and _bits_equal(_host(Cl.contiguous()), Rl)
+    assert (_host(out[:, :, n:]) == 9.0).all()
+    gpu.dd_gemm(vA[0], None, vB[0], None, C_hi=Ch, C_lo=Cl, kblock=kblock)
+    Zh, Zl = exact.sliced_product_kblocks(Ah, np.zeros_like(Al), Bh, np.zeros_like(Bl), kblock, 8)
+    assert _bits_equal(_host(Ch.contiguous()), Zh) and _bits_equal(_host(Cl.contiguous()), Zl)
 
 
 def test_kblocked_workload_within_tolerance(gpu, workload_operands):
