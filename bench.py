@@ -1,9 +1,10 @@
 """Benchmark: effective double-double GFLOP/s (2mnk/t) of C = A·B on one MI355X.
 
 One step is one pass of the whole product over resident inputs, issued through
-the library's stage entry points in exactly the order dd_gemm_ws issues them:
-slice A (row exponents), slice B (column exponents), fused sliced GEMM +
-renormalisation epilogue.  HIP events on the same stream bracket each stage, so
+the library's stage entry points: slice A (row exponents, then slices), slice B
+(column exponents, then slices), fused sliced GEMM + renormalisation epilogue --
+the kernels dd_gemm_ws runs (it issues both exponent passes first, which saves
+about 13 us at 4096^2).  HIP events on the same stream bracket each stage, so
 the dominant kernel's launch duration is measured live inside the timed region.
 
 With a quad-double workload (``--workload qd1024``, ``qd2048``, ``qd4096_exp20``)
@@ -46,7 +47,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dd4096_exp20")
     ap.add_argument("--nslices", type=int, default=8,
-                    help="13-bit slices per entry: 8 = double-double (the metric); 4..7 keep fewer pairs")
+                    help="13-bit slices per entry: 8 = double-double (the metric); 4..7 keep fewer pairs, "
+                         "9..16 a deeper window")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-epilogue", action="store_true", help="skip the stand-alone renormalisation timing")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
