@@ -91,6 +91,46 @@ def test_qd_gemm_ws_replays_in_a_graph(gpu):
         assert np.array_equal(_bits(C), _bits(R)), rep
 
 
+def test_dd_gemm_ws_kb_replays_in_a_graph(gpu):
+    """The k-blocked double-double product: the first block writes C, later
+    blocks go to the workspace's block planes and are added by a kernel, so a
+    replay over a workspace full of garbage still gives the eager result."""
+    import torch
+    m, n, k, kb = 90, 70, 130, 40
+    dAh = torch.empty((m, k), dtype=torch.float64, device="cuda")
+    dAl = torch.empty_like(dAh)
+    dBh = torch.empty((k, n), dtype=torch.float64, device="cuda")
+    dBl = torch.empty_like(dBh)
+    Ch = torch.empty((m, n), dtype=torch.float64, device="cuda")
+    Cl = torch.empty_like(Ch)
+    ws = torch.empty(gpu.workspace_size(m, n, k, kblock=kb), dtype=torch.uint8, device="cuda")
+
+    def load(seed):
+        ah, al = workloads.random_dd((m, k), seed, "signed_exp20")
+        bh, bl = workloads.random_dd((k, n), seed + 1, "normal")
+        for dst, src in ((dAh, ah), (dAl, al), (dBh, bh), (dBl, bl)):
+            dst.copy_(_dev(src))
+
+    load(110)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gpu.dd_gemm(dAh, dAl, dBh, dBl, C_hi=Ch, C_lo=Cl, workspace=ws, kblock=kb)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gpu.dd_gemm(dAh, dAl, dBh, dBl, C_hi=Ch, C_lo=Cl, workspace=ws, kblock=kb)
+    for rep, seed in enumerate((110, 120, 120, 130)):
+        load(seed)
+        Ch.fill_(float("nan"))
+        Cl.fill_(float("nan"))
+        ws.fill_(0x5A)
+        graph.replay()
+        Rh, Rl = gpu.dd_gemm(dAh, dAl, dBh, dBl, kblock=kb)  # eager
+        assert np.array_equal(_bits(Ch), _bits(Rh)), rep
+        assert np.array_equal(_bits(Cl), _bits(Rl)), rep
+
+
 def test_qd_gemm_ws_kb_replays_in_a_graph(gpu):
     """The k-blocked product: its int64 level planes are written by the first
     block's kernel (no clearing pass), so replays start from a clean state."""
