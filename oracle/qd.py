@@ -162,14 +162,39 @@ def level_total(S_units: np.ndarray, i: int, j: int) -> int:
     return sum(int(S_units[l, i, j]) << (DIGIT_BITS * (nl - 1 - l)) for l in range(nl))
 
 
+def rn_unbounded(value: Fraction) -> tuple[float, Fraction]:
+    """(c, v): v is the double-precision number nearest to value with the
+    exponent range unbounded above (53 significant bits, ties to even), c is v
+    as a float -- equal to v, or +-inf once |v| reaches 2^1024, as IEEE
+    round-to-nearest overflows."""
+    try:
+        c = rn(value)
+        return c, Fraction(c)
+    except OverflowError:
+        pass
+    a = abs(value)
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # 2^(e-1) < a < 2^(e+1)
+    if a >= Fraction(2) ** e:
+        e += 1                                                   # now 2^(e-1) <= a < 2^e
+    ulp = Fraction(2) ** (e - 53)
+    q = math.floor(a / ulp)
+    rem = a / ulp - q
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    v = q * ulp if value > 0 else -q * ulp
+    return (math.inf if value > 0 else -math.inf), v
+
+
 def greedy_qd(value: Fraction, terms: int = 4) -> list[float]:
-    """c_0 = RN(value), c_1 = RN(value - c_0), ... (exact remainders)."""
+    """c_0 = RN(value), c_1 = RN(value - c_0), ... (exact remainders).  Beyond
+    the double range a word is +-inf and the next one rounds what is left after
+    the word's unbounded value (rn_unbounded)."""
     out = []
     rest = value
     for _ in range(terms):
-        c = rn(rest)
+        c, v = rn_unbounded(rest)
         out.append(c)
-        rest -= Fraction(c)
+        rest -= v
     return out
 
 

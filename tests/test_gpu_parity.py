@@ -348,6 +348,27 @@ def test_metamorphic_relations_bitwise(gpu):
     assert _bits_equal(R[0], C[0]) and _bits_equal(R[1], C[1])
 
 
+def test_results_beyond_the_double_range_overflow_like_ldexp(gpu):
+    """Entries near 2^600 in both operands: products near 2^1200 become
+    infinities of the right sign (the scaling 2^(E_i + F_j) overflows as ldexp
+    does), rows scaled back into range stay finite, all bit for bit as in the
+    oracle's chain."""
+    rng = np.random.default_rng(77)
+    m, n, k = 20, 18, 24
+    Ah = rng.integers(-9, 10, (m, k)).astype(np.float64) * 2.0 ** 600
+    Bh = rng.integers(-9, 10, (k, n)).astype(np.float64) * 2.0 ** 600
+    Ah[:5] *= 2.0 ** -700                       # these rows' products stay finite
+    Al, Bl = np.zeros_like(Ah), np.zeros_like(Bh)
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), None, _dev(Bh), None)
+    _, Rh, Rl = _oracle_chain(Ah, Al, Bh, Bl)
+    hCh, hCl = _host(Ch), _host(Cl)
+    assert _bits_equal(hCh, Rh) and _bits_equal(hCl, Rl)
+    assert np.isinf(hCh[5:]).any() and np.isfinite(hCh[:5]).all()
+    exact_sign = np.sign((Ah[5:] * 2.0 ** -600) @ (Bh * 2.0 ** -600))   # small integers: exact
+    inf_rows = np.isinf(hCh[5:])
+    assert np.array_equal(np.sign(hCh[5:])[inf_rows], exact_sign[inf_rows])
+
+
 def test_level_planes_with_a_wider_stride(gpu):
     """dd_sliced_gemm / dd_renorm_levels with ldl > n and ldc > n, through the C
     ABI: the level sums and the cascade match the packed-stride calls, and the

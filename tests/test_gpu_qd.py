@@ -191,6 +191,26 @@ def test_qd_subnormal_and_zero_outputs_bit_exact(gpu):
     assert (np.abs(got[0]) < 2.0 ** -1022).any()          # subnormal results occur
 
 
+def test_qd_results_beyond_the_double_range_overflow_like_ldexp(gpu):
+    """Quad-double products near 2^1200 round to infinities of the right sign,
+    with finite rows alongside, bit for bit as in the oracle's chain."""
+    rng = np.random.default_rng(78)
+    m, n, k = 12, 10, 16
+    A = np.zeros((4, m, k))
+    B = np.zeros((4, k, n))
+    A[0] = rng.integers(-9, 10, (m, k)) * 2.0 ** 600
+    A[1] = A[0] * 2.0 ** -60 * rng.choice([-1.0, 1.0], (m, k))   # normalised: below half an ulp of A[0]
+    B[0] = rng.integers(-9, 10, (k, n)) * 2.0 ** 600
+    A[:, :4] *= 2.0 ** -700
+    assert all(qd.is_normalized(A[:, i, p]) for i in range(m) for p in range(k))
+    C = _host(gpu.qd_gemm(_dev(A), _dev(B)))
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert _bits_equal(C, C_ref)
+    over = np.isinf(C[0])
+    assert over[4:].any() and np.isfinite(C[:, :4]).all()
+    assert (C[1][over] != 0).any()          # a finite second word after an infinite first
+
+
 def test_qd_identity_returns_truncated_operand(gpu):
     B = workloads.random_qd((48, 37), 601, "signed_exp20")
     A = np.zeros((4, 48, 48))

@@ -162,6 +162,27 @@ def test_greedy_closed_forms_and_properties():
         assert abs(rest) <= Fraction(math.ulp(c[3])) / 2 if c[3] != 0.0 else rest == 0
 
 
+def test_greedy_beyond_the_double_range():
+    """Words past the largest double become infinities of the value's sign; the
+    next word rounds the exact remainder after the word's unbounded value."""
+    inf = math.inf
+    assert qd.greedy_qd(3 * P ** 1100) == [inf, 0.0, 0.0, 0.0]
+    assert qd.greedy_qd(P ** 1100 + P ** 1000) == [inf, 2.0 ** 1000, 0.0, 0.0]
+    assert qd.greedy_qd(-(P ** 1100) - P ** 1000) == [-inf, -(2.0 ** 1000), 0.0, 0.0]
+    # just below 2^1024: rounds up to 2^1024 (overflow), remainder negative
+    x = P ** 1024 - P ** 969
+    assert qd.greedy_qd(x) == [inf, -(2.0 ** 969), 0.0, 0.0]
+    # the largest double itself, and a tie below it that rounds to even (down)
+    top = P ** 1024 - P ** 971
+    assert qd.greedy_qd(top) == [float(top), 0.0, 0.0, 0.0]
+    assert qd.greedy_qd(top + P ** 970)[0] == inf   # halfway above the (odd) largest double: to even, 2^1024
+    assert qd.greedy_qd(top + P ** 900)[:2] == [float(top), 2.0 ** 900]
+    # unbounded rounding agrees with the float path wherever that is defined
+    for v in (Fraction(1, 3), P ** 1023 * 3 / 2, -(P ** -1070) / 3):
+        c, w = qd.rn_unbounded(v)
+        assert c == qd.rn(v) and w == Fraction(c)
+
+
 def test_renorm_levels_total_and_scale():
     S = np.zeros((16, 1, 2), dtype=np.int64)
     S[0, 0, 0] = 3              # 3 * 2^-26
