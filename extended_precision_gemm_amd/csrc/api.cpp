@@ -167,6 +167,8 @@ size_t dd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int nslices, i
                    align_up(dd_split_slices_bytes_ns(n, kb, nslices)) + align_up(static_cast<size_t>(m) * 4) +
                    align_up(static_cast<size_t>(n) * 4);
     if (block_count(k, kblock) > 1) bytes += 2 * align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
+    if (split_k_parts(m, n, kb, nslices) > 1)  // level planes of a product split over k
+        bytes += align_up(static_cast<size_t>(nslices) * static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
     return bytes;
 }
 
@@ -201,6 +203,10 @@ ddgemm_status_t dd_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_
     if (!levels || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
     if (!size_ok(m * ldl, DDGEMM_NUM_LEVELS)) return DDGEMM_ERROR_INVALID_VALUE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
+    const int64_t parts = split_k_parts(m, n, k, kSlices);
+    if (parts > 1)  // too few tiles to fill the chip: k-parts add into the zeroed planes
+        return launched(launch_sliced_gemm_split(m, n, k, kSlices, A_slices, B_slices, levels, ldl, parts,
+                                                 static_cast<hipStream_t>(stream)));
     return launched(launch_sliced_gemm(m, n, k, kSlices, A_slices, B_slices, levels, ldl, nullptr, nullptr,
                                        nullptr, nullptr, 0, false, static_cast<hipStream_t>(stream)));
 }
@@ -276,6 +282,20 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
     w += align_up(static_cast<size_t>(n) * 4);
     double* T_hi = reinterpret_cast<double*>(w);  // block results after the first (blocks > 1)
     double* T_lo = T_hi + (blocks > 1 ? align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8) / 8 : 0);
+    if (blocks > 1) w += 2 * align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
+    double* L = reinterpret_cast<double*>(w);     // level planes [nslices][m][n] of a product split over k
+    const bool split = split_k_parts(m, n, kb, nslices) > 1;
+
+    // One block's product into (hi, lo) planes: fused, or split over k into the
+    // level planes and renormalised after.
+    auto block_gemm = [&](int64_t kc, double* d_hi, double* d_lo, int64_t ldd, hipStream_t st) {
+        const int64_t parts = split ? split_k_parts(m, n, kc, nslices) : 1;
+        if (parts <= 1)
+            return launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, d_hi, d_lo, ldd, true, st);
+        hipError_t err = launch_sliced_gemm_split(m, n, kc, nslices, A_sl, B_sl, L, n, parts, st);
+        if (err == hipSuccess) err = launch_levels_to_dd(m, n, nslices, L, n, E, F, d_hi, d_lo, ldd, st);
+        return err;
+    };
 
     // Block b covers k indices [b kb, min(k, (b+1) kb)): a separate sliced product
     // with its own exponents; blocks after the first are added into C in
@@ -296,9 +316,9 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
         if (e == hipSuccess) e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s, kSplitSlices);
         if (e != hipSuccess) break;
         if (b == 0) {
-            e = launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, C_hi, C_lo, ldc, true, s);
+            e = block_gemm(kc, C_hi, C_lo, ldc, s);
         } else {
-            e = launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, T_hi, T_lo, n, true, s);
+            e = block_gemm(kc, T_hi, T_lo, n, s);
             if (e == hipSuccess) e = launch_dd_accumulate(m, n, C_hi, C_lo, ldc, T_hi, T_lo, n, s);
         }
     }
@@ -348,10 +368,12 @@ size_t qd_split_slices_bytes(int64_t outer, int64_t k) {
 size_t qd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int64_t kblock) {
     if (validate_qd_blocked_dims(m, n, k, kblock) != DDGEMM_SUCCESS) return 0;
     const int64_t kb = k < kblock ? k : kblock;
-    const size_t units = block_count(k, kb) > 1 ? static_cast<size_t>(m) * static_cast<size_t>(n) * 8 : 0;
+    const bool blocked = block_count(k, kb) > 1;
+    // int64 level planes of a blocked product, or double level planes of one split over k
+    const bool planes = blocked || split_k_parts(m, n, k, kQdSlices) > 1;
+    const size_t level_bytes = planes ? static_cast<size_t>(m) * static_cast<size_t>(n) * 8 * QDGEMM_NUM_LEVELS : 0;
     return align_up(qd_split_slices_bytes(m, kb)) + align_up(qd_split_slices_bytes(n, kb)) +
-           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4) +
-           align_up(units * QDGEMM_NUM_LEVELS);
+           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4) + align_up(level_bytes);
 }
 
 size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
@@ -421,7 +443,8 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
     w += align_up(static_cast<size_t>(m) * 4);
     int32_t* F = reinterpret_cast<int32_t*>(w);
     w += align_up(static_cast<size_t>(n) * 4);
-    int64_t* units = reinterpret_cast<int64_t*>(w);  // [16][m][n] level sums (blocks > 1)
+    int64_t* units = reinterpret_cast<int64_t*>(w);  // [16][m][n]: int64 level sums of the blocks, or double
+                                                     // level planes of a product split over k
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (blocks == 1) {
@@ -429,7 +452,14 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
         if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitExps);
         if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitSlices);
         if (e == hipSuccess) e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitSlices);
-        if (e == hipSuccess) e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s);
+        const int64_t parts = split_k_parts(m, n, k, kQdSlices);
+        if (e == hipSuccess && parts > 1) {  // too few tiles to fill the chip: split over k
+            double* L = reinterpret_cast<double*>(units);
+            e = launch_sliced_gemm_split(m, n, k, kQdSlices, A_sl, B_sl, L, n, parts, s);
+            if (e == hipSuccess) e = launch_levels_to_qd(m, n, L, n, E, F, out, ldc, s);
+        } else if (e == hipSuccess) {
+            e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s);
+        }
         return launched(e);
     }
     // Exponents of the whole rows of A / columns of B; block b covers k indices

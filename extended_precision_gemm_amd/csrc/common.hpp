@@ -65,6 +65,17 @@ hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl
                          const int32_t* F, double* C_hi, double* C_lo, int64_t ldc,
                          hipStream_t stream);
 hipError_t launch_probe_mfma(double* out, hipStream_t stream);
+// Split over k for outputs too small to fill the chip: the k-parts' level sums
+// are added exactly (atomically, in any order) into zeroed level planes
+// [ns][m][ldl], then turned into the result.  split_k_parts() = 1: no split.
+int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns);
+hipError_t launch_sliced_gemm_split(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
+                                    const double* B_slices, double* levels, int64_t ldl, int64_t parts,
+                                    hipStream_t stream);
+hipError_t launch_levels_to_dd(int64_t m, int64_t n, int ns, const double* levels, int64_t ldl, const int32_t* E,
+                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream);
+hipError_t launch_levels_to_qd(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
+                               const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream);
 hipError_t launch_dd_accumulate(int64_t m, int64_t n, double* C_hi, double* C_lo, int64_t ldc, const double* T_hi,
                                 const double* T_lo, int64_t ldt, hipStream_t stream);
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,

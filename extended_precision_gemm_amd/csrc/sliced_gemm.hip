@@ -24,6 +24,8 @@
 // direct-to-LDS loads and read back by the waves as conflict-free
 // 8-byte-per-lane fragment reads straight into the matrix-instruction operand
 // registers.  NBUF stages are in flight; one workgroup barrier per stage.
+#include <type_traits>
+
 #include "common.hpp"
 #include "eft.hpp"
 #include "qd_levels.hpp"
@@ -82,6 +84,7 @@ enum Epilogue : int {
     kEpiUnitsSet = 3,  // store them in integer units to int64 planes
     kEpiUnitsAdd = 4,  // add them in integer units to the int64 planes
     kEpiUnitsQD = 5,   // add them to the int64 planes' values and round that total
+    kEpiAtomicLevels = 6,  // add them, as doubles, into level planes (one k-part of a split product)
 };
 
 // The second launch bound is the minimum number of waves per SIMD (four SIMDs
@@ -152,10 +155,17 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
 #pragma unroll
         for (int r = 0; r < RPW; ++r) acc[l][r] = double4_t{0.0, 0.0, 0.0, 0.0};
 
-    if (nstages > 0) {
+    // Stages [s0, s1): all of them, or this workgroup's k-part of a split product
+    // (blockIdx.y of gridDim.y parts).
+    int64_t s0 = 0, s1 = nstages;
+    if constexpr (EPI == kEpiAtomicLevels) {
+        s0 = nstages * blockIdx.y / gridDim.y;
+        s1 = nstages * (blockIdx.y + 1) / gridDim.y;
+    }
+    if (s1 > s0) {
 #pragma unroll
-        for (int j = 0; j < NBUF - 1; ++j) issue(j < nstages ? j : nstages - 1, j);
-        for (int64_t st = 0; st < nstages; ++st) {
+        for (int j = 0; j < NBUF - 1; ++j) issue(s0 + j < s1 ? s0 + j : s1 - 1, j);
+        for (int64_t st = s0; st < s1; ++st) {
             // Stage st has landed once at most NBUF-2 younger stages are pending.
             wait_vmcnt<(NBUF - 2) * C::kPiecesPerWave>();
             compiler_fence();
@@ -166,12 +176,12 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
             // after the first fragment reads of this stage rather than before
             // them, so the matrix instructions start sooner (measured: +2-3 %).
             const int64_t nxt = st + NBUF - 1;
-            const int64_t nxt_c = nxt < nstages ? nxt : nstages - 1;
+            const int64_t nxt_c = nxt < s1 ? nxt : s1 - 1;
 
-            const double* stage = lds + (st % NBUF) * C::kStageDoubles + lane;
+            const double* stage = lds + ((st - s0) % NBUF) * C::kStageDoubles + lane;
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
-                if (KS > 1 && j == KS / 2) issue(nxt_c, static_cast<int>(nxt % NBUF));
+                if (KS > 1 && j == KS / 2) issue(nxt_c, static_cast<int>((nxt - s0) % NBUF));
                 const double* sa = stage + (RPW * wr) * C::kBlockStage + j * C::kSetDoubles;
                 const double* sb = stage + (C::kTBM + wc) * C::kBlockStage + j * C::kSetDoubles;
                 double a[NS][RPW], b[NS];
@@ -181,7 +191,7 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                     for (int r = 0; r < RPW; ++r) a[s][r] = sa[r * C::kBlockStage + s * kFragDoubles];
                     b[s] = sb[s * kFragDoubles];
                 }
-                if (KS == 1) issue(nxt_c, static_cast<int>(nxt % NBUF));
+                if (KS == 1) issue(nxt_c, static_cast<int>((nxt - s0) % NBUF));
                 // Triangular schedule: pair (s, t) feeds level s + t < NS.
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
@@ -209,6 +219,12 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                 if constexpr (EPI == kEpiLevels) {
 #pragma unroll
                     for (int l = 0; l < NS; ++l) levels[l * plane + row * ldl + col] = S[l];
+                } else if constexpr (EPI == kEpiAtomicLevels) {
+                    // Every part's level sum is a multiple of 2^(-13(l+2)) and their
+                    // total stays below 2^53 such units (the exact-sum bound on the
+                    // whole k), so the additions are exact in any order.
+#pragma unroll
+                    for (int l = 0; l < NS; ++l) atomicAdd(levels + l * plane + row * ldl + col, S[l]);
                 } else if constexpr (EPI == kEpiDD || EPI == kEpiQD) {
                     const int sc = E[row] + F[col];
                     const int64_t idx = row * ldc + col;
@@ -247,7 +263,8 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
     }
 }
 
-// One thread per output entry: cascade its 8 level sums into (hi, lo).
+// One thread per output entry: cascade its NS level sums into (hi, lo).
+template <int NS>
 __global__ void __launch_bounds__(256) renorm_kernel(int64_t m, int64_t n, const double* __restrict__ levels,
                                                      int64_t ldl, int64_t plane, const int32_t* __restrict__ E,
                                                      const int32_t* __restrict__ F, double* __restrict__ C_hi,
@@ -256,13 +273,48 @@ __global__ void __launch_bounds__(256) renorm_kernel(int64_t m, int64_t n, const
     if (col >= n) return;
     const int f = F[col];
     for (int64_t row = blockIdx.y; row < m; row += gridDim.y) {
-        double S[kLevels];
+        double S[NS];
 #pragma unroll
-        for (int l = 0; l < kLevels; ++l) S[l] = levels[l * plane + row * ldl + col];
+        for (int l = 0; l < NS; ++l) S[l] = levels[l * plane + row * ldl + col];
         double hi, lo;
-        renorm_levels<kLevels>(S, E[row] + f, hi, lo);
+        renorm_levels<NS>(S, E[row] + f, hi, lo);
         C_hi[row * ldc + col] = hi;
         C_lo[row * ldc + col] = lo;
+    }
+}
+
+// One thread per output entry: the exact total of its 16 level sums, rounded to
+// the nearest four doubles.
+__global__ void __launch_bounds__(256) qd_levels_kernel(int64_t m, int64_t n, const double* __restrict__ levels,
+                                                        int64_t ldl, int64_t plane, const int32_t* __restrict__ E,
+                                                        const int32_t* __restrict__ F, OutPlanes out, int64_t ldc) {
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (col >= n) return;
+    const int f = F[col];
+    for (int64_t row = blockIdx.y; row < m; row += gridDim.y) {
+        double S[kQdSlices];
+#pragma unroll
+        for (int l = 0; l < kQdSlices; ++l) S[l] = levels[l * plane + row * ldl + col];
+        double c[4];
+        qd_from_levels<kQdSlices>(S, E[row] + f, c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out.c[q][row * ldc + col] = c[q];
+    }
+}
+
+inline unsigned grid_for_levels(int64_t count) {
+    int64_t g = (count + 255) / 256;
+    return static_cast<unsigned>(g < 1 ? 1 : (g > 65536 ? 65536 : g));
+}
+
+// Zero the NS level planes of an m x n product (row stride ldl) with vector stores.
+__global__ void __launch_bounds__(256) zero_levels_kernel(int64_t m, int64_t n, int ns, double* __restrict__ levels,
+                                                          int64_t ldl, int64_t plane) {
+    const int64_t total = ns * m * n;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t l = i / (m * n), r = (i / n) % m, c = i % n;
+        levels[l * plane + r * ldl + c] = 0.0;
     }
 }
 
@@ -323,6 +375,36 @@ hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slice
             OutPlanes{{nullptr, nullptr, nullptr, nullptr}}, 0);
     else
         return hipErrorInvalidValue;  // level planes are offered for the double-double product only
+    return hipGetLastError();
+}
+
+// k-parts for an output whose tiles cannot fill the chip: enough parts for
+// about 256 workgroups, each with at least 16 stages.  1 = no split.
+template <int NS>
+int64_t split_parts_ns(int64_t m, int64_t n, int64_t k) {
+    using Cfg = typename ConfigFor<NS>::type;
+    const int64_t tiles = (m + Cfg::kTBM * 16 - 1) / (Cfg::kTBM * 16) * ((n + Cfg::kTBN * 16 - 1) / (Cfg::kTBN * 16));
+    if (tiles <= 0 || tiles >= 128) return 1;
+    const int64_t nstages = PackGeom(m, k).KB / Cfg::kKS;
+    int64_t parts = (256 + tiles - 1) / tiles;
+    if (parts > nstages / 16) parts = nstages / 16;
+    if (parts > 65535) parts = 65535;
+    return parts < 2 ? 1 : parts;
+}
+
+template <int NS>
+hipError_t launch_split_ns(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
+                           double* levels, int64_t ldl, int64_t parts, hipStream_t stream) {
+    using Cfg = typename ConfigFor<NS>::type;
+    const PackGeom ga(m, k);
+    const int64_t tiles_n = (n + Cfg::kTBN * 16 - 1) / (Cfg::kTBN * 16);
+    const int64_t tiles = (m + Cfg::kTBM * 16 - 1) / (Cfg::kTBM * 16) * tiles_n;
+    if (tiles > 0x7FFFFFFF || parts < 1 || parts > 65535) return hipErrorInvalidValue;
+    const int64_t plane = m * ldl;
+    zero_levels_kernel<<<grid_for_levels(NS * m * n), 256, 0, stream>>>(m, n, NS, levels, ldl, plane);
+    const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(parts));
+    sliced_gemm_kernel<Cfg, kEpiAtomicLevels><<<grid, Cfg::kThreads, 0, stream>>>(
+        m, n, ga.KB, tiles_n, A_slices, B_slices, levels, nullptr, ldl, plane, nullptr, nullptr, OutPlanes{}, 0);
     return hipGetLastError();
 }
 
@@ -393,7 +475,64 @@ hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl
     if (m == 0 || n == 0) return hipSuccess;
     const int64_t gy = m < 65535 ? m : 65535;
     dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
-    renorm_kernel<<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C_hi, C_lo, ldc);
+    renorm_kernel<kLevels><<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C_hi, C_lo, ldc);
+    return hipGetLastError();
+}
+
+// Calls fn(std::integral_constant<int, NS>) for a run-time slice count 4..16.
+template <class Fn>
+auto dispatch_ns(int ns, Fn&& fn) -> decltype(fn(std::integral_constant<int, 8>{})) {
+    switch (ns) {
+        case 4: return fn(std::integral_constant<int, 4>{});
+        case 5: return fn(std::integral_constant<int, 5>{});
+        case 6: return fn(std::integral_constant<int, 6>{});
+        case 7: return fn(std::integral_constant<int, 7>{});
+        case 8: return fn(std::integral_constant<int, 8>{});
+        case 9: return fn(std::integral_constant<int, 9>{});
+        case 10: return fn(std::integral_constant<int, 10>{});
+        case 11: return fn(std::integral_constant<int, 11>{});
+        case 12: return fn(std::integral_constant<int, 12>{});
+        case 13: return fn(std::integral_constant<int, 13>{});
+        case 14: return fn(std::integral_constant<int, 14>{});
+        case 15: return fn(std::integral_constant<int, 15>{});
+        case 16: return fn(std::integral_constant<int, 16>{});
+        default: return decltype(fn(std::integral_constant<int, 8>{}))();
+    }
+}
+
+int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns) {
+    const int64_t p = dispatch_ns(ns, [&](auto c) { return split_parts_ns<decltype(c)::value>(m, n, k); });
+    return p < 1 ? 1 : p;
+}
+
+hipError_t launch_sliced_gemm_split(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
+                                    const double* B_slices, double* levels, int64_t ldl, int64_t parts,
+                                    hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    if (ns < kMinSlices || ns > kMaxSlices) return hipErrorInvalidValue;
+    return dispatch_ns(ns, [&](auto c) {
+        return launch_split_ns<decltype(c)::value>(m, n, k, A_slices, B_slices, levels, ldl, parts, stream);
+    });
+}
+
+hipError_t launch_levels_to_dd(int64_t m, int64_t n, int ns, const double* levels, int64_t ldl, const int32_t* E,
+                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    if (ns < kMinSlices || ns > kMaxSlices) return hipErrorInvalidValue;
+    const int64_t gy = m < 65535 ? m : 65535;
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
+    return dispatch_ns(ns, [&](auto c) {
+        renorm_kernel<decltype(c)::value><<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C_hi, C_lo, ldc);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_levels_to_qd(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
+                               const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    const int64_t gy = m < 65535 ? m : 65535;
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
+    qd_levels_kernel<<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C, ldc);
     return hipGetLastError();
 }
 

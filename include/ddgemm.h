@@ -100,7 +100,12 @@ size_t dd_split_slices_bytes(int64_t outer, int64_t k);
 
 /* Workspace bytes dd_gemm_ws needs for an m×k by k×n product (slices of both
  * operands and both exponent vectors, each region 256-byte aligned); 0 for
- * negative sizes. */
+ * negative sizes.  When the output is too small to fill the chip -- fewer than
+ * 128 tiles of 64×64 (32×64 with 6 or 9..16 slices) and room for at least two
+ * k-parts of 16 stages (a stage is 8 values of k, 4 from 14 slices on) -- the
+ * product is split over k: up to ceil(256 / tiles) parts add their exact level
+ * sums into level planes, and the workspace also holds those nslices m×n
+ * planes.  The split result is bit-identical to the unsplit one. */
 size_t dd_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 
 /*
@@ -132,6 +137,9 @@ ddgemm_status_t dd_split_balanced(int64_t rows, int64_t cols,
  *              ldl >= max(1, n):  S_l[i][j] = sum_{s+t=l} sum_p A_s[i][p] * B_t[p][j]
  *              for l = 0..7, computed exactly (every partial sum is an integer
  *              multiple of 2^(-13(l+2)) below 2^53 units).  k = 0 writes zeros.
+ *              Outputs too small to fill the chip are split over k (see
+ *              dd_gemm_workspace_size): the planes are zeroed and the k-parts
+ *              add into them with atomic adds, exact and so order-independent.
  * Errors: DDGEMM_ERROR_INVALID_VALUE for negative sizes, ldl < max(1, n),
  * k > DDGEMM_K_MAX, NULL pointers with a nonzero extent.
  */

@@ -63,17 +63,49 @@ def test_packed_sizes(ddg):
     assert ws == r(ddg.slices_bytes(m, k)) + r(ddg.slices_bytes(n, k)) + r(4 * m) + r(4 * n)
     assert ddg.workspace_size(-1, 2, 3) == 0
     # beyond the exact-sum bound k is cut into the fewest equal blocks: slices
-    # for one block plus two m×n planes for the block results
+    # for one block plus two m×n planes for the block results, and -- one 64x64
+    # tile cannot fill the chip -- eight level planes for a product split over k
     k2 = ddg.K_MAX + 1
     kb = (k2 + 1) // 2
     assert ddg.workspace_size(3, 5, k2) == (r(ddg.slices_bytes(3, kb)) + r(ddg.slices_bytes(5, kb)) + r(12) + r(20)
-                                            + 2 * r(3 * 5 * 8))
+                                            + 2 * r(3 * 5 * 8) + r(8 * 3 * 5 * 8))
     assert ddg.workspace_size(3, 5, 100, kblock=100) == ddg.workspace_size(3, 5, 100)
     assert ddg.workspace_size(3, 5, 100, kblock=30) == (r(ddg.slices_bytes(3, 30)) + r(ddg.slices_bytes(5, 30))
                                                         + r(12) + r(20) + 2 * r(3 * 5 * 8))
     assert ddg.workspace_size(3, 5, 100, kblock=0) == 0
     assert ddg.workspace_size(3, 5, 100, kblock=ddg.K_MAX + 1) == 0
     assert ddg.workspace_size(3, 5, 0, kblock=0) > 0
+
+
+def _split_parts(m, n, k, ns):
+    """The documented split-over-k rule: fewer than 128 output tiles (64x64, or
+    32x64 for 6 and 9..16 slices) and at least two parts of 16+ stages (a stage
+    is 8 values of k, 4 for 14..16 slices), at most ceil(256 / tiles) parts."""
+    tm = 32 if ns == 6 or ns >= 9 else 64
+    tiles = -(-m // tm) * -(-n // 64)
+    ks = 1 if ns >= 14 else 2
+    stages = -(-k // 16) * 16 // 4 // ks
+    parts = min(-(-256 // tiles), stages // 16)
+    return parts if tiles < 128 and parts >= 2 else 1
+
+
+def test_workspace_holds_level_planes_when_the_product_splits_over_k(ddg):
+    L = ddg.lib
+    r = lambda x: (x + 255) // 256 * 256
+    for (m, n, k, ns) in [(64, 64, 512, 8), (64, 64, 511, 8), (64, 64, 256, 8), (3, 5, 100000, 8),
+                          (1000, 1000, 100000, 8), (700, 900, 4096, 8), (256, 256, 65536, 12),
+                          (100, 80, 5000, 16), (64, 64, 1024, 6)]:
+        base = (r(L.dd_split_slices_bytes_ns(m, k, ns)) + r(L.dd_split_slices_bytes_ns(n, k, ns))
+                + r(4 * m) + r(4 * n))
+        split = _split_parts(m, n, k, ns) > 1
+        assert L.dd_gemm_workspace_size_ns(m, n, k, ns) == base + (r(ns * m * n * 8) if split else 0), (m, n, k, ns)
+    # quad double: sixteen level planes for a split product (32x64 tiles, 4 values of k per stage)
+    for (m, n, k) in [(64, 64, 300), (64, 64, 100000), (2048, 2048, 4096)]:
+        base = r(L.qd_split_slices_bytes(m, k)) + r(L.qd_split_slices_bytes(n, k)) + r(4 * m) + r(4 * n)
+        split = _split_parts(m, n, k, 16) > 1
+        assert L.qd_gemm_workspace_size(m, n, k) == base + (r(16 * m * n * 8) if split else 0), (m, n, k)
+    assert _split_parts(64, 64, 512, 8) == 4 and _split_parts(64, 64, 256, 8) == 2
+    assert _split_parts(700, 900, 4096, 8) == 1 and _split_parts(256, 256, 65536, 12) == 8
 
 
 def test_status_strings(ddg):

@@ -1,0 +1,161 @@
+"""Products split over k (GPU tests).
+
+Outputs too small to fill the chip (a few output tiles, long k) are computed in
+k-parts whose exact level sums are added with atomic adds into zeroed level
+planes.  Integer level sums make the additions exact, so the split result must
+equal, bit for bit, the oracle's unsplit chain, the unsplit fused stage call
+(dd_sliced_gemm_renorm, which has no workspace and never splits), and itself
+on every repetition; the path must also replay in a HIP graph.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import exact, qd
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _bits_equal(a, b):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    return a.shape == b.shape and np.array_equal(a.view(np.int64), b.view(np.int64))
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _split_parts(m, n, k, ns):
+    """The split rule stated in ddgemm.h (dd_gemm_workspace_size)."""
+    tm = 32 if ns == 6 or ns >= 9 else 64
+    tiles = -(-m // tm) * -(-n // 64)
+    ks = 1 if ns >= 14 else 2
+    stages = -(-k // 16) * 16 // 4 // ks
+    parts = min(-(-256 // tiles), stages // 16)
+    return parts if tiles < 128 and parts >= 2 else 1
+
+
+@pytest.mark.parametrize("m,n,k,ns", [(64, 64, 512, 8), (40, 70, 3000, 8), (3, 5, 100000, 8),
+                                      (100, 80, 5000, 16), (64, 64, 1024, 6), (33, 130, 4100, 12)])
+def test_split_dd_product_equals_the_unsplit_chain(gpu, m, n, k, ns):
+    assert _split_parts(m, n, k, ns) > 1
+    _say(f"[split-k dd] {m}x{n}x{k} nslices={ns} parts={_split_parts(m, n, k, ns)}")
+    Ah, Al = workloads.random_dd((m, k), 9100 + k, "signed_exp20")
+    Bh, Bl = workloads.random_dd((k, n), 9101 + k, "uniform")
+    dAh, dAl, dBh, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
+    Ch, Cl = gpu.dd_gemm(dAh, dAl, dBh, dBl, nslices=ns)
+    Rh, Rl = exact.sliced_product(Ah, Al, Bh, Bl, ns)
+    assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
+    # the unsplit fused stage call gives the same bits
+    E, As = gpu.split_balanced(dAh, dAl, 0, nslices=ns)
+    F, Bs = gpu.split_balanced(dBh, dBl, 1, nslices=ns)
+    Uh, Ul = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F, nslices=ns)
+    assert _bits_equal(_host(Uh), Rh) and _bits_equal(_host(Ul), Rl)
+    # and the split is deterministic
+    for _ in range(2):
+        Dh, Dl = gpu.dd_gemm(dAh, dAl, dBh, dBl, nslices=ns)
+        assert _bits_equal(_host(Dh), Rh) and _bits_equal(_host(Dl), Rl)
+
+
+def test_split_level_planes_of_the_stage_call(gpu):
+    """dd_sliced_gemm splits into the caller's level planes (zeroed first, so
+    stale contents do not leak), with a row stride wider than n."""
+    import torch
+    m, n, k = 50, 60, 2500
+    assert _split_parts(m, n, k, 8) > 1
+    Ah, Al = workloads.random_dd((m, k), 9201, "normal")
+    Bh, Bl = workloads.random_dd((k, n), 9202, "signed_exp20")
+    E, As = gpu.split_balanced(_dev(Ah), _dev(Al), 0)
+    F, Bs = gpu.split_balanced(_dev(Bh), _dev(Bl), 1)
+    ldl = n + 3
+    levels = torch.full((8, m, ldl), 7.0, dtype=torch.float64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert gpu.lib.dd_sliced_gemm(m, n, k, As.data_ptr(), Bs.data_ptr(), levels.data_ptr(), ldl, s) == 0
+    _, DA = exact.slice_rows(Ah, Al)
+    _, DB = exact.slice_cols(Bh, Bl)
+    S_ref = exact.level_values(exact.level_sums_units(DA, DB))
+    assert _bits_equal(_host(levels[:, :, :n].contiguous()), S_ref)
+    assert (_host(levels[:, :, n:]) == 7.0).all()
+
+
+@pytest.mark.parametrize("m,n,k", [(40, 33, 3000), (70, 64, 1500)])
+def test_split_qd_product_equals_the_unsplit_chain(gpu, m, n, k):
+    assert _split_parts(m, n, k, 16) > 1
+    _say(f"[split-k qd] {m}x{n}x{k} parts={_split_parts(m, n, k, 16)}")
+    A = workloads.random_qd((m, k), 9300 + k, "signed_exp20")
+    B = workloads.random_qd((k, n), 9301 + k, "uniform")
+    dA, dB = _dev(A), _dev(B)
+    C = _host(gpu.qd_gemm(dA, dB))
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert _bits_equal(C, C_ref)
+    E, As = gpu.qd_split_balanced(dA, 0)
+    F, Bs = gpu.qd_split_balanced(dB, 1)
+    assert _bits_equal(_host(gpu.qd_sliced_gemm_renorm(m, n, k, As, E, Bs, F)), C_ref)
+    assert _bits_equal(_host(gpu.qd_gemm(dA, dB)), C_ref)
+
+
+def test_split_products_replay_in_a_graph(gpu):
+    """The split path zeroes its level planes with a kernel (no memset), so a
+    captured product replays correctly over a workspace full of garbage."""
+    import torch
+    m, n, k = 64, 64, 2048
+    assert _split_parts(m, n, k, 8) > 1 and _split_parts(m, n, k, 16) > 1
+    dAh = torch.empty((m, k), dtype=torch.float64, device="cuda")
+    dAl = torch.empty_like(dAh)
+    dBh = torch.empty((k, n), dtype=torch.float64, device="cuda")
+    dBl = torch.empty_like(dBh)
+    qA = torch.empty((4, m, k), dtype=torch.float64, device="cuda")
+    qB = torch.empty((4, k, n), dtype=torch.float64, device="cuda")
+    Ch = torch.empty((m, n), dtype=torch.float64, device="cuda")
+    Cl = torch.empty_like(Ch)
+    Cq = torch.empty((4, m, n), dtype=torch.float64, device="cuda")
+    ws = torch.empty(gpu.workspace_size(m, n, k), dtype=torch.uint8, device="cuda")
+    wq = torch.empty(gpu.qd_workspace_size(m, n, k), dtype=torch.uint8, device="cuda")
+
+    def load(seed):
+        ah, al = workloads.random_dd((m, k), seed, "signed_exp20")
+        bh, bl = workloads.random_dd((k, n), seed + 1, "normal")
+        for dst, src in ((dAh, ah), (dAl, al), (dBh, bh), (dBl, bl)):
+            dst.copy_(_dev(src))
+        qA.copy_(_dev(workloads.random_qd((m, k), seed + 2, "uniform")))
+        qB.copy_(_dev(workloads.random_qd((k, n), seed + 3, "signed_exp20")))
+
+    def product():
+        gpu.dd_gemm(dAh, dAl, dBh, dBl, C_hi=Ch, C_lo=Cl, workspace=ws)
+        gpu.qd_gemm(qA, qB, C=Cq, workspace=wq)
+
+    load(500)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        product()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        product()
+    for rep, seed in enumerate((500, 510, 510, 520)):
+        load(seed)
+        for t in (Ch, Cl, Cq):
+            t.fill_(float("nan"))
+        ws.fill_(0x3C)
+        wq.fill_(0x3C)
+        graph.replay()
+        Rh, Rl = gpu.dd_gemm(dAh, dAl, dBh, dBl)
+        Rq = gpu.qd_gemm(qA, qB)
+        assert _bits_equal(_host(Ch), _host(Rh)) and _bits_equal(_host(Cl), _host(Rl)), rep
+        assert _bits_equal(_host(Cq), _host(Rq)), rep
