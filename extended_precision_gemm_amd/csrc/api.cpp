@@ -369,11 +369,12 @@ size_t qd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int64_t kblock
     if (validate_qd_blocked_dims(m, n, k, kblock) != DDGEMM_SUCCESS) return 0;
     const int64_t kb = k < kblock ? k : kblock;
     const bool blocked = block_count(k, kb) > 1;
-    // int64 level planes of a blocked product, or double level planes of one split over k
-    const bool planes = blocked || split_k_parts(m, n, k, kQdSlices) > 1;
-    const size_t level_bytes = planes ? static_cast<size_t>(m) * static_cast<size_t>(n) * 8 * QDGEMM_NUM_LEVELS : 0;
+    const bool split = split_k_parts(m, n, kb, kQdSlices) > 1;
+    const size_t planes = static_cast<size_t>(m) * static_cast<size_t>(n) * 8 * QDGEMM_NUM_LEVELS;
+    // int64 level planes of a blocked product; double level planes of a (block) product split over k
     return align_up(qd_split_slices_bytes(m, kb)) + align_up(qd_split_slices_bytes(n, kb)) +
-           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4) + align_up(level_bytes);
+           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4) +
+           (blocked ? align_up(planes) : 0) + (split ? align_up(planes) : 0);
 }
 
 size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
@@ -434,6 +435,7 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
 
     const int64_t kb = k < kblock ? k : kblock;
     const int64_t blocks = block_count(k, kb);
+    const bool split = split_k_parts(m, n, kb, kQdSlices) > 1;
     char* w = static_cast<char*>(workspace);
     double* A_sl = reinterpret_cast<double*>(w);
     w += align_up(qd_split_slices_bytes(m, kb));
@@ -443,8 +445,9 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
     w += align_up(static_cast<size_t>(m) * 4);
     int32_t* F = reinterpret_cast<int32_t*>(w);
     w += align_up(static_cast<size_t>(n) * 4);
-    int64_t* units = reinterpret_cast<int64_t*>(w);  // [16][m][n]: int64 level sums of the blocks, or double
-                                                     // level planes of a product split over k
+    int64_t* units = reinterpret_cast<int64_t*>(w);  // [16][m][n] int64 level sums of the blocks (blocks > 1)
+    if (blocks > 1) w += align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8 * QDGEMM_NUM_LEVELS);
+    double* L = reinterpret_cast<double*>(w);        // [16][m][n] double level planes of a split product
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (blocks == 1) {
@@ -454,7 +457,6 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
         if (e == hipSuccess) e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitSlices);
         const int64_t parts = split_k_parts(m, n, k, kQdSlices);
         if (e == hipSuccess && parts > 1) {  // too few tiles to fill the chip: split over k
-            double* L = reinterpret_cast<double*>(units);
             e = launch_sliced_gemm_split(m, n, k, kQdSlices, A_sl, B_sl, L, n, parts, s);
             if (e == hipSuccess) e = launch_levels_to_qd(m, n, L, n, E, F, out, ldc, s);
         } else if (e == hipSuccess) {
@@ -474,7 +476,13 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
         if (e == hipSuccess) e = launch_qd_slices(kc, n, offset_planes(pb, p0 * ldb), ldb, 1, F, B_sl, s);
         if (e != hipSuccess) break;
         const QdBlockStep step = b == 0 ? kQdFirstBlock : (b + 1 == blocks ? kQdLastBlock : kQdMiddleBlock);
-        e = launch_qd_gemm_block(m, n, kc, A_sl, B_sl, units, step, E, F, out, ldc, s);
+        const int64_t parts = split ? split_k_parts(m, n, kc, kQdSlices) : 1;
+        if (parts > 1) {  // this block split over k, then its exact level sums into the int64 planes
+            e = launch_sliced_gemm_split(m, n, kc, kQdSlices, A_sl, B_sl, L, n, parts, s);
+            if (e == hipSuccess) e = launch_qd_levels_to_units(m, n, L, units, step, E, F, out, ldc, s);
+        } else {
+            e = launch_qd_gemm_block(m, n, kc, A_sl, B_sl, units, step, E, F, out, ldc, s);
+        }
     }
     return launched(e);
 }

@@ -69,6 +69,7 @@ hipError_t launch_probe_mfma(double* out, hipStream_t stream);
 // are added exactly (atomically, in any order) into zeroed level planes
 // [ns][m][ldl], then turned into the result.  split_k_parts() = 1: no split.
 int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns);
+hipError_t launch_zero_levels(int64_t m, int64_t n, int ns, double* levels, int64_t ldl, hipStream_t stream);
 hipError_t launch_sliced_gemm_split(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                                     const double* B_slices, double* levels, int64_t ldl, int64_t parts,
                                     hipStream_t stream);
@@ -92,6 +93,11 @@ enum QdBlockStep { kQdFirstBlock = 0, kQdMiddleBlock = 1, kQdLastBlock = 2 };
 hipError_t launch_qd_gemm_block(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
                                 int64_t* units, QdBlockStep step, const int32_t* E, const int32_t* F,
                                 const OutPlanes& C, int64_t ldc, hipStream_t stream);
+// The same step for a k-block that was split over k: its double level planes
+// [16][m][n] (launch_sliced_gemm_split) into the int64 level planes.
+hipError_t launch_qd_levels_to_units(int64_t m, int64_t n, const double* levels, int64_t* units, QdBlockStep step,
+                                     const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
+                                     hipStream_t stream);
 hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
                           const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
                           hipStream_t stream);

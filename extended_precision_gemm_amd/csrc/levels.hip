@@ -1,0 +1,153 @@
+// Level planes -> results, and the helpers of a product split over k: the
+// double-double cascade of NS level sums ("Multiple Double Arithmetic on NVIDIA
+// Tensor Cores", §2 fifth step; Problem 1.1), the exact four-double rounding of
+// sixteen, zeroing the planes a split product adds into, and moving a split
+// k-block's level sums into the int64 planes of a blocked quad-double product.
+#include "common.hpp"
+#include "dispatch_ns.hpp"
+#include "eft.hpp"
+#include "qd_levels.hpp"
+
+namespace ddg {
+namespace {
+
+// One thread per output entry: cascade its NS level sums into (hi, lo).
+template <int NS>
+__global__ void __launch_bounds__(256) renorm_kernel(int64_t m, int64_t n, const double* __restrict__ levels,
+                                                     int64_t ldl, int64_t plane, const int32_t* __restrict__ E,
+                                                     const int32_t* __restrict__ F, double* __restrict__ C_hi,
+                                                     double* __restrict__ C_lo, int64_t ldc) {
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (col >= n) return;
+    const int f = F[col];
+    for (int64_t row = blockIdx.y; row < m; row += gridDim.y) {
+        double S[NS];
+#pragma unroll
+        for (int l = 0; l < NS; ++l) S[l] = levels[l * plane + row * ldl + col];
+        double hi, lo;
+        renorm_levels<NS>(S, E[row] + f, hi, lo);
+        C_hi[row * ldc + col] = hi;
+        C_lo[row * ldc + col] = lo;
+    }
+}
+
+// One thread per output entry: the exact total of its 16 level sums, rounded to
+// the nearest four doubles.
+__global__ void __launch_bounds__(256) qd_levels_kernel(int64_t m, int64_t n, const double* __restrict__ levels,
+                                                        int64_t ldl, int64_t plane, const int32_t* __restrict__ E,
+                                                        const int32_t* __restrict__ F, OutPlanes out, int64_t ldc) {
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (col >= n) return;
+    const int f = F[col];
+    for (int64_t row = blockIdx.y; row < m; row += gridDim.y) {
+        double S[kQdSlices];
+#pragma unroll
+        for (int l = 0; l < kQdSlices; ++l) S[l] = levels[l * plane + row * ldl + col];
+        double c[4];
+        qd_from_levels<kQdSlices>(S, E[row] + f, c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out.c[q][row * ldc + col] = c[q];
+    }
+}
+
+// One k-block of a blocked quad-double product that was split over k: its 16
+// double level planes (exact integers in units 2^(-13(l+2))) go into the int64
+// level planes as kEpiUnitsSet / kEpiUnitsAdd / kEpiUnitsQD would put them.
+template <int STEP>  // 0: store, 1: add, 2: add and round the total to four doubles
+__global__ void __launch_bounds__(256) qd_units_from_levels_kernel(int64_t m, int64_t n,
+                                                                   const double* __restrict__ levels,
+                                                                   int64_t* __restrict__ units, int64_t plane,
+                                                                   const int32_t* __restrict__ E,
+                                                                   const int32_t* __restrict__ F, OutPlanes out,
+                                                                   int64_t ldc) {
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (col >= n) return;
+    for (int64_t row = blockIdx.y; row < m; row += gridDim.y) {
+        int64_t N[kQdSlices];
+#pragma unroll
+        for (int l = 0; l < kQdSlices; ++l) {
+            const int64_t i = l * plane + row * n + col;
+            N[l] = static_cast<int64_t>(ldexp(levels[i], kSliceBits * (l + 2)));
+            if (STEP != 0) N[l] += units[i];
+            if (STEP != 2) units[i] = N[l];
+        }
+        if constexpr (STEP == 2) {
+            double c[4];
+            qd_from_level_units<kQdSlices>(N, E[row] + F[col], c);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) out.c[q][row * ldc + col] = c[q];
+        }
+    }
+}
+
+inline unsigned grid_for_levels(int64_t count) {
+    int64_t g = (count + 255) / 256;
+    return static_cast<unsigned>(g < 1 ? 1 : (g > 65536 ? 65536 : g));
+}
+
+// Zero the NS level planes of an m x n product (row stride ldl) with vector stores.
+__global__ void __launch_bounds__(256) zero_levels_kernel(int64_t m, int64_t n, int ns, double* __restrict__ levels,
+                                                          int64_t ldl, int64_t plane) {
+    const int64_t total = ns * m * n;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t l = i / (m * n), r = (i / n) % m, c = i % n;
+        levels[l * plane + r * ldl + c] = 0.0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_zero_levels(int64_t m, int64_t n, int ns, double* levels, int64_t ldl, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    zero_levels_kernel<<<grid_for_levels(ns * m * n), 256, 0, stream>>>(m, n, ns, levels, ldl, m * ldl);
+    return hipGetLastError();
+}
+
+hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
+                         const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    const int64_t gy = m < 65535 ? m : 65535;
+    dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
+    renorm_kernel<kLevels><<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C_hi, C_lo, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_levels_to_dd(int64_t m, int64_t n, int ns, const double* levels, int64_t ldl, const int32_t* E,
+                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    if (ns < kMinSlices || ns > kMaxSlices) return hipErrorInvalidValue;
+    const int64_t gy = m < 65535 ? m : 65535;
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
+    return dispatch_ns(ns, [&](auto c) {
+        renorm_kernel<decltype(c)::value><<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C_hi, C_lo, ldc);
+        return hipGetLastError();
+    });
+}
+
+hipError_t launch_levels_to_qd(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
+                               const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    const int64_t gy = m < 65535 ? m : 65535;
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
+    qd_levels_kernel<<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_qd_levels_to_units(int64_t m, int64_t n, const double* levels, int64_t* units, QdBlockStep step,
+                                     const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
+                                     hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    const int64_t gy = m < 65535 ? m : 65535;
+    const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
+    const int64_t plane = m * n;
+    if (step == kQdFirstBlock)
+        qd_units_from_levels_kernel<0><<<grid, 256, 0, stream>>>(m, n, levels, units, plane, E, F, C, ldc);
+    else if (step == kQdMiddleBlock)
+        qd_units_from_levels_kernel<1><<<grid, 256, 0, stream>>>(m, n, levels, units, plane, E, F, C, ldc);
+    else
+        qd_units_from_levels_kernel<2><<<grid, 256, 0, stream>>>(m, n, levels, units, plane, E, F, C, ldc);
+    return hipGetLastError();
+}
+
+}  // namespace ddg

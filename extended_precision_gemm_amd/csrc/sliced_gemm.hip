@@ -24,9 +24,8 @@
 // direct-to-LDS loads and read back by the waves as conflict-free
 // 8-byte-per-lane fragment reads straight into the matrix-instruction operand
 // registers.  NBUF stages are in flight; one workgroup barrier per stage.
-#include <type_traits>
-
 #include "common.hpp"
+#include "dispatch_ns.hpp"
 #include "eft.hpp"
 #include "qd_levels.hpp"
 
@@ -263,61 +262,6 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
     }
 }
 
-// One thread per output entry: cascade its NS level sums into (hi, lo).
-template <int NS>
-__global__ void __launch_bounds__(256) renorm_kernel(int64_t m, int64_t n, const double* __restrict__ levels,
-                                                     int64_t ldl, int64_t plane, const int32_t* __restrict__ E,
-                                                     const int32_t* __restrict__ F, double* __restrict__ C_hi,
-                                                     double* __restrict__ C_lo, int64_t ldc) {
-    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (col >= n) return;
-    const int f = F[col];
-    for (int64_t row = blockIdx.y; row < m; row += gridDim.y) {
-        double S[NS];
-#pragma unroll
-        for (int l = 0; l < NS; ++l) S[l] = levels[l * plane + row * ldl + col];
-        double hi, lo;
-        renorm_levels<NS>(S, E[row] + f, hi, lo);
-        C_hi[row * ldc + col] = hi;
-        C_lo[row * ldc + col] = lo;
-    }
-}
-
-// One thread per output entry: the exact total of its 16 level sums, rounded to
-// the nearest four doubles.
-__global__ void __launch_bounds__(256) qd_levels_kernel(int64_t m, int64_t n, const double* __restrict__ levels,
-                                                        int64_t ldl, int64_t plane, const int32_t* __restrict__ E,
-                                                        const int32_t* __restrict__ F, OutPlanes out, int64_t ldc) {
-    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (col >= n) return;
-    const int f = F[col];
-    for (int64_t row = blockIdx.y; row < m; row += gridDim.y) {
-        double S[kQdSlices];
-#pragma unroll
-        for (int l = 0; l < kQdSlices; ++l) S[l] = levels[l * plane + row * ldl + col];
-        double c[4];
-        qd_from_levels<kQdSlices>(S, E[row] + f, c);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) out.c[q][row * ldc + col] = c[q];
-    }
-}
-
-inline unsigned grid_for_levels(int64_t count) {
-    int64_t g = (count + 255) / 256;
-    return static_cast<unsigned>(g < 1 ? 1 : (g > 65536 ? 65536 : g));
-}
-
-// Zero the NS level planes of an m x n product (row stride ldl) with vector stores.
-__global__ void __launch_bounds__(256) zero_levels_kernel(int64_t m, int64_t n, int ns, double* __restrict__ levels,
-                                                          int64_t ldl, int64_t plane) {
-    const int64_t total = ns * m * n;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t l = i / (m * n), r = (i / n) % m, c = i % n;
-        levels[l * plane + r * ldl + c] = 0.0;
-    }
-}
-
 __global__ void __launch_bounds__(64) probe_mfma_kernel(double* __restrict__ out) {
     const int lane = threadIdx.x;
     const double a = static_cast<double>(lane + 1);
@@ -401,7 +345,8 @@ hipError_t launch_split_ns(int64_t m, int64_t n, int64_t k, const double* A_slic
     const int64_t tiles = (m + Cfg::kTBM * 16 - 1) / (Cfg::kTBM * 16) * tiles_n;
     if (tiles > 0x7FFFFFFF || parts < 1 || parts > 65535) return hipErrorInvalidValue;
     const int64_t plane = m * ldl;
-    zero_levels_kernel<<<grid_for_levels(NS * m * n), 256, 0, stream>>>(m, n, NS, levels, ldl, plane);
+    hipError_t err = launch_zero_levels(m, n, NS, levels, ldl, stream);
+    if (err != hipSuccess) return err;
     const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(parts));
     sliced_gemm_kernel<Cfg, kEpiAtomicLevels><<<grid, Cfg::kThreads, 0, stream>>>(
         m, n, ga.KB, tiles_n, A_slices, B_slices, levels, nullptr, ldl, plane, nullptr, nullptr, OutPlanes{}, 0);
@@ -470,36 +415,6 @@ hipError_t launch_qd_gemm_block(int64_t m, int64_t n, int64_t k, const double* A
     return hipGetLastError();
 }
 
-hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
-                         const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream) {
-    if (m == 0 || n == 0) return hipSuccess;
-    const int64_t gy = m < 65535 ? m : 65535;
-    dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
-    renorm_kernel<kLevels><<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C_hi, C_lo, ldc);
-    return hipGetLastError();
-}
-
-// Calls fn(std::integral_constant<int, NS>) for a run-time slice count 4..16.
-template <class Fn>
-auto dispatch_ns(int ns, Fn&& fn) -> decltype(fn(std::integral_constant<int, 8>{})) {
-    switch (ns) {
-        case 4: return fn(std::integral_constant<int, 4>{});
-        case 5: return fn(std::integral_constant<int, 5>{});
-        case 6: return fn(std::integral_constant<int, 6>{});
-        case 7: return fn(std::integral_constant<int, 7>{});
-        case 8: return fn(std::integral_constant<int, 8>{});
-        case 9: return fn(std::integral_constant<int, 9>{});
-        case 10: return fn(std::integral_constant<int, 10>{});
-        case 11: return fn(std::integral_constant<int, 11>{});
-        case 12: return fn(std::integral_constant<int, 12>{});
-        case 13: return fn(std::integral_constant<int, 13>{});
-        case 14: return fn(std::integral_constant<int, 14>{});
-        case 15: return fn(std::integral_constant<int, 15>{});
-        case 16: return fn(std::integral_constant<int, 16>{});
-        default: return decltype(fn(std::integral_constant<int, 8>{}))();
-    }
-}
-
 int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns) {
     const int64_t p = dispatch_ns(ns, [&](auto c) { return split_parts_ns<decltype(c)::value>(m, n, k); });
     return p < 1 ? 1 : p;
@@ -513,27 +428,6 @@ hipError_t launch_sliced_gemm_split(int64_t m, int64_t n, int64_t k, int ns, con
     return dispatch_ns(ns, [&](auto c) {
         return launch_split_ns<decltype(c)::value>(m, n, k, A_slices, B_slices, levels, ldl, parts, stream);
     });
-}
-
-hipError_t launch_levels_to_dd(int64_t m, int64_t n, int ns, const double* levels, int64_t ldl, const int32_t* E,
-                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream) {
-    if (m == 0 || n == 0) return hipSuccess;
-    if (ns < kMinSlices || ns > kMaxSlices) return hipErrorInvalidValue;
-    const int64_t gy = m < 65535 ? m : 65535;
-    const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
-    return dispatch_ns(ns, [&](auto c) {
-        renorm_kernel<decltype(c)::value><<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C_hi, C_lo, ldc);
-        return hipGetLastError();
-    });
-}
-
-hipError_t launch_levels_to_qd(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
-                               const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream) {
-    if (m == 0 || n == 0) return hipSuccess;
-    const int64_t gy = m < 65535 ? m : 65535;
-    const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
-    qd_levels_kernel<<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C, ldc);
-    return hipGetLastError();
 }
 
 hipError_t launch_probe_mfma(double* out, hipStream_t stream) {

@@ -104,6 +104,11 @@ def test_workspace_holds_level_planes_when_the_product_splits_over_k(ddg):
         base = r(L.qd_split_slices_bytes(m, k)) + r(L.qd_split_slices_bytes(n, k)) + r(4 * m) + r(4 * n)
         split = _split_parts(m, n, k, 16) > 1
         assert L.qd_gemm_workspace_size(m, n, k) == base + (r(16 * m * n * 8) if split else 0), (m, n, k)
+    # a blocked quad-double product whose blocks split: int64 planes and double planes
+    m, n, k, kb = 40, 33, 3000, 1000
+    assert _split_parts(m, n, kb, 16) > 1
+    base = r(L.qd_split_slices_bytes(m, kb)) + r(L.qd_split_slices_bytes(n, kb)) + r(4 * m) + r(4 * n)
+    assert L.qd_gemm_workspace_size_kb(m, n, k, kb) == base + 2 * r(16 * m * n * 8)
     assert _split_parts(64, 64, 512, 8) == 4 and _split_parts(64, 64, 256, 8) == 2
     assert _split_parts(700, 900, 4096, 8) == 1 and _split_parts(256, 256, 65536, 12) == 8
 

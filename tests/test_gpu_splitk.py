@@ -109,6 +109,20 @@ def test_split_qd_product_equals_the_unsplit_chain(gpu, m, n, k):
     assert _bits_equal(_host(gpu.qd_gemm(dA, dB)), C_ref)
 
 
+@pytest.mark.parametrize("m,n,k,kblock", [(40, 33, 3000, 1000), (20, 20, 2500, 700), (50, 40, 1030, 1000)])
+def test_blocked_qd_product_with_split_blocks_equals_the_unblocked_chain(gpu, m, n, k, kblock):
+    """k-blocks of a quad-double product that are themselves split over k: each
+    block's double level planes go into the int64 level planes; the short last
+    block of the third case is too small to split and takes the unsplit path."""
+    _say(f"[split-k qd blocks] {m}x{n}x{k} kblock={kblock}")
+    A = workloads.random_qd((m, k), 9400 + k, "signed_exp20")
+    B = workloads.random_qd((k, n), 9401 + k, "uniform")
+    A[:, :, k // 2:] *= 2.0 ** -40            # blocks whose own exponents would differ
+    C = _host(gpu.qd_gemm(_dev(A), _dev(B), kblock=kblock))
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert _bits_equal(C, C_ref)
+
+
 def test_split_products_replay_in_a_graph(gpu):
     """The split path zeroes its level planes with a kernel (no memset), so a
     captured product replays correctly over a workspace full of garbage."""
