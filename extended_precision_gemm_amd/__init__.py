@@ -82,6 +82,7 @@ _SIGNATURES = {
     "dd_gemm_workspace_size_kb": (_sz, [_i64, _i64, _i64, ctypes.c_int, _i64]),
     "dd_gemm_ws_kb": (_st, [_i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                             _vp, _sz, _vp]),
+    "ddgemm_split_parts": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "ddgemm_status_string": (ctypes.c_char_p, [_st]),
     "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
 }
@@ -147,6 +148,11 @@ def _check_lo(lo, hi, name):
 def k_max(nslices: int = NUM_SLICES) -> int:
     """Largest k for n slices (§2 eq. (5): at most 67,108,865 exact terms per level sum)."""
     return K_MAX if nslices <= NUM_SLICES else 67108865 // nslices
+
+
+def split_parts(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:
+    """k-parts the product entry points use for an m×n×k product (1 = not split)."""
+    return lib.ddgemm_split_parts(m, n, k, nslices)
 
 
 def slices_bytes(outer: int, k: int, nslices: int = NUM_SLICES) -> int:

@@ -204,7 +204,7 @@ ddgemm_status_t dd_sliced_gemm(int64_t m, int64_t n, int64_t k, const double* A_
     if (!size_ok(m * ldl, DDGEMM_NUM_LEVELS)) return DDGEMM_ERROR_INVALID_VALUE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
     const int64_t parts = split_k_parts(m, n, k, kSlices);
-    if (parts > 1)  // too few tiles to fill the chip: k-parts add into the zeroed planes
+    if (parts > 1)  // tiles leave the chip partly idle: k-parts add into the zeroed planes
         return launched(launch_sliced_gemm_split(m, n, k, kSlices, A_slices, B_slices, levels, ldl, parts,
                                                  static_cast<hipStream_t>(stream)));
     return launched(launch_sliced_gemm(m, n, k, kSlices, A_slices, B_slices, levels, ldl, nullptr, nullptr,
@@ -456,7 +456,7 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
         if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitSlices);
         if (e == hipSuccess) e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitSlices);
         const int64_t parts = split_k_parts(m, n, k, kQdSlices);
-        if (e == hipSuccess && parts > 1) {  // too few tiles to fill the chip: split over k
+        if (e == hipSuccess && parts > 1) {  // tiles leave the chip partly idle: split over k
             e = launch_sliced_gemm_split(m, n, k, kQdSlices, A_sl, B_sl, L, n, parts, s);
             if (e == hipSuccess) e = launch_levels_to_qd(m, n, L, n, E, F, out, ldc, s);
         } else if (e == hipSuccess) {
@@ -525,6 +525,11 @@ const char* ddgemm_status_string(ddgemm_status_t status) {
         case DDGEMM_ERROR_DEVICE: return "DDGEMM_ERROR_DEVICE: no current gfx950 device";
     }
     return "unknown ddgemm status";
+}
+
+int64_t ddgemm_split_parts(int64_t m, int64_t n, int64_t k, int nslices) {
+    if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return 0;
+    return split_k_parts(m, n, k, nslices);
 }
 
 ddgemm_status_t ddgemm_probe_mfma_f64(double* out, void* stream) {

@@ -65,7 +65,17 @@ hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl
                          const int32_t* F, double* C_hi, double* C_lo, int64_t ldc,
                          hipStream_t stream);
 hipError_t launch_probe_mfma(double* out, hipStream_t stream);
-// Split over k for outputs too small to fill the chip: the k-parts' level sums
+// Work geometry of the sliced GEMM for ns slices: one workgroup per output tile
+// of tile_m x tile_n, k-blocks of 4 values of k, ks of them per stage; each wave
+// issues mfma_per_stage 16x16x4 FP64 instructions per stage, waves_per_simd
+// waves of a workgroup share a SIMD, and a workgroup holds lds_bytes of LDS.
+// All zero for ns outside 4..16.
+struct GemmGeometry {
+    int tile_m, tile_n, ks, mfma_per_stage, waves_per_simd, lds_bytes;
+};
+GemmGeometry gemm_geometry(int ns);
+
+// Split over k for outputs whose tiles leave the chip partly idle: the k-parts' level sums
 // are added exactly (atomically, in any order) into zeroed level planes
 // [ns][m][ldl], then turned into the result.  split_k_parts() = 1: no split.
 int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns);

@@ -322,20 +322,6 @@ hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slice
     return hipGetLastError();
 }
 
-// k-parts for an output whose tiles cannot fill the chip: enough parts for
-// about 256 workgroups, each with at least 16 stages.  1 = no split.
-template <int NS>
-int64_t split_parts_ns(int64_t m, int64_t n, int64_t k) {
-    using Cfg = typename ConfigFor<NS>::type;
-    const int64_t tiles = (m + Cfg::kTBM * 16 - 1) / (Cfg::kTBM * 16) * ((n + Cfg::kTBN * 16 - 1) / (Cfg::kTBN * 16));
-    if (tiles <= 0 || tiles >= 128) return 1;
-    const int64_t nstages = PackGeom(m, k).KB / Cfg::kKS;
-    int64_t parts = (256 + tiles - 1) / tiles;
-    if (parts > nstages / 16) parts = nstages / 16;
-    if (parts > 65535) parts = 65535;
-    return parts < 2 ? 1 : parts;
-}
-
 template <int NS>
 hipError_t launch_split_ns(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
                            double* levels, int64_t ldl, int64_t parts, hipStream_t stream) {
@@ -415,9 +401,13 @@ hipError_t launch_qd_gemm_block(int64_t m, int64_t n, int64_t k, const double* A
     return hipGetLastError();
 }
 
-int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns) {
-    const int64_t p = dispatch_ns(ns, [&](auto c) { return split_parts_ns<decltype(c)::value>(m, n, k); });
-    return p < 1 ? 1 : p;
+GemmGeometry gemm_geometry(int ns) {
+    return dispatch_ns(ns, [&](auto c) {
+        using Cfg = typename ConfigFor<decltype(c)::value>::type;
+        constexpr int pairs = decltype(c)::value * (decltype(c)::value + 1) / 2;
+        return GemmGeometry{Cfg::kTBM * 16, Cfg::kTBN * 16, Cfg::kKS, pairs * Cfg::kRPW * Cfg::kKS,
+                            Cfg::kWGS * Cfg::kWaves / 4, Cfg::kWGS * Cfg::kNBuf * Cfg::kStageDoubles * 8};
+    });
 }
 
 hipError_t launch_sliced_gemm_split(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,

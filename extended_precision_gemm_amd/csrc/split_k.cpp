@@ -1,0 +1,73 @@
+// Host-side rule for splitting a sliced product over k.  The integer level sums
+// of the method make the split exact: each part's level sums are multiples of
+// 2^-13(l+2) whose total over the whole k stays below 2^53 units (eq. (5) of
+// "Multiple Double Arithmetic on NVIDIA Tensor Cores", §2), so adding the parts
+// in any order gives the unsplit sums bit for bit.  Only the speed depends on
+// the part count, which this file chooses.
+#include "common.hpp"
+
+namespace ddg {
+
+namespace {
+
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kLdsBytesPerCu = 160 * 1024;
+constexpr double kCoResidentShare = 0.93;     // two workgroups on one CU: 0.93 of twice the time of one
+constexpr int64_t kMinStagesPerPart = 16;
+constexpr int64_t kMaxParts = 256;
+constexpr double kClockHz = 2.38e9;           // sustained MFMA clock under load
+constexpr double kMfmaEfficiency = 0.96;      // measured MFMA busy fraction of the GEMM
+constexpr double kMfmaCycles = 64.0;          // one 16x16x4 FP64 MFMA on one SIMD
+constexpr double kAtomicAddsPerSecond = 2e11; // FP64 atomic adds into the level planes
+constexpr double kPlaneBytesPerSecond = 5e12; // zeroing and re-reading the level planes
+constexpr double kSplitLaunchSeconds = 15e-6; // the zeroing and renormalising launches
+constexpr double kMinSaving = 0.9;            // a split must save at least 10 %
+
+}  // namespace
+
+// The part count p minimising the modelled time
+//     T(p) = c(L) ceil(stages / p) t_stage
+//            + [p > 1] (ns m n p / atomic rate + 2 ns m n 8 B / plane rate + launches),
+// where t_stage is one stage of one workgroup alone on its CU (mfma_per_stage
+// MFMAs of 64 cycles for each of the waves sharing a SIMD: one 8-wave workgroup
+// already keeps the MFMA pipes of its CU busy), L = ceil(tiles p / 256) is the
+// most workgroups any CU runs, and c(L) = L, or 0.93 L when two workgroups fit a
+// CU's LDS (4..6 slices, whose waves also stay within the 128 VGPRs of four
+// waves per SIMD) and L >= 2: two co-resident workgroups hide a little of each
+// other's waiting.  The constants were fitted to timings of split products of 1
+// to 640 output tiles with 4..8 and 16 slices; outputs whose tiles fill whole
+// rounds of 256 never split (T(p) >= T(1) for them).  Each part keeps at least
+// 16 stages; at most 256 parts.  1 = no split.
+int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns) {
+    const GemmGeometry g = gemm_geometry(ns);
+    if (g.tile_m <= 0 || g.tile_n <= 0 || m <= 0 || n <= 0 || k <= 0) return 1;
+    const int64_t tiles = (m + g.tile_m - 1) / g.tile_m * ((n + g.tile_n - 1) / g.tile_n);
+    const int64_t stages = PackGeom(m, k).KB / g.ks;
+    const int64_t pmax = stages / kMinStagesPerPart < kMaxParts ? stages / kMinStagesPerPart : kMaxParts;
+    if (pmax < 2) return 1;
+    const bool two_per_cu = g.lds_bytes > 0 && 2 * static_cast<int64_t>(g.lds_bytes) <= kLdsBytesPerCu;
+    const double t_stage =
+        static_cast<double>(g.mfma_per_stage) * g.waves_per_simd * kMfmaCycles / kClockHz / kMfmaEfficiency;
+    const double outputs = static_cast<double>(m) * static_cast<double>(n);
+    auto cost = [&](int64_t p) {
+        const int64_t L = (tiles * p + kComputeUnits - 1) / kComputeUnits;
+        const double load = two_per_cu && L >= 2 ? kCoResidentShare * static_cast<double>(L) : static_cast<double>(L);
+        const double t = load * static_cast<double>((stages + p - 1) / p) * t_stage;
+        if (p == 1) return t;
+        return t + ns * outputs * static_cast<double>(p) / kAtomicAddsPerSecond +
+               2.0 * ns * outputs * 8.0 / kPlaneBytesPerSecond + kSplitLaunchSeconds;
+    };
+    const double t1 = cost(1);
+    int64_t best = 1;
+    double best_t = t1;
+    for (int64_t p = 2; p <= pmax; ++p) {
+        const double t = cost(p);
+        if (t < best_t) {
+            best_t = t;
+            best = p;
+        }
+    }
+    return best > 1 && best_t < kMinSaving * t1 ? best : 1;
+}
+
+}  // namespace ddg

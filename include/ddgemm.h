@@ -100,12 +100,16 @@ size_t dd_split_slices_bytes(int64_t outer, int64_t k);
 
 /* Workspace bytes dd_gemm_ws needs for an m×k by k×n product (slices of both
  * operands and both exponent vectors, each region 256-byte aligned); 0 for
- * negative sizes.  When the output is too small to fill the chip -- fewer than
- * 128 tiles of 64×64 (32×64 with 6 or 9..16 slices) and room for at least two
- * k-parts of 16 stages (a stage is 8 values of k, 4 from 14 slices on) -- the
- * product is split over k: up to ceil(256 / tiles) parts add their exact level
- * sums into level planes, and the workspace also holds those nslices m×n
- * planes.  The split result is bit-identical to the unsplit one. */
+ * negative sizes.  When the output tiles (64×64; 32×64 with 6 or 9..16 slices)
+ * leave part of the chip idle -- a few tiles, or a last round of 256
+ * workgroups far from full -- the product may be split over k into p parts of
+ * at least 16 stages each (a stage is 8 values of k, 4 from 14 slices on),
+ * p <= 256, chosen by a timing model of the rounds of workgroups, the atomic
+ * adds and the level planes, and only where it saves at least 10 %; outputs
+ * that fill whole rounds never split.  ddgemm_split_parts returns p.  The parts
+ * add their exact level sums into level planes, and the workspace also holds
+ * those nslices m×n planes.  The split result is bit-identical to the unsplit
+ * one. */
 size_t dd_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 
 /*
@@ -137,7 +141,7 @@ ddgemm_status_t dd_split_balanced(int64_t rows, int64_t cols,
  *              ldl >= max(1, n):  S_l[i][j] = sum_{s+t=l} sum_p A_s[i][p] * B_t[p][j]
  *              for l = 0..7, computed exactly (every partial sum is an integer
  *              multiple of 2^(-13(l+2)) below 2^53 units).  k = 0 writes zeros.
- *              Outputs too small to fill the chip are split over k (see
+ *              Outputs that leave the chip partly idle are split over k (see
  *              dd_gemm_workspace_size): the planes are zeroed and the k-parts
  *              add into them with atomic adds, exact and so order-independent.
  * Errors: DDGEMM_ERROR_INVALID_VALUE for negative sizes, ldl < max(1, n),
@@ -249,6 +253,12 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
 
 /* Static, human-readable name of a status code. */
 const char* ddgemm_status_string(ddgemm_status_t status);
+
+/* Diagnostics: the number of k-parts the product entry points (dd_gemm*,
+ * dd_sliced_gemm, and with nslices = 16 the quad-double ones) use for an
+ * m×n×k product with nslices slices; 1 = not split.  0 for invalid sizes or
+ * slice counts.  Host-only, needs no device. */
+int64_t ddgemm_split_parts(int64_t m, int64_t n, int64_t k, int nslices);
 
 /* Diagnostics: runs one FP64 16x16x4 matrix instruction on one wave with
  * a-operand lane value (lane + 1) and b-operand lane value 100 * (lane + 1) and

@@ -77,40 +77,55 @@ def test_packed_sizes(ddg):
     assert ddg.workspace_size(3, 5, 0, kblock=0) > 0
 
 
-def _split_parts(m, n, k, ns):
-    """The documented split-over-k rule: fewer than 128 output tiles (64x64, or
-    32x64 for 6 and 9..16 slices) and at least two parts of 16+ stages (a stage
-    is 8 values of k, 4 for 14..16 slices), at most ceil(256 / tiles) parts."""
-    tm = 32 if ns == 6 or ns >= 9 else 64
-    tiles = -(-m // tm) * -(-n // 64)
-    ks = 1 if ns >= 14 else 2
-    stages = -(-k // 16) * 16 // 4 // ks
-    parts = min(-(-256 // tiles), stages // 16)
-    return parts if tiles < 128 and parts >= 2 else 1
+def test_split_parts_query(ddg):
+    """The k-part count the product entry points use (host-only query): outputs
+    whose 64x64 (32x64 for 6 and 9..16 slices) tiles fill whole rounds of 256
+    workgroups never split; every part keeps at least 16 stages (a stage is 8
+    values of k, 4 for 14..16 slices); at most 256 parts; invalid sizes give 0."""
+    sp = ddg.split_parts
+    for k in (64, 4096, 100000, ddg.K_MAX):
+        assert sp(1024, 1024, k, 8) == 1 and sp(4096, 4096, k, 8) == 1 and sp(2048, 1024, k, 8) == 1
+        assert sp(512, 1024, k, 16) == 1 and sp(256, 2048, k, 12) == 1
+        assert sp(1024, 1024, k, 4) == 1 and sp(2048, 2048, k, 6) == 1 and sp(4096, 1024, k, 5) == 1
+    for (m, n, k, ns) in [(1, 1, 10 ** 6, 8), (3, 5, 100000, 8), (64, 64, 2 ** 20, 16), (100, 80, 5000, 16),
+                          (700, 900, 4096, 8), (1024, 512, 4096, 8), (40, 33, 3000, 16), (520, 1030, 900, 12)]:
+        p = sp(m, n, k, ns)
+        ks = 1 if ns >= 14 else 2
+        stages = -(-k // 16) * 16 // 4 // ks
+        assert 2 <= p <= min(256, stages // 16), (m, n, k, ns, p)
+    assert sp(64, 64, 240, 8) == 1          # 30 stages: fewer than two parts of 16
+    assert sp(64, 64, 241, 8) == 2 and sp(64, 64, 256, 8) == 2
+    assert sp(1024, 512, 4096, 8) == 2      # 128 tiles: one half-empty round becomes one full one
+    assert sp(1, 1, 10 ** 6, 8) == 256
+    assert sp(0, 5, 100, 8) == 1 and sp(5, 5, 0, 8) == 1
+    assert sp(-1, 5, 100, 8) == 0 and sp(5, 5, 100, 3) == 0 and sp(5, 5, 100, 17) == 0
 
 
 def test_workspace_holds_level_planes_when_the_product_splits_over_k(ddg):
     L = ddg.lib
     r = lambda x: (x + 255) // 256 * 256
-    for (m, n, k, ns) in [(64, 64, 512, 8), (64, 64, 511, 8), (64, 64, 256, 8), (3, 5, 100000, 8),
+    for (m, n, k, ns) in [(64, 64, 512, 8), (64, 64, 511, 8), (64, 64, 240, 8), (3, 5, 100000, 8),
                           (1000, 1000, 100000, 8), (700, 900, 4096, 8), (256, 256, 65536, 12),
-                          (100, 80, 5000, 16), (64, 64, 1024, 6)]:
+                          (100, 80, 5000, 16), (64, 64, 1024, 6), (1024, 1024, 4096, 8)]:
         base = (r(L.dd_split_slices_bytes_ns(m, k, ns)) + r(L.dd_split_slices_bytes_ns(n, k, ns))
                 + r(4 * m) + r(4 * n))
-        split = _split_parts(m, n, k, ns) > 1
+        split = ddg.split_parts(m, n, k, ns) > 1
         assert L.dd_gemm_workspace_size_ns(m, n, k, ns) == base + (r(ns * m * n * 8) if split else 0), (m, n, k, ns)
+        if ns == 8:
+            assert L.dd_gemm_workspace_size(m, n, k) == L.dd_gemm_workspace_size_ns(m, n, k, ns)
+    assert ddg.split_parts(64, 64, 512, 8) > 1 and ddg.split_parts(64, 64, 240, 8) == 1
+    assert ddg.split_parts(1024, 1024, 4096, 8) == 1
     # quad double: sixteen level planes for a split product (32x64 tiles, 4 values of k per stage)
-    for (m, n, k) in [(64, 64, 300), (64, 64, 100000), (2048, 2048, 4096)]:
+    for (m, n, k) in [(64, 64, 300), (64, 64, 100000), (2048, 2048, 4096), (50, 40, 30)]:
         base = r(L.qd_split_slices_bytes(m, k)) + r(L.qd_split_slices_bytes(n, k)) + r(4 * m) + r(4 * n)
-        split = _split_parts(m, n, k, 16) > 1
+        split = ddg.split_parts(m, n, k, 16) > 1
         assert L.qd_gemm_workspace_size(m, n, k) == base + (r(16 * m * n * 8) if split else 0), (m, n, k)
+    assert ddg.split_parts(64, 64, 300, 16) > 1 and ddg.split_parts(2048, 2048, 4096, 16) == 1
     # a blocked quad-double product whose blocks split: int64 planes and double planes
     m, n, k, kb = 40, 33, 3000, 1000
-    assert _split_parts(m, n, kb, 16) > 1
+    assert ddg.split_parts(m, n, kb, 16) > 1
     base = r(L.qd_split_slices_bytes(m, kb)) + r(L.qd_split_slices_bytes(n, kb)) + r(4 * m) + r(4 * n)
     assert L.qd_gemm_workspace_size_kb(m, n, k, kb) == base + 2 * r(16 * m * n * 8)
-    assert _split_parts(64, 64, 512, 8) == 4 and _split_parts(64, 64, 256, 8) == 2
-    assert _split_parts(700, 900, 4096, 8) == 1 and _split_parts(256, 256, 65536, 12) == 8
 
 
 def test_status_strings(ddg):

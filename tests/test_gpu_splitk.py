@@ -1,8 +1,8 @@
 """Products split over k (GPU tests).
 
-Outputs too small to fill the chip (a few output tiles, long k) are computed in
-k-parts whose exact level sums are added with atomic adds into zeroed level
-planes.  Integer level sums make the additions exact, so the split result must
+Outputs whose tiles leave the chip partly idle (a few output tiles and a long
+k, or a last round of workgroups far from full) are computed in k-parts whose
+exact level sums are added with atomic adds into zeroed level planes.  Integer level sums make the additions exact, so the split result must
 equal, bit for bit, the oracle's unsplit chain, the unsplit fused stage call
 (dd_sliced_gemm_renorm, which has no workspace and never splits), and itself
 on every repetition; the path must also replay in a HIP graph.
@@ -40,21 +40,11 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _split_parts(m, n, k, ns):
-    """The split rule stated in ddgemm.h (dd_gemm_workspace_size)."""
-    tm = 32 if ns == 6 or ns >= 9 else 64
-    tiles = -(-m // tm) * -(-n // 64)
-    ks = 1 if ns >= 14 else 2
-    stages = -(-k // 16) * 16 // 4 // ks
-    parts = min(-(-256 // tiles), stages // 16)
-    return parts if tiles < 128 and parts >= 2 else 1
-
-
 @pytest.mark.parametrize("m,n,k,ns", [(64, 64, 512, 8), (40, 70, 3000, 8), (3, 5, 100000, 8),
                                       (100, 80, 5000, 16), (64, 64, 1024, 6), (33, 130, 4100, 12)])
 def test_split_dd_product_equals_the_unsplit_chain(gpu, m, n, k, ns):
-    assert _split_parts(m, n, k, ns) > 1
-    _say(f"[split-k dd] {m}x{n}x{k} nslices={ns} parts={_split_parts(m, n, k, ns)}")
+    assert gpu.split_parts(m, n, k, ns) > 1
+    _say(f"[split-k dd] {m}x{n}x{k} nslices={ns} parts={gpu.split_parts(m, n, k, ns)}")
     Ah, Al = workloads.random_dd((m, k), 9100 + k, "signed_exp20")
     Bh, Bl = workloads.random_dd((k, n), 9101 + k, "uniform")
     dAh, dAl, dBh, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
@@ -77,7 +67,7 @@ def test_split_level_planes_of_the_stage_call(gpu):
     stale contents do not leak), with a row stride wider than n."""
     import torch
     m, n, k = 50, 60, 2500
-    assert _split_parts(m, n, k, 8) > 1
+    assert gpu.split_parts(m, n, k, 8) > 1
     Ah, Al = workloads.random_dd((m, k), 9201, "normal")
     Bh, Bl = workloads.random_dd((k, n), 9202, "signed_exp20")
     E, As = gpu.split_balanced(_dev(Ah), _dev(Al), 0)
@@ -95,8 +85,8 @@ def test_split_level_planes_of_the_stage_call(gpu):
 
 @pytest.mark.parametrize("m,n,k", [(40, 33, 3000), (70, 64, 1500)])
 def test_split_qd_product_equals_the_unsplit_chain(gpu, m, n, k):
-    assert _split_parts(m, n, k, 16) > 1
-    _say(f"[split-k qd] {m}x{n}x{k} parts={_split_parts(m, n, k, 16)}")
+    assert gpu.split_parts(m, n, k, 16) > 1
+    _say(f"[split-k qd] {m}x{n}x{k} parts={gpu.split_parts(m, n, k, 16)}")
     A = workloads.random_qd((m, k), 9300 + k, "signed_exp20")
     B = workloads.random_qd((k, n), 9301 + k, "uniform")
     dA, dB = _dev(A), _dev(B)
@@ -128,7 +118,7 @@ def test_split_products_replay_in_a_graph(gpu):
     captured product replays correctly over a workspace full of garbage."""
     import torch
     m, n, k = 64, 64, 2048
-    assert _split_parts(m, n, k, 8) > 1 and _split_parts(m, n, k, 16) > 1
+    assert gpu.split_parts(m, n, k, 8) > 1 and gpu.split_parts(m, n, k, 16) > 1
     dAh = torch.empty((m, k), dtype=torch.float64, device="cuda")
     dAl = torch.empty_like(dAh)
     dBh = torch.empty((k, n), dtype=torch.float64, device="cuda")
@@ -173,3 +163,54 @@ def test_split_products_replay_in_a_graph(gpu):
         Rq = gpu.qd_gemm(qA, qB)
         assert _bits_equal(_host(Ch), _host(Rh)) and _bits_equal(_host(Cl), _host(Rl)), rep
         assert _bits_equal(_host(Cq), _host(Rq)), rep
+
+
+@pytest.mark.parametrize("m,n,k,ns", [(700, 900, 4096, 8), (520, 1030, 900, 12), (1000, 1100, 700, 16),
+                                      (1536, 1024, 2048, 8)])
+def test_split_of_partly_idle_rounds(gpu, m, n, k, ns):
+    """Outputs of 128 tiles and more whose last round of workgroups is partly
+    idle: the split product equals the unsplit fused stage call on every entry
+    and the oracle's chain on sampled rows and columns, bit for bit."""
+    parts = gpu.split_parts(m, n, k, ns)
+    assert parts > 1
+    _say(f"[split-k rounds] {m}x{n}x{k} nslices={ns} parts={parts}")
+    Ah, Al = workloads.random_dd((m, k), 9500 + m, "signed_exp20")
+    Bh, Bl = workloads.random_dd((k, n), 9501 + n, "normal")
+    dAh, dAl, dBh, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
+    Ch, Cl = gpu.dd_gemm(dAh, dAl, dBh, dBl, nslices=ns)
+    E, As = gpu.split_balanced(dAh, dAl, 0, nslices=ns)
+    F, Bs = gpu.split_balanced(dBh, dBl, 1, nslices=ns)
+    Uh, Ul = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F, nslices=ns)
+    hCh, hCl = _host(Ch), _host(Cl)
+    assert _bits_equal(hCh, _host(Uh)) and _bits_equal(hCl, _host(Ul))
+    rng = np.random.default_rng(m * n + k)
+    rows = sorted({0, m - 1, *(int(x) for x in rng.integers(0, m, 5))})
+    cols = sorted({0, n - 1, *(int(x) for x in rng.integers(0, n, 5))})
+    E_ref, DA = exact.slice_rows(Ah, Al, rows, ns)
+    F_ref, DB = exact.slice_cols(Bh, Bl, cols, ns)
+    Rh, Rl = exact.renorm_levels(exact.level_values(exact.level_sums_units(DA, DB)), E_ref, F_ref)
+    assert _bits_equal(hCh[np.ix_(rows, cols)], Rh) and _bits_equal(hCl[np.ix_(rows, cols)], Rl)
+
+
+def test_qd_split_of_partly_idle_rounds(gpu):
+    """A quad-double output of 192 tiles (32x64) split over k: bit-identical to
+    the unsplit fused stage call everywhere and to the oracle on sampled entries."""
+    import torch
+    m, n, k = 768, 512, 2048
+    parts = gpu.split_parts(m, n, k, 16)
+    assert parts > 1
+    _say(f"[split-k rounds qd] {m}x{n}x{k} parts={parts}")
+    A = workloads.random_qd((m, k), 9601, "signed_exp20")
+    B = workloads.random_qd((k, n), 9602, "uniform")
+    dA, dB = _dev(A), _dev(B)
+    C = _host(gpu.qd_gemm(dA, dB))
+    E, As = gpu.qd_split_balanced(dA, 0)
+    F, Bs = gpu.qd_split_balanced(dB, 1)
+    assert _bits_equal(C, _host(gpu.qd_sliced_gemm_renorm(m, n, k, As, E, Bs, F)))
+    del As, Bs
+    torch.cuda.empty_cache()
+    for i, j in [(0, 0), (m - 1, n - 1), (381, 17), (5, 500)]:
+        Ei, DA = qd.slice_rows(A, rows=[i])
+        Fj, DB = qd.slice_cols(B, cols=[j])
+        ref = qd.renorm_levels(qd.level_sums(DA, DB), Ei, Fj)[:, 0, 0]
+        assert _bits_equal(C[:, i, j], ref), (i, j)
