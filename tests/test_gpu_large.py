@@ -7,7 +7,8 @@ copies, epilogue) would read or write the wrong place.  The large operand is a
 seeded block repeated along its long side on the device, which keeps input
 generation cheap; outputs of the last repeat must equal those of the first,
 and sampled outputs there are compared bit for bit with the oracle's chain on
-the same rows and columns of the seeded block.
+the same rows and columns of the seeded block.  A last test takes k to the
+exact-sum bound with the largest digits, where the level sums are largest.
 """
 import sys
 
@@ -117,3 +118,50 @@ def test_qd_tall_A_past_2_31_slice_values(gpu):
     ref = qd.renorm_levels(qd.level_sums(DA, DB), E, F)
     last = [(reps - 1) * base + r for r in rows]
     assert _bits_equal(hC[:, last][:, :, cols], ref)
+
+
+# The largest window integer an entry can have: RN(hi + lo) < 2^E forces
+# |x| < 2^E (1 - 2^-54), so N <= 2^104 - 2^50 - 1 (E = 0 for this entry).
+MAX_HI, MAX_LO = 1.0 - 2.0 ** -53, 2.0 ** -54 - 2.0 ** -104
+
+
+@pytest.mark.timeout(600)
+def test_dd_level_sums_exact_at_the_k_bound(gpu):
+    """k at the exact-sum bound (2^23, "Multiple Double Arithmetic on NVIDIA
+    Tensor Cores", §2 eq. (5)) with the largest digits in every slice of every
+    entry: level 7 reaches k * 503189512 ~ 2^51.9 units, inside the 53 exact
+    bits, and each operand's packed slices hold 2^33 doubles (68.7 GB), so a
+    32-bit offset anywhere would fail.  The level-plane stage call (split over
+    k into atomically added parts) must give the closed-form level sums
+    exactly, and the unsplit fused call (one workgroup) the oracle's cascade of
+    them, bit for bit."""
+    import torch
+    m, n, k = 3, 2, gpu.K_MAX
+    assert gpu.split_parts(m, n, k) > 1
+    assert gpu.slices_bytes(m, k) // 8 == 2 ** 33
+    digits = exact.slice_entry(MAX_HI, MAX_LO, 0)
+    assert digits == [8191, 8191, 8191, 8191, 6143, 8191, 8191, 8191]
+    units = [-k * sum(digits[s] * digits[l - s] for s in range(l + 1)) for l in range(8)]
+    assert max(abs(u) for u in units) < 2 ** 53 and abs(units[7]) > 2 ** 51
+    S_units = np.array([np.full((m, n), u, dtype=np.int64) for u in units])
+    S_ref = exact.level_values(S_units)
+    Rh, Rl = exact.renorm_levels(S_ref, np.zeros(m, np.int64), np.zeros(n, np.int64))
+    _free()
+    _say(f"[large] dd k = {k} at the exact-sum bound, m={m} n={n}, largest digits")
+    A_hi = torch.full((m, k), MAX_HI, dtype=torch.float64, device="cuda")
+    A_lo = torch.full((m, k), MAX_LO, dtype=torch.float64, device="cuda")
+    E, As = gpu.split_balanced(A_hi, A_lo, 0)
+    del A_hi, A_lo
+    B_hi = torch.full((k, n), -MAX_HI, dtype=torch.float64, device="cuda")
+    B_lo = torch.full((k, n), -MAX_LO, dtype=torch.float64, device="cuda")
+    F, Bs = gpu.split_balanced(B_hi, B_lo, 1)
+    del B_hi, B_lo
+    assert _host(E).tolist() == [0] * m and _host(F).tolist() == [0] * n
+    _say("[large] split stage call")
+    levels = _host(gpu.sliced_gemm(m, n, k, As, Bs))
+    assert _bits_equal(levels, S_ref)
+    _say("[large] unsplit fused call")
+    Fh, Fl = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F)
+    assert _bits_equal(_host(Fh), Rh) and _bits_equal(_host(Fl), Rl)
+    del As, Bs
+    _free()
