@@ -165,3 +165,45 @@ def test_dd_level_sums_exact_at_the_k_bound(gpu):
     assert _bits_equal(_host(Fh), Rh) and _bits_equal(_host(Fl), Rl)
     del As, Bs
     _free()
+
+
+# A normalised quad double just below 1 whose every component is the largest the
+# one above it allows: window digits 8191 except 6143, 7679 and 8063 (E = 0).
+QD_MAX = [1.0 - 2.0 ** -53, 2.0 ** -54 - 2.0 ** -107, 2.0 ** -108 - 2.0 ** -161, 2.0 ** -162 - 2.0 ** -215]
+
+
+@pytest.mark.timeout(600)
+def test_qd_level_sums_exact_at_the_k_bound(gpu):
+    """The quad-double product at its exact-sum bound (k = 2^22; sixteen pairs on
+    the deepest levels, "Multiple Double Arithmetic on NVIDIA Tensor Cores", §2
+    eq. (5)) with near-largest digits everywhere: the deeper levels reach 2^52
+    units.  The unsplit fused call (one workgroup) and the product entry point
+    (split over k into atomically added parts) must both give the oracle's
+    exact four-double rounding of the closed-form level sums, bit for bit."""
+    import torch
+    m, n, k = 3, 2, gpu.QD_K_MAX
+    assert gpu.split_parts(m, n, k, 16) > 1
+    assert qd.is_normalized(QD_MAX) and qd.entry_exponent(QD_MAX) == 0
+    digits = qd.slice_entry(QD_MAX, 0)
+    units = [-k * sum(digits[s] * digits[l - s] for s in range(l + 1)) for l in range(16)]
+    assert max(abs(u) for u in units) < 2 ** 53 and abs(units[15]) > 2 ** 51
+    S_units = np.array([np.full((m, n), u, dtype=np.int64) for u in units])
+    ref = qd.renorm_levels(S_units, np.zeros(m, np.int64), np.zeros(n, np.int64))
+    _free()
+    _say(f"[large] qd k = {k} at the exact-sum bound, m={m} n={n}, near-largest digits")
+    A = torch.empty((4, m, k), dtype=torch.float64, device="cuda")
+    B = torch.empty((4, k, n), dtype=torch.float64, device="cuda")
+    for c in range(4):
+        A[c].fill_(QD_MAX[c])
+        B[c].fill_(-QD_MAX[c])
+    E, As = gpu.qd_split_balanced(A, 0)
+    F, Bs = gpu.qd_split_balanced(B, 1)
+    assert _host(E).tolist() == [0] * m and _host(F).tolist() == [0] * n
+    _say("[large] unsplit fused call")
+    assert _bits_equal(_host(gpu.qd_sliced_gemm_renorm(m, n, k, As, E, Bs, F)), ref)
+    del As, Bs
+    _free()
+    _say("[large] product entry point, split over k")
+    assert _bits_equal(_host(gpu.qd_gemm(A, B)), ref)
+    del A, B
+    _free()
