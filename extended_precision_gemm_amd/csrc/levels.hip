@@ -80,19 +80,18 @@ __global__ void __launch_bounds__(256) qd_units_from_levels_kernel(int64_t m, in
     }
 }
 
-inline unsigned grid_for_levels(int64_t count) {
-    int64_t g = (count + 255) / 256;
-    return static_cast<unsigned>(g < 1 ? 1 : (g > 65536 ? 65536 : g));
-}
-
-// Zero the NS level planes of an m x n product (row stride ldl) with vector stores.
+// Zero the NS level planes of an m x n product (row stride ldl) with vector
+// stores: workgroup rows y take the planes' rows (plane l, row r) in turn,
+// threads run along each row.
 __global__ void __launch_bounds__(256) zero_levels_kernel(int64_t m, int64_t n, int ns, double* __restrict__ levels,
                                                           int64_t ldl, int64_t plane) {
-    const int64_t total = ns * m * n;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t l = i / (m * n), r = (i / n) % m, c = i % n;
-        levels[l * plane + r * ldl + c] = 0.0;
+    const int64_t rows = ns * m;
+    for (int64_t lr = blockIdx.y; lr < rows; lr += gridDim.y) {
+        const int64_t l = lr / m, r = lr - l * m;
+        double* row = levels + l * plane + r * ldl;
+        for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < n;
+             c += static_cast<int64_t>(gridDim.x) * blockDim.x)
+            row[c] = 0.0;
     }
 }
 
@@ -100,7 +99,10 @@ __global__ void __launch_bounds__(256) zero_levels_kernel(int64_t m, int64_t n, 
 
 hipError_t launch_zero_levels(int64_t m, int64_t n, int ns, double* levels, int64_t ldl, hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;
-    zero_levels_kernel<<<grid_for_levels(ns * m * n), 256, 0, stream>>>(m, n, ns, levels, ldl, m * ldl);
+    const int64_t gx = (n + 255) / 256 < 64 ? (n + 255) / 256 : 64;
+    const int64_t gy = ns * m < 65535 ? ns * m : 65535;
+    const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+    zero_levels_kernel<<<grid, 256, 0, stream>>>(m, n, ns, levels, ldl, m * ldl);
     return hipGetLastError();
 }
 
