@@ -5,7 +5,9 @@ k-block size (or none), which lo planes are present and the entry
 distributions; the product is compared bit for bit with the oracle's chain for
 the same inputs (oracle.exact.sliced_product / sliced_product_kblocks for
 double doubles, oracle.qd.sliced_product for quad doubles).  The grid tests
-elsewhere cover each parameter on its own; these cover their combinations.
+elsewhere cover each parameter on its own; these cover their combinations,
+with a set of small outputs and long k that take the split-over-k path with
+varying part counts.
 """
 import sys
 
@@ -55,6 +57,22 @@ def _dd_cases(count, seed):
     return out
 
 
+def _dd_split_cases(count, seed):
+    """Small outputs with k long enough to split over k (parts vary with the
+    shape, the slice count and the k-block)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        m, n = (int(x) for x in rng.integers(1, 70, 2))
+        k = int(rng.integers(241, 2000))
+        ns = int(rng.integers(4, 17))
+        kb = None if rng.random() < 0.6 else int(rng.integers(241, k + 10))
+        lo_a, lo_b = bool(rng.random() < 0.8), bool(rng.random() < 0.8)
+        da, db = (DISTS[int(x)] for x in rng.integers(0, len(DISTS), 2))
+        out.append((i, m, n, k, ns, kb, lo_a, lo_b, da, db))
+    return out
+
+
 def _qd_cases(count, seed):
     rng = np.random.default_rng(seed)
     out = []
@@ -64,6 +82,20 @@ def _qd_cases(count, seed):
         planes_a, planes_b = (int(x) for x in rng.integers(1, 5, 2))  # components given
         da, db = (DISTS[int(x)] for x in rng.integers(0, len(DISTS), 2))
         out.append((i, m, n, k, kb, planes_a, planes_b, da, db))
+    return out
+
+
+def _qd_split_cases(count, seed):
+    """Quad-double products small enough in m, n and long enough in k to split."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        m, n = (int(x) for x in rng.integers(1, 60, 2))
+        k = int(rng.integers(241, 1200))
+        kb = None if rng.random() < 0.6 else int(rng.integers(241, k + 10))
+        planes_a, planes_b = (int(x) for x in rng.integers(1, 5, 2))
+        da, db = (DISTS[int(x)] for x in rng.integers(0, len(DISTS), 2))
+        out.append((100 + i, m, n, k, kb, planes_a, planes_b, da, db))
     return out
 
 
@@ -86,7 +118,28 @@ def test_random_dd_case_bit_exact(gpu, case):
     assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
 
 
-@pytest.mark.parametrize("case", _qd_cases(15, 20261203), ids=lambda c: f"qd{c[0]}")
+@pytest.mark.parametrize("case", _dd_split_cases(30, 20261204), ids=lambda c: f"ddsplit{c[0]}")
+def test_random_split_dd_case_bit_exact(gpu, case):
+    i, m, n, k, ns, kb, lo_a, lo_b, da, db = case
+    parts = gpu.split_parts(m, n, k if kb is None else min(k, kb), ns)
+    _say(f"[random split dd {i}] m={m} n={n} k={k} nslices={ns} kblock={kb} parts={parts}")
+    Ah, Al = workloads.random_dd((m, k), 7500 + 2 * i, da)
+    Bh, Bl = workloads.random_dd((k, n), 7501 + 2 * i, db)
+    if not lo_a:
+        Al = np.zeros_like(Ah)
+    if not lo_b:
+        Bl = np.zeros_like(Bh)
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al) if lo_a else None, _dev(Bh), _dev(Bl) if lo_b else None,
+                         nslices=ns, kblock=kb)
+    if kb is None or kb >= k:
+        Rh, Rl = exact.sliced_product(Ah, Al, Bh, Bl, ns)
+    else:
+        Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kb, ns)
+    assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
+
+
+@pytest.mark.parametrize("case", _qd_cases(15, 20261203) + _qd_split_cases(10, 20261205),
+                         ids=lambda c: f"qd{c[0]}")
 def test_random_qd_case_bit_exact(gpu, case):
     i, m, n, k, kb, planes_a, planes_b, da, db = case
     _say(f"[random qd {i}] m={m} n={n} k={k} kblock={kb} planes=({planes_a},{planes_b}) dist=({da},{db})")
