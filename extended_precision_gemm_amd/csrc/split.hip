@@ -301,6 +301,78 @@ __global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t 
     }
 }
 
+// One pass per 16-row (AXIS 0) or 16-column (AXIS 1) block whose (hi, lo) fits
+// the workgroup's registers (KB * 32 <= NT * PPT pairs of entries): every
+// thread loads, in packed order, the PPT pairs of entries it will slice, the
+// block's 16 exponents are reduced from those registers, and the slices are
+// cut from them, so the operand is read from HBM exactly once.  Pair q covers
+// packed lanes 2(q % 32), 2(q % 32) + 1 of k-block q / 32; as NT is a multiple
+// of 32, thread t's pairs all lie on outer indices oi, oi + 1 with
+// oi = 2(t % 8).
+template <int AXIS, int NT, int NS, int PPT>
+__global__ void __launch_bounds__(NT) split_block_regs_kernel(int64_t outer, int64_t k, int64_t KB,
+                                                              const double* __restrict__ hi,
+                                                              const double* __restrict__ lo, int64_t ld,
+                                                              int32_t* __restrict__ exps,
+                                                              double* __restrict__ slices) {
+    static_assert(NT % 64 == 0, "whole waves");
+    __shared__ int block_code[16];
+    const int t = threadIdx.x;
+    const int64_t blk = blockIdx.x;
+    const int64_t o0 = blk * 16;
+    const int64_t pairs = KB * 32;
+    const int oi = (t & 7) * 2;
+    if (t < 16) block_code[t] = kNoExp;
+
+    double xh[PPT][2], xl[PPT][2];
+    int c0 = kNoExp, c1 = kNoExp;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int64_t q = t + static_cast<int64_t>(i) * NT;
+        const int64_t p = (q >> 5) * 4 + (((q & 31) * 2) >> 4);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int64_t o = o0 + oi + e;
+            xh[i][e] = 0.0;
+            xl[i][e] = 0.0;
+            if (q < pairs && o < outer && p < k) {
+                const int64_t idx = AXIS == 0 ? o * ld + p : p * ld + o;
+                xh[i][e] = hi[idx];
+                xl[i][e] = lo ? lo[idx] : 0.0;
+            }
+        }
+        c0 = max(c0, entry_exp_code(xh[i][0], xl[i][0]));
+        c1 = max(c1, entry_exp_code(xh[i][1], xl[i][1]));
+    }
+    // lanes l, l ^ 8, l ^ 16, l ^ 32 of a wave share oi; then one LDS max per wave
+#pragma unroll
+    for (int off = 8; off <= 32; off <<= 1) {
+        c0 = max(c0, __shfl_xor(c0, off, 64));
+        c1 = max(c1, __shfl_xor(c1, off, 64));
+    }
+    __syncthreads();  // block_code initialised
+    if ((t & 63) < 8) {
+        atomicMax(&block_code[oi], c0);
+        atomicMax(&block_code[oi + 1], c1);
+    }
+    __syncthreads();
+    if (t < 16 && o0 + t < outer) exps[o0 + t] = decode_exp(block_code[t]);
+    const int e0 = decode_exp(block_code[oi]), e1 = decode_exp(block_code[oi + 1]);
+
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int64_t q = t + static_cast<int64_t>(i) * NT;
+        if (q >= pairs) break;
+        double sl0[NS], sl1[NS];
+        slice_entry<NS>(xh[i][0], xl[i][0], e0, sl0);
+        slice_entry<NS>(xh[i][1], xl[i][1], e1, sl1);
+        const int lane = static_cast<int>(q & 31) * 2;
+        double2* dst = reinterpret_cast<double2*>(slices + (blk * KB + (q >> 5)) * (NS * kFragDoubles) + lane);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) dst[s * (kFragDoubles / 2)] = make_double2(sl0[s], sl1[s]);
+    }
+}
+
 // Blocks needed before the one-pass block kernel beats two streaming passes
 // (measured: 4096 blocks of k = 512 win, 256 blocks of k = 4096 lose).
 constexpr int64_t kFusedMinBlocks = 1024;
@@ -311,6 +383,9 @@ constexpr int64_t kFusedMinBlocks = 1024;
 // (measured on gfx950: 1024^2 29 vs 44 us with 256 MB re-read, 1536^2 61 vs
 // 59 us with 396 MB, 4096^2 483 vs 339 us).
 constexpr int64_t kSmallColsBytes = 24ll << 20;
+// Pairs of entries per thread of the register-resident block kernel: 16 rows
+// (columns) of up to 512 values of k with 1024 threads.
+constexpr int kRegPairs = 4;
 constexpr int64_t kSmallColsReread = 320ll << 20;
 
 template <int NS>
@@ -330,6 +405,17 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
         // One pass per block; k-blocks shared among parts when blocks are few.
         // All of it belongs to the slice phase.
         if (!(phases & kSplitSlices)) return hipSuccess;
+        if (kparts == 1 && g.KB * 32 <= kBlockThreads * kRegPairs) {
+            // the whole block in registers: one read of the operand
+            const unsigned blocks = static_cast<unsigned>(g.RB);
+            if (axis == 0)
+                split_block_regs_kernel<0, kBlockThreads, NS, kRegPairs><<<blocks, kBlockThreads, 0, stream>>>(
+                    outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
+            else
+                split_block_regs_kernel<1, kBlockThreads, NS, kRegPairs><<<blocks, kBlockThreads, 0, stream>>>(
+                    outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
+            return hipGetLastError();
+        }
         const dim3 grid(static_cast<unsigned>(g.RB), static_cast<unsigned>(kparts));
         if (axis == 0)
             split_block_kernel<0, kBlockThreads, NS><<<grid, kBlockThreads, 0, stream>>>(

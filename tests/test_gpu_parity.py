@@ -142,25 +142,44 @@ def test_split_bit_exact_small(gpu, m, n, k):
 
 
 @pytest.mark.parametrize("axis", [0, 1])
-def test_split_block_path_bit_exact(gpu, axis):
-    """Operands with >= 1024 blocks of 16 rows (columns) take the one-pass block
-    kernel; ragged outer size, short k and the edge values of the small tests."""
-    rng = np.random.default_rng(55 + axis)
-    outer, k = 16500, 37
+@pytest.mark.parametrize("k", [37, 300, 512, 513])
+def test_split_block_path_bit_exact(gpu, axis, k):
+    """Operands with >= 1024 blocks of 16 rows (columns) take a one-pass block
+    kernel: up to k = 512 the block's entries stay in registers and are read
+    once, above that they are read twice, the second time from cache.  Ragged
+    outer size, the edge values of the small tests, an all-zero block and an
+    entry far above the rest.  The leading 1040 rows (columns) sliced on their
+    own (65 blocks: the two-pass path) give the same exponents and slices bit
+    for bit; sampled rows (columns), and at k = 37 all of them, equal the
+    oracle's."""
+    rng = np.random.default_rng(55 + axis + 7 * k)
+    outer, lead = 16500, 1040
     hi, lo = _edge_matrix(rng, outer, k)
     hi[200:216, :] = 0.0
     lo[200:216, :] = 0.0                      # a whole all-zero 16-row block
+    hi[16400, 5] = 2.0 ** 300                 # one row far above the others
     if axis == 1:
         hi, lo = np.ascontiguousarray(hi.T), np.ascontiguousarray(lo.T)
+    _say(f"[split block] axis={axis} outer={outer} k={k}")
     E, packed, outer_, k_ = _gpu_split(gpu, hi, lo, axis)
     assert (outer_, k_) == (outer, k)
-    if axis == 0:
-        E_ref, D = exact.slice_rows(hi, lo)
+    sub = (lambda x: x[:lead]) if axis == 0 else (lambda x: x[:, :lead])
+    E2, packed2, _, _ = _gpu_split(gpu, np.ascontiguousarray(sub(hi)), np.ascontiguousarray(sub(lo)), axis)
+    hE = _host(E)
+    assert np.array_equal(hE[:lead], _host(E2))
+    assert _bits_equal(_unpacked(packed, outer, k, range(lead)), _unpacked(packed2, lead, k))
+    if k == 37:
+        rows = list(range(outer))
     else:
-        E_ref, D = exact.slice_cols(hi, lo)
+        rows = sorted({0, 1, 2, 3, 15, 16, 205, lead - 1, lead, 8191, 16383, 16384, 16400, outer - 1}
+                      | {int(x) for x in rng.integers(0, outer, 6)})
+    if axis == 0:
+        E_ref, D = exact.slice_rows(hi, lo, rows)
+    else:
+        E_ref, D = exact.slice_cols(hi, lo, rows)
         D = D.transpose(0, 2, 1)
-    assert np.array_equal(_host(E), E_ref)
-    assert _bits_equal(_unpacked(packed, outer, k), exact.slice_values(D))
+    assert np.array_equal(hE[rows], E_ref)
+    assert _bits_equal(_unpacked(packed, outer, k, rows), exact.slice_values(D))
 
 
 @pytest.mark.parametrize("rows,cols", [(3000, 2500), (64, 30000), (1500, 4100)])
