@@ -374,3 +374,23 @@ def test_qd_valid_call_without_gpu_reports_device_error(ddg):
     C = _arr(P[3], P[3] + 4096, P[3] + 8192, P[3] + 12288)
     assert L.qd_gemm_ws_kb(4, 5, 6, 2, _arr(P[0]), 6, _arr(P[2]), 5, C, 5, P[6],
                            L.qd_gemm_workspace_size_kb(4, 5, 6, 2), None) == ddg.ERROR_DEVICE
+
+
+def test_binding_rejects_host_and_wrong_dtype_tensors(ddg):
+    """The Python binding checks its tensors before any call into the library:
+    float64 only, device memory only, 2-D planes, one to four qd components."""
+    import torch
+    a32 = torch.zeros((4, 4), dtype=torch.float32)
+    a64 = torch.zeros((4, 4), dtype=torch.float64)
+    with pytest.raises(TypeError, match="float64"):
+        ddg.dd_gemm(a32, None, a64, None)
+    with pytest.raises(ValueError, match="device tensor"):
+        ddg.dd_gemm(a64, None, a64, None)
+    with pytest.raises(ValueError, match="device tensor"):
+        ddg.split_balanced(a64, None, 0)
+    with pytest.raises(ValueError, match="one to four"):
+        ddg.qd_gemm([a64] * 5, [a64])
+    with pytest.raises(ValueError, match="one to four"):
+        ddg.qd_gemm([None, a64], [a64])
+    with pytest.raises(ValueError, match="device tensor"):
+        ddg.qd_gemm(torch.zeros((4, 3, 3), dtype=torch.float64), [a64])
