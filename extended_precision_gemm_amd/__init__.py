@@ -83,6 +83,7 @@ _SIGNATURES = {
     "dd_gemm_ws_kb": (_st, [_i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                             _vp, _sz, _vp]),
     "ddgemm_split_parts": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
+    "ddgemm_split_first_row": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "ddgemm_status_string": (ctypes.c_char_p, [_st]),
     "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
 }
@@ -153,6 +154,11 @@ def k_max(nslices: int = NUM_SLICES) -> int:
 def split_parts(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:
     """k-parts the product entry points use for an m×n×k product (1 = not split)."""
     return lib.ddgemm_split_parts(m, n, k, nslices)
+
+
+def split_first_row(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:
+    """First output row of the part split over k (m when not split)."""
+    return lib.ddgemm_split_first_row(m, n, k, nslices)
 
 
 def slices_bytes(outer: int, k: int, nslices: int = NUM_SLICES) -> int:

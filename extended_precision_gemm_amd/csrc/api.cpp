@@ -167,8 +167,10 @@ size_t dd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int nslices, i
                    align_up(dd_split_slices_bytes_ns(n, kb, nslices)) + align_up(static_cast<size_t>(m) * 4) +
                    align_up(static_cast<size_t>(n) * 4);
     if (block_count(k, kblock) > 1) bytes += 2 * align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
-    if (split_k_parts(m, n, kb, nslices) > 1)  // level planes of a product split over k
-        bytes += align_up(static_cast<size_t>(nslices) * static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
+    const SplitPlan plan = split_plan(m, n, kb, nslices, true);
+    if (plan.parts > 1)  // level planes of the rows split over k
+        bytes += align_up(static_cast<size_t>(nslices) * static_cast<size_t>(m - plan.first_row) *
+                          static_cast<size_t>(n) * 8);
     return bytes;
 }
 
@@ -283,17 +285,27 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
     double* T_hi = reinterpret_cast<double*>(w);  // block results after the first (blocks > 1)
     double* T_lo = T_hi + (blocks > 1 ? align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8) / 8 : 0);
     if (blocks > 1) w += 2 * align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
-    double* L = reinterpret_cast<double*>(w);     // level planes [nslices][m][n] of a product split over k
-    const bool split = split_k_parts(m, n, kb, nslices) > 1;
+    double* L = reinterpret_cast<double*>(w);     // level planes [nslices][rows][n] of the rows split over k
+    const SplitPlan plan_kb = split_plan(m, n, kb, nslices, true);
+    const int64_t split_rows = plan_kb.parts > 1 ? m - plan_kb.first_row : 0;  // rows the planes hold
 
-    // One block's product into (hi, lo) planes: fused, or split over k into the
-    // level planes and renormalised after.
+    // One block's product into (hi, lo) planes: fused, or its rows from
+    // plan.first_row on split over k into the level planes and renormalised
+    // after (the rows before it fused, in one launch over whole tile rows).
     auto block_gemm = [&](int64_t kc, double* d_hi, double* d_lo, int64_t ldd, hipStream_t st) {
-        const int64_t parts = split ? split_k_parts(m, n, kc, nslices) : 1;
-        if (parts <= 1)
+        SplitPlan plan = split_rows == 0 ? SplitPlan{m, 1} : (kc == kb ? plan_kb : split_plan(m, n, kc, nslices, true));
+        if (plan.parts > 1 && m - plan.first_row > split_rows) plan = SplitPlan{m, 1};
+        if (plan.parts <= 1)
             return launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, d_hi, d_lo, ldd, true, st);
-        hipError_t err = launch_sliced_gemm_split(m, n, kc, nslices, A_sl, B_sl, L, n, parts, st);
-        if (err == hipSuccess) err = launch_levels_to_dd(m, n, nslices, L, n, E, F, d_hi, d_lo, ldd, st);
+        const int64_t r0 = plan.first_row, mt = m - r0;
+        hipError_t err = hipSuccess;
+        if (r0 > 0)
+            err = launch_sliced_gemm(r0, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, d_hi, d_lo, ldd, true, st);
+        // rows r0.. of the packed A slices start at 16-row block r0 / 16
+        const double* A_tail = A_sl + (r0 / 16) * PackGeom(m, kc).KB * nslices * kFragDoubles;
+        if (err == hipSuccess) err = launch_sliced_gemm_split(mt, n, kc, nslices, A_tail, B_sl, L, n, plan.parts, st);
+        if (err == hipSuccess)
+            err = launch_levels_to_dd(mt, n, nslices, L, n, E + r0, F, d_hi + r0 * ldd, d_lo + r0 * ldd, ldd, st);
         return err;
     };
 
@@ -369,12 +381,15 @@ size_t qd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int64_t kblock
     if (validate_qd_blocked_dims(m, n, k, kblock) != DDGEMM_SUCCESS) return 0;
     const int64_t kb = k < kblock ? k : kblock;
     const bool blocked = block_count(k, kb) > 1;
-    const bool split = split_k_parts(m, n, kb, kQdSlices) > 1;
+    // a blocked product's blocks split whole or not at all; one block may split its later rows only
+    const SplitPlan plan = split_plan(m, n, kb, kQdSlices, !blocked);
     const size_t planes = static_cast<size_t>(m) * static_cast<size_t>(n) * 8 * QDGEMM_NUM_LEVELS;
-    // int64 level planes of a blocked product; double level planes of a (block) product split over k
+    const size_t split_planes =
+        static_cast<size_t>(m - plan.first_row) * static_cast<size_t>(n) * 8 * QDGEMM_NUM_LEVELS;
+    // int64 level planes of a blocked product; double level planes of the rows split over k
     return align_up(qd_split_slices_bytes(m, kb)) + align_up(qd_split_slices_bytes(n, kb)) +
            align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4) +
-           (blocked ? align_up(planes) : 0) + (split ? align_up(planes) : 0);
+           (blocked ? align_up(planes) : 0) + (plan.parts > 1 ? align_up(split_planes) : 0);
 }
 
 size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
@@ -455,10 +470,15 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
         if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitExps);
         if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitSlices);
         if (e == hipSuccess) e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitSlices);
-        const int64_t parts = split_k_parts(m, n, k, kQdSlices);
-        if (e == hipSuccess && parts > 1) {  // tiles leave the chip partly idle: split over k
-            e = launch_sliced_gemm_split(m, n, k, kQdSlices, A_sl, B_sl, L, n, parts, s);
-            if (e == hipSuccess) e = launch_levels_to_qd(m, n, L, n, E, F, out, ldc, s);
+        const SplitPlan plan = split_plan(m, n, k, kQdSlices, true);
+        if (e == hipSuccess && plan.parts > 1) {  // tiles leave the chip partly idle: rows r0.. split over k
+            const int64_t r0 = plan.first_row, mt = m - r0;
+            if (r0 > 0) e = launch_qd_gemm(r0, n, k, A_sl, B_sl, E, F, out, ldc, s);
+            const double* A_tail = A_sl + (r0 / 16) * PackGeom(m, k).KB * kQdSlices * kFragDoubles;
+            OutPlanes out_tail = out;
+            for (int c = 0; c < 4; ++c) out_tail.c[c] = out.c[c] + r0 * ldc;
+            if (e == hipSuccess) e = launch_sliced_gemm_split(mt, n, k, kQdSlices, A_tail, B_sl, L, n, plan.parts, s);
+            if (e == hipSuccess) e = launch_levels_to_qd(mt, n, L, n, E + r0, F, out_tail, ldc, s);
         } else if (e == hipSuccess) {
             e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s);
         }
@@ -529,7 +549,13 @@ const char* ddgemm_status_string(ddgemm_status_t status) {
 
 int64_t ddgemm_split_parts(int64_t m, int64_t n, int64_t k, int nslices) {
     if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return 0;
-    return split_k_parts(m, n, k, nslices);
+    return split_plan(m, n, k, nslices, true).parts;
+}
+
+int64_t ddgemm_split_first_row(int64_t m, int64_t n, int64_t k, int nslices) {
+    if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return -1;
+    const SplitPlan plan = split_plan(m, n, k, nslices, true);
+    return plan.parts > 1 ? plan.first_row : m;
 }
 
 ddgemm_status_t ddgemm_probe_mfma_f64(double* out, void* stream) {

@@ -77,7 +77,14 @@ GemmGeometry gemm_geometry(int ns);
 
 // Split over k for outputs whose tiles leave the chip partly idle: the k-parts' level sums
 // are added exactly (atomically, in any order) into zeroed level planes
-// [ns][m][ldl], then turned into the result.  split_k_parts() = 1: no split.
+// [ns][rows][ldl], then turned into the result.  A plan computes output rows
+// [0, first_row) unsplit and rows [first_row, m) in `parts` k-parts; parts = 1:
+// no split.  Without `tail` the plan splits the whole product or nothing
+// (first_row = 0 when parts > 1); split_k_parts() is that plan's part count.
+struct SplitPlan {
+    int64_t first_row, parts;
+};
+SplitPlan split_plan(int64_t m, int64_t n, int64_t k, int ns, bool tail);
 int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns);
 hipError_t launch_zero_levels(int64_t m, int64_t n, int ns, double* levels, int64_t ldl, hipStream_t stream);
 hipError_t launch_sliced_gemm_split(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,

@@ -99,6 +99,19 @@ def test_split_parts_query(ddg):
     assert sp(1, 1, 10 ** 6, 8) == 256
     assert sp(0, 5, 100, 8) == 1 and sp(5, 5, 0, 8) == 1
     assert sp(-1, 5, 100, 8) == 0 and sp(5, 5, 100, 3) == 0 and sp(5, 5, 100, 17) == 0
+    # the split part starts at a whole tile row; the rows before it run unsplit
+    fr = ddg.split_first_row
+    for (m, n, k, ns) in [(1152, 1152, 1152, 8), (1536, 1024, 4096, 8), (2560, 1024, 4096, 8), (896, 896, 896, 16),
+                          (960, 1280, 4096, 8), (700, 900, 4096, 8), (3, 5, 100000, 8), (1024, 1024, 4096, 8),
+                          (1000, 1100, 700, 16), (520, 1030, 900, 12), (1280, 1280, 1024, 6)]:
+        p, r = sp(m, n, k, ns), fr(m, n, k, ns)
+        tm = 32 if ns == 6 or ns >= 9 else 64
+        assert (r == m) == (p == 1), (m, n, k, ns)
+        assert 0 <= r <= m and (r == m or r % tm == 0), (m, n, k, ns, r)
+    assert fr(1024, 1024, 4096, 8) == 1024 and fr(4096, 4096, 4096, 8) == 4096
+    assert fr(1536, 1024, 4096, 8) == 1024 and sp(1536, 1024, 4096, 8) == 2   # one full round, then 128 tiles in 2
+    assert fr(3, 5, 100000, 8) == 0                                           # one tile: all of it split
+    assert fr(-1, 5, 100, 8) == -1 and fr(5, 5, 100, 3) == -1
 
 
 def test_workspace_holds_level_planes_when_the_product_splits_over_k(ddg):
@@ -106,20 +119,24 @@ def test_workspace_holds_level_planes_when_the_product_splits_over_k(ddg):
     r = lambda x: (x + 255) // 256 * 256
     for (m, n, k, ns) in [(64, 64, 512, 8), (64, 64, 511, 8), (64, 64, 240, 8), (3, 5, 100000, 8),
                           (1000, 1000, 100000, 8), (700, 900, 4096, 8), (256, 256, 65536, 12),
-                          (100, 80, 5000, 16), (64, 64, 1024, 6), (1024, 1024, 4096, 8)]:
+                          (100, 80, 5000, 16), (64, 64, 1024, 6), (1024, 1024, 4096, 8),
+                          (1536, 1024, 4096, 8), (1152, 1152, 1152, 8)]:
         base = (r(L.dd_split_slices_bytes_ns(m, k, ns)) + r(L.dd_split_slices_bytes_ns(n, k, ns))
                 + r(4 * m) + r(4 * n))
         split = ddg.split_parts(m, n, k, ns) > 1
-        assert L.dd_gemm_workspace_size_ns(m, n, k, ns) == base + (r(ns * m * n * 8) if split else 0), (m, n, k, ns)
+        rows = m - ddg.split_first_row(m, n, k, ns)
+        assert L.dd_gemm_workspace_size_ns(m, n, k, ns) == base + (r(ns * rows * n * 8) if split else 0), (m, n, k, ns)
         if ns == 8:
             assert L.dd_gemm_workspace_size(m, n, k) == L.dd_gemm_workspace_size_ns(m, n, k, ns)
     assert ddg.split_parts(64, 64, 512, 8) > 1 and ddg.split_parts(64, 64, 240, 8) == 1
     assert ddg.split_parts(1024, 1024, 4096, 8) == 1
     # quad double: sixteen level planes for a split product (32x64 tiles, 4 values of k per stage)
-    for (m, n, k) in [(64, 64, 300), (64, 64, 100000), (2048, 2048, 4096), (50, 40, 30)]:
+    for (m, n, k) in [(64, 64, 300), (64, 64, 100000), (2048, 2048, 4096), (50, 40, 30), (896, 896, 896)]:
         base = r(L.qd_split_slices_bytes(m, k)) + r(L.qd_split_slices_bytes(n, k)) + r(4 * m) + r(4 * n)
         split = ddg.split_parts(m, n, k, 16) > 1
-        assert L.qd_gemm_workspace_size(m, n, k) == base + (r(16 * m * n * 8) if split else 0), (m, n, k)
+        rows = m - ddg.split_first_row(m, n, k, 16)
+        assert L.qd_gemm_workspace_size(m, n, k) == base + (r(16 * rows * n * 8) if split else 0), (m, n, k)
+    assert ddg.split_first_row(896, 896, 896, 16) > 0
     assert ddg.split_parts(64, 64, 300, 16) > 1 and ddg.split_parts(2048, 2048, 4096, 16) == 1
     # a blocked quad-double product whose blocks split: int64 planes and double planes
     m, n, k, kb = 40, 33, 3000, 1000

@@ -214,3 +214,79 @@ def test_qd_split_of_partly_idle_rounds(gpu):
         Fj, DB = qd.slice_cols(B, cols=[j])
         ref = qd.renorm_levels(qd.level_sums(DA, DB), Ei, Fj)[:, 0, 0]
         assert _bits_equal(C[:, i, j], ref), (i, j)
+
+
+def _sample(rng, size, must):
+    return sorted({x for x in must if 0 <= x < size} | {int(x) for x in rng.integers(0, size, 4)})
+
+
+@pytest.mark.parametrize("m,n,k,ns", [(1150, 1160, 1152, 8), (1536, 1024, 2048, 8), (1280, 1280, 1280, 6),
+                                      (1300, 1300, 1300, 12)])
+def test_split_of_the_last_rows_only(gpu, m, n, k, ns):
+    """Plans that run the leading whole tile rows unsplit and split only the
+    rows from the plan's first split row on: the product equals the unsplit
+    fused stage call on every entry and the oracle's chain on sampled rows and
+    columns (rows on both sides of the first split row included), bit for bit."""
+    r0, parts = gpu.split_first_row(m, n, k, ns), gpu.split_parts(m, n, k, ns)
+    assert 0 < r0 < m and parts > 1
+    _say(f"[split tail] {m}x{n}x{k} nslices={ns} first split row={r0} parts={parts}")
+    Ah, Al = workloads.random_dd((m, k), 9700 + m, "signed_exp20")
+    Bh, Bl = workloads.random_dd((k, n), 9701 + n, "normal")
+    dAh, dAl, dBh, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
+    Ch, Cl = gpu.dd_gemm(dAh, dAl, dBh, dBl, nslices=ns)
+    E, As = gpu.split_balanced(dAh, dAl, 0, nslices=ns)
+    F, Bs = gpu.split_balanced(dBh, dBl, 1, nslices=ns)
+    Uh, Ul = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F, nslices=ns)
+    hCh, hCl = _host(Ch), _host(Cl)
+    assert _bits_equal(hCh, _host(Uh)) and _bits_equal(hCl, _host(Ul))
+    rng = np.random.default_rng(m + n + k + ns)
+    rows = _sample(rng, m, [0, r0 - 1, r0, r0 + 1, m - 1])
+    cols = _sample(rng, n, [0, n - 1])
+    E_ref, DA = exact.slice_rows(Ah, Al, rows, ns)
+    F_ref, DB = exact.slice_cols(Bh, Bl, cols, ns)
+    Rh, Rl = exact.renorm_levels(exact.level_values(exact.level_sums_units(DA, DB)), E_ref, F_ref)
+    assert _bits_equal(hCh[np.ix_(rows, cols)], Rh) and _bits_equal(hCl[np.ix_(rows, cols)], Rl)
+
+
+@pytest.mark.parametrize("kblock", [1152, 1000])
+def test_blocked_product_whose_blocks_split_their_last_rows(gpu, kblock):
+    """A k-blocked product whose blocks split their last rows over k (the last,
+    shorter block may plan differently or not split): sampled entries equal the
+    oracle's blocked chain on the same rows and columns, bit for bit."""
+    m, n, k = 1152, 1152, 2300
+    assert 0 < gpu.split_first_row(m, n, kblock, 8) < m
+    _say(f"[split tail blocks] {m}x{n}x{k} kblock={kblock}")
+    Ah, Al = workloads.random_dd((m, k), 9801 + kblock, "uniform")
+    Bh, Bl = workloads.random_dd((k, n), 9802 + kblock, "signed_exp20")
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl), kblock=kblock)
+    hCh, hCl = _host(Ch), _host(Cl)
+    rng = np.random.default_rng(kblock)
+    r0 = gpu.split_first_row(m, n, kblock, 8)
+    rows = _sample(rng, m, [0, r0 - 1, r0, m - 1])
+    cols = _sample(rng, n, [0, n - 1])
+    Rh, Rl = exact.sliced_product_kblocks(Ah[rows], Al[rows], Bh[:, cols], Bl[:, cols], kblock, 8)
+    assert _bits_equal(hCh[np.ix_(rows, cols)], Rh) and _bits_equal(hCl[np.ix_(rows, cols)], Rl)
+
+
+@pytest.mark.parametrize("m,n,k", [(800, 900, 700), (768, 768, 768)])
+def test_qd_split_of_the_last_rows_only(gpu, m, n, k):
+    """The quad-double product with only its last rows split over k: equal to
+    the unsplit fused call everywhere and to the oracle on sampled entries."""
+    import torch
+    r0, parts = gpu.split_first_row(m, n, k, 16), gpu.split_parts(m, n, k, 16)
+    assert 0 < r0 < m and parts > 1
+    _say(f"[split tail qd] {m}x{n}x{k} first split row={r0} parts={parts}")
+    A = workloads.random_qd((m, k), 9901 + m, "signed_exp20")
+    B = workloads.random_qd((k, n), 9902 + n, "uniform")
+    dA, dB = _dev(A), _dev(B)
+    C = _host(gpu.qd_gemm(dA, dB))
+    E, As = gpu.qd_split_balanced(dA, 0)
+    F, Bs = gpu.qd_split_balanced(dB, 1)
+    assert _bits_equal(C, _host(gpu.qd_sliced_gemm_renorm(m, n, k, As, E, Bs, F)))
+    del As, Bs
+    torch.cuda.empty_cache()
+    for i, j in [(0, 0), (r0 - 1, n - 1), (r0, 3), (m - 1, n // 2)]:
+        Ei, DA = qd.slice_rows(A, rows=[i])
+        Fj, DB = qd.slice_cols(B, cols=[j])
+        ref = qd.renorm_levels(qd.level_sums(DA, DB), Ei, Fj)[:, 0, 0]
+        assert _bits_equal(C[:, i, j], ref), (i, j)
