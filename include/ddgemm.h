@@ -15,7 +15,9 @@
  *   2. dd_sliced_gemm     -- the 36 slice-pair products with s + t <= 7, summed
  *                            exactly per level l = s + t on FP64 MFMA;
  *   3. dd_renorm_levels   -- TwoSum cascade of the 8 level sums into (hi, lo);
- *   dd_sliced_gemm_renorm fuses 2 and 3; dd_gemm / dd_gemm_ws run 1 + 1 + (2+3).
+ *   dd_sliced_gemm_renorm fuses 2 and 3; dd_gemm / dd_gemm_ws run 1 + 1 + (2+3),
+ *   or, for outputs whose tiles leave the chip partly idle, 2 split over k
+ *   for some or all output rows, then 3 for those rows (dd_gemm_workspace_size).
  *
  * Conventions for every entry point
  *   - All matrices are row-major float64 planes in device memory; a
@@ -143,9 +145,10 @@ ddgemm_status_t dd_split_balanced(int64_t rows, int64_t cols,
  *              ldl >= max(1, n):  S_l[i][j] = sum_{s+t=l} sum_p A_s[i][p] * B_t[p][j]
  *              for l = 0..7, computed exactly (every partial sum is an integer
  *              multiple of 2^(-13(l+2)) below 2^53 units).  k = 0 writes zeros.
- *              Outputs that leave the chip partly idle are split over k (see
- *              dd_gemm_workspace_size): the planes are zeroed and the k-parts
- *              add into them with atomic adds, exact and so order-independent.
+ *              Outputs that leave the chip partly idle are split over k, all
+ *              rows at once (the rule of dd_gemm_workspace_size with r = 0):
+ *              the planes are zeroed and the k-parts add into them with atomic
+ *              adds, exact and so order-independent.
  * Errors: DDGEMM_ERROR_INVALID_VALUE for negative sizes, ldl < max(1, n),
  * k > DDGEMM_K_MAX, NULL pointers with a nonzero extent.
  */
