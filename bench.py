@@ -54,6 +54,10 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work of the oracle sample")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (HBM counter calibration)")
+    ap.add_argument("--shape", default=None,
+                    help="M,N,K: time the product entry point (dd_gemm_ws, or qd_gemm_ws with --qd) on that shape "
+                         "with its split-over-k plan, beside the unsplit stage calls (not the metric's line)")
+    ap.add_argument("--qd", action="store_true", help="with --shape: the quad-double product")
     return ap.parse_args()
 
 
@@ -131,6 +135,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.shape:
+        return _run_shape(args)
     w = workloads.by_name(args.workload)
     if w in workloads.QD_WORKLOADS:
         return _run_qd(args, w)
@@ -280,6 +286,97 @@ def main():
             ratio = float((np.abs((gh - Rh) + (gl - Rl)) / bound).max())
             rec["parity_sample"] = {"rows": rows, "max_err_over_bound": ratio, "ok": bool(ratio <= 1.0)}
     print(json.dumps(rec), flush=True)
+
+
+def _run_shape(args):
+    """The product entry point on an arbitrary shape, with the split-over-k plan
+    it takes (rows [0, first_split_row) unsplit, the rest in `parts` k-parts),
+    timed beside the unsplit path (slicing + the fused stage call, which never
+    splits) on the same inputs; the two results must agree bit for bit."""
+    import torch
+
+    import extended_precision_gemm_amd as ddg
+    import workloads
+
+    m, n, k = (int(x) for x in args.shape.split(","))
+    ns = 16 if args.qd else args.nslices
+    dev = torch.device("cuda:0")
+    print(f"[bench] shape m={m} n={n} k={k} ({'qd' if args.qd else f'dd, {ns} slices'})", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    if args.qd:
+        A = torch.from_numpy(workloads.random_qd((m, k), 11, "uniform")).to(dev)
+        B = torch.from_numpy(workloads.random_qd((k, n), 12, "uniform")).to(dev)
+        C = torch.empty((4, m, n), dtype=torch.float64, device=dev)
+        U = torch.empty_like(C)
+        ws = torch.empty(max(ddg.qd_workspace_size(m, n, k), 1), dtype=torch.uint8, device=dev)
+        E, As = ddg.qd_split_balanced(A, 0)
+        F, Bs = ddg.qd_split_balanced(B, 1)
+
+        def product():
+            ddg.qd_gemm(A, B, C=C, workspace=ws, stream=stream)
+
+        def unsplit():
+            ddg.qd_split_balanced(A, 0, E, As, stream)
+            ddg.qd_split_balanced(B, 1, F, Bs, stream)
+            ddg.qd_sliced_gemm_renorm(m, n, k, As, E, Bs, F, U, stream)
+        outs = ((C,), (U,))
+    else:
+        Ah, Al = (torch.from_numpy(x).to(dev) for x in workloads.random_dd((m, k), 11, "uniform"))
+        Bh, Bl = (torch.from_numpy(x).to(dev) for x in workloads.random_dd((k, n), 12, "uniform"))
+        C_hi = torch.empty((m, n), dtype=torch.float64, device=dev)
+        C_lo = torch.empty_like(C_hi)
+        U_hi, U_lo = torch.empty_like(C_hi), torch.empty_like(C_hi)
+        ws = torch.empty(max(ddg.workspace_size(m, n, k, ns), 1), dtype=torch.uint8, device=dev)
+        E, As = ddg.split_balanced(Ah, Al, 0, nslices=ns)
+        F, Bs = ddg.split_balanced(Bh, Bl, 1, nslices=ns)
+
+        def product():
+            ddg.dd_gemm(Ah, Al, Bh, Bl, C_hi=C_hi, C_lo=C_lo, workspace=ws, stream=stream, nslices=ns)
+
+        def unsplit():
+            ddg.split_balanced(Ah, Al, 0, E, As, stream, nslices=ns)
+            ddg.split_balanced(Bh, Bl, 1, F, Bs, stream, nslices=ns)
+            ddg.sliced_gemm_renorm(m, n, k, As, E, Bs, F, U_hi, U_lo, stream, nslices=ns)
+        outs = ((C_hi, C_lo), (U_hi, U_lo))
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps
+
+    print(f"[bench] timing {args.steps} steps of each path", file=sys.stderr, flush=True)
+    t_prod = timed(product)
+    t_unsplit = timed(unsplit)
+    same = all(torch.equal(a.view(torch.int64), b.view(torch.int64)) for a, b in zip(*outs))
+    gf = lambda t: 2.0 * m * n * k / t / 1e9
+    rec = {
+        "metric": "product entry point GFLOP/s (2mnk/t) on the given shape; unsplit stage calls beside it",
+        "value": round(gf(t_prod), 3),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_prod * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": f"{'qd' if args.qd else 'dd'} {m}x{n}x{k}", "m": m, "n": n, "k": k, "slices": ns,
+                   "description": "entries U(-1,1), lo (further components) at 2^-53 relative scale"},
+        "split_plan": {"first_split_row": ddg.split_first_row(m, n, k, ns), "parts": ddg.split_parts(m, n, k, ns)},
+        "unsplit": {"ms_per_step": round(t_unsplit * 1e3, 4), "value": round(gf(t_unsplit), 3)},
+        "speedup_vs_unsplit": round(t_unsplit / t_prod, 3),
+        "bit_identical_to_unsplit": bool(same),
+    }
+    print(json.dumps(rec), flush=True)
+    if not same:
+        sys.exit(3)
 
 
 def _run_qd(args, w):

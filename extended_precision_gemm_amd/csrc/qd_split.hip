@@ -55,17 +55,24 @@ __device__ __forceinline__ void qd_slice_entry(const double (&x)[4], int E, doub
 __global__ void __launch_bounds__(256) qd_exp_rows_kernel(int64_t rows, int64_t cols, QdPlanes X, int64_t ld,
                                                           int32_t* __restrict__ exps) {
     const int lane = threadIdx.x & 63;
+    const int64_t parts = gridDim.y;  // k-parts, as in the double-double row kernel
+    const int64_t p0 = cols * blockIdx.y / parts, p1 = cols * (blockIdx.y + 1) / parts;
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
     for (int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
          row < rows; row += nwaves) {
         int code = kNoExp;
-        for (int64_t p = lane; p < cols; p += 64) {
+        for (int64_t p = p0 + lane; p < p1; p += 64) {
             double x[4];
             load_qd(X, row * ld + p, x);
             code = max(code, qd_entry_code(x));
         }
         code = wave_max(code);
-        if (lane == 0) exps[row] = decode_exp(code);
+        if (lane == 0) {
+            if (parts == 1)
+                exps[row] = decode_exp(code);
+            else if (code != kNoExp)
+                atomicMax(exps + row, code);
+        }
     }
 }
 
@@ -206,7 +213,11 @@ hipError_t launch_qd_exps(int64_t rows, int64_t cols, const QdPlanes& X, int64_t
                           hipStream_t stream) {
     if ((axis == 0 ? rows : cols) == 0) return hipSuccess;
     if (axis == 0) {
-        qd_exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X, ldx, exps);
+        const int64_t parts = exp_row_parts(rows, cols);
+        const dim3 grid(grid_for(rows, 4, 1 << 20), static_cast<unsigned>(parts));
+        if (parts > 1) fill_int_kernel<<<grid_for(rows, 256, 4096), 256, 0, stream>>>(exps, rows, kNoExp);
+        qd_exp_rows_kernel<<<grid, 256, 0, stream>>>(rows, cols, X, ldx, exps);
+        if (parts > 1) decode_exps_kernel<<<grid_for(rows, 256, 4096), 256, 0, stream>>>(exps, rows);
     } else {
         const int64_t parts = exp_col_parts(rows, cols);
         const dim3 grid(grid_for(cols, 16, 1 << 20), static_cast<unsigned>(parts));

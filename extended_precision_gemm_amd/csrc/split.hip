@@ -100,21 +100,32 @@ __device__ __forceinline__ void slice_entry(double hi, double lo, int E, double 
     }
 }
 
-// One wave per row: E[row] = max frexp exponent over the row (axis 0, the A operand).
+// One wave per row and k-part: E[row] = max frexp exponent over the row (axis
+// 0, the A operand).  Part y of gridDim.y covers columns [cols y / parts,
+// cols (y + 1) / parts).  With one part the decoded exponent is stored; with
+// several the encoded maxima are folded into `exps` (cleared to kNoExp) with
+// atomicMax and decoded after.
 __global__ void __launch_bounds__(256) exp_rows_kernel(int64_t rows, int64_t cols,
                                                        const double* __restrict__ hi,
                                                        const double* __restrict__ lo, int64_t ld,
                                                        int32_t* __restrict__ exps) {
     const int lane = threadIdx.x & 63;
+    const int64_t parts = gridDim.y;
+    const int64_t p0 = cols * blockIdx.y / parts, p1 = cols * (blockIdx.y + 1) / parts;
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (blockDim.x >> 6);
     for (int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
          row < rows; row += nwaves) {
         const double* h = hi + row * ld;
         const double* l = lo ? lo + row * ld : nullptr;
         int code = kNoExp;
-        for (int64_t p = lane; p < cols; p += 64) code = max(code, entry_exp_code(h[p], l ? l[p] : 0.0));
+        for (int64_t p = p0 + lane; p < p1; p += 64) code = max(code, entry_exp_code(h[p], l ? l[p] : 0.0));
         code = wave_max(code);
-        if (lane == 0) exps[row] = decode_exp(code);
+        if (lane == 0) {
+            if (parts == 1)
+                exps[row] = decode_exp(code);
+            else if (code != kNoExp)
+                atomicMax(exps + row, code);
+        }
     }
 }
 
@@ -427,7 +438,11 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
     }
     // Otherwise two passes over the operand: exponents, then slices.
     if ((phases & kSplitExps) && axis == 0) {
-        exp_rows_kernel<<<grid_for(rows, 4, 1 << 20), 256, 0, stream>>>(rows, cols, X_hi, X_lo, ldx, exps);
+        const int64_t parts = exp_row_parts(rows, cols);
+        const dim3 grid(grid_for(rows, 4, 1 << 20), static_cast<unsigned>(parts));
+        if (parts > 1) fill_int_kernel<<<grid_for(rows, 256, 4096), 256, 0, stream>>>(exps, rows, kNoExp);
+        exp_rows_kernel<<<grid, 256, 0, stream>>>(rows, cols, X_hi, X_lo, ldx, exps);
+        if (parts > 1) decode_exps_kernel<<<grid_for(rows, 256, 4096), 256, 0, stream>>>(exps, rows);
     } else if (phases & kSplitExps) {
         const int64_t parts = exp_col_parts(rows, cols);
         const dim3 grid(grid_for(cols, 16, 1 << 20), static_cast<unsigned>(parts));

@@ -68,6 +68,20 @@ inline int64_t exp_col_parts(int64_t rows, int64_t cols) {
     return parts;
 }
 
+// k-parts for the row-exponent kernels (one wave per row and part): enough
+// waves to fill the chip when the rows are few, each part at least
+// kMinColsPerPart values long (one part, and so no clearing and decoding
+// launches, from kExpRowMinWaves rows up).
+constexpr int64_t kExpRowMinWaves = 2048;
+constexpr int64_t kMinColsPerPart = 2048;
+inline int64_t exp_row_parts(int64_t rows, int64_t cols) {
+    int64_t parts = (kExpRowMinWaves + rows - 1) / rows;
+    const int64_t most = cols / kMinColsPerPart > 1 ? cols / kMinColsPerPart : 1;
+    if (parts > most) parts = most;
+    if (parts > 65535) parts = 65535;
+    return parts;
+}
+
 inline unsigned grid_for(int64_t work, int64_t per_block, int64_t cap) {
     int64_t g = (work + per_block - 1) / per_block;
     if (g < 1) g = 1;

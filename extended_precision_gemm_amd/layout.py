@@ -13,7 +13,7 @@ no arithmetic on the values.
 """
 from __future__ import annotations
 
-PACK_OUTER = 128
+PACK_OUTER = 64
 PACK_K = 16
 
 

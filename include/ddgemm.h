@@ -93,7 +93,7 @@ typedef enum {
  * s-th 13-bit digit of N = floor(|x| * 2^(104-E)), x = hi + lo exactly and E the
  * balancing exponent of the entry's row (A) or column (B); padding holds +0.0.
  * Total size: Op * Kp * 8 doubles (dd_split_slices_bytes). */
-#define DDGEMM_PACK_OUTER 128
+#define DDGEMM_PACK_OUTER 64  /* the tallest tile: padding rows beyond it are never read */
 #define DDGEMM_PACK_K 16
 
 /* Bytes of packed slices for one operand with `outer` rows (A) / columns (B) and

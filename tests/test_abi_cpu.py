@@ -53,8 +53,9 @@ def test_library_links_no_oracle_code(ddg):
 def test_packed_sizes(ddg):
     assert ddg.slices_bytes(0, 10) == 0
     assert ddg.slices_bytes(10, 0) == 0
-    assert ddg.slices_bytes(1, 1) == 128 * 16 * 8 * 8
-    assert ddg.slices_bytes(129, 17) == 256 * 32 * 8 * 8
+    assert ddg.slices_bytes(1, 1) == 64 * 16 * 8 * 8
+    assert ddg.slices_bytes(129, 17) == 192 * 32 * 8 * 8
+    assert ddg.slices_bytes(128, 17) == 128 * 32 * 8 * 8
     assert ddg.slices_bytes(4096, 4096) == 4096 * 4096 * 64
     assert ddg.slices_bytes(-1, 5) == 0
     m, n, k = 1000, 70, 33
@@ -265,7 +266,7 @@ def test_n_slice_sizes_and_validation(ddg):
     L = ddg.lib
     INV = ddg.ERROR_INVALID_VALUE
     for n in range(ddg.MIN_SLICES, ddg.MAX_SLICES + 1):
-        assert L.dd_split_slices_bytes_ns(130, 33, n) == 256 * 48 * n * 8
+        assert L.dd_split_slices_bytes_ns(130, 33, n) == 192 * 48 * n * 8
         kmax = ddg.k_max(n)
         assert kmax == (8388608 if n <= 8 else 67108865 // n)
         assert L.dd_gemm_workspace_size_ns(4, 4, kmax, n) > 0
@@ -302,7 +303,7 @@ def _arr(*ptrs):
 
 def test_qd_sizes(ddg):
     L = ddg.lib
-    assert L.qd_split_slices_bytes(130, 33) == 256 * 48 * 16 * 8
+    assert L.qd_split_slices_bytes(130, 33) == 192 * 48 * 16 * 8
     assert L.qd_split_slices_bytes(0, 33) == 0
     assert L.qd_split_slices_bytes(-1, 33) == 0
     r = lambda x: (x + 255) // 256 * 256

@@ -130,13 +130,13 @@ def test_dd_level_sums_exact_at_the_k_bound(gpu):
     """k at the exact-sum bound (2^23, "Multiple Double Arithmetic on NVIDIA
     Tensor Cores", §2 eq. (5)) with the largest digits in every slice of every
     entry: level 7 reaches k * 503189512 ~ 2^51.9 units, inside the 53 exact
-    bits, and each operand's packed slices hold 2^33 doubles (68.7 GB), so a
-    32-bit offset anywhere would fail.  The level-plane stage call (split over
+    bits, and A's packed slices hold 2^33 doubles (68.7 GB), so a 32-bit
+    offset anywhere would fail.  The level-plane stage call (split over
     k into atomically added parts) must give the closed-form level sums
     exactly, and the unsplit fused call (one workgroup) the oracle's cascade of
     them, bit for bit."""
     import torch
-    m, n, k = 3, 2, gpu.K_MAX
+    m, n, k = 100, 2, gpu.K_MAX
     assert gpu.split_parts(m, n, k) > 1
     assert gpu.slices_bytes(m, k) // 8 == 2 ** 33
     digits = exact.slice_entry(MAX_HI, MAX_LO, 0)
