@@ -12,7 +12,7 @@ namespace {
 
 constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kLdsBytesPerCu = 160 * 1024;
-constexpr double kCoResidentShare = 0.93;     // two workgroups on one CU: 0.93 of twice the time of one
+constexpr double kCoResidentShare = 0.95;     // two workgroups on one CU: 0.95 of twice the time of one
 constexpr int64_t kMinStagesPerPart = 16;
 constexpr int64_t kMaxParts = 256;
 constexpr double kClockHz = 2.38e9;           // sustained MFMA clock under load
@@ -21,7 +21,7 @@ constexpr double kMfmaCycles = 64.0;          // one 16x16x4 FP64 MFMA on one SI
 constexpr double kAtomicAddsPerSecond = 2e11; // FP64 atomic adds into the level planes
 constexpr double kPlaneBytesPerSecond = 5e12; // zeroing and re-reading the level planes
 constexpr double kSplitLaunchSeconds = 15e-6; // the zeroing and renormalising launches
-constexpr double kMinSaving = 0.9;            // a split must save at least 10 %
+constexpr double kMinSaving = 0.95;           // a split must save at least 5 %
 
 }  // namespace
 
@@ -32,7 +32,7 @@ constexpr double kMinSaving = 0.9;            // a split must save at least 10 %
 // where t_stage is one stage of one workgroup alone on its CU (mfma_per_stage
 // MFMAs of 64 cycles for each of the waves sharing a SIMD: one 8-wave workgroup
 // already keeps the MFMA pipes of its CU busy), L = ceil(tiles p / 256) is the
-// most workgroups any CU runs, and c(L) = L, or 0.93 L when two workgroups fit a
+// most workgroups any CU runs, and c(L) = L, or 0.95 L when two workgroups fit a
 // CU's LDS (4..6 slices, whose waves also stay within the 128 VGPRs of four
 // waves per SIMD) and L >= 2: two co-resident workgroups hide a little of each
 // other's waiting.  The constants were fitted to timings of split products of 1
@@ -71,7 +71,7 @@ struct CostModel {
 // splits the whole product.  Candidates: first_row = 0, and with `tail` the
 // most tile rows that fit 1..4 rounds fewer than the unsplit product takes.
 // Each part keeps at least 16 stages; at most 256 parts; the plan must save
-// 10 % against the unsplit product, else {m, 1}: no split.  Outputs whose
+// 5 % against the unsplit product, else {m, 1}: no split.  Outputs whose
 // tiles fill whole rounds never split.
 SplitPlan split_plan(int64_t m, int64_t n, int64_t k, int ns, bool tail) {
     const SplitPlan none{m, 1};

@@ -109,7 +109,7 @@ size_t dd_split_slices_bytes(int64_t outer, int64_t k);
  * stage is 8 values of k, 4 from 14 slices on), p <= 256, while the rows
  * before r, whole tile rows, run unsplit; r and p are chosen by a timing model
  * of the rounds of workgroups, the atomic adds and the level planes, and only
- * where that saves at least 10 %; outputs that fill whole rounds never split.
+ * where that saves at least 5 %; outputs that fill whole rounds never split.
  * ddgemm_split_parts returns p and ddgemm_split_first_row r.  The parts add
  * their exact level sums into level planes, and the workspace also holds those
  * nslices (m - r)×n planes.  The split result is bit-identical to the unsplit
