@@ -290,3 +290,64 @@ def test_qd_split_of_the_last_rows_only(gpu, m, n, k):
         Fj, DB = qd.slice_cols(B, cols=[j])
         ref = qd.renorm_levels(qd.level_sums(DA, DB), Ei, Fj)[:, 0, 0]
         assert _bits_equal(C[:, i, j], ref), (i, j)
+
+
+def test_last_row_splits_and_row_exponent_parts_replay_in_a_graph(gpu):
+    """Plans that run some rows unsplit and split the rest (head launch, plane
+    zeroing, k-parts, renormalisation), and A operands with few long rows
+    (row exponents in k-parts: fill, atomic maxima, decode), captured once and
+    replayed over a garbage workspace with new inputs: every replay equals the
+    eager product bit for bit."""
+    import torch
+    shapes = [(1150, 1160, 1152), (64, 64, 65536)]
+    assert 0 < gpu.split_first_row(1150, 1160, 1152, 8) < 1150
+    qm, qn, qk = 800, 900, 700
+    assert 0 < gpu.split_first_row(qm, qn, qk, 16) < qm
+    bufs = []
+    for (m, n, k) in shapes:
+        A = [torch.empty((m, k), dtype=torch.float64, device="cuda") for _ in range(2)]
+        B = [torch.empty((k, n), dtype=torch.float64, device="cuda") for _ in range(2)]
+        C = [torch.empty((m, n), dtype=torch.float64, device="cuda") for _ in range(2)]
+        ws = torch.empty(gpu.workspace_size(m, n, k), dtype=torch.uint8, device="cuda")
+        bufs.append((m, n, k, A, B, C, ws))
+    qA = torch.empty((4, qm, qk), dtype=torch.float64, device="cuda")
+    qB = torch.empty((4, qk, qn), dtype=torch.float64, device="cuda")
+    qC = torch.empty((4, qm, qn), dtype=torch.float64, device="cuda")
+    qws = torch.empty(gpu.qd_workspace_size(qm, qn, qk), dtype=torch.uint8, device="cuda")
+
+    def load(seed):
+        for i, (m, n, k, A, B, C, ws) in enumerate(bufs):
+            ah, al = workloads.random_dd((m, k), seed + 10 * i, "signed_exp20")
+            bh, bl = workloads.random_dd((k, n), seed + 10 * i + 1, "normal")
+            for dst, src in ((A[0], ah), (A[1], al), (B[0], bh), (B[1], bl)):
+                dst.copy_(_dev(src))
+        qA.copy_(_dev(workloads.random_qd((qm, qk), seed + 7, "uniform")))
+        qB.copy_(_dev(workloads.random_qd((qk, qn), seed + 8, "signed_exp20")))
+
+    def product():
+        for (m, n, k, A, B, C, ws) in bufs:
+            gpu.dd_gemm(A[0], A[1], B[0], B[1], C_hi=C[0], C_lo=C[1], workspace=ws)
+        gpu.qd_gemm(qA, qB, C=qC, workspace=qws)
+
+    load(700)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        product()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        product()
+    for rep, seed in enumerate((700, 720, 720, 740)):
+        load(seed)
+        for (m, n, k, A, B, C, ws) in bufs:
+            C[0].fill_(float("nan"))
+            C[1].fill_(float("nan"))
+            ws.fill_(0x3C)
+        qC.fill_(float("nan"))
+        qws.fill_(0x3C)
+        graph.replay()
+        for (m, n, k, A, B, C, ws) in bufs:
+            Rh, Rl = gpu.dd_gemm(A[0], A[1], B[0], B[1])
+            assert _bits_equal(_host(C[0]), _host(Rh)) and _bits_equal(_host(C[1]), _host(Rl)), (rep, m, n, k)
+        assert _bits_equal(_host(qC), _host(gpu.qd_gemm(qA, qB))), rep
