@@ -340,8 +340,6 @@ def _run_shape(args):
         outs = ((C_hi, C_lo), (U_hi, U_lo))
 
     def timed(fn):
-        for _ in range(args.warmup):
-            fn()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -349,9 +347,20 @@ def _run_shape(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / args.steps
 
+    # warm both paths up, for at least half a second so that the clocks have
+    # ramped, then time product, unsplit, product: the mean of the two product
+    # runs cancels a drift of the clock over the measurement
+    t0 = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t0 < 0.5:
+        product()
+        unsplit()
+        torch.cuda.synchronize()
+        i += 1
     print(f"[bench] timing {args.steps} steps of each path", file=sys.stderr, flush=True)
-    t_prod = timed(product)
+    t_prod_a = timed(product)
     t_unsplit = timed(unsplit)
+    t_prod = 0.5 * (t_prod_a + timed(product))
     same = all(torch.equal(a.view(torch.int64), b.view(torch.int64)) for a, b in zip(*outs))
     gf = lambda t: 2.0 * m * n * k / t / 1e9
     rec = {
