@@ -84,6 +84,7 @@ _SIGNATURES = {
                             _vp, _sz, _vp]),
     "ddgemm_split_parts": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "ddgemm_split_first_row": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
+    "ddgemm_split_first_tile": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "ddgemm_status_string": (ctypes.c_char_p, [_st]),
     "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
 }
@@ -157,8 +158,13 @@ def split_parts(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:
 
 
 def split_first_row(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:
-    """First output row of the part split over k (m when not split)."""
+    """First row of the tile row holding the first split tile (m when not split)."""
     return lib.ddgemm_split_first_row(m, n, k, nslices)
+
+
+def split_first_tile(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:
+    """First output tile (row-major) split over k; the tiles before it run unsplit."""
+    return lib.ddgemm_split_first_tile(m, n, k, nslices)
 
 
 def slices_bytes(outer: int, k: int, nslices: int = NUM_SLICES) -> int:

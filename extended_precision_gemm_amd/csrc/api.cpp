@@ -142,6 +142,26 @@ int64_t qd_default_kblock(int64_t k) {
     return (k + blocks - 1) / blocks;
 }
 
+// The split tiles of a plan, from plan.first_tile on, are the rest of the tile
+// row holding it, from column c0, and every row below; their level planes
+// [ns][m - first_row][n] start at plan.first_row.  `piece(rows, cols, r, c,
+// levels)` renormalises the rows x cols block at output (r, c) whose level
+// sums start at `levels` (row stride n, plane stride (m - first_row) n).
+template <class Piece>
+hipError_t renorm_split_tiles(int64_t m, int64_t n, int ns, const SplitPlan& plan, const double* L, Piece&& piece) {
+    const GemmGeometry g = gemm_geometry(ns);
+    const int64_t tiles_n = (n + g.tile_n - 1) / g.tile_n;
+    const int64_t r0 = plan.first_row, mt = m - r0;
+    const int64_t c0 = plan.first_tile % tiles_n * g.tile_n;
+    int64_t done = 0;
+    if (c0 > 0) {  // the split tiles of the partly unsplit tile row
+        done = g.tile_m < mt ? g.tile_m : mt;
+        const hipError_t e = piece(done, n - c0, r0, c0, L + c0);
+        if (e != hipSuccess) return e;
+    }
+    return mt > done ? piece(mt - done, n, r0 + done, int64_t{0}, L + done * n) : hipSuccess;
+}
+
 // Plane c of X advanced by `off` entries (a missing plane stays missing).
 QdPlanes offset_planes(const QdPlanes& X, int64_t off) {
     QdPlanes r;
@@ -297,16 +317,19 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
         if (plan.parts > 1 && m - plan.first_row > split_rows) plan = SplitPlan{m, 1};
         if (plan.parts <= 1)
             return launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, d_hi, d_lo, ldd, true, st);
-        const int64_t r0 = plan.first_row, mt = m - r0;
         hipError_t err = hipSuccess;
-        if (r0 > 0)
-            err = launch_sliced_gemm(r0, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, d_hi, d_lo, ldd, true, st);
-        // rows r0.. of the packed A slices start at 16-row block r0 / 16
-        const double* A_tail = A_sl + (r0 / 16) * PackGeom(m, kc).KB * nslices * kFragDoubles;
-        if (err == hipSuccess) err = launch_sliced_gemm_split(mt, n, kc, nslices, A_tail, B_sl, L, n, plan.parts, st);
+        if (plan.first_tile > 0)  // whole rounds of tiles, unsplit
+            err = launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, d_hi, d_lo, ldd, true, st,
+                                     plan.first_tile);
         if (err == hipSuccess)
-            err = launch_levels_to_dd(mt, n, nslices, L, n, E + r0, F, d_hi + r0 * ldd, d_lo + r0 * ldd, ldd, st);
-        return err;
+            err = launch_sliced_gemm_split(m, n, kc, nslices, A_sl, B_sl, L, n, plan.parts, st, plan.first_tile);
+        if (err != hipSuccess) return err;
+        const int64_t plane = (m - plan.first_row) * n;
+        return renorm_split_tiles(m, n, nslices, plan, L, [&](int64_t rows, int64_t cols, int64_t r, int64_t c,
+                                                             const double* lv) {
+            return launch_levels_to_dd(rows, cols, nslices, lv, n, E + r, F + c, d_hi + r * ldd + c,
+                                       d_lo + r * ldd + c, ldd, st, plane);
+        });
     };
 
     // Block b covers k indices [b kb, min(k, (b+1) kb)): a separate sliced product
@@ -471,14 +494,18 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
         if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitSlices);
         if (e == hipSuccess) e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitSlices);
         const SplitPlan plan = split_plan(m, n, k, kQdSlices, true);
-        if (e == hipSuccess && plan.parts > 1) {  // tiles leave the chip partly idle: rows r0.. split over k
-            const int64_t r0 = plan.first_row, mt = m - r0;
-            if (r0 > 0) e = launch_qd_gemm(r0, n, k, A_sl, B_sl, E, F, out, ldc, s);
-            const double* A_tail = A_sl + (r0 / 16) * PackGeom(m, k).KB * kQdSlices * kFragDoubles;
-            OutPlanes out_tail = out;
-            for (int c = 0; c < 4; ++c) out_tail.c[c] = out.c[c] + r0 * ldc;
-            if (e == hipSuccess) e = launch_sliced_gemm_split(mt, n, k, kQdSlices, A_tail, B_sl, L, n, plan.parts, s);
-            if (e == hipSuccess) e = launch_levels_to_qd(mt, n, L, n, E + r0, F, out_tail, ldc, s);
+        if (e == hipSuccess && plan.parts > 1) {  // tiles leave the chip partly idle: the last ones split over k
+            if (plan.first_tile > 0) e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s, plan.first_tile);
+            if (e == hipSuccess)
+                e = launch_sliced_gemm_split(m, n, k, kQdSlices, A_sl, B_sl, L, n, plan.parts, s, plan.first_tile);
+            const int64_t plane = (m - plan.first_row) * n;
+            if (e == hipSuccess)
+                e = renorm_split_tiles(m, n, kQdSlices, plan, L, [&](int64_t rows, int64_t cols, int64_t r,
+                                                                     int64_t c, const double* lv) {
+                    OutPlanes piece_out = out;
+                    for (int q = 0; q < 4; ++q) piece_out.c[q] = out.c[q] + r * ldc + c;
+                    return launch_levels_to_qd(rows, cols, lv, n, E + r, F + c, piece_out, ldc, s, plane);
+                });
         } else if (e == hipSuccess) {
             e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s);
         }
@@ -556,6 +583,11 @@ int64_t ddgemm_split_first_row(int64_t m, int64_t n, int64_t k, int nslices) {
     if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return -1;
     const SplitPlan plan = split_plan(m, n, k, nslices, true);
     return plan.parts > 1 ? plan.first_row : m;
+}
+
+int64_t ddgemm_split_first_tile(int64_t m, int64_t n, int64_t k, int nslices) {
+    if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return -1;
+    return split_plan(m, n, k, nslices, true).first_tile;
 }
 
 ddgemm_status_t ddgemm_probe_mfma_f64(double* out, void* stream) {

@@ -60,7 +60,7 @@ hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const do
 hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                               const double* B_slices, double* levels, int64_t ldl,
                               const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
-                              int64_t ldc, bool fused, hipStream_t stream);
+                              int64_t ldc, bool fused, hipStream_t stream, int64_t tile_count = -1);
 hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
                          const int32_t* F, double* C_hi, double* C_lo, int64_t ldc,
                          hipStream_t stream);
@@ -77,23 +77,30 @@ GemmGeometry gemm_geometry(int ns);
 
 // Split over k for outputs whose tiles leave the chip partly idle: the k-parts' level sums
 // are added exactly (atomically, in any order) into zeroed level planes
-// [ns][rows][ldl], then turned into the result.  A plan computes output rows
-// [0, first_row) unsplit and rows [first_row, m) in `parts` k-parts; parts = 1:
-// no split.  Without `tail` the plan splits the whole product or nothing
-// (first_row = 0 when parts > 1); split_k_parts() is that plan's part count.
+// [ns][rows][ldl], then turned into the result.  A plan computes the output
+// tiles [0, first_tile) (row-major) in one unsplit launch and the tiles from
+// first_tile on in `parts` k-parts; first_row is the first row of first_tile's
+// tile row, where the level planes start.  parts = 1: no split (first_tile =
+// all tiles, first_row = m).  Without `tail` the plan splits the whole product
+// or nothing; split_k_parts() is that plan's part count.
 struct SplitPlan {
-    int64_t first_row, parts;
+    int64_t first_tile, first_row, parts;
 };
 SplitPlan split_plan(int64_t m, int64_t n, int64_t k, int ns, bool tail);
 int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns);
 hipError_t launch_zero_levels(int64_t m, int64_t n, int ns, double* levels, int64_t ldl, hipStream_t stream);
+// The k-parts of the tiles from tile_first on; their level planes hold the rows
+// from tile_first's tile row on (plane stride: those rows times ldl).
 hipError_t launch_sliced_gemm_split(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                                     const double* B_slices, double* levels, int64_t ldl, int64_t parts,
-                                    hipStream_t stream);
+                                    hipStream_t stream, int64_t tile_first = 0);
+// Level planes -> results for an m x n block of outputs; plane < 0: m * ldl.
 hipError_t launch_levels_to_dd(int64_t m, int64_t n, int ns, const double* levels, int64_t ldl, const int32_t* E,
-                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream);
+                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream,
+                               int64_t plane = -1);
 hipError_t launch_levels_to_qd(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
-                               const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream);
+                               const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream,
+                               int64_t plane = -1);
 hipError_t launch_dd_accumulate(int64_t m, int64_t n, double* C_hi, double* C_lo, int64_t ldc, const double* T_hi,
                                 const double* T_lo, int64_t ldt, hipStream_t stream);
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
@@ -117,6 +124,6 @@ hipError_t launch_qd_levels_to_units(int64_t m, int64_t n, const double* levels,
                                      hipStream_t stream);
 hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
                           const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
-                          hipStream_t stream);
+                          hipStream_t stream, int64_t tile_count = -1);
 
 }  // namespace ddg

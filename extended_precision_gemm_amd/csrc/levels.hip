@@ -116,23 +116,27 @@ hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl
 }
 
 hipError_t launch_levels_to_dd(int64_t m, int64_t n, int ns, const double* levels, int64_t ldl, const int32_t* E,
-                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream) {
+                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream,
+                               int64_t plane) {
     if (m == 0 || n == 0) return hipSuccess;
     if (ns < kMinSlices || ns > kMaxSlices) return hipErrorInvalidValue;
+    if (plane < 0) plane = m * ldl;
     const int64_t gy = m < 65535 ? m : 65535;
     const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
     return dispatch_ns(ns, [&](auto c) {
-        renorm_kernel<decltype(c)::value><<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C_hi, C_lo, ldc);
+        renorm_kernel<decltype(c)::value><<<grid, 256, 0, stream>>>(m, n, levels, ldl, plane, E, F, C_hi, C_lo, ldc);
         return hipGetLastError();
     });
 }
 
 hipError_t launch_levels_to_qd(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
-                               const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream) {
+                               const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream,
+                               int64_t plane) {
     if (m == 0 || n == 0) return hipSuccess;
+    if (plane < 0) plane = m * ldl;
     const int64_t gy = m < 65535 ? m : 65535;
     const dim3 grid(static_cast<unsigned>((n + 255) / 256), static_cast<unsigned>(gy));
-    qd_levels_kernel<<<grid, 256, 0, stream>>>(m, n, levels, ldl, m * ldl, E, F, C, ldc);
+    qd_levels_kernel<<<grid, 256, 0, stream>>>(m, n, levels, ldl, plane, E, F, C, ldc);
     return hipGetLastError();
 }
 

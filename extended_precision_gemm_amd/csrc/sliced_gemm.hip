@@ -90,7 +90,7 @@ enum Epilogue : int {
 // per CU): kWGS workgroups of kWaves waves.
 template <class C, int EPI>
 __global__ void __launch_bounds__(C::kThreads, C::kWGS * C::kWaves / 4)
-sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
+sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t tile0,
                    const double* __restrict__ Ap, const double* __restrict__ Bp,
                    double* __restrict__ levels, int64_t* __restrict__ units, int64_t ldl, int64_t plane,
                    const int32_t* __restrict__ E, const int32_t* __restrict__ F,
@@ -105,8 +105,10 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
     const int wave = threadIdx.x >> 6;
     const int wr = wave / C::kTBN;  // block rows RPW*wr .. RPW*wr+RPW-1 of the tile
     const int wc = wave % C::kTBN;  // block column wc of the tile
-    const int64_t tm = static_cast<int64_t>(blockIdx.x) / tiles_n;
-    const int64_t tn = static_cast<int64_t>(blockIdx.x) % tiles_n;
+    // the launch covers tiles tile0 .. tile0 + gridDim.x - 1, row-major over the output
+    const int64_t tile = static_cast<int64_t>(blockIdx.x) + tile0;
+    const int64_t tm = tile / tiles_n;
+    const int64_t tn = tile % tiles_n;
     const int64_t rb0 = tm * C::kTBM, cb0 = tn * C::kTBN;
     const int64_t nstages = KB / KS;  // KB is a multiple of 4 (k is packed to 16)
 
@@ -221,9 +223,11 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n,
                 } else if constexpr (EPI == kEpiAtomicLevels) {
                     // Every part's level sum is a multiple of 2^(-13(l+2)) and their
                     // total stays below 2^53 such units (the exact-sum bound on the
-                    // whole k), so the additions are exact in any order.
+                    // whole k), so the additions are exact in any order.  The planes
+                    // start at the first tile row of the launch.
+                    const int64_t lrow = row - (tile0 / tiles_n) * (C::kTBM * 16);
 #pragma unroll
-                    for (int l = 0; l < NS; ++l) atomicAdd(levels + l * plane + row * ldl + col, S[l]);
+                    for (int l = 0; l < NS; ++l) atomicAdd(levels + l * plane + lrow * ldl + col, S[l]);
                 } else if constexpr (EPI == kEpiDD || EPI == kEpiQD) {
                     const int sc = E[row] + F[col];
                     const int64_t idx = row * ldc + col;
@@ -301,21 +305,23 @@ template <> struct ConfigFor<16> { using type = GemmConfig<2, 4, 1, 2, 1, 16, 1>
 template <int NS>
 hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
                           double* levels, int64_t ldl, const int32_t* E, const int32_t* F, double* C_hi,
-                          double* C_lo, int64_t ldc, bool fused, hipStream_t stream) {
+                          double* C_lo, int64_t ldc, bool fused, hipStream_t stream, int64_t tile_count) {
     using Cfg = typename ConfigFor<NS>::type;
     const PackGeom ga(m, k);
     constexpr int BM = Cfg::kTBM * 16, BN = Cfg::kTBN * 16;
     const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
-    const int64_t tiles = tiles_m * tiles_n;
+    int64_t tiles = tiles_m * tiles_n;
+    if (tile_count >= 0 && tile_count < tiles) tiles = tile_count;  // the first tile_count tiles only
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (tiles == 0) return hipSuccess;
     const int64_t plane = m * ldl;
     if (fused)
         sliced_gemm_kernel<Cfg, kEpiDD><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, nullptr, 0, 0, E, F,
+            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, nullptr, 0, 0, E, F,
             OutPlanes{{C_hi, C_lo, nullptr, nullptr}}, ldc);
     else if constexpr (NS == kSlices)
         sliced_gemm_kernel<Cfg, kEpiLevels><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, A_slices, B_slices, levels, nullptr, ldl, plane, nullptr, nullptr,
+            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, levels, nullptr, ldl, plane, nullptr, nullptr,
             OutPlanes{{nullptr, nullptr, nullptr, nullptr}}, 0);
     else
         return hipErrorInvalidValue;  // level planes are offered for the double-double product only
@@ -324,18 +330,23 @@ hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slice
 
 template <int NS>
 hipError_t launch_split_ns(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
-                           double* levels, int64_t ldl, int64_t parts, hipStream_t stream) {
+                           double* levels, int64_t ldl, int64_t parts, hipStream_t stream, int64_t tile_first) {
     using Cfg = typename ConfigFor<NS>::type;
     const PackGeom ga(m, k);
+    constexpr int BM = Cfg::kTBM * 16;
     const int64_t tiles_n = (n + Cfg::kTBN * 16 - 1) / (Cfg::kTBN * 16);
-    const int64_t tiles = (m + Cfg::kTBM * 16 - 1) / (Cfg::kTBM * 16) * tiles_n;
-    if (tiles > 0x7FFFFFFF || parts < 1 || parts > 65535) return hipErrorInvalidValue;
-    const int64_t plane = m * ldl;
-    hipError_t err = launch_zero_levels(m, n, NS, levels, ldl, stream);
+    const int64_t tiles = (m + BM - 1) / BM * tiles_n;
+    if (tiles > 0x7FFFFFFF || parts < 1 || parts > 65535 || tile_first < 0 || tile_first >= tiles)
+        return hipErrorInvalidValue;
+    // the level planes hold rows row0 .. m-1, row0 the first row of tile_first's tile row
+    const int64_t row0 = tile_first / tiles_n * BM;
+    const int64_t plane = (m - row0) * ldl;
+    hipError_t err = launch_zero_levels(m - row0, n, NS, levels, ldl, stream);
     if (err != hipSuccess) return err;
-    const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(parts));
+    const dim3 grid(static_cast<unsigned>(tiles - tile_first), static_cast<unsigned>(parts));
     sliced_gemm_kernel<Cfg, kEpiAtomicLevels><<<grid, Cfg::kThreads, 0, stream>>>(
-        m, n, ga.KB, tiles_n, A_slices, B_slices, levels, nullptr, ldl, plane, nullptr, nullptr, OutPlanes{}, 0);
+        m, n, ga.KB, tiles_n, tile_first, A_slices, B_slices, levels, nullptr, ldl, plane, nullptr, nullptr,
+        OutPlanes{}, 0);
     return hipGetLastError();
 }
 
@@ -344,37 +355,28 @@ hipError_t launch_split_ns(int64_t m, int64_t n, int64_t k, const double* A_slic
 hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                               const double* B_slices, double* levels, int64_t ldl,
                               const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
-                              int64_t ldc, bool fused, hipStream_t stream) {
+                              int64_t ldc, bool fused, hipStream_t stream, int64_t tile_count) {
     if (m == 0 || n == 0) return hipSuccess;
-    switch (ns) {
-        case 4: return launch_gemm_ns<4>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 5: return launch_gemm_ns<5>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 6: return launch_gemm_ns<6>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 7: return launch_gemm_ns<7>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 8: return launch_gemm_ns<8>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 9: return launch_gemm_ns<9>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 10: return launch_gemm_ns<10>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 11: return launch_gemm_ns<11>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 12: return launch_gemm_ns<12>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 13: return launch_gemm_ns<13>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 14: return launch_gemm_ns<14>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 15: return launch_gemm_ns<15>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        case 16: return launch_gemm_ns<16>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc, fused, stream);
-        default: return hipErrorInvalidValue;
-    }
+    if (ns < kMinSlices || ns > kMaxSlices) return hipErrorInvalidValue;
+    return dispatch_ns(ns, [&](auto c) {
+        return launch_gemm_ns<decltype(c)::value>(m, n, k, A_slices, B_slices, levels, ldl, E, F, C_hi, C_lo, ldc,
+                                                  fused, stream, tile_count);
+    });
 }
 
 hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
                           const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
-                          hipStream_t stream) {
+                          hipStream_t stream, int64_t tile_count) {
     if (m == 0 || n == 0) return hipSuccess;
     using Cfg = ConfigFor<kQdSlices>::type;
     const PackGeom ga(m, k);
     const int64_t tiles_n = (n + Cfg::kTBN * 16 - 1) / (Cfg::kTBN * 16);
-    const int64_t tiles = (m + Cfg::kTBM * 16 - 1) / (Cfg::kTBM * 16) * tiles_n;
+    int64_t tiles = (m + Cfg::kTBM * 16 - 1) / (Cfg::kTBM * 16) * tiles_n;
+    if (tile_count >= 0 && tile_count < tiles) tiles = tile_count;  // the first tile_count tiles only
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (tiles == 0) return hipSuccess;
     sliced_gemm_kernel<Cfg, kEpiQD><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
-        m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, nullptr, 0, 0, E, F, C, ldc);
+        m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, nullptr, 0, 0, E, F, C, ldc);
     return hipGetLastError();
 }
 
@@ -391,13 +393,13 @@ hipError_t launch_qd_gemm_block(int64_t m, int64_t n, int64_t k, const double* A
     const int64_t plane = m * n;  // level plane l of the int64 sums: units[l][row][col], row stride n
     if (step == kQdFirstBlock)
         sliced_gemm_kernel<Cfg, kEpiUnitsSet><<<g, Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0);
+            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0);
     else if (step == kQdMiddleBlock)
         sliced_gemm_kernel<Cfg, kEpiUnitsAdd><<<g, Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0);
+            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0);
     else
         sliced_gemm_kernel<Cfg, kEpiUnitsQD><<<g, Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, A_slices, B_slices, nullptr, units, n, plane, E, F, C, ldc);
+            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, units, n, plane, E, F, C, ldc);
     return hipGetLastError();
 }
 
@@ -412,11 +414,12 @@ GemmGeometry gemm_geometry(int ns) {
 
 hipError_t launch_sliced_gemm_split(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                                     const double* B_slices, double* levels, int64_t ldl, int64_t parts,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, int64_t tile_first) {
     if (m == 0 || n == 0) return hipSuccess;
     if (ns < kMinSlices || ns > kMaxSlices) return hipErrorInvalidValue;
     return dispatch_ns(ns, [&](auto c) {
-        return launch_split_ns<decltype(c)::value>(m, n, k, A_slices, B_slices, levels, ldl, parts, stream);
+        return launch_split_ns<decltype(c)::value>(m, n, k, A_slices, B_slices, levels, ldl, parts, stream,
+                                                   tile_first);
     });
 }
 

@@ -104,15 +104,16 @@ size_t dd_split_slices_bytes(int64_t outer, int64_t k);
  * operands and both exponent vectors, each region 256-byte aligned); 0 for
  * negative sizes.  When the output tiles (64×64; 32×64 with 6 or 9..16 slices)
  * leave part of the chip idle -- a few tiles, or a last round of 256
- * workgroups far from full -- the output rows from some first row r on (r = 0:
- * all of them) may be split over k into p parts of at least 16 stages each (a
- * stage is 8 values of k, 4 from 14 slices on), p <= 256, while the rows
- * before r, whole tile rows, run unsplit; r and p are chosen by a timing model
- * of the rounds of workgroups, the atomic adds and the level planes, and only
- * where that saves at least 5 %; outputs that fill whole rounds never split.
- * ddgemm_split_parts returns p and ddgemm_split_first_row r.  The parts add
- * their exact level sums into level planes, and the workspace also holds those
- * nslices (m - r)×n planes.  The split result is bit-identical to the unsplit
+ * workgroups far from full -- the output tiles from some first tile t on
+ * (row-major; t = 0: all of them) may be split over k into p parts of at least
+ * 16 stages each (a stage is 8 values of k, 4 from 14 slices on), p <= 256,
+ * while the tiles before t, whole rounds of 256 workgroups, run unsplit; t and
+ * p are chosen by a timing model of the rounds of workgroups, the atomic adds
+ * and the level planes, and only where that saves at least 5 %; outputs that
+ * fill whole rounds never split.  ddgemm_split_parts returns p,
+ * ddgemm_split_first_tile t and ddgemm_split_first_row the first row r of t's
+ * tile row.  The parts add their exact level sums into level planes, and the
+ * workspace also holds those nslices (m - r)×n planes.  The split result is bit-identical to the unsplit
  * one. */
 size_t dd_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 
@@ -262,13 +263,16 @@ const char* ddgemm_status_string(ddgemm_status_t status);
 /* Diagnostics: how the product entry points (dd_gemm*, and with nslices = 16
  * the quad-double ones) split an m×n×k product, or one k-block of k values,
  * with nslices slices over k: ddgemm_split_parts gives the number of k-parts
- * (1 = not split; 0 for invalid sizes or slice counts), ddgemm_split_first_row
- * the first output row of the split part (the rows before it run unsplit; m
- * when the product is not split; -1 for invalid arguments).  dd_sliced_gemm
+ * (1 = not split; 0 for invalid sizes or slice counts), ddgemm_split_first_tile
+ * the first split output tile (tiles row-major; the tiles before it run unsplit;
+ * the number of tiles when the product is not split) and ddgemm_split_first_row
+ * the first row of that tile's tile row (m when not split); -1 for invalid
+ * arguments.  dd_sliced_gemm
  * and the blocks of a blocked quad-double product split all rows or none, with
  * the part count of the plan whose first row is 0.  Host-only, needs no device. */
 int64_t ddgemm_split_parts(int64_t m, int64_t n, int64_t k, int nslices);
 int64_t ddgemm_split_first_row(int64_t m, int64_t n, int64_t k, int nslices);
+int64_t ddgemm_split_first_tile(int64_t m, int64_t n, int64_t k, int nslices);
 
 /* Diagnostics: runs one FP64 16x16x4 matrix instruction on one wave with
  * a-operand lane value (lane + 1) and b-operand lane value 100 * (lane + 1) and

@@ -65,10 +65,10 @@ size_t qd_split_slices_bytes(int64_t outer, int64_t k);
 
 /* Workspace bytes qd_gemm_ws needs (slices of both operands for one k-block,
  * both exponent vectors and, when k needs more than one block, sixteen int64
- * m×n level planes, or when a product of one block splits its rows from r on
- * over k as in ddgemm.h (ddgemm_split_parts / ddgemm_split_first_row with 16
- * slices), sixteen double (m - r)×n level planes (the blocks of a blocked
- * product split all rows or none: r = 0);
+ * m×n level planes, or when a product of one block splits its tiles from some
+ * tile on over k as in ddgemm.h (ddgemm_split_parts / ddgemm_split_first_row
+ * with 16 slices: r), sixteen double (m - r)×n level planes (the blocks of a
+ * blocked product split all tiles or none: r = 0);
  * 256-byte aligned regions); 0 for negative sizes or k > QDGEMM_K_MAX_BLOCKED.  The _kb form is for qd_gemm_ws_kb with k-blocks of
  * kblock terms (0 for kblock outside [1, QDGEMM_K_MAX] when k > 0). */
 size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k);

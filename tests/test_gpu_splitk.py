@@ -221,15 +221,20 @@ def _sample(rng, size, must):
 
 
 @pytest.mark.parametrize("m,n,k,ns", [(1150, 1160, 1152, 8), (1536, 1024, 2048, 8), (1280, 1280, 1280, 6),
-                                      (1300, 1300, 1300, 12)])
+                                      (1300, 1300, 1300, 12), (2500, 2600, 900, 8), (1800, 1700, 1500, 8),
+                                      (1300, 1700, 1100, 12)])
 def test_split_of_the_last_rows_only(gpu, m, n, k, ns):
-    """Plans that run the leading whole tile rows unsplit and split only the
-    rows from the plan's first split row on: the product equals the unsplit
-    fused stage call on every entry and the oracle's chain on sampled rows and
-    columns (rows on both sides of the first split row included), bit for bit."""
+    """Plans that run whole rounds of leading tiles unsplit and split only the
+    tiles from the plan's first split tile on -- from the start of a tile row,
+    or from inside one (the rest of that row, then the rows below it, including
+    a last tile row of only 8 rows): the product equals the unsplit fused stage
+    call on every entry and the oracle's chain on sampled rows and columns on
+    both sides of the first split tile, bit for bit."""
     r0, parts = gpu.split_first_row(m, n, k, ns), gpu.split_parts(m, n, k, ns)
+    t0 = gpu.split_first_tile(m, n, k, ns)
+    c0 = t0 % -(-n // 64) * 64
     assert 0 < r0 < m and parts > 1
-    _say(f"[split tail] {m}x{n}x{k} nslices={ns} first split row={r0} parts={parts}")
+    _say(f"[split tail] {m}x{n}x{k} nslices={ns} first split tile={t0} row={r0} col={c0} parts={parts}")
     Ah, Al = workloads.random_dd((m, k), 9700 + m, "signed_exp20")
     Bh, Bl = workloads.random_dd((k, n), 9701 + n, "normal")
     dAh, dAl, dBh, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
@@ -241,7 +246,7 @@ def test_split_of_the_last_rows_only(gpu, m, n, k, ns):
     assert _bits_equal(hCh, _host(Uh)) and _bits_equal(hCl, _host(Ul))
     rng = np.random.default_rng(m + n + k + ns)
     rows = _sample(rng, m, [0, r0 - 1, r0, r0 + 1, m - 1])
-    cols = _sample(rng, n, [0, n - 1])
+    cols = _sample(rng, n, [0, c0 - 1, c0, n - 1])
     E_ref, DA = exact.slice_rows(Ah, Al, rows, ns)
     F_ref, DB = exact.slice_cols(Bh, Bl, cols, ns)
     Rh, Rl = exact.renorm_levels(exact.level_values(exact.level_sums_units(DA, DB)), E_ref, F_ref)
@@ -268,7 +273,7 @@ def test_blocked_product_whose_blocks_split_their_last_rows(gpu, kblock):
     assert _bits_equal(hCh[np.ix_(rows, cols)], Rh) and _bits_equal(hCl[np.ix_(rows, cols)], Rl)
 
 
-@pytest.mark.parametrize("m,n,k", [(800, 900, 700), (768, 768, 768)])
+@pytest.mark.parametrize("m,n,k", [(800, 900, 700), (768, 768, 768), (1000, 1800, 700), (900, 1700, 1000)])
 def test_qd_split_of_the_last_rows_only(gpu, m, n, k):
     """The quad-double product with only its last rows split over k: equal to
     the unsplit fused call everywhere and to the oracle on sampled entries."""
@@ -285,7 +290,8 @@ def test_qd_split_of_the_last_rows_only(gpu, m, n, k):
     assert _bits_equal(C, _host(gpu.qd_sliced_gemm_renorm(m, n, k, As, E, Bs, F)))
     del As, Bs
     torch.cuda.empty_cache()
-    for i, j in [(0, 0), (r0 - 1, n - 1), (r0, 3), (m - 1, n // 2)]:
+    c0 = gpu.split_first_tile(m, n, k, 16) % -(-n // 64) * 64
+    for i, j in [(0, 0), (r0 - 1, n - 1), (r0, 3), (m - 1, n // 2), (r0, max(c0 - 1, 0)), (r0, c0), (m - 1, n - 1)]:
         Ei, DA = qd.slice_rows(A, rows=[i])
         Fj, DB = qd.slice_cols(B, cols=[j])
         ref = qd.renorm_levels(qd.level_sums(DA, DB), Ei, Fj)[:, 0, 0]
