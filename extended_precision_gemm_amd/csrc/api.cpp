@@ -15,6 +15,29 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// A workspace as a sum of 256-byte aligned regions, each a product of sizes in
+// bytes.  The size bound of the arguments (2^58 elements per matrix) does not
+// keep 16 level planes of 8-byte sums within 64 bits, so every product and the
+// total are checked: past 2^62 bytes the workspace is reported as 0 bytes (no
+// such workspace exists), and the entry points reject the sizes.
+class Workspace {
+  public:
+    Workspace& add(uint64_t a, uint64_t b = 1, uint64_t c = 1) {
+        uint64_t x = 0;
+        if (__builtin_mul_overflow(a, b, &x) || __builtin_mul_overflow(x, c, &x) || x > kMaxBytes)
+            ok_ = false;
+        else if ((total_ += align_up(x)) > kMaxBytes)
+            ok_ = false;
+        return *this;
+    }
+    size_t bytes() const { return ok_ ? total_ : 0; }
+
+  private:
+    static constexpr uint64_t kMaxBytes = uint64_t(1) << 62;
+    uint64_t total_ = 0;
+    bool ok_ = true;
+};
+
 // Elements spanned by a rows×cols matrix with row stride ld (0 when empty).
 inline int64_t extent(int64_t rows, int64_t cols, int64_t ld) {
     return (rows == 0 || cols == 0) ? 0 : (rows - 1) * ld + cols;
@@ -183,15 +206,13 @@ size_t dd_split_slices_bytes(int64_t outer, int64_t k) { return dd_split_slices_
 size_t dd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock) {
     if (validate_sizes(m, n, k) != DDGEMM_SUCCESS || !ns_ok(nslices) || !kblock_ok(k, nslices, kblock)) return 0;
     const int64_t kb = k < kblock ? k : kblock;
-    size_t bytes = align_up(dd_split_slices_bytes_ns(m, kb, nslices)) +
-                   align_up(dd_split_slices_bytes_ns(n, kb, nslices)) + align_up(static_cast<size_t>(m) * 4) +
-                   align_up(static_cast<size_t>(n) * 4);
-    if (block_count(k, kblock) > 1) bytes += 2 * align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
+    Workspace ws;
+    ws.add(dd_split_slices_bytes_ns(m, kb, nslices)).add(dd_split_slices_bytes_ns(n, kb, nslices));
+    ws.add(m, 4).add(n, 4);
+    if (block_count(k, kblock) > 1) ws.add(m, n, 8).add(m, n, 8);  // (hi, lo) of the blocks after the first
     const SplitPlan plan = split_plan(m, n, kb, nslices, true);
-    if (plan.parts > 1)  // level planes of the rows split over k
-        bytes += align_up(static_cast<size_t>(nslices) * static_cast<size_t>(m - plan.first_row) *
-                          static_cast<size_t>(n) * 8);
-    return bytes;
+    if (plan.parts > 1) ws.add(nslices, m - plan.first_row, n * 8);  // level planes of the rows split over k
+    return ws.bytes();
 }
 
 size_t dd_gemm_workspace_size_ns(int64_t m, int64_t n, int64_t k, int nslices) {
@@ -287,6 +308,7 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
             return DDGEMM_ERROR_INVALID_VALUE;
     if (overlaps(C_hi, ce, C_lo, ce)) return DDGEMM_ERROR_INVALID_VALUE;
     const size_t need = dd_gemm_workspace_size_kb(m, n, k, nslices, kblock);
+    if (need == 0) return DDGEMM_ERROR_INVALID_VALUE;  // the workspace would pass 2^62 bytes
     if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return DDGEMM_ERROR_WORKSPACE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
@@ -313,9 +335,9 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
     // plan.first_row on split over k into the level planes and renormalised
     // after (the rows before it fused, in one launch over whole tile rows).
     auto block_gemm = [&](int64_t kc, double* d_hi, double* d_lo, int64_t ldd, hipStream_t st) {
-        SplitPlan plan = split_rows == 0 ? SplitPlan{m, 1} : (kc == kb ? plan_kb : split_plan(m, n, kc, nslices, true));
-        if (plan.parts > 1 && m - plan.first_row > split_rows) plan = SplitPlan{m, 1};
-        if (plan.parts <= 1)
+        // a block whose plan needs more rows of level planes than the workspace holds runs unsplit
+        const SplitPlan plan = kc == kb ? plan_kb : split_plan(m, n, kc, nslices, true);
+        if (plan.parts <= 1 || m - plan.first_row > split_rows)
             return launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, d_hi, d_lo, ldd, true, st);
         hipError_t err = hipSuccess;
         if (plan.first_tile > 0)  // whole rounds of tiles, unsplit
@@ -385,9 +407,10 @@ ddgemm_status_t dd_gemm(int64_t m, int64_t n, int64_t k, const double* A_hi, con
     if (!ld_ok(lda, m, k) || !ld_ok(ldb, k, n) || !ld_ok(ldc, m, n)) return DDGEMM_ERROR_INVALID_VALUE;
     if (m == 0 || n == 0) return DDGEMM_SUCCESS;
     if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return DDGEMM_ERROR_INVALID_VALUE;
+    const size_t need = dd_gemm_workspace_size(m, n, k);
+    if (need == 0) return DDGEMM_ERROR_INVALID_VALUE;  // the workspace would pass 2^62 bytes
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t need = dd_gemm_workspace_size(m, n, k);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, need, s) != hipSuccess || !ws) return DDGEMM_ERROR_WORKSPACE;
     st = dd_gemm_ws(m, n, k, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc, ws, need, stream);
@@ -406,13 +429,12 @@ size_t qd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int64_t kblock
     const bool blocked = block_count(k, kb) > 1;
     // a blocked product's blocks split whole or not at all; one block may split its later rows only
     const SplitPlan plan = split_plan(m, n, kb, kQdSlices, !blocked);
-    const size_t planes = static_cast<size_t>(m) * static_cast<size_t>(n) * 8 * QDGEMM_NUM_LEVELS;
-    const size_t split_planes =
-        static_cast<size_t>(m - plan.first_row) * static_cast<size_t>(n) * 8 * QDGEMM_NUM_LEVELS;
-    // int64 level planes of a blocked product; double level planes of the rows split over k
-    return align_up(qd_split_slices_bytes(m, kb)) + align_up(qd_split_slices_bytes(n, kb)) +
-           align_up(static_cast<size_t>(m) * 4) + align_up(static_cast<size_t>(n) * 4) +
-           (blocked ? align_up(planes) : 0) + (plan.parts > 1 ? align_up(split_planes) : 0);
+    Workspace ws;
+    ws.add(qd_split_slices_bytes(m, kb)).add(qd_split_slices_bytes(n, kb)).add(m, 4).add(n, 4);
+    if (blocked) ws.add(QDGEMM_NUM_LEVELS, m, n * 8);  // int64 level planes of a blocked product
+    if (plan.parts > 1)                                // double level planes of the rows split over k
+        ws.add(QDGEMM_NUM_LEVELS, m - plan.first_row, n * 8);
+    return ws.bytes();
 }
 
 size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
@@ -467,6 +489,7 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
             if (overlaps(out.c[c], ce, pa.x[q], ae) || overlaps(out.c[c], ce, pb.x[q], be))
                 return DDGEMM_ERROR_INVALID_VALUE;
     const size_t need = qd_gemm_workspace_size_kb(m, n, k, kblock);
+    if (need == 0) return DDGEMM_ERROR_INVALID_VALUE;  // the workspace would pass 2^62 bytes
     if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return DDGEMM_ERROR_WORKSPACE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
@@ -553,9 +576,10 @@ ddgemm_status_t qd_gemm(int64_t m, int64_t n, int64_t k, const double* const A[4
     if ((st = read_qd_planes(A, m * k, pa)) != DDGEMM_SUCCESS) return st;
     if ((st = read_qd_planes(B, k * n, pb)) != DDGEMM_SUCCESS) return st;
     if ((st = read_out_planes(C, extent(m, n, ldc), out)) != DDGEMM_SUCCESS) return st;
+    const size_t need = qd_gemm_workspace_size(m, n, k);
+    if (need == 0) return DDGEMM_ERROR_INVALID_VALUE;  // the workspace would pass 2^62 bytes
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const size_t need = qd_gemm_workspace_size(m, n, k);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, need, s) != hipSuccess || !ws) return DDGEMM_ERROR_WORKSPACE;
     st = qd_gemm_ws(m, n, k, A, lda, B, ldb, C, ldc, ws, need, stream);

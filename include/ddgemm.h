@@ -102,7 +102,8 @@ size_t dd_split_slices_bytes(int64_t outer, int64_t k);
 
 /* Workspace bytes dd_gemm_ws needs for an m×k by k×n product (slices of both
  * operands and both exponent vectors, each region 256-byte aligned); 0 for
- * negative sizes.  When the output tiles (64×64; 32×64 with 6 or 9..16 slices)
+ * negative sizes, and for sizes whose workspace would pass 2^62 bytes (the
+ * products reject those with DDGEMM_ERROR_INVALID_VALUE).  When the output tiles (64×64; 32×64 with 6 or 9..16 slices)
  * leave part of the chip idle -- a few tiles, or a last round of 256
  * workgroups far from full -- the output tiles from some first tile t on
  * (row-major; t = 0: all of them) may be split over k into p parts of at least

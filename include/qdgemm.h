@@ -69,7 +69,8 @@ size_t qd_split_slices_bytes(int64_t outer, int64_t k);
  * tile on over k as in ddgemm.h (ddgemm_split_parts / ddgemm_split_first_row
  * with 16 slices: r), sixteen double (m - r)×n level planes (the blocks of a
  * blocked product split all tiles or none: r = 0);
- * 256-byte aligned regions); 0 for negative sizes or k > QDGEMM_K_MAX_BLOCKED.  The _kb form is for qd_gemm_ws_kb with k-blocks of
+ * 256-byte aligned regions); 0 for negative sizes, k > QDGEMM_K_MAX_BLOCKED, or a workspace past 2^62 bytes (which
+ * qd_gemm_ws and qd_gemm reject with DDGEMM_ERROR_INVALID_VALUE).  The _kb form is for qd_gemm_ws_kb with k-blocks of
  * kblock terms (0 for kblock outside [1, QDGEMM_K_MAX] when k > 0). */
 size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 size_t qd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int64_t kblock);

@@ -247,6 +247,28 @@ def test_leading_dimensions_whose_extent_would_overflow_are_rejected(ddg):
     assert L.dd_split_balanced(1, 4, P[0], None, 1 << 58, 0, P[1], P[2], None) in (ddg.ERROR_DEVICE, 0)
 
 
+def test_workspaces_past_2_62_bytes_are_rejected(ddg):
+    """Sizes within the 2^58-element bound whose workspace would not fit 64-bit
+    byte counts (sixteen m x n level planes of 8 bytes at m n = 2^58: 2^65
+    bytes) have no workspace size (0), and the products reject them before any
+    device call instead of accepting a wrapped-around size."""
+    L = ddg.lib
+    INV = ddg.ERROR_INVALID_VALUE
+    m = n = 1 << 29
+    assert L.qd_gemm_workspace_size(m, n, ddg.QD_K_MAX + 1) == 0
+    assert L.dd_gemm_workspace_size(m, n, ddg.K_MAX + 1) == 0
+    assert L.dd_gemm_workspace_size(m >> 4, n, ddg.K_MAX + 1) > 1 << 58
+    # disjoint operands: A, B at 2^56, 2^57 (2^55 bytes each), output planes of 2^61 bytes from 2^61 on
+    k = ddg.K_MAX + 1
+    A, B, Ch, Cl = 1 << 56, 1 << 57, 1 << 61, 1 << 62
+    assert L.dd_gemm_ws(m, n, k, A, None, k, B, None, n, Ch, Cl, n, P[0], 1 << 30, None) == INV
+    assert L.dd_gemm(m, n, k, A, None, k, B, None, n, Ch, Cl, n, None) == INV
+    kq = ddg.QD_K_MAX + 1
+    C = _arr(1 << 61, 1 << 62, 3 << 61, 1 << 63)
+    assert L.qd_gemm_ws(m, n, kq, _arr(A), kq, _arr(B), n, C, n, P[0], 1 << 30, None) == INV
+    assert L.qd_gemm(m, n, kq, _arr(A), kq, _arr(B), n, C, n, None) == INV
+
+
 def test_layout_pack_unpack_roundtrip(ddg):
     from extended_precision_gemm_amd import layout
     rng = np.random.default_rng(0)
