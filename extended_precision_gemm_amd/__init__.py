@@ -139,6 +139,29 @@ def _matrix(t, name, shape=None):
     return max(t.stride(0), cols, 1) if rows > 1 else max(cols, 1)
 
 
+def _device(*tensors):
+    """The one device of the given tensors (None entries skipped).  The library
+    runs on the current device, so each product is called under this one."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"operands and results must be on one device, got {sorted(map(str, devs))}")
+    return devs.pop()
+
+
+def _workspace(workspace, need, dev):
+    """A caller's workspace (uint8, contiguous, on the operands' device), or a
+    new one of `need` bytes from PyTorch's allocator."""
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.dtype != torch.uint8:
+        raise TypeError(f"workspace must be uint8, got {workspace.dtype}")
+    if workspace.device != dev:
+        raise ValueError(f"workspace must be a device tensor on {dev}, got {workspace.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace
+
+
 def _check_lo(lo, hi, name):
     if lo is None:
         return
@@ -252,12 +275,12 @@ def _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo):
     k2, n = B_hi.shape
     if k != k2:
         raise ValueError(f"inner dimensions differ: {k} vs {k2}")
-    dev = A_hi.device
+    dev = _device(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
     C_hi = torch.empty((m, n), dtype=torch.float64, device=dev) if C_hi is None else C_hi
     C_lo = torch.empty((m, n), dtype=torch.float64, device=dev) if C_lo is None else C_lo
     ldc = _matrix(C_hi, "C_hi", (m, n))
     _check_lo(C_lo, C_hi, "C_lo")
-    return m, n, k, lda, ldb, ldc, C_hi, C_lo
+    return m, n, k, lda, ldb, ldc, C_hi, C_lo, dev
 
 
 def dd_gemm(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, workspace=None, stream=None,
@@ -269,10 +292,14 @@ def dd_gemm(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, workspace=None, stream
     blocked automatically).
     The workspace comes from PyTorch's allocator unless a uint8 device tensor of
     at least workspace_size(m, n, k, nslices) bytes is given."""
-    m, n, k, lda, ldb, ldc, C_hi, C_lo = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
-    need = workspace_size(m, n, k, nslices, kblock)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=A_hi.device)
+    m, n, k, lda, ldb, ldc, C_hi, C_lo, dev = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
+    workspace = _workspace(workspace, workspace_size(m, n, k, nslices, kblock), dev)
+    with torch.cuda.device(dev):
+        _dd_gemm_call(m, n, k, nslices, kblock, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc, workspace, stream)
+    return C_hi, C_lo
+
+
+def _dd_gemm_call(m, n, k, nslices, kblock, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc, workspace, stream):
     if kblock is not None:
         _check(lib.dd_gemm_ws_kb(m, n, k, nslices, kblock, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo),
                                  ldb, _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(),
@@ -283,14 +310,14 @@ def dd_gemm(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, workspace=None, stream
     else:
         _check(lib.dd_gemm_ws_ns(m, n, k, nslices, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
                                  _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(), _stream(stream)))
-    return C_hi, C_lo
 
 
 def dd_gemm_alloc(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, stream=None):
     """C = A·B through the entry point that allocates its own (stream-ordered) workspace."""
-    m, n, k, lda, ldb, ldc, C_hi, C_lo = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
-    _check(lib.dd_gemm(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
-                       _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
+    m, n, k, lda, ldb, ldc, C_hi, C_lo, dev = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
+    with torch.cuda.device(dev):
+        _check(lib.dd_gemm(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
+                           _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
     return C_hi, C_lo
 
 
@@ -368,8 +395,9 @@ def _qd_gemm_args(A, B, C):
     k2, n = b[0].shape
     if k != k2:
         raise ValueError(f"inner dimensions differ: {k} vs {k2}")
-    C, ldc, pc = _qd_out(C, m, n, a[0].device)
-    return m, n, k, pa, lda, pb, ldb, C, pc, ldc
+    dev = _device(*a, *b, *(C if C is not None else []))
+    C, ldc, pc = _qd_out(C, m, n, dev)
+    return m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev
 
 
 def qd_gemm(A, B, C=None, workspace=None, stream=None, kblock: int | None = None):
@@ -378,23 +406,23 @@ def qd_gemm(A, B, C=None, workspace=None, stream=None, kblock: int | None = None
     uint8 device tensor of at least qd_workspace_size(m, n, k, kblock) bytes is
     given.  ``kblock`` runs the product in k-blocks of that many terms (the
     result does not depend on it); by default k is split only beyond QD_K_MAX."""
-    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _qd_gemm_args(A, B, C)
-    need = qd_workspace_size(m, n, k, kblock)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
-    if kblock is None:
-        _check(lib.qd_gemm_ws(m, n, k, pa, lda, pb, ldb, pc, ldc, _ptr(workspace), workspace.numel(),
-                              _stream(stream)))
-    else:
-        _check(lib.qd_gemm_ws_kb(m, n, k, kblock, pa, lda, pb, ldb, pc, ldc, _ptr(workspace), workspace.numel(),
-                                 _stream(stream)))
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _qd_gemm_args(A, B, C)
+    workspace = _workspace(workspace, qd_workspace_size(m, n, k, kblock), dev)
+    with torch.cuda.device(dev):
+        if kblock is None:
+            _check(lib.qd_gemm_ws(m, n, k, pa, lda, pb, ldb, pc, ldc, _ptr(workspace), workspace.numel(),
+                                  _stream(stream)))
+        else:
+            _check(lib.qd_gemm_ws_kb(m, n, k, kblock, pa, lda, pb, ldb, pc, ldc, _ptr(workspace),
+                                     workspace.numel(), _stream(stream)))
     return C
 
 
 def qd_gemm_alloc(A, B, C=None, stream=None):
     """C = A·B through the entry point that allocates its own (stream-ordered) workspace."""
-    m, n, k, pa, lda, pb, ldb, C, pc, ldc = _qd_gemm_args(A, B, C)
-    _check(lib.qd_gemm(m, n, k, pa, lda, pb, ldb, pc, ldc, _stream(stream)))
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _qd_gemm_args(A, B, C)
+    with torch.cuda.device(dev):
+        _check(lib.qd_gemm(m, n, k, pa, lda, pb, ldb, pc, ldc, _stream(stream)))
     return C
 
 

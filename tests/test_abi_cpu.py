@@ -434,3 +434,22 @@ def test_binding_rejects_host_and_wrong_dtype_tensors(ddg):
         ddg.qd_gemm([None, a64], [a64])
     with pytest.raises(ValueError, match="device tensor"):
         ddg.qd_gemm(torch.zeros((4, 3, 3), dtype=torch.float64), [a64])
+
+
+def test_binding_checks_devices_and_the_callers_workspace(ddg):
+    """Operands and results of a product share one device, on which the call
+    runs; a caller's workspace is a contiguous uint8 tensor on that device (a
+    host buffer would hand the kernels a host pointer)."""
+    import torch
+    cpu = torch.device("cpu")
+    with pytest.raises(ValueError, match="one device"):
+        ddg._device(torch.zeros(1), None, torch.zeros(1, device="meta"))
+    assert ddg._device(torch.zeros(1), None, torch.zeros(2)) == cpu
+    with pytest.raises(TypeError, match="uint8"):
+        ddg._workspace(torch.zeros(4, dtype=torch.float64), 8, cpu)
+    with pytest.raises(ValueError, match="device tensor"):
+        ddg._workspace(torch.zeros(8, dtype=torch.uint8), 8, torch.device("meta"))
+    with pytest.raises(ValueError, match="contiguous"):
+        ddg._workspace(torch.zeros(16, dtype=torch.uint8)[::2], 8, cpu)
+    assert ddg._workspace(None, 0, torch.device("meta")).numel() == 1
+

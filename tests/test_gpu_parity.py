@@ -668,3 +668,23 @@ def test_kblocked_workload_within_tolerance(gpu, workload_operands):
     ratio = float((err / np.einsum("qk,kq->q", np.abs(Ah[qr]), np.abs(Bh[:, qc]))).max())
     _say(f"[parity] dd4096_exp20 in 4 k-blocks: max |C-C_ref|/(|A||B|) = {ratio:.3e}")
     assert ratio <= compare.TOL
+
+
+def test_binding_rejects_a_host_or_mistyped_workspace(gpu):
+    """A caller's workspace must be uint8 device memory on the operands' device;
+    the binding raises before any library call."""
+    import torch
+    A = torch.ones((8, 8), dtype=torch.float64, device="cuda")
+    need = gpu.workspace_size(8, 8, 8)
+    with pytest.raises(ValueError, match="device tensor"):
+        gpu.dd_gemm(A, None, A, None, workspace=torch.empty(need, dtype=torch.uint8))
+    with pytest.raises(TypeError, match="uint8"):
+        gpu.dd_gemm(A, None, A, None, workspace=torch.empty(need, dtype=torch.float64, device="cuda"))
+    with pytest.raises(ValueError, match="device tensor"):
+        gpu.qd_gemm([A], [A], workspace=torch.empty(gpu.qd_workspace_size(8, 8, 8), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="one device"):
+        gpu.dd_gemm(A, None, A, None, C_hi=torch.empty((8, 8), dtype=torch.float64, device="meta"))
+    C_hi, C_lo = gpu.dd_gemm(A, None, A, None, workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(C_hi.cpu(), torch.full((8, 8), 8.0, dtype=torch.float64)) and not C_lo.any()
+
