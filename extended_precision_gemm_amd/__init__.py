@@ -148,11 +148,17 @@ def _device(*tensors):
     return devs.pop()
 
 
-def _workspace(workspace, need, dev):
+def _workspace(workspace, need, dev, stream=None):
     """A caller's workspace (uint8, contiguous, on the operands' device), or a
-    new one of `need` bytes from PyTorch's allocator."""
+    new one of `need` bytes from PyTorch's allocator.  A new workspace is taken
+    on the current stream; when the library runs on another one, the tensor is
+    recorded on that stream, so that the allocator does not hand its memory to
+    a later allocation while the kernels may still use it."""
     if workspace is None:
-        return torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        if stream is not None and ws.is_cuda and stream != torch.cuda.current_stream(dev):
+            ws.record_stream(stream)
+        return ws
     if workspace.dtype != torch.uint8:
         raise TypeError(f"workspace must be uint8, got {workspace.dtype}")
     if workspace.device != dev:
@@ -160,6 +166,37 @@ def _workspace(workspace, need, dev):
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
     return workspace
+
+
+def _buffer(t, name, dtype, numel, dev):
+    """Validate a flat device buffer a stage call reads or writes: the given
+    dtype, contiguous, on device `dev`, at least `numel` elements."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} must be on {dev}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {numel}")
+    return t
+
+
+def _operand_buffers(m, n, k, A_slices, E, B_slices, F, nslices):
+    """The packed slices and exponents of both operands of an m×k by k×n stage
+    call, checked against the sizes the library will touch; returns their device."""
+    dev = A_slices.device
+    _buffer(A_slices, "A_slices", torch.float64, slices_bytes(m, k, nslices) // 8, dev)
+    _buffer(B_slices, "B_slices", torch.float64, slices_bytes(n, k, nslices) // 8, dev)
+    if E is not None:
+        _buffer(E, "E", torch.int32, m, dev)
+    if F is not None:
+        _buffer(F, "F", torch.int32, n, dev)
+    return dev
 
 
 def _check_lo(lo, hi, name):
@@ -212,11 +249,13 @@ def split_balanced(X_hi, X_lo, axis: int, exps=None, slices=None, stream=None, n
     rows, cols = X_hi.shape
     outer = rows if axis == 0 else cols
     k = cols if axis == 0 else rows
-    dev = X_hi.device
+    dev = _device(X_hi, X_lo)
     if exps is None:
         exps = torch.empty(outer, dtype=torch.int32, device=dev)
     if slices is None:
         slices = torch.empty(slices_bytes(outer, k, nslices) // 8, dtype=torch.float64, device=dev)
+    _buffer(exps, "exps", torch.int32, outer, dev)
+    _buffer(slices, "slices", torch.float64, slices_bytes(outer, k, nslices) // 8, dev)
     if nslices == NUM_SLICES:
         _check(lib.dd_split_balanced(rows, cols, _ptr(X_hi), _ptr(X_lo), ldx, axis, _ptr(exps), _ptr(slices),
                                      _stream(stream)))
@@ -228,23 +267,30 @@ def split_balanced(X_hi, X_lo, axis: int, exps=None, slices=None, stream=None, n
 
 def sliced_gemm(m: int, n: int, k: int, A_slices, B_slices, levels=None, stream=None):
     """The eight exact level sums, returned as a (8, m, n) float64 tensor."""
+    dev = _operand_buffers(m, n, k, A_slices, None, B_slices, None, NUM_SLICES)
     if levels is None:
-        levels = torch.empty((NUM_LEVELS, m, n), dtype=torch.float64, device=A_slices.device)
+        levels = torch.empty((NUM_LEVELS, m, n), dtype=torch.float64, device=dev)
     ldl = max(n, 1)
-    if tuple(levels.shape) != (NUM_LEVELS, m, n) or not levels.is_contiguous():
-        raise ValueError("levels must be a contiguous (8, m, n) tensor")
+    if tuple(levels.shape) != (NUM_LEVELS, m, n):
+        raise ValueError(f"levels must be a ({NUM_LEVELS}, m, n) tensor, got {tuple(levels.shape)}")
+    _buffer(levels, "levels", torch.float64, NUM_LEVELS * m * n, dev)
     _check(lib.dd_sliced_gemm(m, n, k, _ptr(A_slices), _ptr(B_slices), _ptr(levels), ldl, _stream(stream)))
     return levels
 
 
 def renorm_levels(levels, E, F, C_hi=None, C_lo=None, stream=None):
+    if levels.dim() != 3 or levels.shape[0] != NUM_LEVELS:
+        raise ValueError(f"levels must be a ({NUM_LEVELS}, m, n) tensor, got {tuple(levels.shape)}")
     _, m, n = levels.shape
-    if not levels.is_contiguous():
-        raise ValueError("levels must be contiguous")
+    dev = levels.device
+    _buffer(levels, "levels", torch.float64, NUM_LEVELS * m * n, dev)
+    _buffer(E, "E", torch.int32, m, dev)
+    _buffer(F, "F", torch.int32, n, dev)
     C_hi = torch.empty((m, n), dtype=torch.float64, device=levels.device) if C_hi is None else C_hi
     C_lo = torch.empty((m, n), dtype=torch.float64, device=levels.device) if C_lo is None else C_lo
     ldc = _matrix(C_hi, "C_hi", (m, n))
     _check_lo(C_lo, C_hi, "C_lo")
+    _device(levels, C_hi, C_lo)
     _check(lib.dd_renorm_levels(m, n, _ptr(levels), max(n, 1), _ptr(E), _ptr(F), _ptr(C_hi), _ptr(C_lo), ldc,
                                 _stream(stream)))
     return C_hi, C_lo
@@ -252,11 +298,14 @@ def renorm_levels(levels, E, F, C_hi=None, C_lo=None, stream=None):
 
 def sliced_gemm_renorm(m, n, k, A_slices, E, B_slices, F, C_hi=None, C_lo=None, stream=None,
                        nslices: int = NUM_SLICES):
-    dev = A_slices.device
+    dev = _operand_buffers(m, n, k, A_slices, E, B_slices, F, nslices)
+    _buffer(E, "E", torch.int32, m, dev)
+    _buffer(F, "F", torch.int32, n, dev)
     C_hi = torch.empty((m, n), dtype=torch.float64, device=dev) if C_hi is None else C_hi
     C_lo = torch.empty((m, n), dtype=torch.float64, device=dev) if C_lo is None else C_lo
     ldc = _matrix(C_hi, "C_hi", (m, n))
     _check_lo(C_lo, C_hi, "C_lo")
+    _device(A_slices, C_hi, C_lo)
     if nslices == NUM_SLICES:
         _check(lib.dd_sliced_gemm_renorm(m, n, k, _ptr(A_slices), _ptr(E), _ptr(B_slices), _ptr(F),
                                          _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
@@ -293,8 +342,8 @@ def dd_gemm(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, workspace=None, stream
     The workspace comes from PyTorch's allocator unless a uint8 device tensor of
     at least workspace_size(m, n, k, nslices) bytes is given."""
     m, n, k, lda, ldb, ldc, C_hi, C_lo, dev = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
-    workspace = _workspace(workspace, workspace_size(m, n, k, nslices, kblock), dev)
     with torch.cuda.device(dev):
+        workspace = _workspace(workspace, workspace_size(m, n, k, nslices, kblock), dev, stream)
         _dd_gemm_call(m, n, k, nslices, kblock, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc, workspace, stream)
     return C_hi, C_lo
 
@@ -371,18 +420,26 @@ def qd_split_balanced(X, axis: int, exps=None, slices=None, stream=None):
     rows, cols = comps[0].shape
     outer = rows if axis == 0 else cols
     k = cols if axis == 0 else rows
-    dev = comps[0].device
+    dev = _device(*comps)
     if exps is None:
         exps = torch.empty(outer, dtype=torch.int32, device=dev)
     if slices is None:
         slices = torch.empty(qd_slices_bytes(outer, k) // 8, dtype=torch.float64, device=dev)
+    _buffer(exps, "exps", torch.int32, outer, dev)
+    _buffer(slices, "slices", torch.float64, qd_slices_bytes(outer, k) // 8, dev)
     _check(lib.qd_split_balanced(rows, cols, arr, ldx, axis, _ptr(exps), _ptr(slices), _stream(stream)))
     return exps, slices
 
 
 def qd_sliced_gemm_renorm(m, n, k, A_slices, E, B_slices, F, C=None, stream=None):
     """Level sums of the 136 slice pairs and the exact four-double epilogue; returns C."""
-    C, ldc, arr = _qd_out(C, m, n, A_slices.device)
+    dev = A_slices.device
+    _buffer(A_slices, "A_slices", torch.float64, qd_slices_bytes(m, k) // 8, dev)
+    _buffer(B_slices, "B_slices", torch.float64, qd_slices_bytes(n, k) // 8, dev)
+    _buffer(E, "E", torch.int32, m, dev)
+    _buffer(F, "F", torch.int32, n, dev)
+    C, ldc, arr = _qd_out(C, m, n, dev)
+    _device(A_slices, *[C[q] for q in range(4)])
     _check(lib.qd_sliced_gemm_renorm(m, n, k, _ptr(A_slices), _ptr(E), _ptr(B_slices), _ptr(F), arr, ldc,
                                      _stream(stream)))
     return C
@@ -407,8 +464,8 @@ def qd_gemm(A, B, C=None, workspace=None, stream=None, kblock: int | None = None
     given.  ``kblock`` runs the product in k-blocks of that many terms (the
     result does not depend on it); by default k is split only beyond QD_K_MAX."""
     m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _qd_gemm_args(A, B, C)
-    workspace = _workspace(workspace, qd_workspace_size(m, n, k, kblock), dev)
     with torch.cuda.device(dev):
+        workspace = _workspace(workspace, qd_workspace_size(m, n, k, kblock), dev, stream)
         if kblock is None:
             _check(lib.qd_gemm_ws(m, n, k, pa, lda, pb, ldb, pc, ldc, _ptr(workspace), workspace.numel(),
                                   _stream(stream)))

@@ -30,6 +30,13 @@ class Workspace {
             ok_ = false;
         return *this;
     }
+    // Packed slices of one operand (dd_split_slices_bytes_ns or qd_split_slices_bytes):
+    // those report 0 bytes for an empty operand and also for one too large to
+    // size, which has no workspace.
+    Workspace& add_slices(size_t slice_bytes, int64_t outer, int64_t k) {
+        if (slice_bytes == 0 && outer > 0 && k > 0) ok_ = false;
+        return add(slice_bytes);
+    }
     size_t bytes() const { return ok_ ? total_ : 0; }
 
   private:
@@ -105,15 +112,6 @@ ddgemm_status_t validate_sizes(int64_t m, int64_t n, int64_t k) {
 ddgemm_status_t validate_gemm_dims(int64_t m, int64_t n, int64_t k) {
     if (validate_sizes(m, n, k) != DDGEMM_SUCCESS || k > DDGEMM_K_MAX) return DDGEMM_ERROR_INVALID_VALUE;
     return DDGEMM_SUCCESS;
-}
-
-// The k-block dd_gemm uses when none is given: all of k when it fits the
-// exact-sum bound, else the fewest equal blocks that do.
-int64_t default_kblock(int64_t k, int ns) {
-    const int64_t km = k_max(ns);
-    if (k <= km) return k;
-    const int64_t blocks = (k + km - 1) / km;
-    return (k + blocks - 1) / blocks;
 }
 
 bool kblock_ok(int64_t k, int ns, int64_t kblock) { return k == 0 || (kblock >= 1 && kblock <= k_max(ns)); }
@@ -194,6 +192,39 @@ QdPlanes offset_planes(const QdPlanes& X, int64_t off) {
 
 }  // namespace
 
+namespace ddg {
+
+int64_t default_kblock(int64_t k, int ns) {
+    const int64_t km = k_max(ns);
+    if (k <= km) return k;
+    const int64_t blocks = (k + km - 1) / km;
+    return (k + blocks - 1) / blocks;
+}
+
+ProductCheck check_dd_product(int64_t m, int64_t n, int64_t k, int ns, int64_t kblock, const double* A_hi,
+                              const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb,
+                              const double* C_hi, const double* C_lo, int64_t ldc) {
+    const ProductCheck bad{DDGEMM_ERROR_INVALID_VALUE, false, 0};
+    if (validate_sizes(m, n, k) != DDGEMM_SUCCESS) return bad;
+    if (!ns_ok(ns) || !kblock_ok(k, ns, kblock)) return bad;
+    if (!ld_ok(lda, m, k) || !ld_ok(ldb, k, n) || !ld_ok(ldc, m, n)) return bad;
+    if (m == 0 || n == 0) return ProductCheck{DDGEMM_SUCCESS, true, 0};
+    if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return bad;
+    const int64_t ae = extent(m, k, lda), be = extent(k, n, ldb), ce = extent(m, n, ldc);
+    for (const double* C : {C_hi, C_lo})
+        if (overlaps(C, ce, A_hi, ae) || overlaps(C, ce, A_lo, ae) || overlaps(C, ce, B_hi, be) ||
+            overlaps(C, ce, B_lo, be))
+            return bad;
+    if (overlaps(C_hi, ce, C_lo, ce)) return bad;
+    const size_t need = dd_gemm_workspace_size_kb(m, n, k, ns, kblock);
+    if (need == 0) return bad;  // the workspace would pass 2^62 bytes
+    return ProductCheck{DDGEMM_SUCCESS, false, need};
+}
+
+ddgemm_status_t check_current_device() { return check_device(); }
+
+}  // namespace ddg
+
 extern "C" {
 
 size_t dd_split_slices_bytes_ns(int64_t outer, int64_t k, int nslices) {
@@ -207,7 +238,8 @@ size_t dd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int nslices, i
     if (validate_sizes(m, n, k) != DDGEMM_SUCCESS || !ns_ok(nslices) || !kblock_ok(k, nslices, kblock)) return 0;
     const int64_t kb = k < kblock ? k : kblock;
     Workspace ws;
-    ws.add(dd_split_slices_bytes_ns(m, kb, nslices)).add(dd_split_slices_bytes_ns(n, kb, nslices));
+    ws.add_slices(dd_split_slices_bytes_ns(m, kb, nslices), m, kb);
+    ws.add_slices(dd_split_slices_bytes_ns(n, kb, nslices), n, kb);
     ws.add(m, 4).add(n, 4);
     if (block_count(k, kblock) > 1) ws.add(m, n, 8).add(m, n, 8);  // (hi, lo) of the blocks after the first
     const SplitPlan plan = split_plan(m, n, kb, nslices, true);
@@ -295,20 +327,11 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
                               const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo,
                               int64_t ldb, double* C_hi, double* C_lo, int64_t ldc, void* workspace,
                               size_t ws_bytes, void* stream) {
-    ddgemm_status_t st = validate_sizes(m, n, k);
-    if (st != DDGEMM_SUCCESS) return st;
-    if (!ns_ok(nslices) || !kblock_ok(k, nslices, kblock)) return DDGEMM_ERROR_INVALID_VALUE;
-    if (!ld_ok(lda, m, k) || !ld_ok(ldb, k, n) || !ld_ok(ldc, m, n)) return DDGEMM_ERROR_INVALID_VALUE;
-    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
-    if (!C_hi || !C_lo || (k > 0 && (!A_hi || !B_hi))) return DDGEMM_ERROR_INVALID_VALUE;
-    const int64_t ae = extent(m, k, lda), be = extent(k, n, ldb), ce = extent(m, n, ldc);
-    for (const double* C : {static_cast<const double*>(C_hi), static_cast<const double*>(C_lo)})
-        if (overlaps(C, ce, A_hi, ae) || overlaps(C, ce, A_lo, ae) || overlaps(C, ce, B_hi, be) ||
-            overlaps(C, ce, B_lo, be))
-            return DDGEMM_ERROR_INVALID_VALUE;
-    if (overlaps(C_hi, ce, C_lo, ce)) return DDGEMM_ERROR_INVALID_VALUE;
-    const size_t need = dd_gemm_workspace_size_kb(m, n, k, nslices, kblock);
-    if (need == 0) return DDGEMM_ERROR_INVALID_VALUE;  // the workspace would pass 2^62 bytes
+    const ProductCheck chk =
+        check_dd_product(m, n, k, nslices, kblock, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc);
+    if (chk.status != DDGEMM_SUCCESS || chk.empty) return chk.status;
+    const size_t need = chk.need;
+    ddgemm_status_t st;
     if (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return DDGEMM_ERROR_WORKSPACE;
     if ((st = check_device()) != DDGEMM_SUCCESS) return st;
@@ -430,7 +453,8 @@ size_t qd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int64_t kblock
     // a blocked product's blocks split whole or not at all; one block may split its later rows only
     const SplitPlan plan = split_plan(m, n, kb, kQdSlices, !blocked);
     Workspace ws;
-    ws.add(qd_split_slices_bytes(m, kb)).add(qd_split_slices_bytes(n, kb)).add(m, 4).add(n, 4);
+    ws.add_slices(qd_split_slices_bytes(m, kb), m, kb).add_slices(qd_split_slices_bytes(n, kb), n, kb);
+    ws.add(m, 4).add(n, 4);
     if (blocked) ws.add(QDGEMM_NUM_LEVELS, m, n * 8);  // int64 level planes of a blocked product
     if (plan.parts > 1)                                // double level planes of the rows split over k
         ws.add(QDGEMM_NUM_LEVELS, m - plan.first_row, n * 8);

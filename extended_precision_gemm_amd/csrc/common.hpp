@@ -53,6 +53,23 @@ struct OutPlanes {
 // phase.
 enum SplitPhase { kSplitExps = 1, kSplitSlices = 2, kSplitAll = 3 };
 
+// Argument checks shared by the double-double product entry points: `status`
+// is the error to report (DDGEMM_SUCCESS when the call may proceed), `empty`
+// marks the no-op m = 0 or n = 0, `need` the workspace bytes otherwise.
+struct ProductCheck {
+    ddgemm_status_t status;
+    bool empty;
+    size_t need;
+};
+ProductCheck check_dd_product(int64_t m, int64_t n, int64_t k, int ns, int64_t kblock, const double* A_hi,
+                              const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb,
+                              const double* C_hi, const double* C_lo, int64_t ldc);
+// The k-block the product uses when none is given: all of k when it fits the
+// exact-sum bound for ns slices, else the fewest equal blocks that do.
+int64_t default_kblock(int64_t k, int ns);
+// DDGEMM_SUCCESS when the current device is a gfx950 (cached per device).
+ddgemm_status_t check_current_device();
+
 // Host-side launch helpers implemented next to their kernels.
 hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
                         int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream,

@@ -453,3 +453,59 @@ def test_binding_checks_devices_and_the_callers_workspace(ddg):
         ddg._workspace(torch.zeros(16, dtype=torch.uint8)[::2], 8, cpu)
     assert ddg._workspace(None, 0, torch.device("meta")).numel() == 1
 
+
+
+def test_workspace_sizes_of_operands_too_large_to_slice_are_rejected(ddg):
+    """An operand whose packed slices cannot be sized (outer·k·n past the
+    2^58-element bound) has no workspace: the size queries give 0 and the
+    products reject the sizes, rather than leaving its slices out."""
+    L = ddg.lib
+    m, k = 1 << 35, 1 << 23
+    assert L.dd_split_slices_bytes(m, k) == 0
+    assert L.dd_gemm_workspace_size(m, 1, k) == 0
+    assert L.qd_gemm_workspace_size(m, 1, 1 << 22) == 0
+    far = [(1 << 62) + (i << 59) for i in range(4)]
+    assert L.dd_gemm_ws(m, 1, k, 1 << 40, None, k, 1 << 41, None, 1, far[0], far[1], 1, P[0], 1 << 40,
+                        None) == ddg.ERROR_INVALID_VALUE
+    C = _arr(far[0], far[1], far[2], far[3])
+    assert L.qd_gemm_ws(m, 1, 1 << 22, _arr(1 << 40), 1 << 22, _arr(1 << 41), 1, C, 1, P[0], 1 << 40,
+                        None) == ddg.ERROR_INVALID_VALUE
+
+
+def test_binding_checks_stage_call_buffers(ddg):
+    """The stage calls check the slices, exponents and level planes they pass on:
+    dtype, contiguity, device memory and length (a short or host buffer would
+    reach the kernels as an out-of-bounds pointer)."""
+    import torch
+    m, n, k = 4, 5, 6
+    f64 = lambda c: torch.zeros(c, dtype=torch.float64)
+    i32 = lambda c: torch.zeros(c, dtype=torch.int32)
+    As, Bs = f64(ddg.slices_bytes(m, k) // 8), f64(ddg.slices_bytes(n, k) // 8)
+    with pytest.raises(ValueError, match="device tensor"):
+        ddg.sliced_gemm(m, n, k, As, Bs)
+    with pytest.raises(ValueError, match="device tensor"):
+        ddg.sliced_gemm_renorm(m, n, k, As, i32(m), Bs, i32(n))
+    with pytest.raises(TypeError, match="float64"):
+        ddg.sliced_gemm(m, n, k, i32(10), Bs)
+    with pytest.raises(ValueError, match=r"\(8, m, n\)"):
+        ddg.renorm_levels(f64((7, m, n)), i32(m), i32(n))
+    with pytest.raises(ValueError, match="device tensor"):
+        ddg.renorm_levels(f64((8, m, n)), i32(m), i32(n))
+    with pytest.raises(ValueError, match="device tensor"):
+        ddg.qd_sliced_gemm_renorm(m, n, k, f64(ddg.qd_slices_bytes(m, k) // 8), i32(m),
+                                  f64(ddg.qd_slices_bytes(n, k) // 8), i32(n))
+    # the checks themselves, on host tensors standing for device ones
+    with pytest.raises(ValueError, match="needs at least"):
+        _buffer_on_host(ddg, f64(3), torch.float64, 4)
+    with pytest.raises(ValueError, match="contiguous"):
+        _buffer_on_host(ddg, f64(8)[::2], torch.float64, 4)
+    with pytest.raises(TypeError, match="int32"):
+        _buffer_on_host(ddg, f64(8), torch.int32, 4)
+    assert _buffer_on_host(ddg, i32(8), torch.int32, 8).numel() == 8
+
+
+def _buffer_on_host(ddg, t, dtype, numel):
+    """ddg._buffer with the device-memory check lifted (host tensors stand in)."""
+    import unittest.mock
+    with unittest.mock.patch.object(type(t), "is_cuda", new=property(lambda self: True)):
+        return ddg._buffer(t, "buf", dtype, numel, t.device)

@@ -428,6 +428,38 @@ def test_nondefault_stream(gpu):
     assert _bits_equal(_host(out[0]), ref[0]) and _bits_equal(_host(out[1]), ref[1])
 
 
+def test_workspace_of_a_call_on_a_stream_that_is_not_current(gpu):
+    """dd_gemm / qd_gemm given a stream that is not the current one take their
+    workspace from the allocator on the current stream; it must stay reserved
+    until the kernels on the given stream are done.  Memory taken and written
+    on the current stream right after the call must not corrupt the result."""
+    import torch
+    m, n, k = 512, 384, 1024
+    Ah, Al = (_dev(x) for x in workloads.random_dd((m, k), 41, "signed_exp20"))
+    Bh, Bl = (_dev(x) for x in workloads.random_dd((k, n), 42, "signed_exp20"))
+    ref = [_host(t) for t in gpu.dd_gemm(Ah, Al, Bh, Bl)]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    out = gpu.dd_gemm(Ah, Al, Bh, Bl, stream=s)
+    junk = torch.empty(gpu.workspace_size(m, n, k), dtype=torch.uint8, device=Ah.device)
+    junk.fill_(0x7F)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert _bits_equal(_host(out[0]), ref[0]) and _bits_equal(_host(out[1]), ref[1])
+    A = _dev(workloads.random_qd((m, k), 43, "uniform"))
+    B = _dev(workloads.random_qd((k, n), 44, "uniform"))
+    qref = _host(gpu.qd_gemm(A, B))
+    torch.cuda.synchronize()
+    s.wait_stream(torch.cuda.current_stream())
+    qout = gpu.qd_gemm(A, B, stream=s)
+    junk = torch.empty(gpu.qd_workspace_size(m, n, k), dtype=torch.uint8, device=A.device)
+    junk.fill_(0x7F)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert _bits_equal(_host(qout), qref)
+
+
 # ---------------------------------------------------------------------------
 # the five workloads at full size
 # ---------------------------------------------------------------------------
