@@ -35,6 +35,7 @@ K_MAX = 8388608
 QD_NUM_SLICES = 16      # the quad-double product
 QD_K_MAX = 4194304
 QD_K_MAX_BLOCKED = 4294967296   # longer qd products run in k-blocks sharing their exponents
+NOALLOC_SCRATCH_BYTES = 256 << 20  # the device array dd_gemm_noalloc works in, per GPU
 
 SUCCESS = 0
 ERROR_INVALID_VALUE = 1
@@ -85,6 +86,7 @@ _SIGNATURES = {
     "ddgemm_split_parts": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "ddgemm_split_first_row": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "ddgemm_split_first_tile": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
+    "dd_gemm_noalloc": (_st, [_i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp]),
     "ddgemm_status_string": (ctypes.c_char_p, [_st]),
     "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
 }
@@ -367,6 +369,17 @@ def dd_gemm_alloc(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, stream=None):
     with torch.cuda.device(dev):
         _check(lib.dd_gemm(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
                            _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
+    return C_hi, C_lo
+
+
+def dd_gemm_noalloc(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, stream=None):
+    """C = A·B through the entry point that allocates nothing: its workspace is
+    the library's own device array of NOALLOC_SCRATCH_BYTES per GPU (products
+    needing more are rejected).  Calls that overlap on one GPU race on it."""
+    m, n, k, lda, ldb, ldc, C_hi, C_lo, dev = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
+    with torch.cuda.device(dev):
+        _check(lib.dd_gemm_noalloc(m, n, k, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
+                                   _ptr(C_hi), _ptr(C_lo), ldc, _stream(stream)))
     return C_hi, C_lo
 
 

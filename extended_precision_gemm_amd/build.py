@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libddgemm.so")
-SOURCES = ["api.cpp", "split_k.cpp", "split.hip", "qd_split.hip", "sliced_gemm.hip", "levels.hip", "accumulate.hip"]
+SOURCES = ["api.cpp", "split_k.cpp", "split.hip", "qd_split.hip", "sliced_gemm.hip", "levels.hip", "accumulate.hip",
+           "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

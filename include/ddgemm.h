@@ -27,7 +27,8 @@
  *     count overflows), else DDGEMM_ERROR_INVALID_VALUE.  A lo pointer may be
  *     NULL, meaning an all-zero lo plane.
  *   - Pointers are owned by the caller; the library keeps none after a call
- *     returns.  Only dd_gemm allocates (stream-ordered, freed on the stream).
+ *     returns.  Only dd_gemm allocates (stream-ordered, freed on the stream);
+ *     dd_gemm_noalloc works in a fixed device array the library holds.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work and returns; errors from the execution itself surface at
  *     the caller's next synchronisation, as with any HIP launch.  Argument
@@ -35,7 +36,7 @@
  *   - Inputs must be finite; pairs need not be normalised (the exact value
  *     hi + lo is sliced).  Outputs must not overlap inputs.
  *   - Calls are reentrant: no global state except a per-device capability
- *     check cached on first use.
+ *     check cached on first use (and dd_gemm_noalloc's per-device array).
  */
 #ifndef DDGEMM_H
 #define DDGEMM_H
@@ -257,6 +258,31 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
                               const double* B_hi, const double* B_lo, int64_t ldb,
                               double* C_hi, double* C_lo, int64_t ldc,
                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The double-double product for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments (minus the workspace), kernels and result as
+ * dd_gemm_ws -- bit for bit -- with the workspace taken from a device array
+ * that the library holds itself: DDGEMM_NOALLOC_SCRATCH_BYTES bytes on every
+ * GPU the call runs on, reserved from the first call on that GPU until the
+ * process ends.  Calls nothing that allocates.
+ *   - Products whose dd_gemm_workspace_size exceeds DDGEMM_NOALLOC_SCRATCH_BYTES
+ *     are rejected with DDGEMM_ERROR_WORKSPACE before anything is enqueued
+ *     (m = n = k = 1024 fits; 2048^3 does not).
+ *   - All calls on one GPU share that GPU's array, which keeps what the last
+ *     call left in it (no call depends on its contents).  Calls ordered on one
+ *     stream are safe; calls whose execution overlaps on one GPU (different
+ *     streams without ordering, or several host threads) race on the array and
+ *     give undefined results.
+ * Errors: as for dd_gemm_ws, plus DDGEMM_ERROR_WORKSPACE as above and
+ * DDGEMM_ERROR_LAUNCH if the array's device address cannot be obtained.
+ */
+#define DDGEMM_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+ddgemm_status_t dd_gemm_noalloc(int64_t m, int64_t n, int64_t k,
+                                const double* A_hi, const double* A_lo, int64_t lda,
+                                const double* B_hi, const double* B_lo, int64_t ldb,
+                                double* C_hi, double* C_lo, int64_t ldc, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* ddgemm_status_string(ddgemm_status_t status);

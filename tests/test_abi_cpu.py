@@ -455,6 +455,28 @@ def test_binding_checks_devices_and_the_callers_workspace(ddg):
 
 
 
+def test_no_alloc_product_validation(ddg):
+    """dd_gemm_noalloc checks its arguments like dd_gemm_ws and rejects products
+    whose workspace exceeds its fixed device array before any device call."""
+    L = ddg.lib
+    INV, WS = ddg.ERROR_INVALID_VALUE, ddg.ERROR_WORKSPACE
+    assert ddg.NOALLOC_SCRATCH_BYTES == 256 << 20
+    assert L.dd_gemm_workspace_size(1024, 1024, 1024) <= ddg.NOALLOC_SCRATCH_BYTES
+    far = [(1 << 40) * (i + 1) for i in range(6)]
+    n = 2048
+    assert L.dd_gemm_workspace_size(n, n, n) > ddg.NOALLOC_SCRATCH_BYTES
+    assert L.dd_gemm_noalloc(n, n, n, far[0], far[1], n, far[2], far[3], n, far[4], far[5], n, None) == WS
+    assert L.dd_gemm_noalloc(-1, 4, 4, P[0], None, 4, P[1], None, 4, P[2], P[3], 4, None) == INV
+    assert L.dd_gemm_noalloc(4, 4, -1, P[0], None, 4, P[1], None, 4, P[2], P[3], 4, None) == INV
+    assert L.dd_gemm_noalloc(4, 4, 4, P[0], None, 3, P[1], None, 4, P[2], P[3], 4, None) == INV   # lda < k
+    assert L.dd_gemm_noalloc(4, 4, 4, None, None, 4, P[1], None, 4, P[2], P[3], 4, None) == INV
+    assert L.dd_gemm_noalloc(4, 4, 4, P[0], None, 4, P[1], None, 4, P[0], P[3], 4, None) == INV   # C aliases A
+    assert L.dd_gemm_noalloc(0, 4, 4, None, None, 4, None, None, 4, None, None, 4, None) == 0      # no-op
+    import torch
+    if not torch.cuda.is_available():
+        assert L.dd_gemm_noalloc(4, 4, 4, P[0], None, 4, P[1], None, 4, P[2], P[3], 4, None) == ddg.ERROR_DEVICE
+
+
 def test_workspace_sizes_of_operands_too_large_to_slice_are_rejected(ddg):
     """An operand whose packed slices cannot be sized (outer·k·n past the
     2^58-element bound) has no workspace: the size queries give 0 and the
