@@ -29,10 +29,16 @@ Readings of points the pages leave open:
   n = 8); pairs below the window (s + t >= n) are not formed.
 * The cascade starts from the smallest level: (h, t) = (S_{n-1}, 0); for l = n-2..0:
   (s, e) = TwoSum(h, S_l), t = t + e, (h, t) = TwoSum(s, t); then both words are
-  scaled by 2^(E_i + F_j).
+  scaled by 2^(E_i + F_j).  That is the stage chain's epilogue.  The product
+  entry points round each entry's exact level total to the nearest double-double
+  instead (nearest_dd): the pages fix no order for adding the parts, and the
+  exact sum rounded once is the most accurate order and the same for any
+  grouping of the slice products (pair_schedule).
 
 Parity status: pinned (the pages' worked example, reconstruction identities,
-brute force on tiny inputs, closed forms; see tests/test_oracle_pins.py).
+brute force on tiny inputs, closed forms; see tests/test_oracle_pins.py, and
+for the pair-packed schedule and the nearest double-double,
+tests/test_oracle_paired_pins.py).
 """
 from __future__ import annotations
 
@@ -246,6 +252,81 @@ def level_target(S_units: np.ndarray, E: int, F: int, i: int, j: int) -> Fractio
     """Exact value sum_l S_units[l][i,j] * 2^(E + F - 13(l+2)) of one output entry."""
     return sum((Fraction(int(S_units[l, i, j])) * Fraction(2) ** (E + F - DIGIT_BITS * (l + 2))
                 for l in range(S_units.shape[0])), Fraction(0))
+
+
+# ---------------------------------------------------------------------------
+# the pair-packed schedule: two slices of A in one 26-bit operand
+# ---------------------------------------------------------------------------
+def pair_schedule(nslices: int = N_SLICES) -> list[tuple[int, int, int, int]]:
+    """The matrix products of the pair-packed schedule, as (s_hi, s_lo, t, g).
+
+    Slices 2u and 2u + 1 of an A entry have the same sign and sit 13 bits apart,
+    so d_2u 2^13 + d_(2u+1) is one exact 26-bit integer; its product with a
+    13-bit B digit d_t is a 39-bit integer that covers the two window pairs
+    (2u, t) and (2u+1, t) at once.  Where only (2u, t) lies in the window
+    (2u + t = n - 1), or A has no slice 2u + 1 (odd n), the product is the
+    single pair (2u, t), written with s_lo = -1.  Every pair s + t <= n - 1 is
+    covered exactly once.  A product's exact value is an integer number of
+    units 2^(-13(g+3)) (g = 2u + t for a packed pair, n - 2 for a single one):
+    g indexes the n - 1 group sums G_g of an output entry, so that its exact
+    windowed total is sum_g G_g 2^(-13(g+3)) (times 2^(E_i + F_j)).
+    """
+    n = nslices
+    out = []
+    for u in range((n + 1) // 2):
+        s0, s1 = 2 * u, 2 * u + 1
+        for t in range(n):
+            if s1 < n and s1 + t <= n - 1:
+                out.append((s0, s1, t, s0 + t))
+            elif s0 + t <= n - 1:
+                out.append((s0, -1, t, n - 2))
+    return out
+
+
+def paired_group_units(DA: np.ndarray, DB: np.ndarray) -> np.ndarray:
+    """G[g] = sum of the schedule's products of group g, in integer units
+    2^(-13(g+3)), g = 0..n-2, from the int64 digit planes DA[s] (m×k) and
+    DB[t] (k×n).  Exact in int64 while k (2^39 + 2^26) n < 2^63."""
+    n = DA.shape[0]
+    m, k = DA.shape[1], DA.shape[2]
+    G = np.zeros((n - 1, m, DB.shape[2]), dtype=np.int64)
+    for s0, s1, t, g in pair_schedule(n):
+        a = DA[s0] * (1 << DIGIT_BITS) + DA[s1] if s1 >= 0 else DA[s0]
+        G[g] += a @ DB[t]
+    return G
+
+
+# ---------------------------------------------------------------------------
+# the product's epilogue: the nearest double-double of the exact total
+# ---------------------------------------------------------------------------
+def nearest_dd(S_units: np.ndarray, E, F):
+    """(C_hi, C_lo) of every entry from its exact level total
+    x = sum_l S_units[l] 2^(E_i + F_j - 13(l+2)): C_hi = RN(x), C_lo =
+    RN(x - C_hi), the double-double nearest to x (ties to even, gradual
+    underflow).  Beyond the double range C_hi is +-inf and C_lo rounds what is
+    left after C_hi's value with an unbounded exponent range (the reading the
+    quad-double words use).  The pages add the parts of an entry in
+    double-double arithmetic without fixing the order; the exact total rounded
+    once is the most accurate such sum and does not depend on how the slice
+    products were grouped."""
+    from .qd import greedy_qd
+    nl, m, n = S_units.shape
+    E = np.asarray(E, dtype=np.int64)
+    F = np.asarray(F, dtype=np.int64)
+    hi = np.zeros((m, n), dtype=np.float64)
+    lo = np.zeros((m, n), dtype=np.float64)
+    for i in range(m):
+        for j in range(n):
+            hi[i, j], lo[i, j] = greedy_qd(level_target(S_units, int(E[i]), int(F[j]), i, j), 2)
+    return hi, lo
+
+
+def paired_product(A_hi, A_lo, B_hi, B_lo, nslices: int = N_SLICES):
+    """The product entry points' chain on one block: slices, the exact sum of
+    the window pairs, rounded to the nearest double-double."""
+    E, DA = slice_rows(A_hi, A_lo, nslices=nslices)
+    F, DB = slice_cols(B_hi, B_lo, nslices=nslices)
+    return nearest_dd(level_sums_units(DA, DB), E, F)
 
 
 # ---------------------------------------------------------------------------
