@@ -1,11 +1,13 @@
 """Benchmark: effective double-double GFLOP/s (2mnk/t) of C = A·B on one MI355X.
 
-One step is one pass of the whole product over resident inputs, issued through
-the library's stage entry points: slice A (row exponents, then slices), slice B
-(column exponents, then slices), fused sliced GEMM + renormalisation epilogue --
-the kernels dd_gemm_ws runs (it issues both exponent passes first, which saves
-about 13 us at 4096^2).  HIP events on the same stream bracket each stage, so
-the dominant kernel's launch duration is measured live inside the timed region.
+One step is one call of the product entry point dd_gemm_ws on resident inputs
+and a preallocated workspace: both operands' exponent passes and slice passes,
+then the pair-packed sliced GEMM on FP64 matrix cores (20 products per
+k-block covering the 36 window slice pairs) with the nearest-double-double
+epilogue fused.  `value` comes from the median step; HIP events on the
+product's stream bracket each step, and the library records one more event
+after the slicing (dd_gemm_ws_timed), so the GEMM's launch duration is
+measured live inside the timed region.
 
 With a quad-double workload (``--workload qd1024``, ``qd2048``, ``qd4096_exp20``)
 the step is the quad-double product: slice A and B into sixteen slices, then
@@ -83,16 +85,6 @@ def _traffic_from_profile(workload: str):
         return None
 
 
-def _timing(ev):
-    """Median and minimum over the timed steps of the per-step GPU times (HIP
-    events on the bench stream): the whole step and its GEMM launch."""
-    import statistics
-    step = [e[0].elapsed_time(e[2]) for e in ev]
-    gemm = [e[1].elapsed_time(e[2]) for e in ev]
-    return {"step_ms_median": round(statistics.median(step), 4), "step_ms_min": round(min(step), 4),
-            "gemm_ms_median": round(statistics.median(gemm), 4), "gemm_ms_min": round(min(gemm), 4)}
-
-
 def _host_info(threads_used):
     """CPU model, logical CPUs and the OpenMP thread setting of the host running the oracle."""
     model = "unknown"
@@ -147,47 +139,53 @@ def main():
     A_hi, A_lo, B_hi, B_lo = (torch.from_numpy(x).to(dev) for x in (Ah, Al, Bh, Bl))
     C_hi = torch.empty((m, n), dtype=torch.float64, device=dev)
     C_lo = torch.empty((m, n), dtype=torch.float64, device=dev)
-    E = torch.empty(m, dtype=torch.int32, device=dev)
-    F = torch.empty(n, dtype=torch.int32, device=dev)
     ns = args.nslices
     pairs = ns * (ns + 1) // 2
-    As = torch.empty(ddg.slices_bytes(m, k, ns) // 8, dtype=torch.float64, device=dev)
-    Bs = torch.empty(ddg.slices_bytes(n, k, ns) // 8, dtype=torch.float64, device=dev)
+    products = ddg.pair_products(ns)
+    ws = torch.empty(max(ddg.workspace_size(m, n, k, ns), 1), dtype=torch.uint8, device=dev)
 
     _calibration_copy(args, dev)
 
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in ev:
+        e[1].record(stream)  # creates the event the library records after slicing
 
     def step(events=None):
         if events:
             events[0].record(stream)
-        ddg.split_balanced(A_hi, A_lo, 0, E, As, stream, nslices=ns)
-        ddg.split_balanced(B_hi, B_lo, 1, F, Bs, stream, nslices=ns)
-        if events:
-            events[1].record(stream)
-        ddg.sliced_gemm_renorm(m, n, k, As, E, Bs, F, C_hi, C_lo, stream, nslices=ns)
+        ddg.dd_gemm_timed(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo, ws, events[1].cuda_event if events else None,
+                          stream, nslices=ns)
         if events:
             events[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] timing {args.steps} steps of dd_gemm_ws", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    import statistics
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    split_ms_l = [e[0].elapsed_time(e[1]) for e in ev]
+    gemm_ms_l = [e[1].elapsed_time(e[2]) for e in ev]
+    step_med = statistics.median(step_ms)
+    split_ms = statistics.median(split_ms_l)
+    gemm_ms = statistics.median(gemm_ms_l)
     ms_per_step = elapsed * 1e3 / args.steps
-    value = 2.0 * m * n * k / (elapsed / args.steps) / 1e9
-    sliced_roof_gflops = PEAK_FP64_MFMA_TFLOPS * 1e3 / pairs
-    gemm_tflops = pairs * 2.0 * m * n * k / (gemm_ms * 1e-3) / 1e12
+    value = 2.0 * m * n * k / (step_med * 1e-3) / 1e9
+    issued_roof_gflops = PEAK_FP64_MFMA_TFLOPS * 1e3 / products
+    pair_roof_gflops = PEAK_FP64_MFMA_TFLOPS * 1e3 / pairs
+    gemm_flops = products * 2.0 * m * n * k       # the FP64 matrix products the kernel issues
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     traffic = _traffic_from_profile(w.name) if ns == 8 else None
-    split_bytes = (16.0 + 8.0 * ns) * (m * k + k * n)   # 16 B read + 8 B per slice written per entry
+    # slicer: 8 B exponent pass + 16 B read + 8 B per slice written per entry
+    split_bytes = (8.0 + 16.0 + 8.0 * ns) * (m * k + k * n)
 
     rec = {
         "metric": METRIC,
@@ -205,33 +203,43 @@ def main():
         "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": w.name, "m": m, "n": n, "k": k, "description": w.description,
-                   "slices": ns, "slice_bits": 13, "pairs": pairs},
-        "pct_sliced_roof": round(100.0 * value / sliced_roof_gflops, 2),
+                   "slices": ns, "slice_bits": 13, "pairs": pairs, "matrix_products": products},
+        "timed": "dd_gemm_ws (slicing + pair-packed sliced GEMM with fused nearest-double-double epilogue), "
+                 "median of the steps' HIP-event times; workspace preallocated, inputs resident",
+        "pct_sliced_roof": round(100.0 * value / issued_roof_gflops, 2),
+        "pct_36pair_roof": round(100.0 * value / pair_roof_gflops, 2),
         "roofline": {
-            "kernel": "sliced_gemm_kernel (fused renormalisation epilogue)",
+            "kernel": "sliced_gemm_kernel, pair-packed schedule (fused nearest double-double epilogue)",
             "bound": "mfma",
             "achieved": round(gemm_tflops, 3),
             "peak": PEAK_FP64_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP64_MFMA_TFLOPS, 4),
             "traffic": traffic,
-            "flops_per_launch": pairs * 2.0 * m * n * k,
+            "flops_per_launch": gemm_flops,
             "launch_ms": round(gemm_ms, 4),
         },
         "stages": {
             "split_ms": round(split_ms, 4),
+            "split_bytes_per_entry": 8 + 16 + 8 * ns,
             "split_GBps": round(split_bytes / (split_ms * 1e-3) / 1e9, 1),
             "split_frac_hbm": round(split_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "gemm_ms": round(gemm_ms, 4),
         },
-        "timing": _timing(ev),
+        "timing": {"step_ms_median": round(step_med, 4), "step_ms_mean": round(statistics.mean(step_ms), 4),
+                   "step_ms_min": round(min(step_ms), 4), "gemm_ms_min": round(min(gemm_ms_l), 4),
+                   "split_ms_min": round(min(split_ms_l), 4)},
     }
 
     # The stand-alone renormalisation (dd_renorm_levels, the stage entry point the
     # fused path does not use), timed on its own outside the timed region:
     # 64 B of level sums read + 16 B of (hi, lo) written per output.
     if not args.no_epilogue and ns == 8:
+        del ws
+        E, As = ddg.split_balanced(A_hi, A_lo, 0, stream=stream)
+        F, Bs = ddg.split_balanced(B_hi, B_lo, 1, stream=stream)
         levels = ddg.sliced_gemm(m, n, k, As, Bs)
+        del As, Bs
         R_hi = torch.empty_like(C_hi)
         R_lo = torch.empty_like(C_lo)
         ddg.renorm_levels(levels, E, F, R_hi, R_lo, stream)
@@ -243,12 +251,12 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ren_ms = e0.elapsed_time(e1) / reps
-        same = bool(torch.equal(R_hi.view(torch.int64), C_hi.view(torch.int64)) and
-                    torch.equal(R_lo.view(torch.int64), C_lo.view(torch.int64)))
+        # the stage chain's cascade and the product's nearest rounding of the same exact totals
+        differ = int((R_hi != C_hi).sum().item() + (R_lo != C_lo).sum().item())
         rec["stages"]["renorm_standalone_ms"] = round(ren_ms, 4)
         rec["stages"]["renorm_GBps"] = round(80.0 * m * n / (ren_ms * 1e-3) / 1e9, 1)
         rec["stages"]["renorm_frac_hbm"] = round(80.0 * m * n / (ren_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-        rec["stages"]["renorm_matches_fused"] = same
+        rec["stages"]["renorm_words_differing_from_nearest"] = differ
         del levels, R_hi, R_lo
 
     if not args.no_cpu_baseline:
@@ -289,10 +297,12 @@ def main():
 
 
 def _run_shape(args):
-    """The product entry point on an arbitrary shape, with the split-over-k plan
-    it takes (rows [0, first_split_row) unsplit, the rest in `parts` k-parts),
-    timed beside the unsplit path (slicing + the fused stage call, which never
-    splits) on the same inputs; the two results must agree bit for bit."""
+    """The product entry point on an arbitrary shape with the split-over-k plan it
+    takes (tiles before the first split tile unsplit, the rest in `parts`
+    k-parts), timed beside the unsplit 36-pair stage chain (slicing + the fused
+    level-cascade call, which never splits) on the same inputs.  The two round
+    the same exact totals differently (nearest double-double vs the level
+    cascade); the line reports how many words differ."""
     import torch
 
     import extended_precision_gemm_amd as ddg
@@ -348,8 +358,8 @@ def _run_shape(args):
         return (time.perf_counter() - t0) / args.steps
 
     # warm both paths up, for at least half a second so that the clocks have
-    # ramped, then time product, unsplit, product: the mean of the two product
-    # runs cancels a drift of the clock over the measurement
+    # ramped, then time product, stage chain, product: the mean of the two
+    # product runs cancels a drift of the clock over the measurement
     t0 = time.perf_counter()
     i = 0
     while i < args.warmup or time.perf_counter() - t0 < 0.5:
@@ -361,10 +371,10 @@ def _run_shape(args):
     t_prod_a = timed(product)
     t_unsplit = timed(unsplit)
     t_prod = 0.5 * (t_prod_a + timed(product))
-    same = all(torch.equal(a.view(torch.int64), b.view(torch.int64)) for a, b in zip(*outs))
+    differ = sum(int((a != b).sum().item()) for a, b in zip(*outs))
     gf = lambda t: 2.0 * m * n * k / t / 1e9
     rec = {
-        "metric": "product entry point GFLOP/s (2mnk/t) on the given shape; unsplit stage calls beside it",
+        "metric": "product entry point GFLOP/s (2mnk/t) on the given shape; unsplit stage chain beside it",
         "value": round(gf(t_prod), 3),
         "unit": "GFLOP/s",
         "n_gpus": 1,
@@ -379,13 +389,11 @@ def _run_shape(args):
         "config": {"workload": f"{'qd' if args.qd else 'dd'} {m}x{n}x{k}", "m": m, "n": n, "k": k, "slices": ns,
                    "description": "entries U(-1,1), lo (further components) at 2^-53 relative scale"},
         "split_plan": {"first_split_row": ddg.split_first_row(m, n, k, ns), "parts": ddg.split_parts(m, n, k, ns)},
-        "unsplit": {"ms_per_step": round(t_unsplit * 1e3, 4), "value": round(gf(t_unsplit), 3)},
-        "speedup_vs_unsplit": round(t_unsplit / t_prod, 3),
-        "bit_identical_to_unsplit": bool(same),
+        "stage_chain": {"ms_per_step": round(t_unsplit * 1e3, 4), "value": round(gf(t_unsplit), 3)},
+        "speedup_vs_stage_chain": round(t_unsplit / t_prod, 3),
+        "words_differing_from_stage_chain": differ,
     }
     print(json.dumps(rec), flush=True)
-    if not same:
-        sys.exit(3)
 
 
 def _run_qd(args, w):
@@ -431,8 +439,11 @@ def _run_qd(args, w):
         step(ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    import statistics
+    step_l = [e[0].elapsed_time(e[2]) for e in ev]
+    gemm_l = [e[1].elapsed_time(e[2]) for e in ev]
     split_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    gemm_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    gemm_ms = sum(gemm_l) / args.steps
     value = 2.0 * m * n * k / (elapsed / args.steps) / 1e9
     gemm_tflops = QD_PAIRS * 2.0 * m * n * k / (gemm_ms * 1e-3) / 1e12
     split_bytes = (32.0 + 128.0) * (m * k + k * n)  # four components read, sixteen slices written
@@ -472,7 +483,8 @@ def _run_qd(args, w):
             "split_frac_hbm": round(split_bytes / (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "gemm_ms": round(gemm_ms, 4),
         },
-        "timing": _timing(ev),
+        "timing": {"step_ms_median": round(statistics.median(step_l), 4), "step_ms_min": round(min(step_l), 4),
+                   "gemm_ms_median": round(statistics.median(gemm_l), 4), "gemm_ms_min": round(min(gemm_l), 4)},
     }
     if not args.no_cpu_baseline:
         from fractions import Fraction

@@ -87,6 +87,11 @@ _SIGNATURES = {
     "ddgemm_split_first_row": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "ddgemm_split_first_tile": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "dd_gemm_noalloc": (_st, [_i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp]),
+    "dd_sliced_gemm_pairs": (_st, [_i64, _i64, _i64, _vp, _vp, _vp, _i64, _vp]),
+    "dd_sliced_gemm_pairs_ns": (_st, [_i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _i64, _vp]),
+    "dd_gemm_ws_timed": (_st, [_i64, _i64, _i64, ctypes.c_int, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
+                               _vp, _sz, _vp, _vp]),
+    "dd_gemm_kblock_max": (_i64, [ctypes.c_int]),
     "ddgemm_status_string": (ctypes.c_char_p, [_st]),
     "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
 }
@@ -209,6 +214,14 @@ def _check_lo(lo, hi, name):
         raise ValueError(f"{name} must have the same strides as its hi plane")
 
 
+def pair_products(nslices: int = NUM_SLICES) -> int:
+    """FP64 matrix products per k-block of the pair-packed schedule (20 for 8
+    slices): slices 2u, 2u+1 of A packed into one operand, every product
+    covering two window pairs but where only one lies in the window."""
+    return sum(1 for u in range((nslices + 1) // 2) for t in range(nslices)
+               if (2 * u + 1 < nslices and 2 * u + 1 + t <= nslices - 1) or 2 * u + t == nslices - 1)
+
+
 def k_max(nslices: int = NUM_SLICES) -> int:
     """Largest k for n slices (§2 eq. (5): at most 67,108,865 exact terms per level sum)."""
     return K_MAX if nslices <= NUM_SLICES else 67108865 // nslices
@@ -317,6 +330,26 @@ def sliced_gemm_renorm(m, n, k, A_slices, E, B_slices, F, C_hi=None, C_lo=None, 
     return C_hi, C_lo
 
 
+def sliced_gemm_pairs(m: int, n: int, k: int, A_slices, B_slices, units=None, stream=None,
+                      nslices: int = NUM_SLICES):
+    """The exact group sums of the pair-packed schedule the product entry points
+    run: an int64 (nslices - 1, m, n) tensor, group g in units 2^(-13(g+3))."""
+    dev = _operand_buffers(m, n, k, A_slices, None, B_slices, None, nslices)
+    if units is None:
+        units = torch.empty((nslices - 1, m, n), dtype=torch.int64, device=dev)
+    if tuple(units.shape) != (nslices - 1, m, n):
+        raise ValueError(f"units must be a ({nslices - 1}, m, n) tensor, got {tuple(units.shape)}")
+    _buffer(units, "units", torch.int64, (nslices - 1) * m * n, dev)
+    _check(lib.dd_sliced_gemm_pairs_ns(m, n, k, nslices, _ptr(A_slices), _ptr(B_slices), _ptr(units), max(n, 1),
+                                       _stream(stream)))
+    return units
+
+
+def kblock_max(nslices: int = NUM_SLICES) -> int:
+    """Largest k-block of the product entry points (longer k runs in blocks)."""
+    return lib.dd_gemm_kblock_max(nslices)
+
+
 def _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo):
     lda = _matrix(A_hi, "A_hi")
     _check_lo(A_lo, A_hi, "A_lo")
@@ -361,6 +394,19 @@ def _dd_gemm_call(m, n, k, nslices, kblock, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_
     else:
         _check(lib.dd_gemm_ws_ns(m, n, k, nslices, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
                                  _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dd_gemm_timed(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo, workspace, after_split, stream=None,
+                  nslices: int = NUM_SLICES):
+    """dd_gemm on the caller's workspace, recording the hipEvent_t handle
+    `after_split` (an int, or None) on the stream once the operands are sliced."""
+    m, n, k, lda, ldb, ldc, C_hi, C_lo, dev = _gemm_args(A_hi, A_lo, B_hi, B_lo, C_hi, C_lo)
+    workspace = _workspace(workspace, workspace_size(m, n, k, nslices), dev, stream)
+    with torch.cuda.device(dev):
+        _check(lib.dd_gemm_ws_timed(m, n, k, nslices, _ptr(A_hi), _ptr(A_lo), lda, _ptr(B_hi), _ptr(B_lo), ldb,
+                                    _ptr(C_hi), _ptr(C_lo), ldc, _ptr(workspace), workspace.numel(), after_split,
+                                    _stream(stream)))
+    return C_hi, C_lo
 
 
 def dd_gemm_alloc(A_hi, A_lo, B_hi, B_lo, C_hi=None, C_lo=None, stream=None):

@@ -114,7 +114,11 @@ ddgemm_status_t validate_gemm_dims(int64_t m, int64_t n, int64_t k) {
     return DDGEMM_SUCCESS;
 }
 
-bool kblock_ok(int64_t k, int ns, int64_t kblock) { return k == 0 || (kblock >= 1 && kblock <= k_max(ns)); }
+// The product entry points run the pair-packed schedule on k-blocks of at most
+// this many values: the slicer's limit and the int64 bound of the group sums.
+inline int64_t product_k_max(int ns) { return k_max(ns) < pair_k_max(ns) ? k_max(ns) : pair_k_max(ns); }
+
+bool kblock_ok(int64_t k, int ns, int64_t kblock) { return k == 0 || (kblock >= 1 && kblock <= product_k_max(ns)); }
 
 int64_t block_count(int64_t k, int64_t kblock) { return k == 0 ? 1 : (k + kblock - 1) / kblock; }
 
@@ -168,9 +172,9 @@ int64_t qd_default_kblock(int64_t k) {
 // [ns][m - first_row][n] start at plan.first_row.  `piece(rows, cols, r, c,
 // levels)` renormalises the rows x cols block at output (r, c) whose level
 // sums start at `levels` (row stride n, plane stride (m - first_row) n).
-template <class Piece>
-hipError_t renorm_split_tiles(int64_t m, int64_t n, int ns, const SplitPlan& plan, const double* L, Piece&& piece) {
-    const GemmGeometry g = gemm_geometry(ns);
+template <class T, class Piece>
+hipError_t renorm_split_tiles(int64_t m, int64_t n, const GemmGeometry& g, const SplitPlan& plan, const T* L,
+                              Piece&& piece) {
     const int64_t tiles_n = (n + g.tile_n - 1) / g.tile_n;
     const int64_t r0 = plan.first_row, mt = m - r0;
     const int64_t c0 = plan.first_tile % tiles_n * g.tile_n;
@@ -195,7 +199,7 @@ QdPlanes offset_planes(const QdPlanes& X, int64_t off) {
 namespace ddg {
 
 int64_t default_kblock(int64_t k, int ns) {
-    const int64_t km = k_max(ns);
+    const int64_t km = product_k_max(ns);
     if (k <= km) return k;
     const int64_t blocks = (k + km - 1) / km;
     return (k + blocks - 1) / blocks;
@@ -242,8 +246,10 @@ size_t dd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int nslices, i
     ws.add_slices(dd_split_slices_bytes_ns(n, kb, nslices), n, kb);
     ws.add(m, 4).add(n, 4);
     if (block_count(k, kblock) > 1) ws.add(m, n, 8).add(m, n, 8);  // (hi, lo) of the blocks after the first
-    const SplitPlan plan = split_plan(m, n, kb, nslices, true);
-    if (plan.parts > 1) ws.add(nslices, m - plan.first_row, n * 8);  // level planes of the rows split over k
+    if (kb > pair_chunk_k(nslices)) ws.add(nslices - 1, m * n, 8);   // int64 group sums between k-chunks
+    const SplitPlan plan = pair_split_plan(m, n, kb, nslices);
+    if (plan.parts > 1)  // int64 group sums of each k-part of the rows split over k
+        ws.add(plan.parts * (nslices - 1), m - plan.first_row, n * 8);
     return ws.bytes();
 }
 
@@ -323,10 +329,36 @@ ddgemm_status_t dd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k, const dou
     return dd_sliced_gemm_renorm_ns(m, n, k, kSlices, A_slices, E, B_slices, F, C_hi, C_lo, ldc, stream);
 }
 
-ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock, const double* A_hi,
-                              const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo,
-                              int64_t ldb, double* C_hi, double* C_lo, int64_t ldc, void* workspace,
-                              size_t ws_bytes, void* stream) {
+ddgemm_status_t dd_sliced_gemm_pairs_ns(int64_t m, int64_t n, int64_t k, int nslices, const double* A_slices,
+                                        const double* B_slices, int64_t* units, int64_t ldu, void* stream) {
+    if (validate_sizes(m, n, k) != DDGEMM_SUCCESS || !ns_ok(nslices) || k > product_k_max(nslices))
+        return DDGEMM_ERROR_INVALID_VALUE;
+    if (!ld_ok(ldu, m, n) || !size_ok(m * ldu, nslices - 1)) return DDGEMM_ERROR_INVALID_VALUE;
+    if (m == 0 || n == 0) return DDGEMM_SUCCESS;
+    if (!units || (k > 0 && (!A_slices || !B_slices))) return DDGEMM_ERROR_INVALID_VALUE;
+    ddgemm_status_t st = check_device();
+    if (st != DDGEMM_SUCCESS) return st;
+    const int64_t plane = m * ldu;
+    return launched(launch_pair_gemm(m, n, k, nslices, A_slices, B_slices, kPairToUnits, nullptr, nullptr,
+                                     OutPlanes{}, 0, units, ldu, plane, 0, 0, -1, 1,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+ddgemm_status_t dd_sliced_gemm_pairs(int64_t m, int64_t n, int64_t k, const double* A_slices,
+                                     const double* B_slices, int64_t* units, int64_t ldu, void* stream) {
+    return dd_sliced_gemm_pairs_ns(m, n, k, kSlices, A_slices, B_slices, units, ldu, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// dd_gemm_ws_kb, and with after_split an event recorded on the stream once the
+// first k-block's operands are sliced (dd_gemm_ws_timed).
+ddgemm_status_t product_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock, const double* A_hi,
+                           const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb,
+                           double* C_hi, double* C_lo, int64_t ldc, void* workspace, size_t ws_bytes, void* stream,
+                           void* after_split) {
     const ProductCheck chk =
         check_dd_product(m, n, k, nslices, kblock, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc);
     if (chk.status != DDGEMM_SUCCESS || chk.empty) return chk.status;
@@ -350,31 +382,43 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
     double* T_hi = reinterpret_cast<double*>(w);  // block results after the first (blocks > 1)
     double* T_lo = T_hi + (blocks > 1 ? align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8) / 8 : 0);
     if (blocks > 1) w += 2 * align_up(static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
-    double* L = reinterpret_cast<double*>(w);     // level planes [nslices][rows][n] of the rows split over k
-    const SplitPlan plan_kb = split_plan(m, n, kb, nslices, true);
-    const int64_t split_rows = plan_kb.parts > 1 ? m - plan_kb.first_row : 0;  // rows the planes hold
+    const int ns = nslices;
+    int64_t* U = nullptr;  // int64 group sums [ns-1][m][n] between k-chunks
+    if (kb > pair_chunk_k(ns)) {
+        U = reinterpret_cast<int64_t*>(w);
+        w += align_up(static_cast<size_t>(ns - 1) * static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
+    }
+    int64_t* P = reinterpret_cast<int64_t*>(w);  // part planes [parts][ns-1][rows][n] of the rows split over k
+    const SplitPlan plan_kb = pair_split_plan(m, n, kb, ns);
+    const int64_t part_cells = plan_kb.parts > 1 ? plan_kb.parts * (m - plan_kb.first_row) : 0;
 
-    // One block's product into (hi, lo) planes: fused, or its rows from
-    // plan.first_row on split over k into the level planes and renormalised
-    // after (the rows before it fused, in one launch over whole tile rows).
+    // One block's product into (hi, lo) planes: the pair-packed schedule with
+    // the nearest double-double of each entry's exact total, or, for the tiles
+    // from plan.first_tile on, the same in k-parts whose group sums are added
+    // and rounded by one more launch (the tiles before it unsplit).
     auto block_gemm = [&](int64_t kc, double* d_hi, double* d_lo, int64_t ldd, hipStream_t st) {
-        // a block whose plan needs more rows of level planes than the workspace holds runs unsplit
-        const SplitPlan plan = kc == kb ? plan_kb : split_plan(m, n, kc, nslices, true);
-        if (plan.parts <= 1 || m - plan.first_row > split_rows)
-            return launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, d_hi, d_lo, ldd, true, st);
+        // a block whose plan needs more part planes than the workspace holds runs unsplit
+        const SplitPlan plan = kc == kb ? plan_kb : pair_split_plan(m, n, kc, ns);
+        const OutPlanes out{{d_hi, d_lo, nullptr, nullptr}};
+        const int64_t mn = m * n;
+        if (plan.parts <= 1 || plan.parts * (m - plan.first_row) > part_cells)
+            return launch_pair_gemm(m, n, kc, ns, A_sl, B_sl, kPairToDD, E, F, out, ldd, U, n, mn, 0, 0, -1, 1, st,
+                                    true);
         hipError_t err = hipSuccess;
         if (plan.first_tile > 0)  // whole rounds of tiles, unsplit
-            err = launch_sliced_gemm(m, n, kc, nslices, A_sl, B_sl, nullptr, 0, E, F, d_hi, d_lo, ldd, true, st,
-                                     plan.first_tile);
+            err = launch_pair_gemm(m, n, kc, ns, A_sl, B_sl, kPairToDD, E, F, out, ldd, U, n, mn, 0, 0,
+                                   plan.first_tile, 1, st, true);
+        const int64_t plane = (m - plan.first_row) * n, part_stride = (ns - 1) * plane;
         if (err == hipSuccess)
-            err = launch_sliced_gemm_split(m, n, kc, nslices, A_sl, B_sl, L, n, plan.parts, st, plan.first_tile);
+            err = launch_pair_gemm(m, n, kc, ns, A_sl, B_sl, kPairToUnits, nullptr, nullptr, OutPlanes{}, 0, P, n,
+                                   plane, part_stride, plan.first_tile, -1, plan.parts, st, true);
         if (err != hipSuccess) return err;
-        const int64_t plane = (m - plan.first_row) * n;
-        return renorm_split_tiles(m, n, nslices, plan, L, [&](int64_t rows, int64_t cols, int64_t r, int64_t c,
-                                                             const double* lv) {
-            return launch_levels_to_dd(rows, cols, nslices, lv, n, E + r, F + c, d_hi + r * ldd + c,
-                                       d_lo + r * ldd + c, ldd, st, plane);
-        });
+        return renorm_split_tiles(m, n, pair_geometry(ns), plan, static_cast<const int64_t*>(P),
+                                  [&](int64_t rows, int64_t cols, int64_t r, int64_t c, const int64_t* cells) {
+                                      const OutPlanes piece{{d_hi + r * ldd + c, d_lo + r * ldd + c, nullptr, nullptr}};
+                                      return launch_pair_parts(rows, cols, ns, 2, cells, n, plane, part_stride,
+                                                               plan.parts, E + r, F + c, piece, ldd, st);
+                                  });
     };
 
     // Block b covers k indices [b kb, min(k, (b+1) kb)): a separate sliced product
@@ -393,7 +437,9 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
         e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s, kSplitExps);
         if (e == hipSuccess) e = launch_split(kc, n, b_hi, b_lo, ldb, 1, nslices, F, B_sl, s, kSplitExps);
         if (e == hipSuccess) e = launch_split(kc, n, b_hi, b_lo, ldb, 1, nslices, F, B_sl, s, kSplitSlices);
-        if (e == hipSuccess) e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s, kSplitSlices);
+        // A in the pair-packed layout the product's GEMM reads
+        if (e == hipSuccess) e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s, kSplitSlices, true);
+        if (e == hipSuccess && b == 0 && after_split) e = hipEventRecord(static_cast<hipEvent_t>(after_split), s);
         if (e != hipSuccess) break;
         if (b == 0) {
             e = block_gemm(kc, C_hi, C_lo, ldc, s);
@@ -404,6 +450,29 @@ ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int6
     }
     return launched(e);
 }
+
+}  // namespace
+
+extern "C" {
+
+ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock, const double* A_hi,
+                              const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo,
+                              int64_t ldb, double* C_hi, double* C_lo, int64_t ldc, void* workspace,
+                              size_t ws_bytes, void* stream) {
+    return product_kb(m, n, k, nslices, kblock, A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo, ldc, workspace,
+                      ws_bytes, stream, nullptr);
+}
+
+ddgemm_status_t dd_gemm_ws_timed(int64_t m, int64_t n, int64_t k, int nslices, const double* A_hi,
+                                 const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb,
+                                 double* C_hi, double* C_lo, int64_t ldc, void* workspace, size_t ws_bytes,
+                                 void* after_split, void* stream) {
+    if (k < 0 || !ns_ok(nslices)) return DDGEMM_ERROR_INVALID_VALUE;
+    return product_kb(m, n, k, nslices, default_kblock(k, nslices), A_hi, A_lo, lda, B_hi, B_lo, ldb, C_hi, C_lo,
+                      ldc, workspace, ws_bytes, stream, after_split);
+}
+
+int64_t dd_gemm_kblock_max(int nslices) { return ns_ok(nslices) ? product_k_max(nslices) : 0; }
 
 ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices, const double* A_hi,
                               const double* A_lo, int64_t lda, const double* B_hi, const double* B_lo,
@@ -547,7 +616,7 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
                 e = launch_sliced_gemm_split(m, n, k, kQdSlices, A_sl, B_sl, L, n, plan.parts, s, plan.first_tile);
             const int64_t plane = (m - plan.first_row) * n;
             if (e == hipSuccess)
-                e = renorm_split_tiles(m, n, kQdSlices, plan, L, [&](int64_t rows, int64_t cols, int64_t r,
+                e = renorm_split_tiles(m, n, gemm_geometry(kQdSlices), plan, L, [&](int64_t rows, int64_t cols, int64_t r,
                                                                      int64_t c, const double* lv) {
                     OutPlanes piece_out = out;
                     for (int q = 0; q < 4; ++q) piece_out.c[q] = out.c[q] + r * ldc + c;
@@ -622,20 +691,32 @@ const char* ddgemm_status_string(ddgemm_status_t status) {
     return "unknown ddgemm status";
 }
 
+}  // extern "C"
+
+namespace {
+// The split plan a product entry point takes: pair-packed for the double-double
+// products, the level schedule for the quad-double one (16 slices).
+SplitPlan product_plan(int64_t m, int64_t n, int64_t k, int ns) {
+    return ns == kQdSlices ? split_plan(m, n, k, ns, true) : pair_split_plan(m, n, k, ns);
+}
+}  // namespace
+
+extern "C" {
+
 int64_t ddgemm_split_parts(int64_t m, int64_t n, int64_t k, int nslices) {
     if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return 0;
-    return split_plan(m, n, k, nslices, true).parts;
+    return product_plan(m, n, k, nslices).parts;
 }
 
 int64_t ddgemm_split_first_row(int64_t m, int64_t n, int64_t k, int nslices) {
     if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return -1;
-    const SplitPlan plan = split_plan(m, n, k, nslices, true);
+    const SplitPlan plan = product_plan(m, n, k, nslices);
     return plan.parts > 1 ? plan.first_row : m;
 }
 
 int64_t ddgemm_split_first_tile(int64_t m, int64_t n, int64_t k, int nslices) {
     if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return -1;
-    return split_plan(m, n, k, nslices, true).first_tile;
+    return product_plan(m, n, k, nslices).first_tile;
 }
 
 ddgemm_status_t ddgemm_probe_mfma_f64(double* out, void* stream) {

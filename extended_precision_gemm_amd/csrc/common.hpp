@@ -71,9 +71,11 @@ int64_t default_kblock(int64_t k, int ns);
 ddgemm_status_t check_current_device();
 
 // Host-side launch helpers implemented next to their kernels.
+// pairs: an A operand (axis 0) in the pair-packed layout the product's GEMM
+// reads (plane 2u = slices 2u + 2u+1, plane 2u+1 = slice 2u).
 hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
                         int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream,
-                        int phases = kSplitAll);
+                        int phases = kSplitAll, bool pairs = false);
 hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                               const double* B_slices, double* levels, int64_t ldl,
                               const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,
@@ -142,5 +144,68 @@ hipError_t launch_qd_levels_to_units(int64_t m, int64_t n, const double* levels,
 hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
                           const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
                           hipStream_t stream, int64_t tile_count = -1);
+
+// The pair-packed schedule (include/ddgemm.h, dd_sliced_gemm_pairs): slices
+// 2u and 2u+1 of an A entry as one exact 26-bit operand, so one product of
+// 39-bit terms covers two window pairs; ns - 1 group sums per output entry,
+// group g counting units 2^(-13(g+3)).
+//   pair_products(ns)   matrix products per k-block and 16x16 block (20 for 8);
+//   pair_term_max(ns)   the largest |group sum| one value of k can add (all digits 8191);
+//   pair_chunk_k(ns)    the most values of k whose FP64 group sums stay below
+//                       2^53 units, i.e. exact, in multiples of 16;
+//   pair_k_max(ns)      the most values of k whose int64 group sums stay below 2^63.
+constexpr int64_t pair_products(int ns) {
+    int64_t c = 0;
+    for (int u = 0; 2 * u < ns; ++u)
+        for (int t = 0; t < ns; ++t)
+            if ((2 * u + 1 < ns && 2 * u + 1 + t <= ns - 1) || 2 * u + t == ns - 1) ++c;
+    return c;
+}
+constexpr int64_t pair_term_max(int ns) {
+    constexpr int64_t d = (int64_t{1} << kSliceBits) - 1;
+    int64_t worst = 0;
+    for (int g = 0; g + 1 < ns; ++g) {
+        int64_t sum = 0;
+        for (int u = 0; 2 * u < ns; ++u)
+            for (int t = 0; t < ns; ++t) {
+                if (2 * u + 1 < ns && 2 * u + 1 + t <= ns - 1) {
+                    if (2 * u + t == g) sum += ((d << kSliceBits) + d) * d;
+                } else if (2 * u + t == ns - 1 && g == ns - 2) {
+                    sum += d * d;
+                }
+            }
+        worst = sum > worst ? sum : worst;
+    }
+    return worst;
+}
+constexpr int64_t pair_chunk_k(int ns) {
+    return (((int64_t{1} << 53) - 1) / pair_term_max(ns)) / kPackK * kPackK;
+}
+constexpr int64_t pair_k_max(int ns) { return INT64_MAX / pair_term_max(ns); }
+static_assert(pair_products(8) == 20 && pair_products(16) == 72, "pair-packed product counts");
+static_assert(pair_chunk_k(8) == 4096 && pair_chunk_k(16) == 2048, "exact FP64 chunks");
+static_assert(pair_k_max(8) == 4194304, "exact int64 group sums");
+
+// What a pair-packed launch produces: the nearest double-double or quad double
+// of each entry, or the group sums in int64 units (stage call, split parts).
+enum PairOut { kPairToDD = 0, kPairToQD = 1, kPairToUnits = 2 };
+// A_prepacked: A_slices in the pair-packed layout (launch_split with pairs),
+// else the standard one (the sums of slice pairs are formed in registers).
+hipError_t launch_pair_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices, const double* B_slices,
+                            PairOut out, const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
+                            int64_t* units, int64_t ldu, int64_t plane, int64_t part_stride, int64_t tile_first,
+                            int64_t count, int64_t parts, hipStream_t stream, bool A_prepacked = false);
+// Geometry of the pair-packed launch for ns slices (mfma_per_stage counts its products).
+GemmGeometry pair_geometry(int ns);
+// Split parts of a pair-packed product -> results: for the rows x cols block of
+// outputs whose group-sum cells start at `units` (group stride `plane`, row
+// stride ldu, part stride part_stride), add the parts' sums and round the exact
+// total to two (C.c[0..1]) or four words.
+hipError_t launch_pair_parts(int64_t rows, int64_t cols, int ns, int words, const int64_t* units, int64_t ldu,
+                             int64_t plane, int64_t part_stride, int64_t parts, const int32_t* E, const int32_t* F,
+                             const OutPlanes& C, int64_t ldc, hipStream_t stream);
+// Split plan of a pair-packed product: tiles [0, first_tile) unsplit, the rest
+// in `parts` k-parts whose group sums go to part planes (no atomics).
+SplitPlan pair_split_plan(int64_t m, int64_t n, int64_t k, int ns);
 
 }  // namespace ddg

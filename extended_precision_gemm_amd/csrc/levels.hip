@@ -6,6 +6,7 @@
 #include "common.hpp"
 #include "dispatch_ns.hpp"
 #include "eft.hpp"
+#include "pair_levels.hpp"
 #include "qd_levels.hpp"
 
 namespace ddg {
@@ -95,7 +96,55 @@ __global__ void __launch_bounds__(256) zero_levels_kernel(int64_t m, int64_t n, 
     }
 }
 
+// One thread per output entry of a pair-packed product split over k: the
+// parts' int64 group sums are added (exact: the whole k stays within the int64
+// bound) and the exact total is rounded to W words.
+template <int NS, int W>
+__global__ void __launch_bounds__(256) pair_parts_kernel(int64_t m, int64_t n, const int64_t* __restrict__ units,
+                                                         int64_t ldu, int64_t plane, int64_t part_stride,
+                                                         int64_t parts, const int32_t* __restrict__ E,
+                                                         const int32_t* __restrict__ F, OutPlanes out, int64_t ldc) {
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (col >= n) return;
+    const int f = F[col];
+    for (int64_t row = blockIdx.y; row < m; row += gridDim.y) {
+        int64_t N[NS - 1];
+#pragma unroll
+        for (int g = 0; g < NS - 1; ++g) N[g] = 0;
+        const int64_t* cell = units + row * ldu + col;
+        for (int64_t p = 0; p < parts; ++p) {
+#pragma unroll
+            for (int g = 0; g < NS - 1; ++g) N[g] += cell[p * part_stride + g * plane];
+        }
+        double c[W];
+        pair_units_round<NS, W>(N, E[row] + f, c);
+#pragma unroll
+        for (int q = 0; q < W; ++q) out.c[q][row * ldc + col] = c[q];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_pair_parts(int64_t rows, int64_t cols, int ns, int words, const int64_t* units, int64_t ldu,
+                             int64_t plane, int64_t part_stride, int64_t parts, const int32_t* E, const int32_t* F,
+                             const OutPlanes& C, int64_t ldc, hipStream_t stream) {
+    if (rows == 0 || cols == 0) return hipSuccess;
+    if (ns < kMinSlices || ns > kMaxSlices || parts < 1 || (words != 2 && words != 4)) return hipErrorInvalidValue;
+    const int64_t gy = rows < 65535 ? rows : 65535;
+    const dim3 grid(static_cast<unsigned>((cols + 255) / 256), static_cast<unsigned>(gy));
+    return dispatch_ns(ns, [&](auto c) {
+        constexpr int NS = decltype(c)::value;
+        if (words == 2)
+            pair_parts_kernel<NS, 2><<<grid, 256, 0, stream>>>(rows, cols, units, ldu, plane, part_stride, parts, E,
+                                                               F, C, ldc);
+        else if constexpr (NS == kQdSlices)
+            pair_parts_kernel<NS, 4><<<grid, 256, 0, stream>>>(rows, cols, units, ldu, plane, part_stride, parts, E,
+                                                               F, C, ldc);
+        else
+            return hipErrorInvalidValue;  // four words: the quad-double product only
+        return hipGetLastError();
+    });
+}
 
 hipError_t launch_zero_levels(int64_t m, int64_t n, int ns, double* levels, int64_t ldl, hipStream_t stream) {
     if (m == 0 || n == 0) return hipSuccess;

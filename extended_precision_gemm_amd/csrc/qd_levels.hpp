@@ -17,14 +17,15 @@
 
 namespace ddg {
 
-// c[0..3] = the nearest quad double of T * 2^base, T an L-limb two's-complement
-// integer (greedy: each word the nearest double of what is left).
-template <int L>
-__device__ __forceinline__ void qd_round_total(WideInt<L> T, int base, double (&c)[4]) {
+// c[0..W-1] = the nearest W-word multiple double of T * 2^base, T an L-limb
+// two's-complement integer (greedy: each word the nearest double of what is
+// left); W = 2 is the nearest double-double, W = 4 the nearest quad double.
+template <int W, int L>
+__device__ __forceinline__ void round_words(WideInt<L> T, int base, double (&c)[W]) {
     bool neg = wide_is_neg(T);
     if (neg) wide_negate(T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < W; ++i) {
         const int b = wide_bit_length(T);
         double v = 0.0;
         bool up = false;
@@ -51,6 +52,11 @@ __device__ __forceinline__ void qd_round_total(WideInt<L> T, int base, double (&
         c[i] = (b > 0 && neg) ? -v : v;  // an exact zero remainder gives +0
         if (up) neg = !neg;
     }
+}
+
+template <int L>
+__device__ __forceinline__ void qd_round_total(WideInt<L> T, int base, double (&c)[4]) {
+    round_words<4, L>(T, base, c);
 }
 
 template <int NL>

@@ -27,6 +27,7 @@
 #include "common.hpp"
 #include "dispatch_ns.hpp"
 #include "eft.hpp"
+#include "pair_levels.hpp"
 #include "qd_levels.hpp"
 
 namespace ddg {
@@ -40,6 +41,14 @@ __device__ __forceinline__ int frag_col(int lane) { return lane & 15; }
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_void_t;
 
+// A value the whole wave holds, moved to scalar registers (a 64-bit division of
+// uniform operands is otherwise left in vector registers).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Order the compiler's memory operations around a hardware barrier or wait
 // without adding any instruction.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -51,8 +60,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int WM, int WN, int KS, int NBUF, int WGS, int NS, int RPW = 2>
+// ISSUE: where a stage's copy of a later stage is issued -- 0 after the first
+// k-block's fragment reads (halfway through a stage of two k-blocks), 1 right
+// after the stage's barrier, before any fragment read.
+template <int WM, int WN, int KS, int NBUF, int WGS, int NS, int RPW = 2, int ISSUE = 0>
 struct GemmConfig {
+    static constexpr int kIssueEarly = ISSUE;
     static constexpr int kWaves = WM * WN;
     static constexpr int kRPW = RPW;                                 // 16-row blocks per wave
     static constexpr int kNBuf = NBUF;
@@ -84,21 +97,85 @@ enum Epilogue : int {
     kEpiUnitsAdd = 4,  // add them in integer units to the int64 planes
     kEpiUnitsQD = 5,   // add them to the int64 planes' values and round that total
     kEpiAtomicLevels = 6,  // add them, as doubles, into level planes (one k-part of a split product)
+    kEpiPairUnits = 7,     // pair-packed schedule: store its group sums in integer units to int64 planes
+};
+
+// One product of the pair-packed schedule: A operand u (slices 2u and 2u+1
+// packed, or slice 2u alone), B slice t, into accumulator acc.
+struct PairProduct {
+    int u, t, acc;
+    bool packed;
+};
+
+// The products of one k-block for NS slices, in issue order: round i holds
+// the i-th product of every accumulator that has one, accumulators 0..NS-2
+// being the groups 2u + t of the packed products and NS - 1 the single ones.
+template <int NS>
+struct PairSchedule {
+    static constexpr int kMax = NS * NS;
+    PairProduct order[kMax] = {};
+    int count = 0;
+    constexpr PairSchedule() {
+        PairProduct all[kMax] = {};
+        int per_acc[NS] = {};
+        int n = 0;
+        for (int u = 0; 2 * u < NS; ++u)
+            for (int t = 0; t < NS; ++t) {
+                if (2 * u + 1 < NS && 2 * u + 1 + t <= NS - 1)
+                    all[n++] = PairProduct{u, t, 2 * u + t, true};
+                else if (2 * u + t == NS - 1)
+                    all[n++] = PairProduct{u, t, NS - 1, false};
+            }
+        for (int i = 0; i < n; ++i) ++per_acc[all[i].acc];
+        int most = 0;
+        for (int g = 0; g < NS; ++g) most = per_acc[g] > most ? per_acc[g] : most;
+        for (int round = 0; round < most; ++round)
+            for (int g = 0; g < NS; ++g) {
+                int seen = 0;
+                for (int i = 0; i < n; ++i)
+                    if (all[i].acc == g && seen++ == round) order[count++] = all[i];
+            }
+    }
+};
+
+// Extra arguments of the pair-packed schedule.  Every chunk_stages stages of
+// k (0: never) the exact group sums leave the accumulators for int64 planes,
+// so that no FP64 sum ever holds more than the terms it adds exactly;
+// `units` + blockIdx.y part_stride + g plane + (row - row_off) ldl + col is
+// the cell of group g of output (row, col) in those planes (k-part blockIdx.y
+// of a split product).
+struct PairArgs {
+    int64_t chunk_stages, part_stride, row_off;
 };
 
 // The second launch bound is the minimum number of waves per SIMD (four SIMDs
 // per CU): kWGS workgroups of kWaves waves.
-template <class C, int EPI>
+//
+// PAIRED selects the pair-packed schedule (include/ddgemm.h,
+// dd_sliced_gemm_pairs): slices 2u and 2u+1 of A are added into one exact
+// 26-bit operand in registers, and each product covers two window pairs, NS - 1
+// group accumulators in place of NS levels (20 products per k-block for eight
+// slices instead of 36).
+// PREPACKED (pair-packed schedule only): A_slices come in the pair-packed
+// layout (plane 2u = slices 2u + 2u+1, plane 2u+1 = slice 2u), so no sum is
+// formed in the k loop.
+template <class C, int EPI, bool PAIRED = false, bool PREPACKED = false>
 __global__ void __launch_bounds__(C::kThreads, C::kWGS * C::kWaves / 4)
 sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t tile0,
                    const double* __restrict__ Ap, const double* __restrict__ Bp,
                    double* __restrict__ levels, int64_t* __restrict__ units, int64_t ldl, int64_t plane,
                    const int32_t* __restrict__ E, const int32_t* __restrict__ F,
-                   OutPlanes out, int64_t ldc) {
+                   OutPlanes out, int64_t ldc, PairArgs pair) {
     constexpr int KS = C::kKS;
     constexpr int RPW = C::kRPW;
     constexpr int NBUF = C::kNBuf;
     constexpr int NS = C::kNS;
+    // accumulators per 16x16 block: NS levels, or for the pair-packed schedule
+    // its NS - 1 groups with the single products of the deepest group apart
+    // (accumulator NS - 1), so that no FP64 sum chains more than half the
+    // products of a k-block
+    constexpr int NACC = NS;
+
     __shared__ __attribute__((aligned(1024))) double lds[NBUF * C::kStageDoubles];
 
     const int lane = threadIdx.x & 63;
@@ -110,7 +187,9 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t ti
     const int64_t tm = tile / tiles_n;
     const int64_t tn = tile % tiles_n;
     const int64_t rb0 = tm * C::kTBM, cb0 = tn * C::kTBN;
-    const int64_t nstages = KB / KS;  // KB is a multiple of 4 (k is packed to 16)
+    // stages of KS k-blocks: KB <= 2^21 (k within the exact-sum bound), so the
+    // stage counters are 32-bit and compare in scalar registers
+    const int nstages = static_cast<int>(KB / KS);  // KB is a multiple of 4 (k is packed to 16)
 
     // A stage in LDS is the runs of its blocks back to back (A blocks first,
     // then B blocks), kBlockStage doubles each.  1 KB piece q of it is copied by
@@ -124,12 +203,14 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t ti
 #pragma unroll
     for (int i = 0; i < C::kPiecesPerWave; ++i) {
         if constexpr (C::kEvenPieces && C::kBlockStage % 128 == 0) {
-            // every piece inside one block's run: the block is uniform per piece
-            const int q = i * C::kWaves + wave;
+            // every piece inside one block's run: the block is uniform per piece,
+            // so the piece's base and LDS offset live in scalar registers and a
+            // copy is a scalar base plus the lane's 16-byte offset
+            const int q = i * C::kWaves + uwave;
             const int blk = q / (C::kBlockStage / 128), pc = q % (C::kBlockStage / 128);
             const double* base = blk < C::kTBM ? Ap + (rb0 + blk) * KB * C::kSetDoubles
                                                : Bp + (cb0 + blk - C::kTBM) * KB * C::kSetDoubles;
-            src[i] = base + pc * 128 + lane * 2;
+            src[i] = base + pc * 128;
             dst[i] = blk * C::kBlockStage + pc * 128;
         } else {
             int q = i * C::kWaves + uwave;
@@ -142,31 +223,75 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t ti
             dst[i] = q * 128;
         }
     }
+    // the lane's part of a piece's address (the uneven path keeps it in src)
+    constexpr bool kScalarBase = C::kEvenPieces && C::kBlockStage % 128 == 0;
+    const int lane_off = kScalarBase ? lane * 2 : 0;
     auto issue = [&](int64_t st, int buf) {
 #pragma unroll
         for (int i = 0; i < C::kPiecesPerWave; ++i)
             if (C::kEvenPieces || i + 1 < C::kPiecesPerWave || i * C::kWaves + uwave < C::kPieces)
-                __builtin_amdgcn_global_load_lds((global_void_t*)(src[i] + st * C::kBlockStage),
+                __builtin_amdgcn_global_load_lds((global_void_t*)(src[i] + st * C::kBlockStage + lane_off),
                                                  (lds_void_t*)(lds + buf * C::kStageDoubles + dst[i]), 16, 0, 0);
     };
 
-    double4_t acc[NS][RPW];
+    double4_t acc[NACC][RPW];
 #pragma unroll
-    for (int l = 0; l < NS; ++l)
+    for (int l = 0; l < NACC; ++l)
 #pragma unroll
         for (int r = 0; r < RPW; ++r) acc[l][r] = double4_t{0.0, 0.0, 0.0, 0.0};
 
     // Stages [s0, s1): all of them, or this workgroup's k-part of a split product
     // (blockIdx.y of gridDim.y parts).
-    int64_t s0 = 0, s1 = nstages;
-    if constexpr (EPI == kEpiAtomicLevels) {
-        s0 = nstages * blockIdx.y / gridDim.y;
-        s1 = nstages * (blockIdx.y + 1) / gridDim.y;
+    int s0 = 0, s1 = nstages;
+    if constexpr (EPI == kEpiAtomicLevels || EPI == kEpiPairUnits) {
+        s0 = static_cast<int>(uniform64(static_cast<int64_t>(nstages) * blockIdx.y / gridDim.y));
+        s1 = static_cast<int>(uniform64(static_cast<int64_t>(nstages) * (blockIdx.y + 1) / gridDim.y));
     }
+
+    const int64_t col = (cb0 + wc) * 16 + frag_col(lane);
+    // The int64 cell of group g = 0 of output (row, col); group g is g planes on.
+    int64_t* const part_units = units + static_cast<int64_t>(blockIdx.y) * pair.part_stride;
+    auto unit_cell = [&](int64_t row) { return part_units + (row - pair.row_off) * ldl + col; };
+    // Pair-packed schedule: move the group sums into the int64 planes (store
+    // the first time, add later) and restart the accumulators from zero.
+    bool flushed = false;
+    auto flush = [&]() {
+        // Row offset of this lane's cells, opaque to the compiler so that the
+        // cell addresses are formed here, at a flush, rather than hoisted out of
+        // the k loop into registers the matrix operands need.
+        int64_t row_lane = (rb0 + RPW * wr) * 16 + frag_row(lane, 0);
+        asm volatile("" : "+v"(row_lane));
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = row_lane + r * 16 + 4 * v;
+                if (row < m && col < n) {
+                    int64_t* u = unit_cell(row);
+#pragma unroll
+                    for (int g = 0; g < NS - 1; ++g) {
+                        int64_t x = pair_group_units(acc[g][r][v], g);
+                        if (g == NS - 2) x += pair_group_units(acc[NS - 1][r][v], g);
+                        if (flushed) x += u[g * plane];
+                        u[g * plane] = x;
+                    }
+                }
+            }
+#pragma unroll
+        for (int l = 0; l < NACC; ++l)
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) acc[l][r] = double4_t{0.0, 0.0, 0.0, 0.0};
+        flushed = true;
+        // the stage waits count vector-memory operations: drain these stores here
+        wait_vmcnt<0>();
+    };
+    int since_flush = 0;
+    const int chunk_stages = static_cast<int>(pair.chunk_stages);
+
     if (s1 > s0) {
 #pragma unroll
         for (int j = 0; j < NBUF - 1; ++j) issue(s0 + j < s1 ? s0 + j : s1 - 1, j);
-        for (int64_t st = s0; st < s1; ++st) {
+        for (int st = s0; st < s1; ++st) {
             // Stage st has landed once at most NBUF-2 younger stages are pending.
             wait_vmcnt<(NBUF - 2) * C::kPiecesPerWave>();
             compiler_fence();
@@ -176,13 +301,14 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t ti
             // finished reading (certified by the barrier above); it is issued
             // after the first fragment reads of this stage rather than before
             // them, so the matrix instructions start sooner (measured: +2-3 %).
-            const int64_t nxt = st + NBUF - 1;
-            const int64_t nxt_c = nxt < s1 ? nxt : s1 - 1;
+            const int nxt = st + NBUF - 1;
+            const int nxt_c = nxt < s1 ? nxt : s1 - 1;
 
             const double* stage = lds + ((st - s0) % NBUF) * C::kStageDoubles + lane;
+            if (C::kIssueEarly) issue(nxt_c, static_cast<int>((nxt - s0) % NBUF));
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
-                if (KS > 1 && j == KS / 2) issue(nxt_c, static_cast<int>((nxt - s0) % NBUF));
+                if (!C::kIssueEarly && KS > 1 && j == KS / 2) issue(nxt_c, static_cast<int>((nxt - s0) % NBUF));
                 const double* sa = stage + (RPW * wr) * C::kBlockStage + j * C::kSetDoubles;
                 const double* sb = stage + (C::kTBM + wc) * C::kBlockStage + j * C::kSetDoubles;
                 double a[NS][RPW], b[NS];
@@ -192,22 +318,100 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t ti
                     for (int r = 0; r < RPW; ++r) a[s][r] = sa[r * C::kBlockStage + s * kFragDoubles];
                     b[s] = sb[s * kFragDoubles];
                 }
-                if (KS == 1) issue(nxt_c, static_cast<int>((nxt - s0) % NBUF));
-                // Triangular schedule: pair (s, t) feeds level s + t < NS.
+                if (!C::kIssueEarly && KS == 1) issue(nxt_c, static_cast<int>((nxt - s0) % NBUF));
+                if constexpr (PAIRED) {
+                    // Slices 2u and 2u+1 of an entry share its sign and sit 13
+                    // bits apart: their sum is an exact 26-bit operand.  Product
+                    // (u, t) covers pairs (2u, t), (2u+1, t) into group 2u + t;
+                    // where only (2u, t) is in the window it runs alone, into the
+                    // single products' accumulator.  The products are issued in
+                    // rounds -- round i holds the i-th product of every
+                    // accumulator -- so that two products into one accumulator
+                    // are never adjacent.
+                    constexpr int NU = (NS + 1) / 2;
+                    double ap[NU][RPW];  // packed operands (pair-packed layout: the planes themselves)
 #pragma unroll
-                for (int s = 0; s < NS; ++s)
+                    for (int u = 0; u < NU; ++u)
 #pragma unroll
-                    for (int t = 0; s + t < NS; ++t)
+                        for (int r = 0; r < RPW; ++r) {
+                            if constexpr (PREPACKED)
+                                ap[u][r] = a[2 * u][r];
+                            else
+                                ap[u][r] = 2 * u + 1 < NS ? a[2 * u][r] + a[2 * u + 1][r] : a[2 * u][r];
+                        }
+                    // slice 2u alone: plane 2u + 1 of the pair-packed layout (the
+                    // last plane itself for an odd count), else plane 2u
+                    auto single = [&](int u, int r) {
+                        if constexpr (PREPACKED) return 2 * u + 1 < NS ? a[2 * u + 1][r] : a[2 * u][r];
+                        return a[2 * u][r];
+                    };
+                    constexpr PairSchedule<NS> sched{};
 #pragma unroll
-                        for (int r = 0; r < RPW; ++r)
-                            acc[s + t][r] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s][r], b[t], acc[s + t][r], 0, 0, 0);
+                    for (int i = 0; i < sched.count; ++i)
+#pragma unroll
+                        for (int r = 0; r < RPW; ++r) {
+                            const PairProduct p = sched.order[i];
+                            const double x = p.packed ? ap[p.u][r] : single(p.u, r);
+                            acc[p.acc][r] = __builtin_amdgcn_mfma_f64_16x16x4f64(x, b[p.t], acc[p.acc][r], 0, 0, 0);
+                        }
+                } else {
+                    // Triangular schedule: pair (s, t) feeds level s + t < NS.
+#pragma unroll
+                    for (int s = 0; s < NS; ++s)
+#pragma unroll
+                        for (int t = 0; s + t < NS; ++t)
+#pragma unroll
+                            for (int r = 0; r < RPW; ++r)
+                                acc[s + t][r] =
+                                    __builtin_amdgcn_mfma_f64_16x16x4f64(a[s][r], b[t], acc[s + t][r], 0, 0, 0);
+                }
+            }
+            if constexpr (PAIRED) {
+                if (chunk_stages > 0 && ++since_flush == chunk_stages && st + 1 < s1) {
+                    flush();
+                    since_flush = 0;
+                }
             }
         }
         // No direct-to-LDS copy may still be in flight when the workgroup ends.
         wait_vmcnt<0>();
     }
 
-    const int64_t col = (cb0 + wc) * 16 + frag_col(lane);
+    if constexpr (PAIRED) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = (rb0 + RPW * wr + r) * 16 + frag_row(lane, v);
+                if (row < m && col < n) {
+                    int64_t N[NS - 1];
+                    int64_t* u = flushed || EPI == kEpiPairUnits ? unit_cell(row) : nullptr;
+#pragma unroll
+                    for (int g = 0; g < NS - 1; ++g) {
+                        N[g] = pair_group_units(acc[g][r][v], g);
+                        if (g == NS - 2) N[g] += pair_group_units(acc[NS - 1][r][v], g);
+                        if (flushed) N[g] += u[g * plane];
+                    }
+                    if constexpr (EPI == kEpiPairUnits) {
+#pragma unroll
+                        for (int g = 0; g < NS - 1; ++g) u[g * plane] = N[g];
+                    } else if constexpr (EPI == kEpiDD) {
+                        double c[2];
+                        pair_units_round<NS, 2>(N, E[row] + F[col], c);
+                        out.c[0][row * ldc + col] = c[0];
+                        out.c[1][row * ldc + col] = c[1];
+                    } else {
+                        static_assert(EPI == kEpiQD, "pair-packed epilogues: units, dd, qd");
+                        double c[4];
+                        pair_units_round<NS, 4>(N, E[row] + F[col], c);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) out.c[q][row * ldc + col] = c[q];
+                    }
+                }
+            }
+        }
+        return;
+    } else {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
 #pragma unroll
@@ -264,6 +468,7 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t ti
             }
         }
     }
+    }
 }
 
 __global__ void __launch_bounds__(64) probe_mfma_kernel(double* __restrict__ out) {
@@ -302,6 +507,14 @@ template <> struct ConfigFor<14> { using type = GemmConfig<2, 4, 1, 2, 1, 14, 1>
 template <> struct ConfigFor<15> { using type = GemmConfig<2, 4, 1, 2, 1, 15, 1>; };
 template <> struct ConfigFor<16> { using type = GemmConfig<2, 4, 1, 2, 1, 16, 1>; };
 
+// Launch configuration of the pair-packed schedule per slice count.  Eight
+// slices: sixteen waves of one 16x16 block each (64x64 tile, four waves per
+// SIMD), two k-blocks per stage -- measured at 4096^3 against two-block strips
+// of eight waves (68.5 TFLOP/s), two 32x64 workgroups per CU (67.2), one or
+// more k-blocks per stage with two to four stages (65.2-69.4): 70.3 TFLOP/s.
+template <int NS> struct PairConfigFor { using type = typename ConfigFor<NS>::type; };
+template <> struct PairConfigFor<8> { using type = GemmConfig<4, 4, 2, 2, 1, 8, 1>; };
+
 template <int NS>
 hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
                           double* levels, int64_t ldl, const int32_t* E, const int32_t* F, double* C_hi,
@@ -318,11 +531,11 @@ hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slice
     if (fused)
         sliced_gemm_kernel<Cfg, kEpiDD><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
             m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, nullptr, 0, 0, E, F,
-            OutPlanes{{C_hi, C_lo, nullptr, nullptr}}, ldc);
+            OutPlanes{{C_hi, C_lo, nullptr, nullptr}}, ldc, PairArgs{});
     else if constexpr (NS == kSlices)
         sliced_gemm_kernel<Cfg, kEpiLevels><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
             m, n, ga.KB, tiles_n, 0, A_slices, B_slices, levels, nullptr, ldl, plane, nullptr, nullptr,
-            OutPlanes{{nullptr, nullptr, nullptr, nullptr}}, 0);
+            OutPlanes{{nullptr, nullptr, nullptr, nullptr}}, 0, PairArgs{});
     else
         return hipErrorInvalidValue;  // level planes are offered for the double-double product only
     return hipGetLastError();
@@ -346,11 +559,85 @@ hipError_t launch_split_ns(int64_t m, int64_t n, int64_t k, const double* A_slic
     const dim3 grid(static_cast<unsigned>(tiles - tile_first), static_cast<unsigned>(parts));
     sliced_gemm_kernel<Cfg, kEpiAtomicLevels><<<grid, Cfg::kThreads, 0, stream>>>(
         m, n, ga.KB, tiles_n, tile_first, A_slices, B_slices, levels, nullptr, ldl, plane, nullptr, nullptr,
-        OutPlanes{}, 0);
+        OutPlanes{}, 0, PairArgs{});
+    return hipGetLastError();
+}
+
+// The pair-packed schedule over the output tiles [tile_first, tile_first +
+// count) (count < 0: to the last tile), row-major, in `parts` k-parts.
+//   epi = kEpiDD / kEpiQD: one part; the nearest double-double / quad double
+//         of each entry's exact total into C.  When k needs more than one
+//         chunk, `units` holds the chunk planes [NS-1][m][ldu] (absolute rows).
+//   epi = kEpiPairUnits: each part stores its group sums into its own planes,
+//         part p at units + p part_stride, rows from tile_first's tile row on.
+template <int NS, bool PREPACKED>
+hipError_t launch_pair_ns(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices, int epi,
+                          const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc, int64_t* units,
+                          int64_t ldu, int64_t plane, int64_t part_stride, int64_t tile_first, int64_t count,
+                          int64_t parts, hipStream_t stream) {
+    using Cfg = typename PairConfigFor<NS>::type;
+    const PackGeom ga(m, k);
+    constexpr int BM = Cfg::kTBM * 16, BN = Cfg::kTBN * 16;
+    const int64_t tiles_n = (n + BN - 1) / BN;
+    const int64_t tiles = (m + BM - 1) / BM * tiles_n;
+    if (tile_first < 0 || tile_first > tiles || parts < 1 || parts > 65535) return hipErrorInvalidValue;
+    const int64_t launch = count < 0 || tile_first + count > tiles ? tiles - tile_first : count;
+    if (launch > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (launch == 0) return hipSuccess;
+    if (epi != kEpiPairUnits && parts != 1) return hipErrorInvalidValue;
+    constexpr int64_t kStageK = 4 * Cfg::kKS;
+    const int64_t chunk_stages = pair_chunk_k(NS) / kStageK;
+    const int64_t part_stages = (ga.KB / Cfg::kKS + parts - 1) / parts;
+    if (epi != kEpiPairUnits && part_stages > chunk_stages && !units) return hipErrorInvalidValue;
+    const PairArgs pa{chunk_stages, part_stride, epi == kEpiPairUnits ? tile_first / tiles_n * BM : 0};
+    const dim3 grid(static_cast<unsigned>(launch), static_cast<unsigned>(parts));
+    // the products read pre-packed A; the group sums also serve the stage call,
+    // which takes the standard layout
+    if (epi == kEpiDD && PREPACKED)
+        sliced_gemm_kernel<Cfg, kEpiDD, true, true><<<grid, Cfg::kThreads, 0, stream>>>(
+            m, n, ga.KB, tiles_n, tile_first, A_slices, B_slices, nullptr, units, ldu, plane, E, F, C, ldc, pa);
+    else if (epi == kEpiQD && PREPACKED) {
+        if constexpr (NS == kQdSlices)
+            sliced_gemm_kernel<Cfg, kEpiQD, true, true><<<grid, Cfg::kThreads, 0, stream>>>(
+                m, n, ga.KB, tiles_n, tile_first, A_slices, B_slices, nullptr, units, ldu, plane, E, F, C, ldc, pa);
+        else
+            return hipErrorInvalidValue;  // four words: the quad-double product only
+    } else if (epi == kEpiPairUnits)
+        sliced_gemm_kernel<Cfg, kEpiPairUnits, true, PREPACKED><<<grid, Cfg::kThreads, 0, stream>>>(
+            m, n, ga.KB, tiles_n, tile_first, A_slices, B_slices, nullptr, units, ldu, plane, nullptr, nullptr,
+            OutPlanes{}, 0, pa);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_pair_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices, const double* B_slices,
+                            PairOut out, const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
+                            int64_t* units, int64_t ldu, int64_t plane, int64_t part_stride, int64_t tile_first,
+                            int64_t count, int64_t parts, hipStream_t stream, bool A_prepacked) {
+    if (m == 0 || n == 0) return hipSuccess;
+    if (ns < kMinSlices || ns > kMaxSlices) return hipErrorInvalidValue;
+    const int epi = out == kPairToDD ? kEpiDD : out == kPairToQD ? kEpiQD : kEpiPairUnits;
+    return dispatch_ns(ns, [&](auto c) {
+        constexpr int NS = decltype(c)::value;
+        if (A_prepacked)
+            return launch_pair_ns<NS, true>(m, n, k, A_slices, B_slices, epi, E, F, C, ldc, units, ldu, plane,
+                                            part_stride, tile_first, count, parts, stream);
+        return launch_pair_ns<NS, false>(m, n, k, A_slices, B_slices, epi, E, F, C, ldc, units, ldu, plane,
+                                         part_stride, tile_first, count, parts, stream);
+    });
+}
+
+GemmGeometry pair_geometry(int ns) {
+    return dispatch_ns(ns, [&](auto c) {
+        using Cfg = typename PairConfigFor<decltype(c)::value>::type;
+        return GemmGeometry{Cfg::kTBM * 16, Cfg::kTBN * 16, Cfg::kKS,
+                            static_cast<int>(pair_products(decltype(c)::value)) * Cfg::kRPW * Cfg::kKS,
+                            Cfg::kWGS * Cfg::kWaves / 4, Cfg::kWGS * Cfg::kNBuf * Cfg::kStageDoubles * 8};
+    });
+}
 
 hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                               const double* B_slices, double* levels, int64_t ldl,
@@ -376,7 +663,7 @@ hipError_t launch_qd_gemm(int64_t m, int64_t n, int64_t k, const double* A_slice
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (tiles == 0) return hipSuccess;
     sliced_gemm_kernel<Cfg, kEpiQD><<<static_cast<unsigned>(tiles), Cfg::kThreads, 0, stream>>>(
-        m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, nullptr, 0, 0, E, F, C, ldc);
+        m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, nullptr, 0, 0, E, F, C, ldc, PairArgs{});
     return hipGetLastError();
 }
 
@@ -393,13 +680,13 @@ hipError_t launch_qd_gemm_block(int64_t m, int64_t n, int64_t k, const double* A
     const int64_t plane = m * n;  // level plane l of the int64 sums: units[l][row][col], row stride n
     if (step == kQdFirstBlock)
         sliced_gemm_kernel<Cfg, kEpiUnitsSet><<<g, Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0);
+            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0, PairArgs{});
     else if (step == kQdMiddleBlock)
         sliced_gemm_kernel<Cfg, kEpiUnitsAdd><<<g, Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0);
+            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, units, n, plane, nullptr, nullptr, OutPlanes{}, 0, PairArgs{});
     else
         sliced_gemm_kernel<Cfg, kEpiUnitsQD><<<g, Cfg::kThreads, 0, stream>>>(
-            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, units, n, plane, E, F, C, ldc);
+            m, n, ga.KB, tiles_n, 0, A_slices, B_slices, nullptr, units, n, plane, E, F, C, ldc, PairArgs{});
     return hipGetLastError();
 }
 

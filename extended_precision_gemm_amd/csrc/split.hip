@@ -100,6 +100,20 @@ __device__ __forceinline__ void slice_entry(double hi, double lo, int E, double 
     }
 }
 
+// The pair-packed layout of an A operand, read by the product's pair-packed
+// GEMM: plane 2u holds slices 2u and 2u+1 added -- one exact 26-bit value, as
+// the two share the entry's sign and sit 13 bits apart -- and plane 2u+1 holds
+// slice 2u alone; with an odd count the last plane keeps the last slice.
+template <int NS>
+__device__ __forceinline__ void pair_pack(double (&sl)[NS]) {
+#pragma unroll
+    for (int u = 0; 2 * u + 1 < NS; ++u) {
+        const double single = sl[2 * u];
+        sl[2 * u] = sl[2 * u] + sl[2 * u + 1];
+        sl[2 * u + 1] = single;
+    }
+}
+
 // One wave per row and k-part: E[row] = max frexp exponent over the row (axis
 // 0, the A operand).  Part y of gridDim.y covers columns [cols y / parts,
 // cols (y + 1) / parts).  With one part the decoded exponent is stored; with
@@ -178,7 +192,7 @@ __global__ void __launch_bounds__(NT) exp_cols_block_kernel(int64_t rows, int64_
 
 // One thread per packed (fragment, lane) position; writes the NS slices of
 // its entry.  AXIS 0: entry (o, p) is X[o][p]; AXIS 1: it is X[p][o].
-template <int AXIS, int NS>
+template <int AXIS, int NS, bool PK = false>
 __global__ void __launch_bounds__(256) slice_kernel(int64_t outer, int64_t k, int64_t KB,
                                                     int64_t total, const double* __restrict__ hi,
                                                     const double* __restrict__ lo, int64_t ld,
@@ -200,6 +214,7 @@ __global__ void __launch_bounds__(256) slice_kernel(int64_t outer, int64_t k, in
         }
         double sl[NS];
         slice_entry<NS>(x_hi, x_lo, E, sl);
+        if constexpr (PK) pair_pack<NS>(sl);
         double* dst = slices + frag * (NS * kFragDoubles) + lane;
 #pragma unroll
         for (int q = 0; q < NS; ++q) dst[q * kFragDoubles] = sl[q];
@@ -212,7 +227,7 @@ __global__ void __launch_bounds__(256) slice_kernel(int64_t outer, int64_t k, in
 // cache rather than HBM and no atomics are needed.  With several parts every
 // part computes the block's exponents (its re-reads hit the cache while the
 // operand fits there) and part 0 stores them.
-template <int AXIS, int NT, int NS>
+template <int AXIS, int NT, int NS, bool PK = false>
 __global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t k, int64_t KB,
                                                          const double* __restrict__ hi,
                                                          const double* __restrict__ lo, int64_t ld,
@@ -306,6 +321,10 @@ __global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t 
             }
             slice_entry<NS>(x_hi, x_lo, block_exp[oi + e], e == 0 ? sl0 : sl1);
         }
+        if constexpr (PK) {
+            pair_pack<NS>(sl0);
+            pair_pack<NS>(sl1);
+        }
         double2* dst = reinterpret_cast<double2*>(slices + (blk * KB + kb) * (NS * kFragDoubles) + lane);
 #pragma unroll
         for (int s = 0; s < NS; ++s) dst[s * (kFragDoubles / 2)] = make_double2(sl0[s], sl1[s]);
@@ -320,7 +339,7 @@ __global__ void __launch_bounds__(NT) split_block_kernel(int64_t outer, int64_t 
 // packed lanes 2(q % 32), 2(q % 32) + 1 of k-block q / 32; as NT is a multiple
 // of 32, thread t's pairs all lie on outer indices oi, oi + 1 with
 // oi = 2(t % 8).
-template <int AXIS, int NT, int NS, int PPT>
+template <int AXIS, int NT, int NS, int PPT, bool PK = false>
 __global__ void __launch_bounds__(NT) split_block_regs_kernel(int64_t outer, int64_t k, int64_t KB,
                                                               const double* __restrict__ hi,
                                                               const double* __restrict__ lo, int64_t ld,
@@ -377,6 +396,10 @@ __global__ void __launch_bounds__(NT) split_block_regs_kernel(int64_t outer, int
         double sl0[NS], sl1[NS];
         slice_entry<NS>(xh[i][0], xl[i][0], e0, sl0);
         slice_entry<NS>(xh[i][1], xl[i][1], e1, sl1);
+        if constexpr (PK) {
+            pair_pack<NS>(sl0);
+            pair_pack<NS>(sl1);
+        }
         const int lane = static_cast<int>(q & 31) * 2;
         double2* dst = reinterpret_cast<double2*>(slices + (blk * KB + (q >> 5)) * (NS * kFragDoubles) + lane);
 #pragma unroll
@@ -402,7 +425,7 @@ constexpr int64_t kSmallColsReread = 320ll << 20;
 template <int NS>
 hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
                            int64_t ldx, int axis, int32_t* exps, double* slices, hipStream_t stream,
-                           int phases) {
+                           int phases, bool pairs) {
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     if (outer == 0) return hipSuccess;
@@ -419,7 +442,10 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
         if (kparts == 1 && g.KB * 32 <= kBlockThreads * kRegPairs) {
             // the whole block in registers: one read of the operand
             const unsigned blocks = static_cast<unsigned>(g.RB);
-            if (axis == 0)
+            if (axis == 0 && pairs)
+                split_block_regs_kernel<0, kBlockThreads, NS, kRegPairs, true><<<blocks, kBlockThreads, 0, stream>>>(
+                    outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
+            else if (axis == 0)
                 split_block_regs_kernel<0, kBlockThreads, NS, kRegPairs><<<blocks, kBlockThreads, 0, stream>>>(
                     outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
             else
@@ -428,7 +454,10 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
             return hipGetLastError();
         }
         const dim3 grid(static_cast<unsigned>(g.RB), static_cast<unsigned>(kparts));
-        if (axis == 0)
+        if (axis == 0 && pairs)
+            split_block_kernel<0, kBlockThreads, NS, true><<<grid, kBlockThreads, 0, stream>>>(
+                outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
+        else if (axis == 0)
             split_block_kernel<0, kBlockThreads, NS><<<grid, kBlockThreads, 0, stream>>>(
                 outer, k, g.KB, X_hi, X_lo, ldx, exps, slices);
         else
@@ -455,7 +484,9 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
     if (!(phases & kSplitSlices) || g.doubles(NS) == 0) return hipSuccess;
     const int64_t total = g.RB * g.KB * kFragDoubles;
     const unsigned grid = grid_for(total, 256, 1 << 20);
-    if (axis == 0)
+    if (axis == 0 && pairs)
+        slice_kernel<0, NS, true><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X_hi, X_lo, ldx, exps, slices);
+    else if (axis == 0)
         slice_kernel<0, NS><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X_hi, X_lo, ldx, exps, slices);
     else
         slice_kernel<1, NS><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X_hi, X_lo, ldx, exps, slices);
@@ -466,21 +497,21 @@ hipError_t launch_split_ns(int64_t rows, int64_t cols, const double* X_hi, const
 
 hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
                         int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream,
-                        int phases) {
+                        int phases, bool pairs) {
     switch (ns) {
-        case 4: return launch_split_ns<4>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 5: return launch_split_ns<5>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 6: return launch_split_ns<6>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 7: return launch_split_ns<7>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 8: return launch_split_ns<8>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 9: return launch_split_ns<9>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 10: return launch_split_ns<10>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 11: return launch_split_ns<11>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 12: return launch_split_ns<12>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 13: return launch_split_ns<13>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 14: return launch_split_ns<14>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 15: return launch_split_ns<15>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
-        case 16: return launch_split_ns<16>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases);
+        case 4: return launch_split_ns<4>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 5: return launch_split_ns<5>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 6: return launch_split_ns<6>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 7: return launch_split_ns<7>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 8: return launch_split_ns<8>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 9: return launch_split_ns<9>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 10: return launch_split_ns<10>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 11: return launch_split_ns<11>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 12: return launch_split_ns<12>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 13: return launch_split_ns<13>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 14: return launch_split_ns<14>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 15: return launch_split_ns<15>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
+        case 16: return launch_split_ns<16>(rows, cols, X_hi, X_lo, ldx, axis, exps, slices, stream, phases, pairs);
         default: return hipErrorInvalidValue;
     }
 }

@@ -48,7 +48,7 @@ struct CostModel {
     bool two_per_cu;
     double t_stage;
 
-    CostModel(int64_t m, int64_t k, int ns_) : g(gemm_geometry(ns_)), ns(ns_), stages(0) {
+    CostModel(int64_t m, int64_t k, int ns_, const GemmGeometry& geom) : g(geom), ns(ns_), stages(0) {
         stages = g.ks > 0 ? PackGeom(m, k).KB / g.ks : 0;
         two_per_cu = g.lds_bytes > 0 && 2 * static_cast<int64_t>(g.lds_bytes) <= kLdsBytesPerCu;
         t_stage = static_cast<double>(g.mfma_per_stage) * g.waves_per_simd * kMfmaCycles / kClockHz / kMfmaEfficiency;
@@ -84,7 +84,7 @@ SplitPlan split_plan(int64_t m, int64_t n, int64_t k, int ns, bool tail) {
     // whole rounds: a split could only trade the co-residency of two workgroups
     // on a CU (4..6 slices) for atomics, measured under 2 % (1024² x 100000, 4 slices)
     if (tiles % kComputeUnits == 0) return none;
-    const CostModel cm(m, k, ns);
+    const CostModel cm(m, k, ns, g);
     const int64_t pmax = cm.stages / kMinStagesPerPart < kMaxParts ? cm.stages / kMinStagesPerPart : kMaxParts;
     if (pmax < 2) return none;
     const double outputs = static_cast<double>(m) * static_cast<double>(n);
@@ -116,5 +116,59 @@ SplitPlan split_plan(int64_t m, int64_t n, int64_t k, int ns, bool tail) {
 }
 
 int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns) { return split_plan(m, n, k, ns, false).parts; }
+
+// The pair-packed product splits the same way, with other costs for the split
+// tiles: no atomics and no zeroing; each k-part stores the ns - 1 int64 group
+// sums of its outputs, and one more launch adds the parts and rounds:
+//     T = c(L) ceil(stages / p) t_stage
+//         + [p > 1] (2 p (ns - 1) outputs 8 B / plane rate + launches),
+// t_stage from the pair-packed product count.  The plan must save 5 %.
+namespace {
+constexpr double kPairMinSaving = 0.95;
+}  // namespace
+
+SplitPlan pair_split_plan(int64_t m, int64_t n, int64_t k, int ns) {
+    const GemmGeometry g = pair_geometry(ns);
+    if (g.tile_m <= 0 || g.tile_n <= 0 || m <= 0 || n <= 0 || k <= 0) return SplitPlan{0, m, 1};
+    const int64_t tiles_m = (m + g.tile_m - 1) / g.tile_m, tiles_n = (n + g.tile_n - 1) / g.tile_n;
+    const int64_t tiles = tiles_m * tiles_n;
+    const SplitPlan none{tiles, m, 1};
+    if (tiles % kComputeUnits == 0) return none;
+    const CostModel cm(m, k, ns, g);
+    const int64_t pmax = cm.stages / kMinStagesPerPart < kMaxParts ? cm.stages / kMinStagesPerPart : kMaxParts;
+    if (pmax < 2) return none;
+    auto cost = [&](int64_t t, double outputs, int64_t p) {
+        const double base = cm.time(t, outputs, 1);  // the rounds of one part's stages, below
+        if (p == 1) return base;
+        const int64_t L = (t * p + kComputeUnits - 1) / kComputeUnits;
+        const double load = cm.two_per_cu && L >= 2 ? kCoResidentShare * static_cast<double>(L) : static_cast<double>(L);
+        return load * static_cast<double>((cm.stages + p - 1) / p) * cm.t_stage +
+               2.0 * p * (ns - 1) * outputs * 8.0 / kPlaneBytesPerSecond + kSplitLaunchSeconds;
+    };
+    const double outputs = static_cast<double>(m) * static_cast<double>(n);
+    const double t1 = cost(tiles, outputs, 1);
+    const int64_t rounds = (tiles + kComputeUnits - 1) / kComputeUnits;
+    int64_t heads[5] = {0, -1, -1, -1, -1};
+    for (int r = 1; r <= 4; ++r)
+        if (rounds > r) heads[r] = kComputeUnits * (rounds - r);
+    SplitPlan best = none;
+    double best_t = t1;
+    for (int64_t h : heads) {
+        if (h < 0) continue;
+        const int64_t row0 = h / tiles_n * g.tile_m;
+        const double tile_outputs = static_cast<double>(g.tile_m) * static_cast<double>(g.tile_n);
+        const double tail_outputs = std::min(static_cast<double>(tiles - h) * tile_outputs,
+                                             static_cast<double>(m - row0) * static_cast<double>(n));
+        const double t_head = h > 0 ? cost(h, outputs - tail_outputs, 1) + kSplitLaunchSeconds : 0.0;
+        for (int64_t p = 2; p <= pmax; ++p) {
+            const double t = t_head + cost(tiles - h, tail_outputs, p);
+            if (t < best_t) {
+                best_t = t;
+                best = SplitPlan{h, row0, p};
+            }
+        }
+    }
+    return best.parts > 1 && best_t < kPairMinSaving * t1 ? best : none;
+}
 
 }  // namespace ddg

@@ -15,9 +15,14 @@
  *   2. dd_sliced_gemm     -- the 36 slice-pair products with s + t <= 7, summed
  *                            exactly per level l = s + t on FP64 MFMA;
  *   3. dd_renorm_levels   -- TwoSum cascade of the 8 level sums into (hi, lo);
- *   dd_sliced_gemm_renorm fuses 2 and 3; dd_gemm / dd_gemm_ws run 1 + 1 + (2+3),
- *   or, for outputs whose tiles leave the chip partly idle, 2 split over k
- *   for some or all output rows, then 3 for those rows (dd_gemm_workspace_size).
+ *   dd_sliced_gemm_renorm fuses 2 and 3.
+ * The product entry points (dd_gemm, dd_gemm_ws, ...) run 1 for both operands
+ * and then the same 36 slice-pair products grouped two to a matrix
+ * instruction (dd_sliced_gemm_pairs: 20 instructions per k instead of 36),
+ * with the epilogue fused: each entry's exact windowed total -- the same
+ * total the level sums of 2 add up to -- rounded once to the nearest
+ * double-double.  Outputs whose tiles leave the chip partly idle are split
+ * over k for some or all output rows (dd_gemm_workspace_size).
  *
  * Conventions for every entry point
  *   - All matrices are row-major float64 planes in device memory; a
@@ -102,7 +107,9 @@ typedef enum {
 size_t dd_split_slices_bytes(int64_t outer, int64_t k);
 
 /* Workspace bytes dd_gemm_ws needs for an m×k by k×n product (slices of both
- * operands and both exponent vectors, each region 256-byte aligned); 0 for
+ * operands and both exponent vectors, each region 256-byte aligned, plus 7
+ * int64 m×n planes of group sums when k exceeds 4096, the most values whose
+ * FP64 group sums stay exact, see dd_sliced_gemm_pairs); 0 for
  * negative sizes, and for sizes whose workspace would pass 2^62 bytes (the
  * products reject those with DDGEMM_ERROR_INVALID_VALUE).  When the output tiles (64×64; 32×64 with 6 or 9..16 slices)
  * leave part of the chip idle -- a few tiles, or a last round of 256
@@ -114,9 +121,10 @@ size_t dd_split_slices_bytes(int64_t outer, int64_t k);
  * and the level planes, and only where that saves at least 2 %; outputs that
  * fill whole rounds never split.  ddgemm_split_parts returns p,
  * ddgemm_split_first_tile t and ddgemm_split_first_row the first row r of t's
- * tile row.  The parts add their exact level sums into level planes, and the
- * workspace also holds those nslices (m - r)×n planes.  The split result is bit-identical to the unsplit
- * one. */
+ * tile row.  Each part stores the exact int64 group sums of its outputs in
+ * planes of its own (no atomics), and one more launch adds the parts and
+ * rounds; the workspace also holds those p (nslices - 1) (m - r)×n int64
+ * planes.  The split result is bit-identical to the unsplit one. */
 size_t dd_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 
 /*
@@ -184,14 +192,46 @@ ddgemm_status_t dd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k,
                                       double* C_hi, double* C_lo, int64_t ldc, void* stream);
 
 /*
+ * Group sums of the pair-packed schedule, the exact sums the product entry
+ * points round (stage call, for bit-exact tests).  Slices 2u and 2u+1 of an
+ * entry of A have its sign and sit 13 bits apart, so d_2u 2^13 + d_(2u+1) is
+ * one exact 26-bit operand, and its product with a 13-bit slice of B covers the
+ * window pairs (2u, t) and (2u+1, t) at once ("Multiple Double Arithmetic on
+ * NVIDIA Tensor Cores", §2 eqs. (1)-(4); every product and partial sum stays
+ * an exact FP64 integer of units, as in §2 eq. (5), for 39-bit products):
+ * where only (2u, t) is in the window (2u + t = 7) it runs alone.  That covers
+ * the 36 window pairs with 20 products per k (the fewest: a product covers at
+ * most two pairs of opposite index-sum parity, and 20 of the 36 pairs have an
+ * odd index sum).  Product (u, t) adds into group g = 2u + t, a single pair
+ * into group 6; group g counts units 2^(-13(g+3)), so the exact windowed total
+ * of entry (i, j) is 2^(E_i + F_j) sum_g G_g 2^(-13(g+3)) -- the same total as
+ * sum_l S_l 2^(-13(l+2)) from dd_sliced_gemm.
+ *   units : 7 int64 planes (n - 1 with the _ns variant), plane g at
+ *           units + g*m*ldu, each m×n with row stride ldu >= max(1, n):
+ *           G_g[i][j] exactly.  The kernels keep FP64 sums over at most 4096
+ *           values of k (the most whose largest group sum stays below 2^53)
+ *           and add them into the int64 planes; k <= dd_gemm_kblock_max(n)
+ *           (2^22 for 8 slices) keeps every group sum below 2^63.
+ * Errors: DDGEMM_ERROR_INVALID_VALUE for negative sizes, ldu < max(1, n),
+ * k > dd_gemm_kblock_max(n), NULL pointers with a nonzero extent.
+ */
+ddgemm_status_t dd_sliced_gemm_pairs(int64_t m, int64_t n, int64_t k,
+                                     const double* A_slices, const double* B_slices,
+                                     int64_t* units, int64_t ldu, void* stream);
+
+/*
  * C = A·B for double-double A (m×k) and B (k×n) ("Multiple Double Arithmetic on
  * NVIDIA Tensor Cores", §2 overview, steps 1-5).  Overwrites C (no alpha/beta).
  * m = 0 or n = 0: no-op.  k = 0: C = 0.  k beyond DDGEMM_K_MAX is processed in
- * the fewest equal k-blocks within it, as dd_gemm_ws_kb describes.  Accuracy: the product of the operands
- * truncated to 104 bits below their row/column exponents, minus the slice pairs
- * below the double-double window, renormalised; on inputs whose entries sit
- * within a few binades of their row/column maximum this is within
- * 1e-28 * (|A||B|)_ij of the exact product.
+ * the fewest equal k-blocks within it (dd_gemm_kblock_max), as dd_gemm_ws_kb
+ * describes.  Result: the nearest double-double (C_hi = RN(x), C_lo =
+ * RN(x - C_hi), gradual underflow honoured) of x = the exact sum of the 36
+ * window slice-pair products, i.e. the product of the operands truncated to
+ * 104 bits below their row/column exponents minus the pairs below the
+ * window; on inputs whose entries sit within a few binades of their
+ * row/column maximum this is within 1e-28 * (|A||B|)_ij of the exact product.
+ * Beyond the double range C_hi is +-inf and C_lo rounds what is left after
+ * C_hi's value with an unbounded exponent range.
  *   dd_gemm     allocates its workspace with hipMallocAsync/hipFreeAsync on
  *               `stream` (DDGEMM_ERROR_WORKSPACE if that fails).
  *   dd_gemm_ws  uses the caller's workspace of ws_bytes >= dd_gemm_workspace_size
@@ -215,13 +255,16 @@ ddgemm_status_t dd_gemm_ws(int64_t m, int64_t n, int64_t k,
  * packed layout is the one described above with n slices per fragment in place
  * of 8 (slice s of entry (o, p) at ((((o/16)*KB + p/4)*n + s)*64) + (p%4)*16 +
  * o%16); for n = 8 every call equals its counterpart without the suffix.  The
- * product C is the renormalised sum of the n level sums; per entry it is
- * within 2^(-13n) (2^F_j sum_p |a_ip| + 2^E_i sum_p |b_pj| + n k 2^(E_i+F_j))
- * + 2^-90 (|A||B|)_ij of the exact product, E_i and F_j the row/column
- * exponents (for n > 8 the last term covers the cascade alone, and a larger n
- * shrinks the rest).  Errors: as for the counterparts, plus
+ * product C is the nearest double-double of the exact sum of the n(n+1)/2
+ * window pairs (n - 1 groups, n^2/4 + n/2 matrix products per k rounded up:
+ * 6 for n = 4, 20 for n = 8, 72 for n = 16); per entry it is within
+ * 2^(-13n) (2^F_j sum_p |a_ip| + 2^E_i sum_p |b_pj| + n k 2^(E_i+F_j))
+ * + 2^-104 |C_ij| of the exact product, E_i and F_j the row/column exponents.
+ * The stage chain's cascade (dd_sliced_gemm_renorm_ns) adds at most 2^-104
+ * of the level magnitudes instead.  Errors: as for the counterparts, plus
  * DDGEMM_ERROR_INVALID_VALUE for n outside [DDGEMM_MIN_SLICES, DDGEMM_MAX_SLICES]
- * and k > DDGEMM_K_MAX_NS(n).
+ * and k > DDGEMM_K_MAX_NS(n) (the products: k-blocks beyond
+ * dd_gemm_kblock_max(n)).
  */
 size_t dd_split_slices_bytes_ns(int64_t outer, int64_t k, int nslices);
 size_t dd_gemm_workspace_size_ns(int64_t m, int64_t n, int64_t k, int nslices);
@@ -233,6 +276,9 @@ ddgemm_status_t dd_sliced_gemm_renorm_ns(int64_t m, int64_t n, int64_t k, int ns
                                          const double* A_slices, const int32_t* E,
                                          const double* B_slices, const int32_t* F,
                                          double* C_hi, double* C_lo, int64_t ldc, void* stream);
+ddgemm_status_t dd_sliced_gemm_pairs_ns(int64_t m, int64_t n, int64_t k, int nslices,
+                                        const double* A_slices, const double* B_slices,
+                                        int64_t* units, int64_t ldu, void* stream);
 ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices,
                               const double* A_hi, const double* A_lo, int64_t lda,
                               const double* B_hi, const double* B_lo, int64_t ldb,
@@ -250,7 +296,7 @@ ddgemm_status_t dd_gemm_ws_ns(int64_t m, int64_t n, int64_t k, int nslices,
  * workspace: slices are sized by kblock, plus two m×n planes when there is more
  * than one block (dd_gemm_workspace_size_kb).
  * Errors: as for dd_gemm_ws_ns, plus DDGEMM_ERROR_INVALID_VALUE for k > 0 and
- * kblock outside [1, DDGEMM_K_MAX_NS(n)].
+ * kblock outside [1, dd_gemm_kblock_max(n)].
  */
 size_t dd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock);
 ddgemm_status_t dd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t kblock,
@@ -283,6 +329,26 @@ ddgemm_status_t dd_gemm_noalloc(int64_t m, int64_t n, int64_t k,
                                 const double* A_hi, const double* A_lo, int64_t lda,
                                 const double* B_hi, const double* B_lo, int64_t ldb,
                                 double* C_hi, double* C_lo, int64_t ldc, void* stream);
+
+/*
+ * dd_gemm_ws_ns with a measurement mark: `after_split` (a hipEvent_t, or NULL)
+ * is recorded on `stream` once both operands of the first k-block are sliced,
+ * so that the time from it to the end of the call is the product's
+ * matrix-core part alone (with one k-block: k <= dd_gemm_kblock_max(n)).
+ * Otherwise identical to dd_gemm_ws_ns, bit for bit.
+ */
+ddgemm_status_t dd_gemm_ws_timed(int64_t m, int64_t n, int64_t k, int nslices,
+                                 const double* A_hi, const double* A_lo, int64_t lda,
+                                 const double* B_hi, const double* B_lo, int64_t ldb,
+                                 double* C_hi, double* C_lo, int64_t ldc,
+                                 void* workspace, size_t ws_bytes, void* after_split, void* stream);
+
+/* The largest k-block of the product entry points with n slices per entry
+ * (longer k is cut into the fewest equal blocks within it): the smaller of
+ * DDGEMM_K_MAX_NS(n) and the most values of k whose int64 group sums
+ * (dd_sliced_gemm_pairs) stay below 2^63 -- 4,194,304 for 8 slices,
+ * 2,097,152 for 16.  0 for n outside [DDGEMM_MIN_SLICES, DDGEMM_MAX_SLICES]. */
+int64_t dd_gemm_kblock_max(int nslices);
 
 /* Static, human-readable name of a status code. */
 const char* ddgemm_status_string(ddgemm_status_t status);

@@ -222,12 +222,14 @@ def sliced_product(A_hi, A_lo, B_hi, B_lo, nslices: int = N_SLICES):
     return renorm_levels(level_values(level_sums_units(DA, DB)), E, F)
 
 
-def sliced_product_kblocks(A_hi, A_lo, B_hi, B_lo, kblock: int, nslices: int = N_SLICES):
+def sliced_product_kblocks(A_hi, A_lo, B_hi, B_lo, kblock: int, nslices: int = N_SLICES, nearest: bool = False):
     """k split into consecutive blocks of kblock columns of A (rows of B); each
     block is an independent sliced product (its own balancing exponents, so the
     exact-sum bound of §2 eq. (5) holds per block), and the block results are
     added into the running (C_hi, C_lo), first block first, with the oracle's
-    accurate double-word addition."""
+    accurate double-word addition.  Each block's result is the level cascade,
+    or with `nearest` the nearest double-double of its exact total (the
+    product entry points' chain)."""
     from . import native
     A_hi = np.asarray(A_hi, dtype=np.float64)
     B_hi = np.asarray(B_hi, dtype=np.float64)
@@ -238,7 +240,8 @@ def sliced_product_kblocks(A_hi, A_lo, B_hi, B_lo, kblock: int, nslices: int = N
     C_hi = C_lo = None
     for p0 in starts:
         p1 = min(k, p0 + kblock)
-        Th, Tl = sliced_product(A_hi[:, p0:p1], A_lo[:, p0:p1], B_hi[p0:p1, :], B_lo[p0:p1, :], nslices)
+        block = paired_product if nearest else sliced_product
+        Th, Tl = block(A_hi[:, p0:p1], A_lo[:, p0:p1], B_hi[p0:p1, :], B_lo[p0:p1, :], nslices)
         if C_hi is None:
             C_hi, C_lo = Th, Tl
             continue

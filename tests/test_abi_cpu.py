@@ -63,18 +63,25 @@ def test_packed_sizes(ddg):
     r = lambda x: (x + 255) // 256 * 256
     assert ws == r(ddg.slices_bytes(m, k)) + r(ddg.slices_bytes(n, k)) + r(4 * m) + r(4 * n)
     assert ddg.workspace_size(-1, 2, 3) == 0
-    # beyond the exact-sum bound k is cut into the fewest equal blocks: slices
-    # for one block plus two m×n planes for the block results, and -- one 64x64
-    # tile cannot fill the chip -- eight level planes for a product split over k
+    # beyond the product's k-block limit (the int64 bound of the pair-packed
+    # group sums, 2^22 for 8 slices) k is cut into the fewest equal blocks:
+    # slices for one block, two m×n planes for the block results, seven int64
+    # group-sum planes between k-chunks of 4096 and -- one 64x64 tile cannot
+    # fill the chip -- seven int64 planes for each k-part of the split
+    kmax = ddg.kblock_max(8)
+    assert kmax == 1 << 22
     k2 = ddg.K_MAX + 1
-    kb = (k2 + 1) // 2
+    kb = -(-k2 // 3)
+    parts = ddg.split_parts(3, 5, kb)
+    assert parts > 1 and ddg.split_first_row(3, 5, kb) == 0
     assert ddg.workspace_size(3, 5, k2) == (r(ddg.slices_bytes(3, kb)) + r(ddg.slices_bytes(5, kb)) + r(12) + r(20)
-                                            + 2 * r(3 * 5 * 8) + r(8 * 3 * 5 * 8))
+                                            + 2 * r(3 * 5 * 8) + r(7 * 3 * 5 * 8) + r(parts * 7 * 3 * 5 * 8))
     assert ddg.workspace_size(3, 5, 100, kblock=100) == ddg.workspace_size(3, 5, 100)
     assert ddg.workspace_size(3, 5, 100, kblock=30) == (r(ddg.slices_bytes(3, 30)) + r(ddg.slices_bytes(5, 30))
                                                         + r(12) + r(20) + 2 * r(3 * 5 * 8))
     assert ddg.workspace_size(3, 5, 100, kblock=0) == 0
-    assert ddg.workspace_size(3, 5, 100, kblock=ddg.K_MAX + 1) == 0
+    assert ddg.workspace_size(3, 5, 100, kblock=kmax + 1) == 0
+    assert ddg.workspace_size(3, 5, 100, kblock=kmax) == ddg.workspace_size(3, 5, 100)
     assert ddg.workspace_size(3, 5, 0, kblock=0) > 0
 
 
@@ -115,18 +122,28 @@ def test_split_parts_query(ddg):
     assert fr(-1, 5, 100, 8) == -1 and fr(5, 5, 100, 3) == -1
 
 
-def test_workspace_holds_level_planes_when_the_product_splits_over_k(ddg):
+# the most values of k whose FP64 group sums of the pair-packed schedule stay exact
+PAIR_CHUNK = {4: 8192, 5: 8176, 6: 5456, 7: 5456, 8: 4096, 9: 4080, 10: 3264, 11: 3264, 12: 2720, 13: 2720,
+              14: 2336, 15: 2336, 16: 2048}
+
+
+def test_workspace_holds_group_sum_planes_for_chunks_and_split_parts(ddg):
+    """The double-double product's workspace: slices and exponents, plus n - 1
+    int64 group-sum planes of m×n when k needs more than one exact FP64 chunk,
+    plus n - 1 int64 planes of the split rows for every k-part of a split."""
     L = ddg.lib
     r = lambda x: (x + 255) // 256 * 256
     for (m, n, k, ns) in [(64, 64, 512, 8), (64, 64, 511, 8), (64, 64, 240, 8), (3, 5, 100000, 8),
                           (1000, 1000, 100000, 8), (700, 900, 4096, 8), (256, 256, 65536, 12),
                           (100, 80, 5000, 16), (64, 64, 1024, 6), (1024, 1024, 4096, 8),
-                          (1536, 1024, 4096, 8), (1152, 1152, 1152, 8)]:
+                          (1536, 1024, 4096, 8), (1152, 1152, 1152, 8), (2048, 2048, 8192, 8)]:
         base = (r(L.dd_split_slices_bytes_ns(m, k, ns)) + r(L.dd_split_slices_bytes_ns(n, k, ns))
                 + r(4 * m) + r(4 * n))
-        split = ddg.split_parts(m, n, k, ns) > 1
+        chunks = r((ns - 1) * m * n * 8) if k > PAIR_CHUNK[ns] else 0
+        parts = ddg.split_parts(m, n, k, ns)
         rows = m - ddg.split_first_row(m, n, k, ns)
-        assert L.dd_gemm_workspace_size_ns(m, n, k, ns) == base + (r(ns * rows * n * 8) if split else 0), (m, n, k, ns)
+        split = r(parts * (ns - 1) * rows * n * 8) if parts > 1 else 0
+        assert L.dd_gemm_workspace_size_ns(m, n, k, ns) == base + chunks + split, (m, n, k, ns)
         if ns == 8:
             assert L.dd_gemm_workspace_size(m, n, k) == L.dd_gemm_workspace_size_ns(m, n, k, ns)
     assert ddg.split_parts(64, 64, 512, 8) > 1 and ddg.split_parts(64, 64, 240, 8) == 1
@@ -284,6 +301,21 @@ def test_layout_pack_unpack_roundtrip(ddg):
             assert packed[idx] == planes[s, o, p]
 
 
+def _pair_term_max(n):
+    """The largest group sum one value of k adds in the pair-packed schedule
+    (digits 8191): packed products (2u, 2u+1) x t into group 2u + t, singles
+    (2u + t = n - 1) into group n - 2."""
+    d = 8191
+    groups = [0] * (n - 1)
+    for u in range((n + 1) // 2):
+        for t in range(n):
+            if 2 * u + 1 < n and 2 * u + 1 + t <= n - 1:
+                groups[2 * u + t] += (d * 8192 + d) * d
+            elif 2 * u + t == n - 1:
+                groups[n - 2] += d * d
+    return max(groups)
+
+
 def test_n_slice_sizes_and_validation(ddg):
     L = ddg.lib
     INV = ddg.ERROR_INVALID_VALUE
@@ -291,11 +323,14 @@ def test_n_slice_sizes_and_validation(ddg):
         assert L.dd_split_slices_bytes_ns(130, 33, n) == 192 * 48 * n * 8
         kmax = ddg.k_max(n)
         assert kmax == (8388608 if n <= 8 else 67108865 // n)
-        assert L.dd_gemm_workspace_size_ns(4, 4, kmax, n) > 0
-        assert L.dd_gemm_workspace_size_ns(4, 4, kmax + 1, n) == L.dd_gemm_workspace_size_kb(4, 4, kmax + 1, n,
-                                                                                             (kmax + 2) // 2)
-        assert L.dd_gemm_workspace_size_kb(4, 4, 10, n, kmax + 1) == 0
-        assert L.dd_gemm_ws_kb(4, 4, 10, n, kmax + 1, P[0], None, 10, P[1], None, 4, P[2], P[3], 4, P[4], 1 << 30,
+        # the product's k-blocks: the smaller of the slicer's limit and the int64 bound of the group sums
+        kbm = ddg.kblock_max(n)
+        assert kbm == min(kmax, (2 ** 63 - 1) // _pair_term_max(n))
+        assert L.dd_gemm_workspace_size_ns(4, 4, kbm, n) > 0
+        assert L.dd_gemm_workspace_size_ns(4, 4, kbm + 1, n) == L.dd_gemm_workspace_size_kb(4, 4, kbm + 1, n,
+                                                                                            (kbm + 2) // 2)
+        assert L.dd_gemm_workspace_size_kb(4, 4, 10, n, kbm + 1) == 0
+        assert L.dd_gemm_ws_kb(4, 4, 10, n, kbm + 1, P[0], None, 10, P[1], None, 4, P[2], P[3], 4, P[4], 1 << 30,
                                None) == INV
         assert L.dd_gemm_ws_kb(4, 4, 10, n, 0, P[0], None, 10, P[1], None, 4, P[2], P[3], 4, P[4], 1 << 30,
                                None) == INV

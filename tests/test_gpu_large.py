@@ -50,9 +50,10 @@ def _free():
 
 
 def _dd_chain(ah, al, bh, bl, rows, cols):
+    """The product entry points' chain on a block: nearest double-double of the exact level totals."""
     E, DA = exact.slice_rows(ah, al, rows)
     F, DB = exact.slice_cols(bh, bl, cols)
-    return exact.renorm_levels(exact.level_values(exact.level_sums_units(DA, DB)), E, F)
+    return exact.nearest_dd(exact.level_sums_units(DA, DB), E, F)
 
 
 @pytest.mark.timeout(600)
@@ -163,6 +164,48 @@ def test_dd_level_sums_exact_at_the_k_bound(gpu):
     _say("[large] unsplit fused call")
     Fh, Fl = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F)
     assert _bits_equal(_host(Fh), Rh) and _bits_equal(_host(Fl), Rl)
+    del As, Bs
+    _free()
+
+
+@pytest.mark.timeout(600)
+def test_dd_pair_group_sums_exact_at_the_product_k_bound(gpu):
+    """k at the product's k-block limit (2^22 for 8 slices: the most values of k
+    whose int64 group sums of the pair-packed schedule stay below 2^63) with
+    the largest digits in every slice of every entry: the deepest group reaches
+    ~2^62.9 units after 1024 chunks of exact FP64 sums.  The group-sum stage
+    call (one workgroup, every chunk) gives the closed form exactly, and the
+    product (split over k into parts) the oracle's nearest double-double of it."""
+    import torch
+    m, n, k = 64, 3, gpu.kblock_max(8)
+    assert k == 1 << 22 and gpu.split_parts(m, n, k) > 1
+    digits = exact.slice_entry(MAX_HI, MAX_LO, 0)
+    DA = np.array(digits, dtype=np.int64).reshape(8, 1, 1)
+    DB = -DA.reshape(8, 1, 1)
+    G1 = exact.paired_group_units(DA, DB)[:, 0, 0]                 # one value of k
+    G = [int(g) * k for g in G1]
+    assert max(abs(g) for g in G) < 2 ** 63 and abs(G[6]) > 2 ** 62
+    S_units = np.array([np.full((m, n), -k * sum(digits[s] * digits[l - s] for s in range(l + 1)), dtype=np.int64)
+                        for l in range(8)])
+    Rh, Rl = exact.nearest_dd(S_units[:, :1, :1], [0], [0])
+    _free()
+    _say(f"[large] pair group sums at k = {k}, m={m} n={n}, largest digits")
+    A_hi = torch.full((m, k), MAX_HI, dtype=torch.float64, device="cuda")
+    A_lo = torch.full((m, k), MAX_LO, dtype=torch.float64, device="cuda")
+    B_hi = torch.full((k, n), -MAX_HI, dtype=torch.float64, device="cuda")
+    B_lo = torch.full((k, n), -MAX_LO, dtype=torch.float64, device="cuda")
+    _say("[large] product (split over k)")
+    Ch, Cl = gpu.dd_gemm(A_hi, A_lo, B_hi, B_lo)
+    assert (_host(Ch) == Rh[0, 0]).all() and (_host(Cl) == Rl[0, 0]).all()
+    del Ch, Cl
+    E, As = gpu.split_balanced(A_hi, A_lo, 0)
+    del A_hi, A_lo
+    F, Bs = gpu.split_balanced(B_hi, B_lo, 1)
+    del B_hi, B_lo
+    _say("[large] group-sum stage call (one workgroup, 1024 chunks)")
+    units = _host(gpu.sliced_gemm_pairs(m, n, k, As, Bs))
+    for g in range(7):
+        assert (units[g] == G[g]).all(), g
     del As, Bs
     _free()
 

@@ -238,11 +238,14 @@ def test_split_largest_digits(gpu):
 # level sums, cascade, and the whole sliced chain
 # ---------------------------------------------------------------------------
 def _oracle_chain(Ah, Al, Bh, Bl, rows=None, cols=None):
+    """Level sums, the stage chain's cascade and the product's nearest double-double."""
     E, DA = exact.slice_rows(Ah, Al, rows)
     F, DB = exact.slice_cols(Bh, Bl, cols)
-    S = exact.level_values(exact.level_sums_units(DA, DB))
+    S_units = exact.level_sums_units(DA, DB)
+    S = exact.level_values(S_units)
     Ch, Cl = exact.renorm_levels(S, E, F)
-    return S, Ch, Cl
+    Nh, Nl = exact.nearest_dd(S_units, E, F)
+    return S, Ch, Cl, Nh, Nl
 
 
 def _gpu_chain(gpu, Ah, Al, Bh, Bl):
@@ -261,15 +264,15 @@ def test_sliced_chain_bit_exact_small(gpu, m, n, k):
     rng = np.random.default_rng(7 + m + 3 * n + 5 * k)
     Ah, Al = _edge_matrix(rng, m, k)
     Bh, Bl = _edge_matrix(rng, k, n)
-    S, Ch_ref, Cl_ref = _oracle_chain(Ah, Al, Bh, Bl)
+    S, Ch_ref, Cl_ref, Nh_ref, Nl_ref = _oracle_chain(Ah, Al, Bh, Bl)
     levels, Ch, Cl, Fh, Fl = _gpu_chain(gpu, Ah, Al, Bh, Bl)
     assert _bits_equal(_host(levels), S), "level sums"
     assert _bits_equal(_host(Ch), Ch_ref) and _bits_equal(_host(Cl), Cl_ref), "cascade"
     assert _bits_equal(_host(Fh), Ch_ref) and _bits_equal(_host(Fl), Cl_ref), "fused epilogue"
     Gh, Gl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))
-    assert _bits_equal(_host(Gh), Ch_ref) and _bits_equal(_host(Gl), Cl_ref), "dd_gemm_ws"
+    assert _bits_equal(_host(Gh), Nh_ref) and _bits_equal(_host(Gl), Nl_ref), "dd_gemm_ws"
     Hh, Hl = gpu.dd_gemm_alloc(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))
-    assert _bits_equal(_host(Hh), Ch_ref) and _bits_equal(_host(Hl), Cl_ref), "dd_gemm"
+    assert _bits_equal(_host(Hh), Nh_ref) and _bits_equal(_host(Hl), Nl_ref), "dd_gemm"
 
 
 def test_level_sums_exact_at_the_bound(gpu):
@@ -283,6 +286,39 @@ def test_level_sums_exact_at_the_bound(gpu):
     for l in range(8):
         expect = -k * sum(MAX_DIGITS[s] * MAX_DIGITS[l - s] for s in range(l + 1))
         assert np.all(levels[l] * 2.0 ** (13 * (l + 2)) == expect), l
+
+
+@pytest.mark.parametrize("m,n,k,ns", [(40, 50, 8292, 8), (33, 70, 4096, 8), (20, 30, 4097, 8),
+                                      (45, 17, 4133, 16), (21, 40, 12000, 5), (30, 30, 5500, 12)])
+def test_pair_group_sums_across_exact_chunks(gpu, m, n, k, ns):
+    """The pair-packed schedule's group sums, bit for bit against the oracle,
+    for k at, just past and several times past the most values whose FP64 group
+    sums stay exact (4096 for 8 slices): the kernel moves them into int64
+    planes chunk by chunk."""
+    rng = np.random.default_rng(m * n + k + ns)
+    Ah, Al = _edge_matrix(rng, m, k)
+    Bh, Bl = _edge_matrix(rng, k, n)
+    _, DA = exact.slice_rows(Ah, Al, nslices=ns)
+    _, DB = exact.slice_cols(Bh, Bl, nslices=ns)
+    _, As = gpu.split_balanced(_dev(Ah), _dev(Al), 0, nslices=ns)
+    _, Bs = gpu.split_balanced(_dev(Bh), _dev(Bl), 1, nslices=ns)
+    G = gpu.sliced_gemm_pairs(m, n, k, As, Bs, nslices=ns)
+    assert np.array_equal(_host(G), exact.paired_group_units(DA, DB))
+
+
+def test_unsplit_product_across_exact_chunks(gpu):
+    """A product whose 256 output tiles fill one round (never split) with k past
+    one exact FP64 chunk: the int64 chunk planes of the workspace carry the
+    group sums; sampled entries equal the oracle's nearest chain bit for bit."""
+    m, n, k = 1024, 1024, 4200
+    assert gpu.split_parts(m, n, k) == 1
+    Ah, Al = workloads.random_dd((m, k), 71, "signed_exp20")
+    Bh, Bl = workloads.random_dd((k, n), 72, "normal")
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))
+    rows = [0, 1, 511, 1023]
+    cols = [0, 63, 64, 1023]
+    _, _, _, Nh, Nl = _oracle_chain(Ah, Al, Bh, Bl, rows, cols)
+    assert _bits_equal(_host(Ch)[np.ix_(rows, cols)], Nh) and _bits_equal(_host(Cl)[np.ix_(rows, cols)], Nl)
 
 
 # ---------------------------------------------------------------------------
@@ -379,9 +415,13 @@ def test_results_beyond_the_double_range_overflow_like_ldexp(gpu):
     Ah[:5] *= 2.0 ** -700                       # these rows' products stay finite
     Al, Bl = np.zeros_like(Ah), np.zeros_like(Bh)
     Ch, Cl = gpu.dd_gemm(_dev(Ah), None, _dev(Bh), None)
-    _, Rh, Rl = _oracle_chain(Ah, Al, Bh, Bl)
+    _, Sh, Sl, Rh, Rl = _oracle_chain(Ah, Al, Bh, Bl)
     hCh, hCl = _host(Ch), _host(Cl)
     assert _bits_equal(hCh, Rh) and _bits_equal(hCl, Rl)
+    E, As = gpu.split_balanced(_dev(Ah), None, 0)
+    F, Bs = gpu.split_balanced(_dev(Bh), None, 1)
+    Fh, Fl = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F)  # the stage chain's cascade
+    assert _bits_equal(_host(Fh), Sh) and _bits_equal(_host(Fl), Sl)
     assert np.isinf(hCh[5:]).any() and np.isfinite(hCh[:5]).all()
     exact_sign = np.sign((Ah[5:] * 2.0 ** -600) @ (Bh * 2.0 ** -600))   # small integers: exact
     inf_rows = np.isinf(hCh[5:])
@@ -510,16 +550,22 @@ def test_workload_parity(gpu, workload_operands, name):
     del levels
     Fh, Fl = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F)
     assert _bits_equal(_host(Fh), _host(Rh)) and _bits_equal(_host(Fl), _host(Rl)), "fused == two-step"
-    del Rh, Rl, As, Bs
+    assert _bits_equal(_host(Fh[ri][:, ci]), Ch_ref) and _bits_equal(_host(Fl[ri][:, ci]), Cl_ref), "cascade"
+    del Rh, Rl, Fh, Fl
+
+    _say(f"[parity] {name}: pair-packed group sums (sampled {len(rows)}x{len(cols)} block)")
+    G = gpu.sliced_gemm_pairs(m, n, k, As, Bs)
+    assert np.array_equal(_host(G[:, ri][:, :, ci].contiguous()), exact.paired_group_units(DA, DB)), "group sums"
+    del G, As, Bs
     torch.cuda.empty_cache()
 
     _say(f"[parity] {name}: dd_gemm end to end")
     Ch, Cl = gpu.dd_gemm(dA, dAl, dB, dBl)
     hCh, hCl = _host(Ch), _host(Cl)
-    assert _bits_equal(hCh, _host(Fh)) and _bits_equal(hCl, _host(Fl)), "dd_gemm == stage calls"
+    Nh_ref, Nl_ref = exact.nearest_dd(exact.level_sums_units(DA, DB), E_s, F_s)
     sub_h = hCh[np.ix_(rows, cols)]
     sub_l = hCl[np.ix_(rows, cols)]
-    assert _bits_equal(sub_h, Ch_ref) and _bits_equal(sub_l, Cl_ref), "sliced chain vs oracle"
+    assert _bits_equal(sub_h, Nh_ref) and _bits_equal(sub_l, Nl_ref), "product vs oracle's nearest chain"
 
     if m * n * k <= 1024 ** 3:
         _say(f"[parity] {name}: classical oracle, all {m * n} entries")
@@ -585,8 +631,11 @@ def test_n_slice_chain_bit_exact(gpu, nslices, m, n, k):
                        exact.slice_values(DB).transpose(0, 2, 1))
     Fh, Fl = gpu.sliced_gemm_renorm(m, n, k, gA, gE, gB, gF, nslices=nslices)
     assert _bits_equal(_host(Fh), Ch_ref) and _bits_equal(_host(Fl), Cl_ref)
+    G = gpu.sliced_gemm_pairs(m, n, k, gA, gB, nslices=nslices)
+    assert np.array_equal(_host(G), exact.paired_group_units(DA, DB))
+    Nh_ref, Nl_ref = exact.nearest_dd(exact.level_sums_units(DA, DB), E, F)
     Gh, Gl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl), nslices=nslices)
-    assert _bits_equal(_host(Gh), Ch_ref) and _bits_equal(_host(Gl), Cl_ref)
+    assert _bits_equal(_host(Gh), Nh_ref) and _bits_equal(_host(Gl), Nl_ref)
 
 
 @pytest.mark.timeout(600)
@@ -636,7 +685,7 @@ def test_more_slices_recover_entries_far_below_the_row_maximum(gpu):
         hCh, hCl = _host(Ch), _host(Cl)
         E, DA = exact.slice_rows(Ah, Al, nslices=nslices)
         F, DB = exact.slice_cols(Bh, Bl, nslices=nslices)
-        Sh, Sl = exact.renorm_levels(exact.level_values(exact.level_sums_units(DA, DB)), E, F)
+        Sh, Sl = exact.nearest_dd(exact.level_sums_units(DA, DB), E, F)
         assert _bits_equal(hCh, Sh) and _bits_equal(hCl, Sl)
         worst[nslices] = float((np.abs((hCh[rows, cols] - Rh) + (hCl[rows, cols] - Rl)) / absab).max())
     _say(f"[parity] wide-range rows: n=8 {worst[8]:.3e}, n=13 {worst[13]:.3e} (tolerance {compare.TOL})")
@@ -655,7 +704,7 @@ def test_kblocked_chain_bit_exact(gpu, nslices, m, n, k):
     Bh, Bl = _edge_matrix(rng, k, n)
     dA, dAl, dB, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
     for kblock in (16, 33, 100, k, k + 5):
-        Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kblock, nslices)
+        Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kblock, nslices, nearest=True)
         Ch, Cl = gpu.dd_gemm(dA, dAl, dB, dBl, nslices=nslices, kblock=kblock)
         assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl), kblock
 
@@ -678,11 +727,11 @@ def test_kblocked_strided_operands_and_null_lo(gpu):
     out = torch.full((2, m, n + 6), 9.0, dtype=torch.float64, device="cuda")
     Ch, Cl = out[0, :, :n], out[1, :, :n]
     gpu.dd_gemm(vA[0], vA[1], vB[0], vB[1], C_hi=Ch, C_lo=Cl, kblock=kblock)
-    Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kblock, 8)
+    Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kblock, 8, nearest=True)
     assert _bits_equal(_host(Ch.contiguous()), Rh) and _bits_equal(_host(Cl.contiguous()), Rl)
     assert (_host(out[:, :, n:]) == 9.0).all()
     gpu.dd_gemm(vA[0], None, vB[0], None, C_hi=Ch, C_lo=Cl, kblock=kblock)
-    Zh, Zl = exact.sliced_product_kblocks(Ah, np.zeros_like(Al), Bh, np.zeros_like(Bl), kblock, 8)
+    Zh, Zl = exact.sliced_product_kblocks(Ah, np.zeros_like(Al), Bh, np.zeros_like(Bl), kblock, 8, nearest=True)
     assert _bits_equal(_host(Ch.contiguous()), Zh) and _bits_equal(_host(Cl.contiguous()), Zl)
 
 

@@ -3,8 +3,9 @@
 Each case draws a ragged shape spanning up to a few tiles, a slice count, a
 k-block size (or none), which lo planes are present and the entry
 distributions; the product is compared bit for bit with the oracle's chain for
-the same inputs (oracle.exact.sliced_product / sliced_product_kblocks for
-double doubles, oracle.qd.sliced_product for quad doubles).  The grid tests
+the same inputs (oracle.exact.paired_product / sliced_product_kblocks with the
+nearest double-double per block for double doubles, oracle.qd.sliced_product
+for quad doubles).  The grid tests
 elsewhere cover each parameter on its own; these cover their combinations,
 with a set of small outputs and long k that take the split-over-k path with
 varying part counts.
@@ -112,9 +113,9 @@ def test_random_dd_case_bit_exact(gpu, case):
     Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al) if lo_a else None, _dev(Bh), _dev(Bl) if lo_b else None,
                          nslices=ns, kblock=kb)
     if kb is None or kb >= k:
-        Rh, Rl = exact.sliced_product(Ah, Al, Bh, Bl, ns)
+        Rh, Rl = exact.paired_product(Ah, Al, Bh, Bl, ns)
     else:
-        Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kb, ns)
+        Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kb, ns, nearest=True)
     assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
 
 
@@ -132,9 +133,9 @@ def test_random_split_dd_case_bit_exact(gpu, case):
     Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al) if lo_a else None, _dev(Bh), _dev(Bl) if lo_b else None,
                          nslices=ns, kblock=kb)
     if kb is None or kb >= k:
-        Rh, Rl = exact.sliced_product(Ah, Al, Bh, Bl, ns)
+        Rh, Rl = exact.paired_product(Ah, Al, Bh, Bl, ns)
     else:
-        Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kb, ns)
+        Rh, Rl = exact.sliced_product_kblocks(Ah, Al, Bh, Bl, kb, ns, nearest=True)
     assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
 
 

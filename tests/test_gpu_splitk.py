@@ -1,11 +1,15 @@
 """Products split over k (GPU tests).
 
 Outputs whose tiles leave the chip partly idle (a few output tiles and a long
-k, or a last round of workgroups far from full) are computed in k-parts whose
-exact level sums are added with atomic adds into zeroed level planes.  Integer level sums make the additions exact, so the split result must
-equal, bit for bit, the oracle's unsplit chain, the unsplit fused stage call
-(dd_sliced_gemm_renorm, which has no workspace and never splits), and itself
-on every repetition; the path must also replay in a HIP graph.
+k, or a last round of workgroups far from full) are computed in k-parts.  The
+double-double product runs the pair-packed schedule: each part stores the
+exact int64 group sums of its outputs in planes of its own, and one more
+launch adds the parts and rounds each entry's exact total to the nearest
+double-double -- no atomics.  Exact integer sums make the split result equal,
+bit for bit, the oracle's chain on the same inputs, the nearest rounding of the
+unsplit group sums (dd_sliced_gemm_pairs), and itself on every repetition; the
+path must also replay in a HIP graph.  The level stage call (dd_sliced_gemm)
+and the quad-double product split into level planes with exact atomic adds.
 """
 import sys
 
@@ -40,6 +44,37 @@ def _say(msg):
     sys.stdout.flush()
 
 
+def _nearest_of_groups(G, E, F):
+    """(hi, lo) = (RN(x), RN(x - hi)) for x = 2^(E_i + F_j) sum_g G_g 2^(-13(g+3)), from
+    int64 group sums, with Python's correctly rounded int -> float conversion;
+    for results in the normal range (the inputs here keep them there)."""
+    import math
+    ng, m, n = G.shape
+    hi = np.empty((m, n))
+    lo = np.empty((m, n))
+    for i in range(m):
+        for j in range(n):
+            T = 0
+            for g in range(ng):
+                T += int(G[g, i, j]) << (13 * (ng - 1 - g))
+            h = float(T)
+            r = T - int(h)
+            sc = int(E[i]) + int(F[j]) - 13 * (ng + 2)
+            hi[i, j] = math.ldexp(h, sc)
+            lo[i, j] = math.ldexp(float(r), sc)
+    return hi, lo
+
+
+def _unsplit_reference(gpu, dAh, dAl, dBh, dBl, ns):
+    """The nearest double-double of the unsplit group sums (one launch, no parts)."""
+    m, k = dAh.shape
+    n = dBh.shape[1]
+    E, As = gpu.split_balanced(dAh, dAl, 0, nslices=ns)
+    F, Bs = gpu.split_balanced(dBh, dBl, 1, nslices=ns)
+    G = _host(gpu.sliced_gemm_pairs(m, n, k, As, Bs, nslices=ns))
+    return _nearest_of_groups(G, _host(E), _host(F))
+
+
 @pytest.mark.parametrize("m,n,k,ns", [(64, 64, 512, 8), (40, 70, 3000, 8), (3, 5, 100000, 8),
                                       (100, 80, 5000, 16), (64, 64, 1024, 6), (33, 130, 4100, 12)])
 def test_split_dd_product_equals_the_unsplit_chain(gpu, m, n, k, ns):
@@ -49,13 +84,11 @@ def test_split_dd_product_equals_the_unsplit_chain(gpu, m, n, k, ns):
     Bh, Bl = workloads.random_dd((k, n), 9101 + k, "uniform")
     dAh, dAl, dBh, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
     Ch, Cl = gpu.dd_gemm(dAh, dAl, dBh, dBl, nslices=ns)
-    Rh, Rl = exact.sliced_product(Ah, Al, Bh, Bl, ns)
+    Rh, Rl = exact.paired_product(Ah, Al, Bh, Bl, ns)
     assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
-    # the unsplit fused stage call gives the same bits
-    E, As = gpu.split_balanced(dAh, dAl, 0, nslices=ns)
-    F, Bs = gpu.split_balanced(dBh, dBl, 1, nslices=ns)
-    Uh, Ul = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F, nslices=ns)
-    assert _bits_equal(_host(Uh), Rh) and _bits_equal(_host(Ul), Rl)
+    # the unsplit group sums round to the same bits
+    Uh, Ul = _unsplit_reference(gpu, dAh, dAl, dBh, dBl, ns)
+    assert _bits_equal(Uh, Rh) and _bits_equal(Ul, Rl)
     # and the split is deterministic
     for _ in range(2):
         Dh, Dl = gpu.dd_gemm(dAh, dAl, dBh, dBl, nslices=ns)
@@ -178,17 +211,15 @@ def test_split_of_partly_idle_rounds(gpu, m, n, k, ns):
     Bh, Bl = workloads.random_dd((k, n), 9501 + n, "normal")
     dAh, dAl, dBh, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
     Ch, Cl = gpu.dd_gemm(dAh, dAl, dBh, dBl, nslices=ns)
-    E, As = gpu.split_balanced(dAh, dAl, 0, nslices=ns)
-    F, Bs = gpu.split_balanced(dBh, dBl, 1, nslices=ns)
-    Uh, Ul = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F, nslices=ns)
     hCh, hCl = _host(Ch), _host(Cl)
-    assert _bits_equal(hCh, _host(Uh)) and _bits_equal(hCl, _host(Ul))
+    Uh, Ul = _unsplit_reference(gpu, dAh, dAl, dBh, dBl, ns)
+    assert _bits_equal(hCh, Uh) and _bits_equal(hCl, Ul)
     rng = np.random.default_rng(m * n + k)
     rows = sorted({0, m - 1, *(int(x) for x in rng.integers(0, m, 5))})
     cols = sorted({0, n - 1, *(int(x) for x in rng.integers(0, n, 5))})
     E_ref, DA = exact.slice_rows(Ah, Al, rows, ns)
     F_ref, DB = exact.slice_cols(Bh, Bl, cols, ns)
-    Rh, Rl = exact.renorm_levels(exact.level_values(exact.level_sums_units(DA, DB)), E_ref, F_ref)
+    Rh, Rl = exact.nearest_dd(exact.level_sums_units(DA, DB), E_ref, F_ref)
     assert _bits_equal(hCh[np.ix_(rows, cols)], Rh) and _bits_equal(hCl[np.ix_(rows, cols)], Rl)
 
 
@@ -239,17 +270,15 @@ def test_split_of_the_last_rows_only(gpu, m, n, k, ns):
     Bh, Bl = workloads.random_dd((k, n), 9701 + n, "normal")
     dAh, dAl, dBh, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
     Ch, Cl = gpu.dd_gemm(dAh, dAl, dBh, dBl, nslices=ns)
-    E, As = gpu.split_balanced(dAh, dAl, 0, nslices=ns)
-    F, Bs = gpu.split_balanced(dBh, dBl, 1, nslices=ns)
-    Uh, Ul = gpu.sliced_gemm_renorm(m, n, k, As, E, Bs, F, nslices=ns)
     hCh, hCl = _host(Ch), _host(Cl)
-    assert _bits_equal(hCh, _host(Uh)) and _bits_equal(hCl, _host(Ul))
+    Uh, Ul = _unsplit_reference(gpu, dAh, dAl, dBh, dBl, ns)
+    assert _bits_equal(hCh, Uh) and _bits_equal(hCl, Ul)
     rng = np.random.default_rng(m + n + k + ns)
     rows = _sample(rng, m, [0, r0 - 1, r0, r0 + 1, m - 1])
     cols = _sample(rng, n, [0, c0 - 1, c0, n - 1])
     E_ref, DA = exact.slice_rows(Ah, Al, rows, ns)
     F_ref, DB = exact.slice_cols(Bh, Bl, cols, ns)
-    Rh, Rl = exact.renorm_levels(exact.level_values(exact.level_sums_units(DA, DB)), E_ref, F_ref)
+    Rh, Rl = exact.nearest_dd(exact.level_sums_units(DA, DB), E_ref, F_ref)
     assert _bits_equal(hCh[np.ix_(rows, cols)], Rh) and _bits_equal(hCl[np.ix_(rows, cols)], Rl)
 
 
@@ -269,7 +298,7 @@ def test_blocked_product_whose_blocks_split_their_last_rows(gpu, kblock):
     r0 = gpu.split_first_row(m, n, kblock, 8)
     rows = _sample(rng, m, [0, r0 - 1, r0, m - 1])
     cols = _sample(rng, n, [0, n - 1])
-    Rh, Rl = exact.sliced_product_kblocks(Ah[rows], Al[rows], Bh[:, cols], Bl[:, cols], kblock, 8)
+    Rh, Rl = exact.sliced_product_kblocks(Ah[rows], Al[rows], Bh[:, cols], Bl[:, cols], kblock, 8, nearest=True)
     assert _bits_equal(hCh[np.ix_(rows, cols)], Rh) and _bits_equal(hCl[np.ix_(rows, cols)], Rl)
 
 
