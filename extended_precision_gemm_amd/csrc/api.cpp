@@ -433,12 +433,8 @@ ddgemm_status_t product_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t
         const double* a_lo = A_lo ? A_lo + p0 : nullptr;
         const double* b_hi = B_hi ? B_hi + p0 * ldb : nullptr;
         const double* b_lo = B_lo ? B_lo + p0 * ldb : nullptr;
-        // Both exponent passes first: one right behind a slice pass's writes runs at half speed.
-        e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s, kSplitExps);
-        if (e == hipSuccess) e = launch_split(kc, n, b_hi, b_lo, ldb, 1, nslices, F, B_sl, s, kSplitExps);
-        if (e == hipSuccess) e = launch_split(kc, n, b_hi, b_lo, ldb, 1, nslices, F, B_sl, s, kSplitSlices);
         // A in the pair-packed layout the product's GEMM reads
-        if (e == hipSuccess) e = launch_split(m, kc, a_hi, a_lo, lda, 0, nslices, E, A_sl, s, kSplitSlices, true);
+        e = launch_split_operands(m, n, kc, a_hi, a_lo, lda, b_hi, b_lo, ldb, nslices, E, A_sl, F, B_sl, s);
         if (e == hipSuccess && b == 0 && after_split) e = hipEventRecord(static_cast<hipEvent_t>(after_split), s);
         if (e != hipSuccess) break;
         if (b == 0) {

@@ -46,12 +46,14 @@ struct OutPlanes {
     double* c[4];
 };
 
-// Phases of an operand's split: the exponent pass and the slice pass, so that a
-// product can run both operands' exponent passes before either slice pass
-// (measured: an exponent pass right behind a slice pass's gigabyte of writes
-// runs at half speed).  An operand sliced in one pass does it all in the slice
-// phase.
+// Phases of an operand's split: the exponent pass and the slice pass, so that
+// the quad-double product can run both operands' exponent passes before either
+// slice pass.  An operand sliced in one pass does it all in the slice phase.
 enum SplitPhase { kSplitExps = 1, kSplitSlices = 2, kSplitAll = 3 };
+
+// Columns per workgroup of the streaming column-exponent pass.
+constexpr int64_t kExpColChunk = 512;
+inline int64_t exp_col_chunks(int64_t cols) { return (cols + kExpColChunk - 1) / kExpColChunk; }
 
 // Argument checks shared by the double-double product entry points: `status`
 // is the error to report (DDGEMM_SUCCESS when the call may proceed), `empty`
@@ -76,6 +78,10 @@ ddgemm_status_t check_current_device();
 hipError_t launch_split(int64_t rows, int64_t cols, const double* X_hi, const double* X_lo,
                         int64_t ldx, int axis, int ns, int32_t* exps, double* slices, hipStream_t stream,
                         int phases = kSplitAll, bool pairs = false);
+// Both operands of a product: exponents and slices, A pair-packed.
+hipError_t launch_split_operands(int64_t m, int64_t n, int64_t k, const double* A_hi, const double* A_lo,
+                                 int64_t lda, const double* B_hi, const double* B_lo, int64_t ldb, int ns, int32_t* E,
+                                 double* A_slices, int32_t* F, double* B_slices, hipStream_t stream);
 hipError_t launch_sliced_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                               const double* B_slices, double* levels, int64_t ldl,
                               const int32_t* E, const int32_t* F, double* C_hi, double* C_lo,

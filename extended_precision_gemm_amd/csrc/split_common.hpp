@@ -11,6 +11,9 @@ namespace {
 constexpr int kNoExp = 0;          // encoded "no nonzero entry seen"
 constexpr int kExpBias = 4096;     // encoded exponent = frexp exponent + bias (>= 1)
 constexpr uint64_t kMant = (1ull << 52) - 1;
+// A balancing exponent replaced by this value marks its row (column) for the
+// exact pass: it holds a pair whose leading word is not RN(hi + lo).
+constexpr int32_t kUnnormalised = INT32_MIN;
 
 // frexp exponent of a nonzero finite double: smallest e with |x| < 2^e.
 __device__ __forceinline__ int frexp_exponent(double x) {

@@ -117,8 +117,8 @@ size_t dd_split_slices_bytes(int64_t outer, int64_t k);
  * (row-major; t = 0: all of them) may be split over k into p parts of at least
  * 16 stages each (a stage is 8 values of k, 4 from 14 slices on), p <= 256,
  * while the tiles before t, whole rounds of 256 workgroups, run unsplit; t and
- * p are chosen by a timing model of the rounds of workgroups, the atomic adds
- * and the level planes, and only where that saves at least 2 %; outputs that
+ * p are chosen by a timing model of the rounds of workgroups and of the part
+ * planes' traffic, and only where that saves at least 5 %; outputs that
  * fill whole rounds never split.  ddgemm_split_parts returns p,
  * ddgemm_split_first_tile t and ddgemm_split_first_row the first row r of t's
  * tile row.  Each part stores the exact int64 group sums of its outputs in

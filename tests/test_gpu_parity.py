@@ -769,3 +769,56 @@ def test_binding_rejects_a_host_or_mistyped_workspace(gpu):
     torch.cuda.synchronize()
     assert torch.equal(C_hi.cpu(), torch.full((8, 8), 8.0, dtype=torch.float64)) and not C_lo.any()
 
+
+
+@pytest.mark.timeout(600)
+def test_product_recomputes_rows_and_columns_with_unnormalised_pairs(gpu):
+    """The product entry points take a row's (column's) balancing exponent from
+    the leading words when both operands are sliced in two passes; a row or
+    column holding a pair whose leading word is not RN(hi + lo) is recomputed
+    from (hi, lo) ("Multiple Double Arithmetic on NVIDIA Tensor Cores", §3,
+    balancing; Problems 3.3 and 3.4 for opposite signs and leading zeros).
+    1280^3 takes that path for both operands; pairs planted in some rows of A
+    and columns of B move the exact exponent up or down from the leading
+    words' one, or leave it.  The product equals the oracle's nearest chain bit
+    for bit on those rows and columns and on sampled others, and the stage
+    call's exponents equal the oracle's."""
+    import torch
+    m = n = k = 1280
+    rng = np.random.default_rng(1280)
+    Ah, Al = _edge_matrix(rng, m, k)
+    Bh, Bl = _edge_matrix(rng, k, n)
+    # A rows: r0 exponent down (1 - 0.75 = 0.25 the largest), r1 a zero leading
+    # word with a large trailing one (exponent up), r2 |lo| >> |hi| on a 16-row
+    # block boundary, r3 an unnormalised pair that leaves the exponent
+    r0, r1, r2, r3 = 37, 600, 1023, 1279
+    Ah[r0] *= 2.0 ** -8
+    Al[r0] *= 2.0 ** -8
+    Ah[r0, 5], Al[r0, 5] = 1.0, -0.75
+    Ah[r1, 700], Al[r1, 700] = 0.0, 3.0
+    Ah[r2, 0], Al[r2, 0] = 2.0 ** -30, 2.0 ** 20
+    Ah[r3, 9], Al[r3, 9] = 2.0 ** -40, -2.0 ** -45
+    # B columns the same way
+    c0, c1, c2, c3 = 16, 400, 1100, 1279
+    Bh[:, c0] *= 2.0 ** -8
+    Bl[:, c0] *= 2.0 ** -8
+    Bh[3, c0], Bl[3, c0] = -1.0, 0.75
+    Bh[1279, c1], Bl[1279, c1] = 0.0, -5.0
+    Bh[640, c2], Bl[640, c2] = -2.0 ** -30, 2.0 ** 25
+    Bh[11, c3], Bl[11, c3] = 2.0 ** -40, 2.0 ** -46 * 3
+    assert Bh.nbytes + Bl.nbytes > 24 << 20  # B is sliced in two passes
+    rows = np.union1d([r0, r1, r2, r3], _sample_indices(rng, m, 6))
+    cols = np.union1d([c0, c1, c2, c3], _sample_indices(rng, n, 6))
+    E_s, DA = exact.slice_rows(Ah, Al, rows)
+    F_s, DB = exact.slice_cols(Bh, Bl, cols)
+    Eh = exact.balancing_exponents(Ah[rows], np.zeros_like(Ah[rows]), 0)
+    assert np.any(Eh != E_s), "some planted pair moves its row's exponent"
+    _say(f"[parity] unnormalised pairs: product {m}x{n}x{k}")
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))
+    Nh_ref, Nl_ref = exact.nearest_dd(exact.level_sums_units(DA, DB), E_s, F_s)
+    hCh, hCl = _host(Ch), _host(Cl)
+    assert _bits_equal(hCh[np.ix_(rows, cols)], Nh_ref) and _bits_equal(hCl[np.ix_(rows, cols)], Nl_ref)
+    E, _ = gpu.split_balanced(_dev(Ah), _dev(Al), 0)
+    F, _ = gpu.split_balanced(_dev(Bh), _dev(Bl), 1)
+    assert np.array_equal(_host(E), exact.balancing_exponents(Ah, Al, 0))
+    assert np.array_equal(_host(F), exact.balancing_exponents(Bh, Bl, 1))
