@@ -63,25 +63,16 @@ def _parse():
     return ap.parse_args()
 
 
-def _traffic_from_profile(workload: str):
+def _traffic_from_profile(workload: str, product: str = "dd"):
     """HBM bytes per GEMM launch from the committed counter summary, if it was
-    taken on the current kernel source; None otherwise."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"sliced_gemm_renorm_{workload}_hbm_traffic.txt")
-    if not os.path.exists(path):
-        return None
-    vals = {}
-    for line in open(path):
-        if ":" in line and not line.lstrip().startswith("#"):
-            key, val = line.split(":", 1)
-            vals[key.strip()] = val.strip()
-    src = os.path.join(ROOT, "extended_precision_gemm_amd", "csrc", "sliced_gemm.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if vals.get("kernel_source_sha256_16") != sha:
+    taken on the current kernel sources; None otherwise."""
+    from extended_precision_gemm_amd import profiling
+    path = os.path.join(ROOT, "profiles", f"{product}_product_{workload}_hbm_traffic.txt")
+    if profiling.read_summary_value(path, "kernel_source_sha256_16") != profiling.source_hash():
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return float(profiling.read_summary_value(path, "hbm_bytes_per_launch"))
+    except (TypeError, ValueError):
         return None
 
 
@@ -473,7 +464,7 @@ def _run_qd(args, w):
             "peak": PEAK_FP64_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP64_MFMA_TFLOPS, 4),
-            "traffic": _traffic_from_profile(w.name),
+            "traffic": _traffic_from_profile(w.name, "qd"),
             "flops_per_launch": QD_PAIRS * 2.0 * m * n * k,
             "launch_ms": round(gemm_ms, 4),
         },
