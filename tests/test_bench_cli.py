@@ -2,10 +2,8 @@
 without a GPU, and that the HBM traffic of the dominant kernel is taken from
 the committed counter summary only while that summary was taken on the
 current GEMM source."""
-import hashlib
 import importlib.util
 import os
-import shutil
 import subprocess
 import sys
 
@@ -51,27 +49,37 @@ def _summary_values(path):
     return vals
 
 
-@pytest.mark.parametrize("workload", ["dd4096_exp20", "qd4096_exp20"])
-def test_traffic_is_read_only_for_the_profiled_source(workload, tmp_path):
+@pytest.mark.parametrize("workload,product", [("dd4096_exp20", "dd"), ("qd4096_exp20", "qd")])
+def test_traffic_is_read_only_for_the_profiled_source(workload, product, monkeypatch):
     bench = _bench_module()
-    path = os.path.join(ROOT, "profiles", f"sliced_gemm_renorm_{workload}_hbm_traffic.txt")
+    from extended_precision_gemm_amd import profiling
+    path = os.path.join(ROOT, "profiles", f"{product}_product_{workload}_hbm_traffic.txt")
     vals = _summary_values(path)
-    src = os.path.join(ROOT, "extended_precision_gemm_amd", "csrc", "sliced_gemm.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    got = bench._traffic_from_profile(workload)
-    if vals["kernel_source_sha256_16"] == sha:
+    got = bench._traffic_from_profile(workload, product)
+    if vals["kernel_source_sha256_16"] == profiling.source_hash():
         assert got == float(vals["hbm_bytes_per_launch"]) and got > 0
     else:
         assert got is None
-    # a copy of the tree whose GEMM source differs by one byte reads no traffic
-    fake = tmp_path / "root"
-    (fake / "profiles").mkdir(parents=True)
-    (fake / "extended_precision_gemm_amd" / "csrc").mkdir(parents=True)
-    shutil.copy(path, fake / "profiles")
-    (fake / "extended_precision_gemm_amd" / "csrc" / "sliced_gemm.hip").write_bytes(open(src, "rb").read() + b"\n")
-    bench.ROOT = str(fake)
-    assert bench._traffic_from_profile(workload) is None
+    # a GEMM source that differs from the profiled one reads no traffic
+    monkeypatch.setattr(profiling, "source_hash", lambda: "0" * 16)
+    assert bench._traffic_from_profile(workload, product) is None
     assert bench._traffic_from_profile("no_such_workload") is None
+
+
+def test_source_hash_covers_the_gemm_sources(tmp_path, monkeypatch):
+    """One byte more in any of the GEMM's sources changes the hash."""
+    from extended_precision_gemm_amd import profiling
+    base = profiling.source_hash()
+    for f in profiling.GEMM_SOURCES:
+        pkg = tmp_path / f.replace(".", "_")
+        (pkg / "csrc").mkdir(parents=True)
+        for g in profiling.GEMM_SOURCES:
+            data = open(os.path.join(profiling._PKG, "csrc", g), "rb").read()
+            (pkg / "csrc" / g).write_bytes(data + (b"\n" if g == f else b""))
+        monkeypatch.setattr(profiling, "_PKG", str(pkg))
+        assert profiling.source_hash() != base
+        monkeypatch.undo()
+    assert profiling.source_hash() == base
 
 
 def test_profiles_of_the_gemm_carry_one_source_hash():
