@@ -80,6 +80,7 @@ _SIGNATURES = {
     "qd_gemm_ws": (_st, [_i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp, _sz, _vp]),
     "qd_gemm_workspace_size_kb": (_sz, [_i64, _i64, _i64, _i64]),
     "qd_gemm_ws_kb": (_st, [_i64, _i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp, _sz, _vp]),
+    "qd_gemm_ws_timed": (_st, [_i64, _i64, _i64, _pp, _i64, _pp, _i64, _pp, _i64, _vp, _sz, _vp, _vp]),
     "dd_gemm_workspace_size_kb": (_sz, [_i64, _i64, _i64, ctypes.c_int, _i64]),
     "dd_gemm_ws_kb": (_st, [_i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                             _vp, _sz, _vp]),
@@ -531,6 +532,17 @@ def qd_gemm(A, B, C=None, workspace=None, stream=None, kblock: int | None = None
         else:
             _check(lib.qd_gemm_ws_kb(m, n, k, kblock, pa, lda, pb, ldb, pc, ldc, _ptr(workspace),
                                      workspace.numel(), _stream(stream)))
+    return C
+
+
+def qd_gemm_timed(A, B, C, workspace, after_split, stream=None):
+    """qd_gemm on the caller's workspace, recording the hipEvent_t handle
+    `after_split` (an int, or None) on the stream once the operands are sliced."""
+    m, n, k, pa, lda, pb, ldb, C, pc, ldc, dev = _qd_gemm_args(A, B, C)
+    with torch.cuda.device(dev):
+        workspace = _workspace(workspace, qd_workspace_size(m, n, k), dev, stream)
+        _check(lib.qd_gemm_ws_timed(m, n, k, pa, lda, pb, ldb, pc, ldc, _ptr(workspace), workspace.numel(),
+                                    after_split, _stream(stream)))
     return C
 
 

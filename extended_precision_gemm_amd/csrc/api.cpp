@@ -161,6 +161,11 @@ ddgemm_status_t validate_qd_blocked_dims(int64_t m, int64_t n, int64_t k, int64_
 }
 
 // All of k when it fits one sliced product, else the fewest equal blocks that do.
+// The quad-double product takes the pair-packed schedule when k is one block
+// within the group sums' int64 bound (k <= 2^21); longer k keeps the level
+// schedule of R23, whose blocks share exponents and add exactly.
+bool qd_pairs(int64_t k, int64_t kb) { return kb >= k && k <= pair_k_max(kQdSlices); }
+
 int64_t qd_default_kblock(int64_t k) {
     if (k <= QDGEMM_K_MAX) return k;
     const int64_t blocks = (k + QDGEMM_K_MAX - 1) / QDGEMM_K_MAX;
@@ -186,6 +191,39 @@ hipError_t renorm_split_tiles(int64_t m, int64_t n, const GemmGeometry& g, const
     }
     return mt > done ? piece(mt - done, n, r0 + done, int64_t{0}, L + done * n) : hipSuccess;
 }
+
+// One k-block of a pair-packed product (A pre-packed) into `out` (words = 2:
+// the nearest double-double; 4: the nearest quad double): with the plan `plan`
+// the tiles from plan.first_tile on run in k-parts whose int64 group sums go
+// to the part planes P and are added and rounded by one more launch, the
+// tiles before it unsplit; a plan that needs more part planes than
+// `part_cells` (rows of n entries over all parts) runs unsplit.  U: the chunk
+// planes when k exceeds one exact chunk.
+hipError_t pair_block_gemm(int64_t m, int64_t n, int64_t kc, int ns, int words, const double* A_sl,
+                           const double* B_sl, const int32_t* E, const int32_t* F, const OutPlanes& out, int64_t ldd,
+                           int64_t* U, int64_t* P, int64_t part_cells, const SplitPlan& plan, hipStream_t st) {
+    const PairOut kind = words == 4 ? kPairToQD : kPairToDD;
+    const int64_t mn = m * n;
+    if (plan.parts <= 1 || plan.parts * (m - plan.first_row) > part_cells)
+        return launch_pair_gemm(m, n, kc, ns, A_sl, B_sl, kind, E, F, out, ldd, U, n, mn, 0, 0, -1, 1, st, true);
+    hipError_t err = hipSuccess;
+    if (plan.first_tile > 0)  // whole rounds of tiles, unsplit
+        err = launch_pair_gemm(m, n, kc, ns, A_sl, B_sl, kind, E, F, out, ldd, U, n, mn, 0, 0, plan.first_tile, 1, st,
+                               true);
+    const int64_t plane = (m - plan.first_row) * n, part_stride = (ns - 1) * plane;
+    if (err == hipSuccess)
+        err = launch_pair_gemm(m, n, kc, ns, A_sl, B_sl, kPairToUnits, nullptr, nullptr, OutPlanes{}, 0, P, n, plane,
+                               part_stride, plan.first_tile, -1, plan.parts, st, true);
+    if (err != hipSuccess) return err;
+    return renorm_split_tiles(m, n, pair_geometry(ns), plan, static_cast<const int64_t*>(P),
+                              [&](int64_t rows, int64_t cols, int64_t r, int64_t c, const int64_t* cells) {
+                                  OutPlanes piece = out;
+                                  for (int q = 0; q < words; ++q) piece.c[q] = out.c[q] + r * ldd + c;
+                                  return launch_pair_parts(rows, cols, ns, words, cells, n, plane, part_stride,
+                                                           plan.parts, E + r, F + c, piece, ldd, st);
+                              });
+}
+
 
 // Plane c of X advanced by `off` entries (a missing plane stays missing).
 QdPlanes offset_planes(const QdPlanes& X, int64_t off) {
@@ -392,33 +430,12 @@ ddgemm_status_t product_kb(int64_t m, int64_t n, int64_t k, int nslices, int64_t
     const SplitPlan plan_kb = pair_split_plan(m, n, kb, ns);
     const int64_t part_cells = plan_kb.parts > 1 ? plan_kb.parts * (m - plan_kb.first_row) : 0;
 
-    // One block's product into (hi, lo) planes: the pair-packed schedule with
-    // the nearest double-double of each entry's exact total, or, for the tiles
-    // from plan.first_tile on, the same in k-parts whose group sums are added
-    // and rounded by one more launch (the tiles before it unsplit).
+    // One block's product into (hi, lo) planes (see pair_block_gemm); a shorter
+    // last block is planned for its own k.
     auto block_gemm = [&](int64_t kc, double* d_hi, double* d_lo, int64_t ldd, hipStream_t st) {
-        // a block whose plan needs more part planes than the workspace holds runs unsplit
         const SplitPlan plan = kc == kb ? plan_kb : pair_split_plan(m, n, kc, ns);
-        const OutPlanes out{{d_hi, d_lo, nullptr, nullptr}};
-        const int64_t mn = m * n;
-        if (plan.parts <= 1 || plan.parts * (m - plan.first_row) > part_cells)
-            return launch_pair_gemm(m, n, kc, ns, A_sl, B_sl, kPairToDD, E, F, out, ldd, U, n, mn, 0, 0, -1, 1, st,
-                                    true);
-        hipError_t err = hipSuccess;
-        if (plan.first_tile > 0)  // whole rounds of tiles, unsplit
-            err = launch_pair_gemm(m, n, kc, ns, A_sl, B_sl, kPairToDD, E, F, out, ldd, U, n, mn, 0, 0,
-                                   plan.first_tile, 1, st, true);
-        const int64_t plane = (m - plan.first_row) * n, part_stride = (ns - 1) * plane;
-        if (err == hipSuccess)
-            err = launch_pair_gemm(m, n, kc, ns, A_sl, B_sl, kPairToUnits, nullptr, nullptr, OutPlanes{}, 0, P, n,
-                                   plane, part_stride, plan.first_tile, -1, plan.parts, st, true);
-        if (err != hipSuccess) return err;
-        return renorm_split_tiles(m, n, pair_geometry(ns), plan, static_cast<const int64_t*>(P),
-                                  [&](int64_t rows, int64_t cols, int64_t r, int64_t c, const int64_t* cells) {
-                                      const OutPlanes piece{{d_hi + r * ldd + c, d_lo + r * ldd + c, nullptr, nullptr}};
-                                      return launch_pair_parts(rows, cols, ns, 2, cells, n, plane, part_stride,
-                                                               plan.parts, E + r, F + c, piece, ldd, st);
-                                  });
+        return pair_block_gemm(m, n, kc, ns, 2, A_sl, B_sl, E, F, OutPlanes{{d_hi, d_lo, nullptr, nullptr}}, ldd, U,
+                               P, part_cells, plan, st);
     };
 
     // Block b covers k indices [b kb, min(k, (b+1) kb)): a separate sliced product
@@ -515,11 +532,18 @@ size_t qd_gemm_workspace_size_kb(int64_t m, int64_t n, int64_t k, int64_t kblock
     if (validate_qd_blocked_dims(m, n, k, kblock) != DDGEMM_SUCCESS) return 0;
     const int64_t kb = k < kblock ? k : kblock;
     const bool blocked = block_count(k, kb) > 1;
-    // a blocked product's blocks split whole or not at all; one block may split its later rows only
-    const SplitPlan plan = split_plan(m, n, kb, kQdSlices, !blocked);
     Workspace ws;
     ws.add_slices(qd_split_slices_bytes(m, kb), m, kb).add_slices(qd_split_slices_bytes(n, kb), n, kb);
     ws.add(m, 4).add(n, 4);
+    if (qd_pairs(k, kb)) {
+        if (kb > pair_chunk_k(kQdSlices)) ws.add(kQdSlices - 1, m * n, 8);  // int64 group sums between k-chunks
+        const SplitPlan plan = pair_split_plan(m, n, kb, kQdSlices);
+        if (plan.parts > 1)  // int64 group sums of each k-part of the rows split over k
+            ws.add(plan.parts * (kQdSlices - 1), m - plan.first_row, n * 8);
+        return ws.bytes();
+    }
+    // a blocked product's blocks split whole or not at all; one block may split its later rows only
+    const SplitPlan plan = split_plan(m, n, kb, kQdSlices, !blocked);
     if (blocked) ws.add(QDGEMM_NUM_LEVELS, m, n * 8);  // int64 level planes of a blocked product
     if (plan.parts > 1)                                // double level planes of the rows split over k
         ws.add(QDGEMM_NUM_LEVELS, m - plan.first_row, n * 8);
@@ -560,9 +584,15 @@ ddgemm_status_t qd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k, const dou
     return launched(launch_qd_gemm(m, n, k, A_slices, B_slices, E, F, out, ldc, static_cast<hipStream_t>(stream)));
 }
 
-ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, const double* const A[4],
+}  // extern "C"
+
+namespace {
+
+// The quad-double product; `after_split` (a hipEvent_t, or null) is recorded
+// on the stream once the first k-block's operands are sliced.
+ddgemm_status_t qd_product_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, const double* const A[4],
                               int64_t lda, const double* const B[4], int64_t ldb, double* const C[4], int64_t ldc,
-                              void* workspace, size_t ws_bytes, void* stream) {
+                              void* workspace, size_t ws_bytes, void* stream, void* after_split) {
     ddgemm_status_t st = validate_qd_blocked_dims(m, n, k, kblock);
     if (st != DDGEMM_SUCCESS) return st;
     if (!ld_ok(lda, m, k) || !ld_ok(ldb, k, n) || !ld_ok(ldc, m, n)) return DDGEMM_ERROR_INVALID_VALUE;
@@ -600,11 +630,30 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
     double* L = reinterpret_cast<double*>(w);        // [16][m][n] double level planes of a split product
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (qd_pairs(k, kb)) {
+        // the pair-packed schedule (R25) with the nearest quad double of each
+        // entry's exact total; A sliced pre-packed
+        int64_t* U = reinterpret_cast<int64_t*>(w);  // [15][m][n] group sums between k-chunks
+        if (k > pair_chunk_k(kQdSlices))
+            w += align_up(static_cast<size_t>(kQdSlices - 1) * static_cast<size_t>(m) * static_cast<size_t>(n) * 8);
+        int64_t* P = reinterpret_cast<int64_t*>(w);  // part planes of the rows split over k
+        const SplitPlan plan = pair_split_plan(m, n, k, kQdSlices);
+        const int64_t part_cells = plan.parts > 1 ? plan.parts * (m - plan.first_row) : 0;
+        hipError_t e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitExps);  // both exponent passes first
+        if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitExps);
+        if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitSlices);
+        if (e == hipSuccess) e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitSlices, true);
+        if (e == hipSuccess && after_split) e = hipEventRecord(static_cast<hipEvent_t>(after_split), s);
+        if (e == hipSuccess)
+            e = pair_block_gemm(m, n, k, kQdSlices, 4, A_sl, B_sl, E, F, out, ldc, U, P, part_cells, plan, s);
+        return launched(e);
+    }
     if (blocks == 1) {
         hipError_t e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitExps);  // both exponent passes first
         if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitExps);
         if (e == hipSuccess) e = launch_qd_split(k, n, pb, ldb, 1, F, B_sl, s, kSplitSlices);
         if (e == hipSuccess) e = launch_qd_split(m, k, pa, lda, 0, E, A_sl, s, kSplitSlices);
+        if (e == hipSuccess && after_split) e = hipEventRecord(static_cast<hipEvent_t>(after_split), s);
         const SplitPlan plan = split_plan(m, n, k, kQdSlices, true);
         if (e == hipSuccess && plan.parts > 1) {  // tiles leave the chip partly idle: the last ones split over k
             if (plan.first_tile > 0) e = launch_qd_gemm(m, n, k, A_sl, B_sl, E, F, out, ldc, s, plan.first_tile);
@@ -633,6 +682,7 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
         const int64_t kc = k - p0 < kb ? k - p0 : kb;
         e = launch_qd_slices(m, kc, offset_planes(pa, p0), lda, 0, E, A_sl, s);
         if (e == hipSuccess) e = launch_qd_slices(kc, n, offset_planes(pb, p0 * ldb), ldb, 1, F, B_sl, s);
+        if (e == hipSuccess && b == 0 && after_split) e = hipEventRecord(static_cast<hipEvent_t>(after_split), s);
         if (e != hipSuccess) break;
         const QdBlockStep step = b == 0 ? kQdFirstBlock : (b + 1 == blocks ? kQdLastBlock : kQdMiddleBlock);
         const int64_t parts = split ? split_k_parts(m, n, kc, kQdSlices) : 1;
@@ -644,6 +694,24 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, c
         }
     }
     return launched(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock, const double* const A[4],
+                              int64_t lda, const double* const B[4], int64_t ldb, double* const C[4], int64_t ldc,
+                              void* workspace, size_t ws_bytes, void* stream) {
+    return qd_product_kb(m, n, k, kblock, A, lda, B, ldb, C, ldc, workspace, ws_bytes, stream, nullptr);
+}
+
+ddgemm_status_t qd_gemm_ws_timed(int64_t m, int64_t n, int64_t k, const double* const A[4], int64_t lda,
+                                 const double* const B[4], int64_t ldb, double* const C[4], int64_t ldc,
+                                 void* workspace, size_t ws_bytes, void* after_split, void* stream) {
+    if (k < 0) return DDGEMM_ERROR_INVALID_VALUE;
+    return qd_product_kb(m, n, k, qd_default_kblock(k), A, lda, B, ldb, C, ldc, workspace, ws_bytes, stream,
+                         after_split);
 }
 
 ddgemm_status_t qd_gemm_ws(int64_t m, int64_t n, int64_t k, const double* const A[4], int64_t lda,
@@ -690,10 +758,11 @@ const char* ddgemm_status_string(ddgemm_status_t status) {
 }  // extern "C"
 
 namespace {
-// The split plan a product entry point takes: pair-packed for the double-double
-// products, the level schedule for the quad-double one (16 slices).
+// The split plan a product entry point takes: the pair-packed schedule's, but
+// for 16 slices beyond the pair-packed int64 bound, where the quad-double
+// product keeps the level schedule.
 SplitPlan product_plan(int64_t m, int64_t n, int64_t k, int ns) {
-    return ns == kQdSlices ? split_plan(m, n, k, ns, true) : pair_split_plan(m, n, k, ns);
+    return ns == kQdSlices && k > pair_k_max(ns) ? split_plan(m, n, k, ns, true) : pair_split_plan(m, n, k, ns);
 }
 }  // namespace
 

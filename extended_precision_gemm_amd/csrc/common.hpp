@@ -128,12 +128,13 @@ hipError_t launch_levels_to_qd(int64_t m, int64_t n, const double* levels, int64
                                int64_t plane = -1);
 hipError_t launch_dd_accumulate(int64_t m, int64_t n, double* C_hi, double* C_lo, int64_t ldc, const double* T_hi,
                                 const double* T_lo, int64_t ldt, hipStream_t stream);
+// pairs: an A operand (axis 0) in the pair-packed layout (as launch_split).
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
-                           double* slices, hipStream_t stream, int phases = kSplitAll);
+                           double* slices, hipStream_t stream, int phases = kSplitAll, bool pairs = false);
 hipError_t launch_qd_exps(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
                           hipStream_t stream);
 hipError_t launch_qd_slices(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis,
-                            const int32_t* exps, double* slices, hipStream_t stream);
+                            const int32_t* exps, double* slices, hipStream_t stream, bool pairs = false);
 // Quad-double k-blocks that share their balancing exponents: the 16 level sums
 // of a block, in integer units, are stored into (first block) or added to
 // (later blocks) int64 level planes [16][m][n]; the last block adds its own and

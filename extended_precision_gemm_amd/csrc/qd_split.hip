@@ -122,8 +122,11 @@ __global__ void __launch_bounds__(NT) qd_exp_cols_block_kernel(int64_t rows, int
 }
 
 // One thread per packed (fragment, lane) position; writes the 16 slices of its
-// entry.  AXIS 0: entry (o, p) is X[o][p]; AXIS 1: it is X[p][o].
-template <int AXIS>
+// entry.  AXIS 0: entry (o, p) is X[o][p]; AXIS 1: it is X[p][o].  PK: the
+// pair-packed layout of an A operand that the product's pair-packed GEMM reads
+// -- plane 2u holds slices 2u and 2u+1 added (one exact 26-bit value, as the
+// two share the entry's sign and sit 13 bits apart), plane 2u+1 slice 2u alone.
+template <int AXIS, bool PK = false>
 __global__ void __launch_bounds__(256) qd_slice_kernel(int64_t outer, int64_t k, int64_t KB, int64_t total,
                                                        QdPlanes X, int64_t ld, const int32_t* __restrict__ exps,
                                                        double* __restrict__ slices) {
@@ -141,6 +144,14 @@ __global__ void __launch_bounds__(256) qd_slice_kernel(int64_t outer, int64_t k,
         }
         double sl[kQdSlices];
         qd_slice_entry(x, E, sl);
+        if constexpr (PK) {
+#pragma unroll
+            for (int u = 0; u < kQdSlices / 2; ++u) {
+                const double single = sl[2 * u];
+                sl[2 * u] = sl[2 * u] + sl[2 * u + 1];
+                sl[2 * u + 1] = single;
+            }
+        }
         double* dst = slices + frag * (kQdSlices * kFragDoubles) + lane;
 #pragma unroll
         for (int s = 0; s < kQdSlices; ++s) dst[s * kFragDoubles] = sl[s];
@@ -229,14 +240,16 @@ hipError_t launch_qd_exps(int64_t rows, int64_t cols, const QdPlanes& X, int64_t
 }
 
 hipError_t launch_qd_slices(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis,
-                            const int32_t* exps, double* slices, hipStream_t stream) {
+                            const int32_t* exps, double* slices, hipStream_t stream, bool pairs) {
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     const PackGeom g(outer, k);
     if (outer == 0 || g.doubles(kQdSlices) == 0) return hipSuccess;
     const int64_t total = g.RB * g.KB * kFragDoubles;
     const unsigned grid = grid_for(total, 256, 1 << 20);
-    if (axis == 0)
+    if (axis == 0 && pairs)
+        qd_slice_kernel<0, true><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X, ldx, exps, slices);
+    else if (axis == 0)
         qd_slice_kernel<0><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X, ldx, exps, slices);
     else
         qd_slice_kernel<1><<<grid, 256, 0, stream>>>(outer, k, g.KB, total, X, ldx, exps, slices);
@@ -244,7 +257,7 @@ hipError_t launch_qd_slices(int64_t rows, int64_t cols, const QdPlanes& X, int64
 }
 
 hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_t ldx, int axis, int32_t* exps,
-                           double* slices, hipStream_t stream, int phases) {
+                           double* slices, hipStream_t stream, int phases, bool pairs) {
     const int64_t outer = axis == 0 ? rows : cols;
     const int64_t k = axis == 0 ? cols : rows;
     if (outer == 0) return hipSuccess;
@@ -266,7 +279,7 @@ hipError_t launch_qd_split(int64_t rows, int64_t cols, const QdPlanes& X, int64_
         if (err != hipSuccess) return err;
     }
     if (!(phases & kSplitSlices)) return hipSuccess;
-    return launch_qd_slices(rows, cols, X, ldx, axis, exps, slices, stream);
+    return launch_qd_slices(rows, cols, X, ldx, axis, exps, slices, stream, pairs);
 }
 
 }  // namespace ddg

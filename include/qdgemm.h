@@ -63,13 +63,19 @@ extern "C" {
  * 0 for negative sizes. */
 size_t qd_split_slices_bytes(int64_t outer, int64_t k);
 
-/* Workspace bytes qd_gemm_ws needs (slices of both operands for one k-block,
- * both exponent vectors and, when k needs more than one block, sixteen int64
- * m×n level planes, or when a product of one block splits its tiles from some
- * tile on over k as in ddgemm.h (ddgemm_split_parts / ddgemm_split_first_row
- * with 16 slices: r), sixteen double (m - r)×n level planes (the blocks of a
- * blocked product split all tiles or none: r = 0);
- * 256-byte aligned regions); 0 for negative sizes, k > QDGEMM_K_MAX_BLOCKED, or a workspace past 2^62 bytes (which
+/* Workspace bytes qd_gemm_ws needs: slices of both operands for one k-block
+ * and both exponent vectors (256-byte aligned regions), plus
+ *   - for a product of one k-block with k <= 2^21 (the pair-packed schedule of
+ *     ddgemm.h, dd_sliced_gemm_pairs, with 16 slices: 72 matrix products per
+ *     k-block): 15 int64 m×n planes of group sums when k exceeds 2048, the most
+ *     values whose FP64 group sums stay exact, and when its tiles from some
+ *     tile on split over k (ddgemm_split_parts / ddgemm_split_first_row with 16
+ *     slices: p parts from row r) p 15 int64 (m - r)×n part planes;
+ *   - otherwise (the level schedule: 136 products per k-block): sixteen int64
+ *     m×n level planes when k needs more than one block, and when the product
+ *     splits over k, sixteen double (m - r)×n level planes (the blocks of a
+ *     blocked product split all tiles or none: r = 0).
+ * 0 for negative sizes, k > QDGEMM_K_MAX_BLOCKED, or a workspace past 2^62 bytes (which
  * qd_gemm_ws and qd_gemm reject with DDGEMM_ERROR_INVALID_VALUE).  The _kb form is for qd_gemm_ws_kb with k-blocks of
  * kblock terms (0 for kblock outside [1, QDGEMM_K_MAX] when k > 0). */
 size_t qd_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
@@ -110,7 +116,11 @@ ddgemm_status_t qd_sliced_gemm_renorm(int64_t m, int64_t n, int64_t k,
 
 /*
  * C = A·B for quad-double A (m×k) and B (k×n).  Overwrites C.  m = 0 or n = 0:
- * no-op; k = 0: C = 0.  Per entry the result is within
+ * no-op; k = 0: C = 0.  Every entry is the nearest quad double of the exact
+ * total of its window slice products (as qd_sliced_gemm_renorm rounds it),
+ * whatever the schedule: up to k = 2^21 in one block the 136 slice pairs run as
+ * 72 pair-packed matrix products (ddgemm.h, dd_sliced_gemm_pairs), beyond that
+ * as sixteen exact levels.  Per entry the result is within
  *     2^-208 (2^F_j sum_p |a_ip| + 2^E_i sum_p |b_pj| + 16 k 2^(E_i+F_j))
  *     + 2^-200 (|A||B|)_ij
  * of the exact product (E_i, F_j the row/column exponents): the truncation of
@@ -146,6 +156,15 @@ ddgemm_status_t qd_gemm_ws_kb(int64_t m, int64_t n, int64_t k, int64_t kblock,
                               const double* const B[4], int64_t ldb,
                               double* const C[4], int64_t ldc,
                               void* workspace, size_t ws_bytes, void* stream);
+
+/* qd_gemm_ws recording the hipEvent_t `after_split` (NULL: none) on `stream`
+ * once the operands of the first k-block are sliced, so that a caller can time
+ * the slicing and the GEMM apart inside one product. */
+ddgemm_status_t qd_gemm_ws_timed(int64_t m, int64_t n, int64_t k,
+                                 const double* const A[4], int64_t lda,
+                                 const double* const B[4], int64_t ldb,
+                                 double* const C[4], int64_t ldc,
+                                 void* workspace, size_t ws_bytes, void* after_split, void* stream);
 
 #ifdef __cplusplus
 }

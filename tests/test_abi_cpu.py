@@ -148,14 +148,23 @@ def test_workspace_holds_group_sum_planes_for_chunks_and_split_parts(ddg):
             assert L.dd_gemm_workspace_size(m, n, k) == L.dd_gemm_workspace_size_ns(m, n, k, ns)
     assert ddg.split_parts(64, 64, 512, 8) > 1 and ddg.split_parts(64, 64, 240, 8) == 1
     assert ddg.split_parts(1024, 1024, 4096, 8) == 1
-    # quad double: sixteen level planes for a split product (32x64 tiles, 4 values of k per stage)
+    # quad double, one block within the pair-packed int64 bound (k <= 2^21): the
+    # same group-sum planes with 16 slices -- 15 chunk planes beyond k = 2048,
+    # 15 part planes per k-part of a split
     for (m, n, k) in [(64, 64, 300), (64, 64, 100000), (2048, 2048, 4096), (50, 40, 30), (896, 896, 896)]:
         base = r(L.qd_split_slices_bytes(m, k)) + r(L.qd_split_slices_bytes(n, k)) + r(4 * m) + r(4 * n)
-        split = ddg.split_parts(m, n, k, 16) > 1
+        chunks = r(15 * m * n * 8) if k > PAIR_CHUNK[16] else 0
+        parts = ddg.split_parts(m, n, k, 16)
         rows = m - ddg.split_first_row(m, n, k, 16)
-        assert L.qd_gemm_workspace_size(m, n, k) == base + (r(16 * rows * n * 8) if split else 0), (m, n, k)
-    assert ddg.split_first_row(896, 896, 896, 16) > 0
+        split = r(parts * 15 * rows * n * 8) if parts > 1 else 0
+        assert L.qd_gemm_workspace_size(m, n, k) == base + chunks + split, (m, n, k)
+        assert parts == ddg.split_parts(m, n, k, 12 + 4)  # the dd product with 16 slices plans alike
     assert ddg.split_parts(64, 64, 300, 16) > 1 and ddg.split_parts(2048, 2048, 4096, 16) == 1
+    # beyond it, sixteen double level planes for a split (32x64 tiles, 4 values of k per stage)
+    m, n, k = 64, 64, (1 << 21) + 4
+    base = r(L.qd_split_slices_bytes(m, k)) + r(L.qd_split_slices_bytes(n, k)) + r(4 * m) + r(4 * n)
+    parts = ddg.split_parts(m, n, k, 16)
+    assert parts > 1 and L.qd_gemm_workspace_size(m, n, k) == base + r(16 * m * n * 8)
     # a blocked quad-double product whose blocks split: int64 planes and double planes
     m, n, k, kb = 40, 33, 3000, 1000
     assert ddg.split_parts(m, n, kb, 16) > 1
@@ -416,6 +425,12 @@ def test_qd_argument_validation(ddg):
     assert gemm(ws=P[6] + 8) == WS
     assert gemm(m=0, A=None, B=None, C=None) == 0                           # empty: no-op
     assert L.qd_gemm(0, 5, 6, None, 6, None, 5, None, 5, None) == 0
+    # the timed form checks the same arguments and the same workspace
+    timed = lambda **kw: L.qd_gemm_ws_timed(kw.get("m", 4), 5, kw.get("k", 6), A, 6, B, 5, kw.get("C", C), 5,
+                                            P[6], kw.get("ws_bytes", need), None, None)
+    assert timed(m=-1) == INV and timed(k=-1) == INV and timed(ws_bytes=need - 1) == WS
+    assert timed(C=_arr(P[0], P[3] + 4096, P[3] + 8192, P[3] + 12288)) == INV
+    assert timed(m=0) == 0
 
     def gemm_kb(kb, m=4, n=5, k=6, ws_bytes=1 << 30):
         return L.qd_gemm_ws_kb(m, n, k, kb, A, max(k, 1), B, n, C, n, P[6], ws_bytes, None)
@@ -449,6 +464,8 @@ def test_qd_valid_call_without_gpu_reports_device_error(ddg):
     C = _arr(P[3], P[3] + 4096, P[3] + 8192, P[3] + 12288)
     assert L.qd_gemm_ws_kb(4, 5, 6, 2, _arr(P[0]), 6, _arr(P[2]), 5, C, 5, P[6],
                            L.qd_gemm_workspace_size_kb(4, 5, 6, 2), None) == ddg.ERROR_DEVICE
+    assert L.qd_gemm_ws_timed(4, 5, 6, _arr(P[0]), 6, _arr(P[2]), 5, C, 5, P[6], L.qd_gemm_workspace_size(4, 5, 6),
+                              None, None) == ddg.ERROR_DEVICE
 
 
 def test_binding_rejects_host_and_wrong_dtype_tensors(ddg):
