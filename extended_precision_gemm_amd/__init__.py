@@ -85,6 +85,7 @@ _SIGNATURES = {
     "dd_gemm_ws_kb": (_st, [_i64, _i64, _i64, ctypes.c_int, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64,
                             _vp, _sz, _vp]),
     "ddgemm_split_parts": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
+    "ddgemm_small_product": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int]),
     "ddgemm_split_first_row": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "ddgemm_split_first_tile": (_i64, [_i64, _i64, _i64, ctypes.c_int]),
     "dd_gemm_noalloc": (_st, [_i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp]),
@@ -231,6 +232,11 @@ def k_max(nslices: int = NUM_SLICES) -> int:
 def split_parts(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:
     """k-parts the product entry points use for an m×n×k product (1 = not split)."""
     return lib.ddgemm_split_parts(m, n, k, nslices)
+
+
+def small_product(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> bool:
+    """Whether the product entry points run the small-output kernel for m×n×k."""
+    return bool(lib.ddgemm_small_product(m, n, k, nslices))
 
 
 def split_first_row(m: int, n: int, k: int, nslices: int = NUM_SLICES) -> int:

@@ -193,7 +193,8 @@ hipError_t renorm_split_tiles(int64_t m, int64_t n, const GemmGeometry& g, const
 }
 
 // One k-block of a pair-packed product (A pre-packed) into `out` (words = 2:
-// the nearest double-double; 4: the nearest quad double): with the plan `plan`
+// the nearest double-double; 4: the nearest quad double): the small-output
+// kernel where pair_small_product picks it; otherwise, with the plan `plan`
 // the tiles from plan.first_tile on run in k-parts whose int64 group sums go
 // to the part planes P and are added and rounded by one more launch, the
 // tiles before it unsplit; a plan that needs more part planes than
@@ -202,6 +203,8 @@ hipError_t renorm_split_tiles(int64_t m, int64_t n, const GemmGeometry& g, const
 hipError_t pair_block_gemm(int64_t m, int64_t n, int64_t kc, int ns, int words, const double* A_sl,
                            const double* B_sl, const int32_t* E, const int32_t* F, const OutPlanes& out, int64_t ldd,
                            int64_t* U, int64_t* P, int64_t part_cells, const SplitPlan& plan, hipStream_t st) {
+    if (pair_small_product(m, n, kc, ns))  // a few outputs, a short k: 4-wave workgroups per 16×16 block
+        return launch_small_pair_gemm(m, n, kc, ns, words, A_sl, B_sl, E, F, out, ldd, st);
     const PairOut kind = words == 4 ? kPairToQD : kPairToDD;
     const int64_t mn = m * n;
     if (plan.parts <= 1 || plan.parts * (m - plan.first_row) > part_cells)
@@ -777,6 +780,11 @@ int64_t ddgemm_split_first_row(int64_t m, int64_t n, int64_t k, int nslices) {
     if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return -1;
     const SplitPlan plan = product_plan(m, n, k, nslices);
     return plan.parts > 1 ? plan.first_row : m;
+}
+
+int ddgemm_small_product(int64_t m, int64_t n, int64_t k, int nslices) {
+    if (!ns_ok(nslices) || validate_sizes(m, n, k) != DDGEMM_SUCCESS) return 0;
+    return pair_small_product(m, n, k, nslices) ? 1 : 0;
 }
 
 int64_t ddgemm_split_first_tile(int64_t m, int64_t n, int64_t k, int nslices) {

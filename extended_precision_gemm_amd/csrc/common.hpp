@@ -214,5 +214,12 @@ hipError_t launch_pair_parts(int64_t rows, int64_t cols, int ns, int words, cons
 // Split plan of a pair-packed product: tiles [0, first_tile) unsplit, the rest
 // in `parts` k-parts whose group sums go to part planes (no atomics).
 SplitPlan pair_split_plan(int64_t m, int64_t n, int64_t k, int ns);
+// A product of a few outputs and a short k (within one exact chunk) runs as one
+// 4-wave workgroup per 16×16 output block when a timing model of that beats
+// the tiled kernel's plan; pair_split_plan does not split such a product.
+bool pair_small_product(int64_t m, int64_t n, int64_t k, int ns);
+hipError_t launch_small_pair_gemm(int64_t m, int64_t n, int64_t k, int ns, int words, const double* A_slices,
+                                  const double* B_slices, const int32_t* E, const int32_t* F, const OutPlanes& C,
+                                  int64_t ldc, hipStream_t stream);
 
 }  // namespace ddg

@@ -613,6 +613,115 @@ hipError_t launch_pair_ns(int64_t m, int64_t n, int64_t k, const double* A_slice
 
 }  // namespace
 
+namespace {
+
+// The pair-packed product of a few outputs: one workgroup of four waves per
+// 16×16 output block, wave w taking the k-blocks w, w + 4, ... with the
+// fragments of the next two of them loaded while the current one's products
+// issue; no LDS staging (every fragment is read once, straight into
+// registers).  The four waves' group sums are added through LDS -- exactly,
+// as every one is an integer multiple of its group's unit and k is within one
+// exact chunk -- and wave w rounds the entries of accumulator component w (a
+// quarter of the block's rows) as the tiled kernel does.  A pre-packed.
+template <int NS, int W>
+__global__ void __launch_bounds__(256) small_pair_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t blocks_n,
+                                                              const double* __restrict__ Ap,
+                                                              const double* __restrict__ Bp,
+                                                              const int32_t* __restrict__ E,
+                                                              const int32_t* __restrict__ F, OutPlanes out,
+                                                              int64_t ldc) {
+    constexpr int kSet = NS * kFragDoubles;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t bi = blockIdx.x / blocks_n, bj = blockIdx.x % blocks_n;  // uniform
+    const double* a0 = Ap + bi * KB * kSet + lane;
+    const double* b0 = Bp + bj * KB * kSet + lane;
+    double4_t acc[NS];
+#pragma unroll
+    for (int l = 0; l < NS; ++l) acc[l] = double4_t{0.0, 0.0, 0.0, 0.0};
+    // k-block kb's fragments (kb clamped to the last one: a load past the end
+    // refetches it and is never used)
+    auto load = [&](double (&a)[NS], double (&b)[NS], int64_t kb) {
+        const int64_t c = kb < KB ? kb : KB - 1;
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            a[q] = a0[c * kSet + q * kFragDoubles];
+            b[q] = b0[c * kSet + q * kFragDoubles];
+        }
+    };
+    constexpr PairSchedule<NS> sched{};
+    auto issue = [&](const double (&a)[NS], const double (&b)[NS]) {
+#pragma unroll
+        for (int i = 0; i < sched.count; ++i) {
+            const PairProduct pr = sched.order[i];
+            // packed: plane 2u; alone: plane 2u + 1 (the last plane itself for an odd count)
+            const double x = pr.packed ? a[2 * pr.u] : a[2 * pr.u + 1 < NS ? 2 * pr.u + 1 : 2 * pr.u];
+            acc[pr.acc] = __builtin_amdgcn_mfma_f64_16x16x4f64(x, b[pr.t], acc[pr.acc], 0, 0, 0);
+        }
+    };
+    double a_0[NS], b_0[NS], a_1[NS], b_1[NS];
+    int64_t kb = w;  // < KB: k >= 1 pads to at least 4 k-blocks
+    load(a_0, b_0, kb);
+    load(a_1, b_1, kb + 4);
+    for (; kb < KB; kb += 8) {  // uniform over the wave
+        issue(a_0, b_0);
+        load(a_0, b_0, kb + 8);
+        if (kb + 4 < KB) issue(a_1, b_1);
+        load(a_1, b_1, kb + 12);
+    }
+    __shared__ double4_t red[4][NS][kFragDoubles];
+#pragma unroll
+    for (int l = 0; l < NS; ++l) red[w][l][lane] = acc[l];
+    __syncthreads();
+    // wave w: component w of every accumulator, i.e. rows 4 w' + (lane >> 4)... of its lanes
+    double sum[NS];
+#pragma unroll
+    for (int l = 0; l < NS; ++l) {
+        sum[l] = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sum[l] += red[j][l][lane][w];
+    }
+    const int64_t col = bj * 16 + frag_col(lane);
+    const int64_t row = bi * 16 + frag_row(lane, w);
+    if (row < m && col < n) {
+        int64_t N[NS - 1];
+#pragma unroll
+        for (int g = 0; g < NS - 1; ++g) {
+            N[g] = pair_group_units(sum[g], g);
+            if (g == NS - 2) N[g] += pair_group_units(sum[NS - 1], g);
+        }
+        double c[W];
+        pair_units_round<NS, W>(N, E[row] + F[col], c);
+#pragma unroll
+        for (int q = 0; q < W; ++q) out.c[q][row * ldc + col] = c[q];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_small_pair_gemm(int64_t m, int64_t n, int64_t k, int ns, int words, const double* A_slices,
+                                  const double* B_slices, const int32_t* E, const int32_t* F, const OutPlanes& C,
+                                  int64_t ldc, hipStream_t stream) {
+    if (m == 0 || n == 0) return hipSuccess;
+    if (ns < kMinSlices || ns > kMaxSlices || k > pair_chunk_k(ns) || (words != 2 && words != 4))
+        return hipErrorInvalidValue;
+    const PackGeom ga(m, k);
+    const int64_t blocks_m = (m + 15) / 16, blocks_n = (n + 15) / 16;
+    if (blocks_m * blocks_n > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const unsigned grid = static_cast<unsigned>(blocks_m * blocks_n);
+    return dispatch_ns(ns, [&](auto c) -> hipError_t {
+        constexpr int NS = decltype(c)::value;
+        if (words == 2)
+            small_pair_gemm_kernel<NS, 2><<<grid, 256, 0, stream>>>(m, n, ga.KB, blocks_n, A_slices, B_slices, E, F,
+                                                                    C, ldc);
+        else if constexpr (NS == kQdSlices)
+            small_pair_gemm_kernel<NS, 4><<<grid, 256, 0, stream>>>(m, n, ga.KB, blocks_n, A_slices, B_slices, E, F,
+                                                                    C, ldc);
+        else
+            return hipErrorInvalidValue;  // four words: the quad-double product only
+        return hipGetLastError();
+    });
+}
+
 hipError_t launch_pair_gemm(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices, const double* B_slices,
                             PairOut out, const int32_t* E, const int32_t* F, const OutPlanes& C, int64_t ldc,
                             int64_t* units, int64_t ldu, int64_t plane, int64_t part_stride, int64_t tile_first,

@@ -791,6 +791,23 @@ __global__ void __launch_bounds__(256) exp_rows_fix_kernel(int64_t m, int64_t ka
         split_block<1, 256, NS, false, true>(b - row_wgs, 0, 1, n, ka, KBb, b_hi, b_lo, ldb, F, B_sl);
 }
 
+// Both operands of a small product in one launch of the one-pass block
+// kernel: workgroups [0, na) take A's 16-row blocks (pair-packed) in ka_parts
+// k-parts each, the rest B's 16-column blocks in kb_parts k-parts.
+template <int NS>
+__global__ void __launch_bounds__(1024) split_both_block_kernel(
+    int64_t m, int64_t k, int64_t KB, const double* __restrict__ a_hi, const double* __restrict__ a_lo, int64_t lda,
+    int32_t* __restrict__ E, double* __restrict__ A_sl, int64_t ka_parts, int64_t na, int64_t n,
+    const double* __restrict__ b_hi, const double* __restrict__ b_lo, int64_t ldb, int32_t* __restrict__ F,
+    double* __restrict__ B_sl, int64_t kb_parts) {
+    const int64_t b = blockIdx.x;
+    if (b < na)
+        split_block<0, 1024, NS, true, false>(b / ka_parts, b % ka_parts, ka_parts, m, k, KB, a_hi, a_lo, lda, E, A_sl);
+    else
+        split_block<1, 1024, NS, false, false>((b - na) / kb_parts, (b - na) % kb_parts, kb_parts, n, k, KB, b_hi, b_lo,
+                                              ldb, F, B_sl);
+}
+
 // Blocks needed before the one-pass block kernel beats two streaming passes
 // (measured: 4096 blocks of k = 512 win, 256 blocks of k = 4096 lose).
 constexpr int64_t kFusedMinBlocks = 1024;
@@ -805,6 +822,9 @@ constexpr int64_t kSmallColsBytes = 24ll << 20;
 // (columns) of up to 512 values of k with 1024 threads.
 constexpr int kRegPairs = 4;
 constexpr int64_t kSmallColsReread = 320ll << 20;
+// An A operand of at most this many bytes of (hi, lo) also takes the one-pass
+// block kernels.
+constexpr int64_t kSmallRowsBytes = 2ll << 20;
 // Streaming column-exponent pass: row parts enough for this many workgroups of
 // 512 columns, each part at least kMinRowsPerStreamPart rows (which also keeps
 // the parts' partial maxima, 4 bytes per column and part, within the slice
@@ -819,7 +839,9 @@ inline bool one_pass(const PackGeom& g, int64_t rows, int64_t cols, int axis, in
     if (kparts > g.KB) kparts = g.KB;
     const int64_t bytes = rows * cols * 16;
     const bool small_cols = axis == 1 && bytes <= kSmallColsBytes && bytes * kparts <= kSmallColsReread;
-    return g.doubles(ns) > 0 && (g.RB >= kFusedMinBlocks || small_cols);
+    // a small A operand: one launch rather than three of a few microseconds each
+    const bool small_rows = axis == 0 && bytes <= kSmallRowsBytes && bytes * kparts <= kSmallColsReread;
+    return g.doubles(ns) > 0 && (g.RB >= kFusedMinBlocks || small_cols || small_rows);
 }
 
 // Row parts of the streaming column-exponent pass over a rows x cols operand.
@@ -969,9 +991,18 @@ hipError_t launch_operands_ns(int64_t m, int64_t n, int64_t k, const double* A_h
                               const double* B_hi, const double* B_lo, int64_t ldb, int32_t* E, double* A_sl,
                               int32_t* F, double* B_sl, hipStream_t stream) {
     const PackGeom ga(m, k), gb(n, k);
-    int64_t kparts;
-    if (m == 0 || n == 0 || k == 0 || one_pass(ga, m, k, 0, NS, kparts) || one_pass(gb, k, n, 1, NS, kparts) ||
-        exp_row_parts(m, k) > 1) {
+    int64_t ka_parts, kb_parts;
+    const bool a1 = m > 0 && k > 0 && one_pass(ga, m, k, 0, NS, ka_parts);
+    const bool b1 = n > 0 && k > 0 && one_pass(gb, k, n, 1, NS, kb_parts);
+    if (a1 && b1 && !(ka_parts == 1 && ga.KB * 32 <= kBlockThreads * kRegPairs)) {
+        // both small: one launch (A's blocks are not held in registers here)
+        const int64_t na = ga.RB * ka_parts, grid = na + gb.RB * kb_parts;
+        if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+        split_both_block_kernel<NS><<<static_cast<unsigned>(grid), 1024, 0, stream>>>(
+            m, k, ga.KB, A_hi, A_lo, lda, E, A_sl, ka_parts, na, n, B_hi, B_lo, ldb, F, B_sl, kb_parts);
+        return hipGetLastError();
+    }
+    if (m == 0 || n == 0 || k == 0 || a1 || b1 || exp_row_parts(m, k) > 1) {
         hipError_t e = launch_split_ns<NS>(k, n, B_hi, B_lo, ldb, 1, F, B_sl, stream, kSplitAll, false);
         if (e == hipSuccess) e = launch_split_ns<NS>(m, k, A_hi, A_lo, lda, 0, E, A_sl, stream, kSplitAll, true);
         return e;

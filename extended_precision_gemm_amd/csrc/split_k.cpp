@@ -123,20 +123,30 @@ int64_t split_k_parts(int64_t m, int64_t n, int64_t k, int ns) { return split_pl
 //     T = c(L) ceil(stages / p) t_stage
 //         + [p > 1] (2 p (ns - 1) outputs 8 B / plane rate + launches),
 // t_stage from the pair-packed product count.  The plan must save 5 %.
+// Its parts may be as short as one stage: with no atomics a part costs only its
+// planes, and a product of a few tiles and a short k (64^3: one tile, 8 stages)
+// then spreads over as many workgroups as it has stages.
 namespace {
 constexpr double kPairMinSaving = 0.95;
+constexpr int64_t kPairMinStagesPerPart = 1;
 }  // namespace
 
-SplitPlan pair_split_plan(int64_t m, int64_t n, int64_t k, int ns) {
+namespace {
+
+struct PairPlanCost {
+    SplitPlan plan;
+    double seconds;
+};
+
+PairPlanCost pair_plan_cost(int64_t m, int64_t n, int64_t k, int ns) {
     const GemmGeometry g = pair_geometry(ns);
-    if (g.tile_m <= 0 || g.tile_n <= 0 || m <= 0 || n <= 0 || k <= 0) return SplitPlan{0, m, 1};
+    if (g.tile_m <= 0 || g.tile_n <= 0 || m <= 0 || n <= 0 || k <= 0) return PairPlanCost{SplitPlan{0, m, 1}, 0.0};
     const int64_t tiles_m = (m + g.tile_m - 1) / g.tile_m, tiles_n = (n + g.tile_n - 1) / g.tile_n;
     const int64_t tiles = tiles_m * tiles_n;
     const SplitPlan none{tiles, m, 1};
-    if (tiles % kComputeUnits == 0) return none;
     const CostModel cm(m, k, ns, g);
-    const int64_t pmax = cm.stages / kMinStagesPerPart < kMaxParts ? cm.stages / kMinStagesPerPart : kMaxParts;
-    if (pmax < 2) return none;
+    const int64_t pmax = cm.stages / kPairMinStagesPerPart < kMaxParts ? cm.stages / kPairMinStagesPerPart : kMaxParts;
+    if (tiles % kComputeUnits == 0 || pmax < 2) return PairPlanCost{none, cm.time(tiles, 0.0, 1)};
     auto cost = [&](int64_t t, double outputs, int64_t p) {
         const double base = cm.time(t, outputs, 1);  // the rounds of one part's stages, below
         if (p == 1) return base;
@@ -168,7 +178,46 @@ SplitPlan pair_split_plan(int64_t m, int64_t n, int64_t k, int ns) {
             }
         }
     }
-    return best.parts > 1 && best_t < kPairMinSaving * t1 ? best : none;
+    return best.parts > 1 && best_t < kPairMinSaving * t1 ? PairPlanCost{best, best_t} : PairPlanCost{none, t1};
+}
+
+// The small-output kernel: every 16×16 block on its own CU (at most 256 of
+// them), each of its four waves working through a quarter of the k-blocks.  A
+// wave's k-block costs its products' MFMA time, but no less than the latency
+// of its 2 ns fragment loads with two k-blocks in flight (measured: 1.4 us per
+// k-block with 8 slices, 64x64 to 128x128 outputs); plus the fixed cost of a
+// launch and the rounding.
+constexpr int64_t kSmallBlocksMax = 256;
+constexpr double kSmallLaunchSeconds = 4e-6;
+constexpr double kSmallKBlockSeconds8 = 1.4e-6;
+
+double small_seconds(int64_t m, int64_t n, int64_t k, int ns) {
+    const int64_t blocks = ((m + 15) / 16) * ((n + 15) / 16);
+    if (blocks > kSmallBlocksMax || k > pair_chunk_k(ns)) return 1e30;
+    const int64_t kb = PackGeom(m, k).KB;
+    const double mfma = static_cast<double>(pair_products(ns)) * kMfmaCycles / kClockHz / kMfmaEfficiency;
+    const double latency = kSmallKBlockSeconds8 * ns / 8.0;
+    return static_cast<double>((kb + 3) / 4) * (mfma > latency ? mfma : latency) + kSmallLaunchSeconds;
+}
+
+}  // namespace
+
+bool pair_small_product(int64_t m, int64_t n, int64_t k, int ns) {
+    if (m <= 0 || n <= 0 || k <= 0) return false;
+    const double t_small = small_seconds(m, n, k, ns);
+    if (t_small >= 1e30) return false;
+    const PairPlanCost c = pair_plan_cost(m, n, k, ns);
+    // the tiled plan's time counts its split launches but not its own launch
+    return t_small < c.seconds + kSmallLaunchSeconds;
+}
+
+SplitPlan pair_split_plan(int64_t m, int64_t n, int64_t k, int ns) {
+    if (pair_small_product(m, n, k, ns)) {
+        const GemmGeometry g = pair_geometry(ns);
+        const int64_t tiles = ((m + g.tile_m - 1) / g.tile_m) * ((n + g.tile_n - 1) / g.tile_n);
+        return SplitPlan{tiles, m, 1};
+    }
+    return pair_plan_cost(m, n, k, ns).plan;
 }
 
 }  // namespace ddg

@@ -115,7 +115,7 @@ size_t dd_split_slices_bytes(int64_t outer, int64_t k);
  * leave part of the chip idle -- a few tiles, or a last round of 256
  * workgroups far from full -- the output tiles from some first tile t on
  * (row-major; t = 0: all of them) may be split over k into p parts of at least
- * 16 stages each (a stage is 8 values of k, 4 from 14 slices on), p <= 256,
+ * one stage each (a stage is 8 values of k, 4 from 14 slices on), p <= 256,
  * while the tiles before t, whole rounds of 256 workgroups, run unsplit; t and
  * p are chosen by a timing model of the rounds of workgroups and of the part
  * planes' traffic, and only where that saves at least 5 %; outputs that
@@ -366,6 +366,14 @@ const char* ddgemm_status_string(ddgemm_status_t status);
 int64_t ddgemm_split_parts(int64_t m, int64_t n, int64_t k, int nslices);
 int64_t ddgemm_split_first_row(int64_t m, int64_t n, int64_t k, int nslices);
 int64_t ddgemm_split_first_tile(int64_t m, int64_t n, int64_t k, int nslices);
+/* 1 when the product entry points compute an m×n×k product with nslices slices
+ * (16: also the quad-double product) by the small-output kernel -- one 4-wave
+ * workgroup per 16×16 output block, the waves sharing k, their exact group sums
+ * added in LDS, no split and no second launch -- else 0 (also for invalid
+ * sizes).  It is taken for at most 256 such blocks and k within one exact FP64
+ * chunk (dd_sliced_gemm_pairs) where a timing model of it beats the tiled
+ * kernel's plan. */
+int ddgemm_small_product(int64_t m, int64_t n, int64_t k, int nslices);
 
 /* Diagnostics: runs one FP64 16x16x4 matrix instruction on one wave with
  * a-operand lane value (lane + 1) and b-operand lane value 100 * (lane + 1) and

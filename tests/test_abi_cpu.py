@@ -88,7 +88,7 @@ def test_packed_sizes(ddg):
 def test_split_parts_query(ddg):
     """The k-part count the product entry points use (host-only query): outputs
     whose 64x64 (32x64 for 6 and 9..16 slices) tiles fill whole rounds of 256
-    workgroups never split; every part keeps at least 16 stages (a stage is 8
+    workgroups never split; every part keeps at least one stage (a stage is 8
     values of k, 4 for 14..16 slices); at most 256 parts; invalid sizes give 0."""
     sp = ddg.split_parts
     for k in (64, 4096, 100000, ddg.K_MAX):
@@ -100,9 +100,11 @@ def test_split_parts_query(ddg):
         p = sp(m, n, k, ns)
         ks = 1 if ns >= 14 else 2
         stages = -(-k // 16) * 16 // 4 // ks
-        assert 2 <= p <= min(256, stages // 16), (m, n, k, ns, p)
-    assert sp(64, 64, 240, 8) == 1          # 30 stages: fewer than two parts of 16
-    assert sp(64, 64, 241, 8) == 2 and sp(64, 64, 256, 8) == 2
+        assert 2 <= p <= min(256, stages), (m, n, k, ns, p)
+    # one tile and a short k: the small-output kernel, not a split
+    assert sp(64, 64, 240, 8) == 1 and ddg.small_product(64, 64, 240, 8)
+    # one tile and a k beyond one exact chunk: one part per workgroup slot, one stage or more each
+    assert sp(64, 64, 8192, 8) > 100
     assert sp(1024, 512, 4096, 8) == 2      # 128 tiles: one half-empty round becomes one full one
     assert sp(1, 1, 10 ** 6, 8) == 256
     assert sp(0, 5, 100, 8) == 1 and sp(5, 5, 0, 8) == 1
@@ -146,7 +148,7 @@ def test_workspace_holds_group_sum_planes_for_chunks_and_split_parts(ddg):
         assert L.dd_gemm_workspace_size_ns(m, n, k, ns) == base + chunks + split, (m, n, k, ns)
         if ns == 8:
             assert L.dd_gemm_workspace_size(m, n, k) == L.dd_gemm_workspace_size_ns(m, n, k, ns)
-    assert ddg.split_parts(64, 64, 512, 8) > 1 and ddg.split_parts(64, 64, 240, 8) == 1
+    assert ddg.split_parts(64, 64, 8192, 8) > 1 and ddg.split_parts(64, 64, 240, 8) == 1
     assert ddg.split_parts(1024, 1024, 4096, 8) == 1
     # quad double, one block within the pair-packed int64 bound (k <= 2^21): the
     # same group-sum planes with 16 slices -- 15 chunk planes beyond k = 2048,
@@ -170,6 +172,20 @@ def test_workspace_holds_group_sum_planes_for_chunks_and_split_parts(ddg):
     assert ddg.split_parts(m, n, kb, 16) > 1
     base = r(L.qd_split_slices_bytes(m, kb)) + r(L.qd_split_slices_bytes(n, kb)) + r(4 * m) + r(4 * n)
     assert L.qd_gemm_workspace_size_kb(m, n, k, kb) == base + 2 * r(16 * m * n * 8)
+
+
+def test_small_product_query(ddg):
+    """Small outputs with a short k take the small-output kernel and never
+    split; a k beyond one exact chunk, many output blocks or bad sizes do not."""
+    for (m, n, k, ns) in [(64, 64, 64, 8), (1, 1, 1, 8), (100, 100, 100, 8), (16, 16, 16, 4), (48, 80, 60, 16)]:
+        assert ddg.small_product(m, n, k, ns) and ddg.split_parts(m, n, k, ns) == 1
+    assert not ddg.small_product(64, 64, PAIR_CHUNK[8] + 1, 8)        # beyond one exact FP64 chunk
+    assert not ddg.small_product(48, 80, PAIR_CHUNK[16] + 1, 16)
+    assert not ddg.small_product(272, 272, 64, 8)                      # 289 blocks of 16x16
+    assert not ddg.small_product(4096, 4096, 4096, 8)
+    assert not ddg.small_product(128, 128, 1024, 8)  # 64 k-blocks a wave: the split is modelled faster
+    assert not ddg.small_product(-1, 4, 4, 8) and not ddg.small_product(4, 4, 4, 3)
+    assert not ddg.small_product(0, 4, 4, 8) and not ddg.small_product(4, 4, 0, 8)
 
 
 def test_status_strings(ddg):

@@ -75,8 +75,8 @@ def _unsplit_reference(gpu, dAh, dAl, dBh, dBl, ns):
     return _nearest_of_groups(G, _host(E), _host(F))
 
 
-@pytest.mark.parametrize("m,n,k,ns", [(64, 64, 512, 8), (40, 70, 3000, 8), (3, 5, 100000, 8),
-                                      (100, 80, 5000, 16), (64, 64, 1024, 6), (33, 130, 4100, 12)])
+@pytest.mark.parametrize("m,n,k,ns", [(64, 64, 8192, 8), (40, 70, 3000, 8), (3, 5, 100000, 8),
+                                      (100, 80, 5000, 16), (64, 64, 2048, 6), (33, 130, 4100, 12)])
 def test_split_dd_product_equals_the_unsplit_chain(gpu, m, n, k, ns):
     assert gpu.split_parts(m, n, k, ns) > 1
     _say(f"[split-k dd] {m}x{n}x{k} nslices={ns} parts={gpu.split_parts(m, n, k, ns)}")
@@ -386,3 +386,30 @@ def test_last_row_splits_and_row_exponent_parts_replay_in_a_graph(gpu):
             Rh, Rl = gpu.dd_gemm(A[0], A[1], B[0], B[1])
             assert _bits_equal(_host(C[0]), _host(Rh)) and _bits_equal(_host(C[1]), _host(Rl)), (rep, m, n, k)
         assert _bits_equal(_host(qC), _host(gpu.qd_gemm(qA, qB))), rep
+
+
+@pytest.mark.parametrize("m,n,k,ns", [(64, 64, 64, 8), (1, 1, 1, 8), (17, 33, 5, 8), (100, 100, 100, 8),
+                                      (250, 7, 100, 5), (16, 16, 16, 4), (48, 80, 60, 16), (200, 200, 64, 7),
+                                      (130, 65, 33, 8), (256, 256, 256, 8)])
+def test_small_products_equal_the_oracle(gpu, m, n, k, ns):
+    """Products of a few outputs and a short k run as one 4-wave workgroup per
+    16x16 output block whose waves split k and add their exact group sums
+    through LDS: the nearest double-double of the exact total, as everywhere."""
+    assert gpu.small_product(m, n, k, ns) and gpu.split_parts(m, n, k, ns) == 1
+    _say(f"[small] {m}x{n}x{k} nslices={ns}")
+    Ah, Al = workloads.random_dd((m, k), 9400 + k + m, "signed_exp20")
+    Bh, Bl = workloads.random_dd((k, n), 9401 + k + n, "uniform")
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl), nslices=ns)
+    Rh, Rl = exact.paired_product(Ah, Al, Bh, Bl, ns)
+    assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 64, 64), (48, 80, 100), (16, 100, 40)])
+def test_small_qd_products_equal_the_oracle(gpu, m, n, k):
+    assert gpu.small_product(m, n, k, 16)
+    _say(f"[small qd] {m}x{n}x{k}")
+    A = workloads.random_qd((m, k), 9500 + k, "signed_exp20")
+    B = workloads.random_qd((k, n), 9501 + k, "uniform")
+    C = _host(gpu.qd_gemm(_dev(A), _dev(B)))
+    _, _, _, C_ref = qd.sliced_product(A, B)
+    assert _bits_equal(C, C_ref)
