@@ -352,17 +352,21 @@ def exact_entries(A_hi, A_lo, B_hi, B_lo, rows, cols) -> list[Fraction]:
 
 
 def error_bound(A_hi, B_hi, E, F, nslices: int, rows=None, cols=None):
-    """Upper bound on |C - A·B| for the sliced product with n slices, per entry.
+    """Upper bound on |C - A·B| for the sliced product with n slices, per entry,
+    against the exact product.
 
     Cutting each entry below 2^E_i (2^F_j) loses less than 2^(E_i - 13n)
     (2^(F_j - 13n)), so one product term is off by less than
     2^(-13n) (|a| 2^F_j + |b| 2^E_i); the pairs with s + t >= n that are not formed
-    add at most (n-1) 2^(E_i + F_j - 13n) per term; the final cascade adds at most
-    2^-104 of the level magnitudes, and a classical double-double reference to
-    compare with is itself off by well under 2^-90 (|A||B|)_ij.  With the lo words
-    below 2^-52 of hi, |a| and |b| are bounded by 1.000001 |a_hi|, |b_hi|:
+    add at most (n-1) 2^(E_i + F_j - 13n) per term.  Adding the parts of an entry
+    costs at most 2^-104 of the sum of their magnitudes: the level cascade's
+    TwoSum steps, or, for the nearest double-double of the exact total,
+    |T - hi - lo| <= 2^-106 |T| (1 + 2^-52).  The digits of one entry share its
+    sign, so the level (or group) magnitudes add up to at most (|A||B|)_ij.  With
+    the lo words below 2^-52 of hi, |a| and |b| are bounded by 1.000001 |a_hi|,
+    |b_hi|:
         bound_ij = 2^(-13n) (2^F_j S_a[i] + 2^E_i S_b[j] + n k 2^(E_i+F_j))
-                   + 2^-90 (|A||B|)_ij
+                   + 2^-104 (|A||B|)_ij
     with S_a[i] = sum_p |a_ip|, S_b[j] = sum_p |b_pj| (times 1.000001).
     """
     A = np.abs(np.asarray(A_hi, dtype=np.float64)) * 1.000001
@@ -375,9 +379,9 @@ def error_bound(A_hi, B_hi, E, F, nslices: int, rows=None, cols=None):
     if rows is None:
         absAB = A @ B
         return 2.0 ** (-DIGIT_BITS * nslices) * (np.outer(Sa, v) + np.outer(w, Sb) + nslices * k * np.outer(w, v)) \
-            + 2.0 ** -90 * absAB
+            + 2.0 ** -104 * absAB
     rows = np.asarray(rows)
     cols = np.asarray(cols)
     absAB = np.einsum("qk,kq->q", A[rows, :], B[:, cols])
     return 2.0 ** (-DIGIT_BITS * nslices) * (Sa[rows] * v[cols] + w[rows] * Sb[cols]
-                                             + nslices * k * w[rows] * v[cols]) + 2.0 ** -90 * absAB
+                                             + nslices * k * w[rows] * v[cols]) + 2.0 ** -104 * absAB
