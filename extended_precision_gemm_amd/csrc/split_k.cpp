@@ -23,7 +23,7 @@ constexpr double kMfmaCycles = 64.0;          // one 16x16x4 FP64 MFMA on one SI
 constexpr double kAtomicAddsPerSecond = 2e11; // FP64 atomic adds into the level planes
 constexpr double kPlaneBytesPerSecond = 5e12; // zeroing and re-reading the level planes
 constexpr double kSplitLaunchSeconds = 15e-6; // the zeroing and renormalising launches
-constexpr double kMinSaving = 0.98;           // a split must save at least 2 %
+constexpr double kMinSaving = 0.95;           // a split must save at least 5 %
 
 }  // namespace
 
@@ -72,7 +72,7 @@ struct CostModel {
 // first_tile = 0, and with `tail` the tiles of exactly 1..4 rounds of 256
 // workgroups fewer than the unsplit product takes, so that the unsplit launch
 // ends on a round boundary and only the last, partly idle rounds are split.
-// Each part keeps at least 16 stages; at most 256 parts; the plan must save 2 %
+// Each part keeps at least 16 stages; at most 256 parts; the plan must save 5 %
 // against the unsplit product, else no split.  Outputs whose tiles fill whole
 // rounds never split.
 SplitPlan split_plan(int64_t m, int64_t n, int64_t k, int ns, bool tail) {
