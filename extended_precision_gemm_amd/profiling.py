@@ -45,8 +45,10 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 SLICE_BITS = 13
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# the sources whose change makes the GEMM's counter figures stale
-GEMM_SOURCES = ("sliced_gemm.hip", "pair_levels.hpp", "qd_levels.hpp", "wide_int.hpp", "common.hpp")
+# the sources whose change makes the GEMM's counter figures stale: the kernels
+# and the host code that picks their launches (plans, the small-output path)
+GEMM_SOURCES = ("sliced_gemm.hip", "pair_levels.hpp", "qd_levels.hpp", "wide_int.hpp", "common.hpp", "api.cpp",
+                "split_k.cpp")
 
 
 def source_hash(files=GEMM_SOURCES) -> str:

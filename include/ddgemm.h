@@ -222,9 +222,9 @@ ddgemm_status_t dd_sliced_gemm_pairs(int64_t m, int64_t n, int64_t k,
 /*
  * C = A·B for double-double A (m×k) and B (k×n) ("Multiple Double Arithmetic on
  * NVIDIA Tensor Cores", §2 overview, steps 1-5).  Overwrites C (no alpha/beta).
- * m = 0 or n = 0: no-op.  k = 0: C = 0.  k beyond DDGEMM_K_MAX is processed in
- * the fewest equal k-blocks within it (dd_gemm_kblock_max), as dd_gemm_ws_kb
- * describes.  Result: the nearest double-double (C_hi = RN(x), C_lo =
+ * m = 0 or n = 0: no-op.  k = 0: C = 0.  k beyond dd_gemm_kblock_max(8) =
+ * 4,194,304 is processed in the fewest equal k-blocks within it, as
+ * dd_gemm_ws_kb describes.  Result: the nearest double-double (C_hi = RN(x), C_lo =
  * RN(x - C_hi), gradual underflow honoured) of x = the exact sum of the 36
  * window slice-pair products, i.e. the product of the operands truncated to
  * 104 bits below their row/column exponents minus the pairs below the
