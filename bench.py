@@ -46,7 +46,8 @@ def _parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 3, and at least half a second of them, so that the clocks have ramped up)")
     ap.add_argument("--workload", default="dd4096_exp20")
     ap.add_argument("--nslices", type=int, default=8,
                     help="13-bit slices per entry: 8 = double-double (the metric); 4..7 keep fewer pairs, "
@@ -101,6 +102,20 @@ def _calibration_copy(args, dev):
         del x, y
 
 
+def _warm_up(step, steps):
+    """Run untimed steps: exactly `steps` if given, else at least 3 and at least
+    half a second of them (short steps need that many for the clocks to ramp
+    up).  Returns the number run."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while (i < steps) if steps is not None else (i < 3 or time.perf_counter() - t0 < 0.5):
+        step()
+        torch.cuda.synchronize()
+        i += 1
+    return i
+
+
 def main():
     args = _parse()
     if args.gpus != 1:
@@ -150,9 +165,7 @@ def main():
         if events:
             events[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = _warm_up(step, args.warmup)
     print(f"[bench] timing {args.steps} steps of dd_gemm_ws", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -354,13 +367,11 @@ def _run_shape(args):
     # warm both paths up, for at least half a second so that the clocks have
     # ramped, then time product, stage chain, product: the mean of the two
     # product runs cancels a drift of the clock over the measurement
-    t0 = time.perf_counter()
-    i = 0
-    while i < args.warmup or time.perf_counter() - t0 < 0.5:
+    def both():
         product()
         unsplit()
-        torch.cuda.synchronize()
-        i += 1
+
+    args.warmup = _warm_up(both, args.warmup)
     print(f"[bench] timing {args.steps} steps of each path", file=sys.stderr, flush=True)
     t_prod_a = timed(product)
     t_unsplit = timed(unsplit)
@@ -424,9 +435,7 @@ def _run_qd(args, w):
         if events:
             events[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = _warm_up(step, args.warmup)
     print(f"[bench] timing {args.steps} steps of qd_gemm_ws", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(args.steps):

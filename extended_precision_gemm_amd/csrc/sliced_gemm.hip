@@ -512,7 +512,12 @@ template <> struct ConfigFor<16> { using type = GemmConfig<2, 4, 1, 2, 1, 16, 1>
 // SIMD), two k-blocks per stage -- measured at 4096^3 against two-block strips
 // of eight waves (68.5 TFLOP/s), two 32x64 workgroups per CU (67.2), one or
 // more k-blocks per stage with two to four stages (65.2-69.4): 70.3 TFLOP/s.
+// Five slices take the same shape (4096^3: 17.63 against 18.12 ms for the
+// 32x16 strips of eight waves); for four, six and seven slices the strips stay
+// faster (11.40 / 22.91 / 30.22 against 12.73 / 23.08 / 30.37 ms), and from
+// nine slices on sixteen waves would spill.
 template <int NS> struct PairConfigFor { using type = typename ConfigFor<NS>::type; };
+template <> struct PairConfigFor<5> { using type = GemmConfig<4, 4, 2, 2, 1, 5, 1>; };
 template <> struct PairConfigFor<8> { using type = GemmConfig<4, 4, 2, 2, 1, 8, 1>; };
 
 template <int NS>

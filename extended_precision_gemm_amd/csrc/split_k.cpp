@@ -50,7 +50,10 @@ struct CostModel {
 
     CostModel(int64_t m, int64_t k, int ns_, const GemmGeometry& geom) : g(geom), ns(ns_), stages(0) {
         stages = g.ks > 0 ? PackGeom(m, k).KB / g.ks : 0;
-        two_per_cu = g.lds_bytes > 0 && 2 * static_cast<int64_t>(g.lds_bytes) <= kLdsBytesPerCu;
+        // a second workgroup fits where its LDS does and the first leaves its
+        // waves room: workgroups of four waves per SIMD take a SIMD's registers
+        two_per_cu = g.lds_bytes > 0 && 2 * static_cast<int64_t>(g.lds_bytes) <= kLdsBytesPerCu &&
+                     g.waves_per_simd <= 2;
         t_stage = static_cast<double>(g.mfma_per_stage) * g.waves_per_simd * kMfmaCycles / kClockHz / kMfmaEfficiency;
     }
     double time(int64_t tiles, double outputs, int64_t p) const {

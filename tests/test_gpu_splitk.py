@@ -404,6 +404,45 @@ def test_small_products_equal_the_oracle(gpu, m, n, k, ns):
     assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
 
 
+def _edge_dd(rng, rows, cols):
+    """A seeded (hi, lo) matrix with the slicer's edge entries: an all-zero row
+    and column, an unnormalised pair, opposite signs, a negative zero,
+    subnormals, and entries 2^-12 .. 2^2 apart."""
+    hi = rng.uniform(-1, 1, (rows, cols)) * np.ldexp(1.0, rng.integers(-12, 3, (rows, cols)))
+    lo_raw = hi * 2.0 ** -53 * rng.uniform(-1, 1, (rows, cols))
+    s = hi + lo_raw
+    lo = lo_raw - (s - hi)
+    hi = s
+    if rows > 2 and cols > 2:
+        hi[1, :] = 0.0
+        lo[1, :] = 0.0
+        hi[:, 2] = 0.0
+        lo[:, 2] = 0.0
+        hi[0, 0], lo[0, 0] = 1.0, -0.75
+        hi[0, 1], lo[0, 1] = 0.5, -2.0 ** -60
+        hi[2, 0], lo[2, 0] = -0.0, 0.0
+        hi[-1, -1], lo[-1, -1] = 2.0 ** -1074, 0.0
+        hi[-1, 0], lo[-1, 0] = 3 * 2.0 ** -1060, -2.0 ** -1074
+    return hi, lo
+
+
+@pytest.mark.parametrize("m,n,k,ns", [(64, 64, 64, 8), (33, 17, 50, 8), (3, 40, 7, 8), (20, 20, 128, 6),
+                                      (40, 24, 30, 12), (16, 48, 64, 16)])
+def test_small_products_on_edge_entries(gpu, m, n, k, ns):
+    """The small-output path (both operands sliced in one launch, then one
+    4-wave workgroup per 16x16 block) with zero rows and columns, unnormalised
+    pairs, opposite signs, negative zeros and subnormals in both operands: the
+    product equals the oracle's pair-packed chain bit for bit."""
+    assert gpu.small_product(m, n, k, ns)
+    _say(f"[small edge] {m}x{n}x{k} nslices={ns}")
+    rng = np.random.default_rng(7100 + m + n + k + ns)
+    Ah, Al = _edge_dd(rng, m, k)
+    Bh, Bl = _edge_dd(rng, k, n)
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl), nslices=ns)
+    Rh, Rl = exact.paired_product(Ah, Al, Bh, Bl, ns)
+    assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
+
+
 @pytest.mark.parametrize("m,n,k", [(64, 64, 64), (48, 80, 100), (16, 100, 40)])
 def test_small_qd_products_equal_the_oracle(gpu, m, n, k):
     assert gpu.small_product(m, n, k, 16)
