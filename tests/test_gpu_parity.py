@@ -428,6 +428,33 @@ def test_results_beyond_the_double_range_overflow_like_ldexp(gpu):
     assert np.array_equal(np.sign(hCh[5:])[inf_rows], exact_sign[inf_rows])
 
 
+def test_results_near_the_bottom_of_the_double_range_underflow_gradually(gpu):
+    """Entries near 2^-500 with rows scaled down by up to 2^-47: the products'
+    leading words run from normal doubles near 2^-1000 into subnormals, and
+    the trailing words of the normal ones are subnormal.  The nearest
+    double-double honours gradual underflow (each word rounded at 2^-1074
+    where it reaches that far), as in the oracle's pair-packed chain, bit for
+    bit."""
+    rng = np.random.default_rng(79)
+    m, n, k = 24, 20, 30
+    sign = lambda shape: np.where(rng.integers(0, 2, shape) == 1, 1.0, -1.0)
+    Ah = rng.uniform(1, 2, (m, k)) * sign((m, k)) * 2.0 ** -500
+    Bh = rng.uniform(1, 2, (k, n)) * sign((k, n)) * 2.0 ** -505
+    Ah *= np.ldexp(1.0, -rng.integers(0, 48, (m, 1)))
+    Al = Ah * 2.0 ** -53 * rng.uniform(-1, 1, (m, k))
+    t = Ah + Al
+    Al, Ah = Al - (t - Ah), t
+    Bl = Bh * 2.0 ** -53 * rng.uniform(-1, 1, (k, n))
+    t = Bh + Bl
+    Bl, Bh = Bl - (t - Bh), t
+    Rh, Rl = exact.paired_product(Ah, Al, Bh, Bl, 8)
+    tiny = 2.0 ** -1022
+    assert (np.abs(Rh) >= tiny).sum() > 50 and ((np.abs(Rh) < tiny) & (Rh != 0)).sum() > 50
+    assert ((Rl != 0) & (np.abs(Rl) < tiny)).sum() > 50
+    Ch, Cl = gpu.dd_gemm(_dev(Ah), _dev(Al), _dev(Bh), _dev(Bl))
+    assert _bits_equal(_host(Ch), Rh) and _bits_equal(_host(Cl), Rl)
+
+
 def test_level_planes_with_a_wider_stride(gpu):
     """dd_sliced_gemm / dd_renorm_levels with ldl > n and ldc > n, through the C
     ABI: the level sums and the cascade match the packed-stride calls, and the
