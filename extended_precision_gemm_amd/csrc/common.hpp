@@ -119,10 +119,6 @@ hipError_t launch_zero_levels(int64_t m, int64_t n, int ns, double* levels, int6
 hipError_t launch_sliced_gemm_split(int64_t m, int64_t n, int64_t k, int ns, const double* A_slices,
                                     const double* B_slices, double* levels, int64_t ldl, int64_t parts,
                                     hipStream_t stream, int64_t tile_first = 0);
-// Level planes -> results for an m x n block of outputs; plane < 0: m * ldl.
-hipError_t launch_levels_to_dd(int64_t m, int64_t n, int ns, const double* levels, int64_t ldl, const int32_t* E,
-                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream,
-                               int64_t plane = -1);
 hipError_t launch_levels_to_qd(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
                                const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream,
                                int64_t plane = -1);

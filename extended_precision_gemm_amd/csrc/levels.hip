@@ -202,18 +202,6 @@ hipError_t launch_renorm(int64_t m, int64_t n, const double* levels, int64_t ldl
     return hipGetLastError();
 }
 
-hipError_t launch_levels_to_dd(int64_t m, int64_t n, int ns, const double* levels, int64_t ldl, const int32_t* E,
-                               const int32_t* F, double* C_hi, double* C_lo, int64_t ldc, hipStream_t stream,
-                               int64_t plane) {
-    if (m == 0 || n == 0) return hipSuccess;
-    if (ns < kMinSlices || ns > kMaxSlices) return hipErrorInvalidValue;
-    if (plane < 0) plane = m * ldl;
-    return dispatch_ns(ns, [&](auto c) {
-        launch_renorm_ns<decltype(c)::value>(m, n, levels, ldl, plane, E, F, C_hi, C_lo, ldc, stream);
-        return hipGetLastError();
-    });
-}
-
 hipError_t launch_levels_to_qd(int64_t m, int64_t n, const double* levels, int64_t ldl, const int32_t* E,
                                const int32_t* F, const OutPlanes& C, int64_t ldc, hipStream_t stream,
                                int64_t plane) {
