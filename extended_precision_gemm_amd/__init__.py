@@ -96,6 +96,7 @@ _SIGNATURES = {
     "dd_gemm_kblock_max": (_i64, [ctypes.c_int]),
     "ddgemm_status_string": (ctypes.c_char_p, [_st]),
     "ddgemm_probe_mfma_f64": (_st, [_vp, _vp]),
+    "ddgemm_probe_pair_round": (_st, [_i64, ctypes.c_int, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -563,4 +564,23 @@ def qd_gemm_alloc(A, B, C=None, stream=None):
 def probe_mfma_f64(device="cuda", stream=None):
     out = torch.empty((64, 4), dtype=torch.float64, device=device)
     _check(lib.ddgemm_probe_mfma_f64(_ptr(out), _stream(stream)))
+    return out
+
+
+def probe_pair_round(units, scale, out=None, stream=None, nslices: int = NUM_SLICES):
+    """The products' exit rounding on given group sums (diagnostics):
+    ``units`` int64 (count, nslices - 1) on a device, ``scale`` int32 (count,);
+    returns float64 (count, 2): the nearest double-double of each entry's exact
+    total sum_g units[i, g] 2^(scale[i] - 13(g + 3))."""
+    if units.dim() != 2 or units.shape[1] != nslices - 1:
+        raise ValueError(f"units must have shape (count, {nslices - 1}), got {tuple(units.shape)}")
+    dev = units.device
+    count = units.shape[0]
+    _buffer(units, "units", torch.int64, count * (nslices - 1), dev)
+    _buffer(scale, "scale", torch.int32, count, dev)
+    if out is None:
+        out = torch.empty((count, 2), dtype=torch.float64, device=dev)
+    _buffer(out, "out", torch.float64, 2 * count, dev)
+    with torch.cuda.device(dev):
+        _check(lib.ddgemm_probe_pair_round(count, nslices, _ptr(units), _ptr(scale), _ptr(out), _stream(stream)))
     return out

@@ -163,6 +163,25 @@ __global__ void __launch_bounds__(256) pair_parts_kernel(int64_t m, int64_t n, c
     }
 }
 
+// The double-double exit's rounding on given group sums (diagnostics): entry i
+// has NS - 1 int64 group sums units[i (NS - 1) + g], group g counting units
+// 2^(sc[i] - 13(g + 3)), and gets the nearest double-double of their exact
+// total, as the pair-packed products' exit computes it.
+template <int NS>
+__global__ void __launch_bounds__(256) pair_round_probe_kernel(int64_t count, const int64_t* __restrict__ units,
+                                                               const int32_t* __restrict__ sc,
+                                                               double* __restrict__ out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    int64_t N[NS - 1];
+#pragma unroll
+    for (int g = 0; g < NS - 1; ++g) N[g] = units[i * (NS - 1) + g];
+    double c[2];
+    pair_units_round<NS, 2>(N, sc[i], c);
+    out[2 * i] = c[0];
+    out[2 * i + 1] = c[1];
+}
+
 }  // namespace
 
 hipError_t launch_pair_parts(int64_t rows, int64_t cols, int ns, int words, const int64_t* units, int64_t ldu,
@@ -230,3 +249,21 @@ hipError_t launch_qd_levels_to_units(int64_t m, int64_t n, const double* levels,
 }
 
 }  // namespace ddg
+
+extern "C" ddgemm_status_t ddgemm_probe_pair_round(int64_t count, int nslices, const int64_t* units,
+                                                   const int32_t* scale, double* out, void* stream) {
+    using namespace ddg;
+    if (count < 0 || count > (int64_t(1) << 38) || nslices < kMinSlices || nslices > kMaxSlices)
+        return DDGEMM_ERROR_INVALID_VALUE;
+    if (count == 0) return DDGEMM_SUCCESS;
+    if (!units || !scale || !out) return DDGEMM_ERROR_INVALID_VALUE;
+    const ddgemm_status_t st = check_current_device();
+    if (st != DDGEMM_SUCCESS) return st;
+    const unsigned grid = static_cast<unsigned>((count + 255) / 256);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = dispatch_ns(nslices, [&](auto c) {
+        pair_round_probe_kernel<decltype(c)::value><<<grid, 256, 0, s>>>(count, units, scale, out);
+        return hipGetLastError();
+    });
+    return e == hipSuccess ? DDGEMM_SUCCESS : DDGEMM_ERROR_LAUNCH;
+}

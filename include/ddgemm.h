@@ -382,6 +382,21 @@ int ddgemm_small_product(int64_t m, int64_t n, int64_t k, int nslices);
  * the packed format assumes.  Errors: DDGEMM_ERROR_INVALID_VALUE for NULL out. */
 ddgemm_status_t ddgemm_probe_mfma_f64(double* out, void* stream);
 
+/* Diagnostics: the pair-packed products' exit rounding ("Multiple Double
+ * Arithmetic on NVIDIA Tensor Cores", §2 overview, fifth step: the parts of an
+ * entry added into a double-double; here the exact total rounded once) on
+ * given group sums.  Entry i (0 <= i < count) has nslices - 1 int64 group sums
+ * units[i * (nslices - 1) + g], group g counting units 2^(scale[i] - 13(g + 3)),
+ * and gets out[2 i] = RN(x), out[2 i + 1] = RN(x - out[2 i]) for their exact
+ * total x (ties to even, gradual underflow, overflow as the products give it).
+ * Device pointers; the sums must stay below 2^63 in magnitude with the carries
+ * between groups, as the products' own do.  Used to test the exit at ties and
+ * at the ends of the exponent range.  Errors: DDGEMM_ERROR_INVALID_VALUE for
+ * count < 0 or > 2^38, nslices outside [DDGEMM_MIN_SLICES, DDGEMM_MAX_SLICES],
+ * or a NULL pointer with count > 0. */
+ddgemm_status_t ddgemm_probe_pair_round(int64_t count, int nslices, const int64_t* units, const int32_t* scale,
+                                        double* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

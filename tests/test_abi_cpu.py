@@ -254,6 +254,13 @@ def test_stage_argument_validation(ddg):
     assert L.dd_renorm_levels(4, 4, P[0], 4, None, P[2], P[3], P[4], 4, None) == INV
     assert L.dd_sliced_gemm_renorm(4, 4, 4, P[0], P[1], P[2], P[3], P[4], P[5], 3, None) == INV
     assert L.ddgemm_probe_mfma_f64(None, None) == INV
+    assert L.ddgemm_probe_pair_round(-1, 8, P[0], P[1], P[2], None) == INV          # count < 0
+    assert L.ddgemm_probe_pair_round(2 ** 38 + 1, 8, P[0], P[1], P[2], None) == INV
+    assert L.ddgemm_probe_pair_round(4, 3, P[0], P[1], P[2], None) == INV           # slice count
+    assert L.ddgemm_probe_pair_round(4, 17, P[0], P[1], P[2], None) == INV
+    assert L.ddgemm_probe_pair_round(4, 8, None, P[1], P[2], None) == INV
+    assert L.ddgemm_probe_pair_round(4, 8, P[0], P[1], None, None) == INV
+    assert L.ddgemm_probe_pair_round(0, 8, None, None, None, None) == 0               # empty
 
 
 def test_valid_call_without_gpu_reports_device_error(ddg):
