@@ -811,12 +811,17 @@ __global__ void __launch_bounds__(1024) split_both_block_kernel(
 // Blocks needed before the one-pass block kernel beats two streaming passes
 // (measured: 4096 blocks of k = 512 win, 256 blocks of k = 4096 lose).
 constexpr int64_t kFusedMinBlocks = 1024;
+// Workgroups a one-pass launch of fewer blocks shares their k-blocks among
+// (every part re-reads its whole block for the exponents, so fewer parts read
+// less: B of 1024^2 27.5 -> about 19 us, the 1024^3 slicing 50.4 -> 42.2 us, 512^3
+// 30.6 -> 23.8 us against 1024 workgroups; results bit-identical).
+constexpr int64_t kOnePassWorkgroups = 256;
 // A B operand (column exponents: two passes take four launches) of at most
 // kSmallColsBytes of (hi, lo) is sliced in one pass with its k-blocks shared
 // among enough workgroups, as long as the parts' exponent re-reads (every part
 // re-reads its block) stay within kSmallColsReread bytes and so hit the cache
-// (measured on gfx950: 1024^2 29 vs 44 us with 256 MB re-read, 1536^2 61 vs
-// 59 us with 396 MB, 4096^2 483 vs 339 us).
+// (measured on gfx950 with parts for 1024 workgroups: 1024^2 29 vs 44 us
+// with 256 MB re-read, 1536^2 61 vs 59 us with 396 MB, 4096^2 483 vs 339 us).
 constexpr int64_t kSmallColsBytes = 24ll << 20;
 // Pairs of entries per thread of the register-resident block kernel: 16 rows
 // (columns) of up to 512 values of k with 1024 threads.
@@ -835,7 +840,7 @@ constexpr int64_t kMinRowsPerStreamPart = 32;
 // Whether an operand is sliced by the one-pass block kernels (true) or in two
 // passes; kparts: the k-parts a one-pass launch shares a block among.
 inline bool one_pass(const PackGeom& g, int64_t rows, int64_t cols, int axis, int ns, int64_t& kparts) {
-    kparts = (kFusedMinBlocks + g.RB - 1) / g.RB;
+    kparts = (kOnePassWorkgroups + g.RB - 1) / g.RB;
     if (kparts > g.KB) kparts = g.KB;
     const int64_t bytes = rows * cols * 16;
     const bool small_cols = axis == 1 && bytes <= kSmallColsBytes && bytes * kparts <= kSmallColsReread;
