@@ -626,6 +626,54 @@ def test_workload_parity(gpu, workload_operands, name):
             assert abs(tot - expect) <= bound
 
 
+@pytest.mark.parametrize("name", ["dd1024", "dd4096_exp20"])
+def test_timed_entry_point_equals_the_product(gpu, workload_operands, name):
+    """dd_gemm_ws_timed, the call the benchmark times (preallocated workspace,
+    an event recorded after the slicing), writes the product of dd_gemm_ws bit
+    for bit, with and without the event."""
+    import torch
+    w = workloads.by_name(name)
+    _say(f"[parity] {name}: dd_gemm_ws_timed against dd_gemm_ws")
+    Ah, Al, Bh, Bl = workload_operands(name)
+    dA, dAl, dB, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
+    Ch, Cl = gpu.dd_gemm(dA, dAl, dB, dBl)
+    ws = torch.empty(gpu.workspace_size(w.m, w.n, w.k), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    start, after_split, end = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    after_split.record(stream)  # creates the event the library records
+    for event in (after_split, None):
+        Th = torch.full_like(Ch, float("nan"))
+        Tl = torch.full_like(Cl, float("nan"))
+        start.record(stream)
+        gpu.dd_gemm_timed(dA, dAl, dB, dBl, Th, Tl, ws, event.cuda_event if event else None, stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        assert _bits_equal(_host(Th), _host(Ch)) and _bits_equal(_host(Tl), _host(Cl))
+        if event:
+            t_split, t_all = start.elapsed_time(after_split), start.elapsed_time(end)
+            _say(f"[parity] {name}: slicing {t_split:.3f} of {t_all:.3f} ms")
+            assert 0.0 <= t_split <= t_all
+
+
+def test_timed_qd_entry_point_equals_the_product(gpu):
+    """qd_gemm_ws_timed on the 1024^3 quad-double workload writes qd_gemm_ws's
+    product bit for bit, with and without its event."""
+    import torch
+    w = workloads.by_name("qd1024")
+    A, B = workloads.make_qd_operands(w)
+    dA, dB = _dev(A), _dev(B)
+    C = gpu.qd_gemm(dA, dB)
+    ws = torch.empty(gpu.qd_workspace_size(w.m, w.n, w.k), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    after_split = torch.cuda.Event(enable_timing=True)
+    after_split.record(stream)
+    for event in (after_split, None):
+        T = torch.full_like(C, float("nan"))
+        gpu.qd_gemm_timed(dA, dB, T, ws, event.cuda_event if event else None, stream)
+        torch.cuda.synchronize()
+        assert _bits_equal(_host(T), _host(C))
+
+
 # ---------------------------------------------------------------------------
 # fewer slices per entry (n = 4: the pages' quarters of a leading double)
 # ---------------------------------------------------------------------------
