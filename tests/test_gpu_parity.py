@@ -853,27 +853,73 @@ def test_binding_rejects_a_host_or_mistyped_workspace(gpu):
 
 
 
+@pytest.mark.parametrize("with_lo", [True, False])
+def test_one_pass_B_beside_two_pass_A(gpu, with_lo):
+    """A product whose B is sliced in one pass and whose A takes two passes
+    (600 x 160 x 1000): A's exponents from the leading words, its rows holding
+    an unnormalised pair recomputed by the exact pass.  A is an unaligned
+    window of a wider matrix (odd offset and leading dimension: no 16-byte
+    loads), with unnormalised pairs planted in its rows, or with no trailing
+    words.  The product equals the oracle's nearest chain bit for bit on
+    sampled rows and columns (planted ones included) and the call on
+    contiguous operands."""
+    import torch
+    m, n, k = 600, 160, 1000
+    rng = np.random.default_rng(600 + with_lo)
+    Ah, Al = _edge_matrix(rng, m, k)
+    Bh, Bl = _edge_matrix(rng, k, n)
+    planted = [0, 37, 300, m - 1]
+    Ah[37] *= 2.0 ** -8
+    Al[37] *= 2.0 ** -8
+    Ah[37, 5], Al[37, 5] = 1.0, -0.75        # exponent down
+    Ah[300, 999], Al[300, 999] = 0.0, 3.0     # exponent up
+    Ah[m - 1, 0], Al[m - 1, 0] = 2.0 ** -30, 2.0 ** 20
+    if not with_lo:
+        Al = np.zeros_like(Ah)
+    assert Bh.nbytes + Bl.nbytes <= 24 << 20 and Ah.nbytes + Al.nbytes > 2 << 20  # B one pass, A two
+    Abig = torch.zeros((2, m, k + 3), dtype=torch.float64, device="cuda")
+    Abig[0, :, 1:k + 1] = _dev(Ah)
+    Abig[1, :, 1:k + 1] = _dev(Al)
+    a_lo = Abig[1, :, 1:k + 1] if with_lo else None
+    rows = np.union1d(planted, _sample_indices(rng, m, 6))
+    cols = _sample_indices(rng, n, 6)
+    E_s, DA = exact.slice_rows(Ah, Al, rows)
+    F_s, DB = exact.slice_cols(Bh, Bl, cols)
+    if with_lo:
+        Eh = exact.balancing_exponents(Ah[rows], np.zeros_like(Ah[rows]), 0)
+        assert np.any(Eh != E_s), "some planted pair moves its row's exponent"
+    _say(f"[parity] one-pass B beside two-pass A: {m}x{n}x{k}, lo {with_lo}")
+    Ch, Cl = gpu.dd_gemm(Abig[0, :, 1:k + 1], a_lo, _dev(Bh), _dev(Bl))
+    Nh_ref, Nl_ref = exact.nearest_dd(exact.level_sums_units(DA, DB), E_s, F_s)
+    hCh, hCl = _host(Ch), _host(Cl)
+    assert _bits_equal(hCh[np.ix_(rows, cols)], Nh_ref) and _bits_equal(hCl[np.ix_(rows, cols)], Nl_ref)
+    Rh, Rl = gpu.dd_gemm(_dev(Ah), _dev(Al) if with_lo else None, _dev(Bh), _dev(Bl))
+    assert _bits_equal(hCh, _host(Rh)) and _bits_equal(hCl, _host(Rl))
+
+
 @pytest.mark.timeout(600)
-def test_product_recomputes_rows_and_columns_with_unnormalised_pairs(gpu):
+@pytest.mark.parametrize("size", [1280, 1024])
+def test_product_recomputes_rows_and_columns_with_unnormalised_pairs(gpu, size):
     """The product entry points take a row's (column's) balancing exponent from
     the leading words when both operands are sliced in two passes; a row or
     column holding a pair whose leading word is not RN(hi + lo) is recomputed
     from (hi, lo) ("Multiple Double Arithmetic on NVIDIA Tensor Cores", §3,
     balancing; Problems 3.3 and 3.4 for opposite signs and leading zeros).
-    1280^3 takes that path for both operands; pairs planted in some rows of A
-    and columns of B move the exact exponent up or down from the leading
-    words' one, or leave it.  The product equals the oracle's nearest chain bit
-    for bit on those rows and columns and on sampled others, and the stage
-    call's exponents equal the oracle's."""
+    1280^3 takes that path for both operands, 1024^3 for A beside a B
+    sliced in one pass.
+    Pairs planted in some rows of A and columns of B move the exact exponent
+    up or down from the leading words' one, or leave it.  The product equals
+    the oracle's nearest chain bit for bit on those rows and columns and on
+    sampled others, and the stage call's exponents equal the oracle's."""
     import torch
-    m = n = k = 1280
-    rng = np.random.default_rng(1280)
+    m = n = k = size
+    rng = np.random.default_rng(size)
     Ah, Al = _edge_matrix(rng, m, k)
     Bh, Bl = _edge_matrix(rng, k, n)
     # A rows: r0 exponent down (1 - 0.75 = 0.25 the largest), r1 a zero leading
     # word with a large trailing one (exponent up), r2 |lo| >> |hi| on a 16-row
     # block boundary, r3 an unnormalised pair that leaves the exponent
-    r0, r1, r2, r3 = 37, 600, 1023, 1279
+    r0, r1, r2, r3 = 37, 600, 1023, m - 1
     Ah[r0] *= 2.0 ** -8
     Al[r0] *= 2.0 ** -8
     Ah[r0, 5], Al[r0, 5] = 1.0, -0.75
@@ -881,14 +927,15 @@ def test_product_recomputes_rows_and_columns_with_unnormalised_pairs(gpu):
     Ah[r2, 0], Al[r2, 0] = 2.0 ** -30, 2.0 ** 20
     Ah[r3, 9], Al[r3, 9] = 2.0 ** -40, -2.0 ** -45
     # B columns the same way
-    c0, c1, c2, c3 = 16, 400, 1100, 1279
+    c0, c1, c2, c3 = 16, 400, n - 180, n - 1
     Bh[:, c0] *= 2.0 ** -8
     Bl[:, c0] *= 2.0 ** -8
     Bh[3, c0], Bl[3, c0] = -1.0, 0.75
-    Bh[1279, c1], Bl[1279, c1] = 0.0, -5.0
+    Bh[k - 1, c1], Bl[k - 1, c1] = 0.0, -5.0
     Bh[640, c2], Bl[640, c2] = -2.0 ** -30, 2.0 ** 25
     Bh[11, c3], Bl[11, c3] = 2.0 ** -40, 2.0 ** -46 * 3
-    assert Bh.nbytes + Bl.nbytes > 24 << 20  # B is sliced in two passes
+    # B sliced in two passes at 1280^3, in one pass at 1024^3
+    assert (Bh.nbytes + Bl.nbytes > 24 << 20) == (size == 1280)
     rows = np.union1d([r0, r1, r2, r3], _sample_indices(rng, m, 6))
     cols = np.union1d([c0, c1, c2, c3], _sample_indices(rng, n, 6))
     E_s, DA = exact.slice_rows(Ah, Al, rows)
