@@ -63,9 +63,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // ISSUE: where a stage's copy of a later stage is issued -- 0 after the first
 // k-block's fragment reads (halfway through a stage of two k-blocks), 1 right
 // after the stage's barrier, before any fragment read.
-template <int WM, int WN, int KS, int NBUF, int WGS, int NS, int RPW = 2, int ISSUE = 0>
+// DEFER (pair-packed schedule only): the last DEFER products of a stage's last
+// k-block are issued after the next stage's barrier, beside its first fragment
+// reads, so that the matrix pipe has work while those reads are in flight.
+template <int WM, int WN, int KS, int NBUF, int WGS, int NS, int RPW = 2, int ISSUE = 0, int DEFER = 0>
 struct GemmConfig {
     static constexpr int kIssueEarly = ISSUE;
+    static constexpr int kDefer = DEFER;
     static constexpr int kWaves = WM * WN;
     static constexpr int kRPW = RPW;                                 // 16-row blocks per wave
     static constexpr int kNBuf = NBUF;
@@ -286,6 +290,27 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t ti
         wait_vmcnt<0>();
     };
     int since_flush = 0;
+    // The products a stage's last k-block defers to the next stage (DEFER): their
+    // operands wait in dx, db, which hold zeros before the first stage and after
+    // a flush.  A product of zeros changes an accumulator at most from -0 to +0,
+    // and the pair-packed schedule reads its accumulators only as integers
+    // (pair_group_units), so the results are those of the undeferred order.
+    constexpr int kDefer = PAIRED ? C::kDefer : 0;
+    constexpr PairSchedule<NS> dsched{};
+    static_assert(kDefer >= 0 && kDefer <= dsched.count, "deferred products of one k-block");
+    constexpr int kDeferSlots = kDefer > 0 ? kDefer : 1;
+    double dx[kDeferSlots][RPW] = {}, db[kDeferSlots] = {};
+    auto run_deferred = [&]() {
+        if constexpr (kDefer > 0) {
+#pragma unroll
+            for (int d = 0; d < kDefer; ++d)
+#pragma unroll
+                for (int r = 0; r < RPW; ++r) {
+                    const PairProduct p = dsched.order[dsched.count - kDefer + d];
+                    acc[p.acc][r] = __builtin_amdgcn_mfma_f64_16x16x4f64(dx[d][r], db[d], acc[p.acc][r], 0, 0, 0);
+                }
+        }
+    };
     const int chunk_stages = static_cast<int>(pair.chunk_stages);
 
     if (s1 > s0) {
@@ -346,13 +371,21 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t ti
                         return a[2 * u][r];
                     };
                     constexpr PairSchedule<NS> sched{};
+                    // the previous stage's deferred products, beside this stage's
+                    // first fragment reads
+                    if (j == 0) run_deferred();
 #pragma unroll
                     for (int i = 0; i < sched.count; ++i)
 #pragma unroll
                         for (int r = 0; r < RPW; ++r) {
                             const PairProduct p = sched.order[i];
                             const double x = p.packed ? ap[p.u][r] : single(p.u, r);
-                            acc[p.acc][r] = __builtin_amdgcn_mfma_f64_16x16x4f64(x, b[p.t], acc[p.acc][r], 0, 0, 0);
+                            if (j == KS - 1 && i >= sched.count - kDefer) {
+                                dx[i - (sched.count - kDefer)][r] = x;
+                                db[i - (sched.count - kDefer)] = b[p.t];
+                            } else {
+                                acc[p.acc][r] = __builtin_amdgcn_mfma_f64_16x16x4f64(x, b[p.t], acc[p.acc][r], 0, 0, 0);
+                            }
                         }
                 } else {
                     // Triangular schedule: pair (s, t) feeds level s + t < NS.
@@ -368,11 +401,19 @@ sliced_gemm_kernel(int64_t m, int64_t n, int64_t KB, int64_t tiles_n, int64_t ti
             }
             if constexpr (PAIRED) {
                 if (chunk_stages > 0 && ++since_flush == chunk_stages && st + 1 < s1) {
+                    run_deferred();
+#pragma unroll
+                    for (int d = 0; d < kDeferSlots; ++d) {
+#pragma unroll
+                        for (int r = 0; r < RPW; ++r) dx[d][r] = 0.0;
+                        db[d] = 0.0;
+                    }
                     flush();
                     since_flush = 0;
                 }
             }
         }
+        run_deferred();  // the last stage's
         // No direct-to-LDS copy may still be in flight when the workgroup ends.
         wait_vmcnt<0>();
     }
@@ -515,10 +556,18 @@ template <> struct ConfigFor<16> { using type = GemmConfig<2, 4, 1, 2, 1, 16, 1>
 // Five slices take the same shape (4096^3: 17.63 against 18.12 ms for the
 // 32x16 strips of eight waves); for four, six and seven slices the strips stay
 // faster (11.40 / 22.91 / 30.22 against 12.73 / 23.08 / 30.37 ms), and from
-// nine slices on sixteen waves would spill.
+// nine slices on sixteen waves would spill.  With eight slices the last six
+// of a stage's 40 products wait for the next stage's barrier (DEFER; 122
+// VGPRs, four waves per SIMD still): GEMM 4096^3 37.33 -> 36.93-36.96 ms,
+// 65536x512x512 9.60 -> 9.48, 1024^3 0.601 -> 0.592 (two, eight, ten or
+// twelve deferred: less), every output unchanged.  Sixteen slices (the quad
+// double's 72 products, two waves per SIMD) defer eight: qd 2048^3 17.77 ->
+// 17.62 ms, the 16-slice double-double GEMM at 2048^3 17.35 -> 17.23 (four:
+// less, twelve: the same with more registers; 248 of 256 VGPRs).
 template <int NS> struct PairConfigFor { using type = typename ConfigFor<NS>::type; };
 template <> struct PairConfigFor<5> { using type = GemmConfig<4, 4, 2, 2, 1, 5, 1>; };
-template <> struct PairConfigFor<8> { using type = GemmConfig<4, 4, 2, 2, 1, 8, 1>; };
+template <> struct PairConfigFor<8> { using type = GemmConfig<4, 4, 2, 2, 1, 8, 1, 0, 6>; };
+template <> struct PairConfigFor<16> { using type = GemmConfig<2, 4, 1, 2, 1, 16, 1, 0, 8>; };
 
 template <int NS>
 hipError_t launch_gemm_ns(int64_t m, int64_t n, int64_t k, const double* A_slices, const double* B_slices,
