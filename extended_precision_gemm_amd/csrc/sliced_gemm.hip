@@ -531,19 +531,23 @@ template <> struct ConfigFor<4> { using type = GemmConfig<2, 4, 2, 2, 1, 4>; };
 template <> struct ConfigFor<5> { using type = GemmConfig<2, 4, 2, 2, 1, 5>; };
 // Six slices: one 16x16 block per wave (32x64 tile) measured faster than two
 // (73.2 vs 71.6 TFLOP/s at 4096^3; slower for 4, 5 and 7 slices).
-template <> struct ConfigFor<6> { using type = GemmConfig<2, 4, 2, 2, 1, 6, 1>; };
-template <> struct ConfigFor<7> { using type = GemmConfig<2, 4, 2, 2, 1, 7>; };
+// DEFER, for the pair-packed products of 6, 7, 9, 11, 12 and 13 slices: GEMM
+// at 4096^3 22.80 -> 22.50, 30.11 -> 29.91, 49.79 -> 47.86, 69.92 -> 67.98,
+// 79.59 -> 78.87, 93.43 -> 92.03 ms; with 4 or 5 slices (four waves per SIMD
+// no longer fit), 10, 14 and 15 it measured slower.
+template <> struct ConfigFor<6> { using type = GemmConfig<2, 4, 2, 2, 1, 6, 1, 0, 3>; };
+template <> struct ConfigFor<7> { using type = GemmConfig<2, 4, 2, 2, 1, 7, 2, 0, 4>; };
 template <> struct ConfigFor<8> { using type = GemmConfig<2, 4, 2, 2, 1, 8>; };
 // Nine to sixteen slices (wide double-double windows, the quad-double product):
 // up to 16 level accumulators of one 16x16 block per wave (at most 128
 // registers) and a 32x64 tile.  Two k-blocks per stage while two stages fit
 // the 160 KB of LDS (up to 13 slices: 78 KB a stage; measured at 4096^3 with
 // 9..13 slices: 69.5-72.8 -> 74.2-75.7 TFLOP/s), one from 14 slices on.
-template <> struct ConfigFor<9> { using type = GemmConfig<2, 4, 2, 2, 1, 9, 1>; };
+template <> struct ConfigFor<9> { using type = GemmConfig<2, 4, 2, 2, 1, 9, 1, 0, 6>; };
 template <> struct ConfigFor<10> { using type = GemmConfig<2, 4, 2, 2, 1, 10, 1>; };
-template <> struct ConfigFor<11> { using type = GemmConfig<2, 4, 2, 2, 1, 11, 1>; };
-template <> struct ConfigFor<12> { using type = GemmConfig<2, 4, 2, 2, 1, 12, 1>; };
-template <> struct ConfigFor<13> { using type = GemmConfig<2, 4, 2, 2, 1, 13, 1>; };
+template <> struct ConfigFor<11> { using type = GemmConfig<2, 4, 2, 2, 1, 11, 1, 0, 6>; };
+template <> struct ConfigFor<12> { using type = GemmConfig<2, 4, 2, 2, 1, 12, 1, 0, 6>; };
+template <> struct ConfigFor<13> { using type = GemmConfig<2, 4, 2, 2, 1, 13, 1, 0, 6>; };
 template <> struct ConfigFor<14> { using type = GemmConfig<2, 4, 1, 2, 1, 14, 1>; };
 template <> struct ConfigFor<15> { using type = GemmConfig<2, 4, 1, 2, 1, 15, 1>; };
 template <> struct ConfigFor<16> { using type = GemmConfig<2, 4, 1, 2, 1, 16, 1>; };
