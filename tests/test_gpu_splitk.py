@@ -95,6 +95,33 @@ def test_split_dd_product_equals_the_unsplit_chain(gpu, m, n, k, ns):
         assert _bits_equal(_host(Dh), Rh) and _bits_equal(_host(Dl), Rl)
 
 
+@pytest.mark.parametrize("m,n,k,ns", [(512, 512, 32768, 8), (512, 512, 20000, 16)])
+def test_split_parts_longer_than_an_exact_chunk(gpu, m, n, k, ns):
+    """k-parts longer than the exact FP64 range of the group sums (4096 values
+    of k with 8 slices, 2048 with 16): each part moves its group sums to int64
+    inside the part, after the products a stage defers past the next barrier.
+    The product equals the unsplit stage call's group sums rounded, bit for
+    bit, and the oracle's nearest chain on sampled rows and columns."""
+    chunk = {8: 4096, 16: 2048}[ns]
+    parts = gpu.split_parts(m, n, k, ns)
+    assert parts > 1 and k // parts > chunk
+    _say(f"[split-k dd] {m}x{n}x{k} nslices={ns} parts={parts}: {k // parts} values of k a part")
+    Ah, Al = workloads.random_dd((m, k), 9300 + ns, "signed_exp20")
+    Bh, Bl = workloads.random_dd((k, n), 9301 + ns, "uniform")
+    dAh, dAl, dBh, dBl = _dev(Ah), _dev(Al), _dev(Bh), _dev(Bl)
+    Ch, Cl = gpu.dd_gemm(dAh, dAl, dBh, dBl, nslices=ns)
+    hCh, hCl = _host(Ch), _host(Cl)
+    Uh, Ul = _unsplit_reference(gpu, dAh, dAl, dBh, dBl, ns)
+    assert _bits_equal(hCh, Uh) and _bits_equal(hCl, Ul)
+    rng = np.random.default_rng(ns)
+    rows = np.unique(np.concatenate([[0, m - 1], rng.integers(0, m, 5)]))
+    cols = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 5)]))
+    E_s, DA = exact.slice_rows(Ah, Al, rows, nslices=ns)
+    F_s, DB = exact.slice_cols(Bh, Bl, cols, nslices=ns)
+    Nh, Nl = exact.nearest_dd(exact.level_sums_units(DA, DB), E_s, F_s)
+    assert _bits_equal(hCh[np.ix_(rows, cols)], Nh) and _bits_equal(hCl[np.ix_(rows, cols)], Nl)
+
+
 def test_split_level_planes_of_the_stage_call(gpu):
     """dd_sliced_gemm splits into the caller's level planes (zeroed first, so
     stale contents do not leak), with a row stride wider than n."""
